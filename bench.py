@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of one GDN layer's speculative verify + commit step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic drafts for one GDN
+layer (h = 8, d_k = d_v = 256, FP32 state): verification (chain kernel for
+chain workloads, tree-masked factorized kernels otherwise) followed by the
+accepted-path commit from the factor record.  Steps rotate over enough
+distinct layer states (default 1 GiB in total, several times the 256 MB
+Infinity Cache) that every state read comes from HBM.
+
+Prints one JSON line:
+  value           verified draft nodes per second (B * N per step), measured on
+                  a HIP-graph replay of K steps (no host launch overhead)
+  roofline        dominant kernel: algorithmic bytes per launch / its average
+                  duration from HIP events around each launch, against 8 TB/s
+  cpu_baseline    the CPU oracle (per-path fp64 replay + commit replay) on a
+                  bounded number of steps of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from linear_attention_gdn_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def bytes_verify(d: W.Draft, tree: bool) -> int:
+    """Algorithmic HBM bytes of one verification launch (inputs read once,
+    outputs and factor record written once; no scratch)."""
+    es = 2 if d.dtype == "bf16" else 4
+    B, N, H, dk, dv = d.B, d.N, d.H, d.dk, d.dv
+    state = B * H * dv * dk * 4
+    qkv = B * N * H * (2 * dk + dv) * es
+    bg = B * N * H * 8
+    out = B * N * H * dv * 4
+    rec = B * H * N * (dv * 4 + 4 + dk * es) + B * N * 12
+    par = B * N * 4 if tree else 0
+    return state + qkv + bg + out + rec + par
+
+
+def bytes_commit(d: W.Draft, plens: np.ndarray) -> float:
+    """Algorithmic bytes of one commit: every sequence with a non-empty path
+    reads and writes its state once and reads its path's u', k and G."""
+    es = 2 if d.dtype == "bf16" else 4
+    B, N, H, dk, dv = d.B, d.N, d.H, d.dk, d.dv
+    tot = 0.0
+    for n in plens:
+        if n > 0:
+            tot += 2 * H * dv * dk * 4 + H * n * (dv * 4 + dk * es + 4) + N * 8
+    return tot + B * 4
+
+
+def draw_lasts(d: W.Draft, rng, count: int, chain: bool) -> np.ndarray:
+    out = np.empty((count, d.B), dtype=np.int32)
+    for i in range(count):
+        for b in range(d.B):
+            if chain:
+                out[i, b] = int(rng.integers(0, d.N + 1)) - 1
+            else:
+                mean = 3.0 if d.N <= 32 else 4.0
+                out[i, b] = W.accept_leaf_geometric(d.parents[b], rng, mean)
+    return out
+
+
+def path_lengths(d: W.Draft, lasts: np.ndarray) -> np.ndarray:
+    depth = np.stack([W.depths_of(d.parents[b]) for b in range(d.B)])
+    return np.array([[0 if l < 0 else depth[b, l] for b, l in enumerate(row)] for row in lasts])
+
+
+def cpu_baseline(d: W.Draft, lasts: np.ndarray, budget_s: float):
+    from oracle import oracle as O
+
+    threads = O.set_threads(0)
+    q, k, v = d.q64(), d.k64(), d.v64()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.tree_verify(d.S0, d.parents, q, k, v, d.beta, d.g, d.scale)
+        O.commit(d.S0, d.parents, k, v, d.beta, d.g, lasts[steps % len(lasts)])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": steps * d.B * d.N / el, "unit": "nodes/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} steps of {d.name} (verify by per-path fp64 replay + commit "
+                      f"replay) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="chain8-b1-h8-d256", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--rotate-mib", type=int, default=1024,
+                    help="total size of the rotating layer states")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the verify/commit path shards over "
+              "(sequence, head, state-row tile) units with no exchange, so there is no "
+              "multi-GPU step to time; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from linear_attention_gdn_amd import gdnspec as G
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    d = W.WORKLOADS[args.workload](0)
+    chain = args.workload.startswith("chain")
+    B, N, H, dk, dv = d.B, d.N, d.H, d.dk, d.dv
+    code = G.GDN_BF16 if d.dtype == "bf16" else G.GDN_F32
+
+    state_bytes = B * H * dv * dk * 4
+    R = max(1, (args.rotate_mib << 20) // state_bytes)
+    S0 = torch.from_numpy(d.S0).to(dev)
+    states = [S0.clone() for _ in range(R)]
+    bf = lambda x: torch.from_numpy(x.view(np.int16).copy()).to(dev).view(torch.bfloat16)
+    f = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+    q, k, v = bf(d.q), bf(d.k), bf(d.v)
+    beta, g = f(d.beta), f(d.g)
+    parents = torch.from_numpy(d.parents).to(dev)
+    out = torch.empty(B, N, H, dv, device=dev)
+    rec = G.FactorRecord.empty(B, N, H, dk, dv, code, device=dev)
+    rng = np.random.default_rng(1234)
+    total = args.warmup + args.steps
+    lasts_np = draw_lasts(d, rng, total, chain)
+    lasts = torch.from_numpy(lasts_np).to(dev)
+
+    def verify(i):
+        S = states[i % R]
+        if chain:
+            G.gdn_chain_verify(S, q, k, v, beta, g, out, rec)
+        else:
+            G.gdn_tree_verify(S, parents, q, k, v, beta, g, out, rec)
+
+    def commit(i):
+        G.gdn_commit_path(states[i % R], rec, lasts[i])
+
+    # warmup (eager)
+    for i in range(args.warmup):
+        verify(i)
+        commit(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    timed = range(args.warmup, total)
+    if args.no_graph:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in timed:
+            verify(i)
+            commit(i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    else:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in timed:
+                    verify(i)
+                    commit(i)
+        stream.wait_stream(s)
+        graph.replay()  # first replay uploads the graph; not timed
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = B * N / (elapsed / args.steps)
+
+    # per-kernel durations: event pairs around each launch on the stream the
+    # library launches on (torch's current stream)
+    nper = min(args.steps, 400)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * nper)]
+    for j in range(nper):
+        i = args.warmup + j
+        evs[4 * j].record(stream)
+        verify(i)
+        evs[4 * j + 1].record(stream)
+        evs[4 * j + 2].record(stream)
+        commit(i)
+        evs[4 * j + 3].record(stream)
+    torch.cuda.synchronize()
+    t_ver = np.array([evs[4 * j].elapsed_time(evs[4 * j + 1]) for j in range(nper)])
+    t_com = np.array([evs[4 * j + 2].elapsed_time(evs[4 * j + 3]) for j in range(nper)])
+    plens = path_lengths(d, lasts_np[args.warmup:args.warmup + nper])
+    b_ver = bytes_verify(d, not chain)
+    b_com = np.mean([bytes_commit(d, p) for p in plens])
+    kernels = {
+        "verify": {"name": "gdn_chain_verify" if chain else "gdn_tree_verify",
+                   "avg_us": float(t_ver.mean() * 1e3), "bytes": int(b_ver),
+                   "gbs": float(b_ver / (t_ver.mean() * 1e-3) / 1e9)},
+        "commit": {"name": "gdn_commit_path", "avg_us": float(t_com.mean() * 1e3),
+                   "bytes": float(b_com), "gbs": float(b_com / (t_com.mean() * 1e-3) / 1e9)},
+    }
+    if not chain:
+        flops = 4.0 * B * H * N * dk * dv
+        kernels["verify"]["fp32_equiv_tflops"] = float(flops / (t_ver.mean() * 1e-3) / 1e12)
+    dom = "verify" if t_ver.sum() >= t_com.sum() else "commit"
+    kd = kernels[dom]
+    roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": kd["name"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, lasts_np, args.cpu_seconds)
+
+    line = {
+        "metric": "verified draft nodes/sec per GDN layer (h=8,d=256)",
+        "value": round(value, 1),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": d.name, "B": B, "N": N, "H": H, "dk": dk, "dv": dv,
+                   "qkv_dtype": d.dtype, "state_dtype": "f32", "rotating_states": R,
+                   "timing": "eager" if args.no_graph else "hip_graph",
+                   "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+// extern "C" entry points of libgdnspec: argument validation, error text and
+// dispatch to the gfx950 kernels.  Every check here runs on the host before
+// anything is enqueued; nothing is allocated.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "gdn_common.h"
+
+namespace gdn {
+hipError_t launch_chain_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
+                               const void* q, const void* k, const void* v, const float* beta,
+                               const float* g, float scale, float* out, void* factors,
+                               hipStream_t stream);
+hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
+                              const int32_t* parents, const void* q, const void* k,
+                              const void* v, const float* beta, const float* g, float scale,
+                              float* out, void* factors, void* workspace, uint64_t* mask_out,
+                              int32_t* dev_status, hipStream_t stream);
+hipError_t launch_commit(int B, int N, int H, int dk, int dv, int dtype, float* S,
+                         const void* factors, const int32_t* last, int32_t* path_out,
+                         int32_t* path_len, int32_t* dev_status, hipStream_t stream);
+}  // namespace gdn
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return status;
+}
+
+int ok() {
+  g_error.clear();
+  return GDN_OK;
+}
+
+bool sizes_ok(int B, int N, int H, int dk, int dv) {
+  return B >= 0 && N >= 0 && N <= gdn::kMaxNodes && H >= 1 && dk >= 8 && dk <= gdn::kMaxDim &&
+         dk % 8 == 0 && dv >= 4 && dv <= gdn::kMaxDim && dv % 4 == 0 &&
+         (long long)B * H * N * gdn::kMaxDim < (1ll << 40);
+}
+
+int check_sizes(const char* fn, int B, int N, int H, int dk, int dv) {
+  if (!sizes_ok(B, N, H, dk, dv))
+    return fail(GDN_ERR_SHAPE,
+                "%s: unsupported sizes B=%d N=%d H=%d dk=%d dv=%d (need B>=0, 0<=N<=64, H>=1, "
+                "8<=dk<=256 with dk%%8==0, 4<=dv<=256 with dv%%4==0)",
+                fn, B, N, H, dk, dv);
+  return GDN_OK;
+}
+
+int check_dtype(const char* fn, int dtype) {
+  if (dtype != GDN_BF16 && dtype != GDN_F32)
+    return fail(GDN_ERR_ARG, "%s: qkv_dtype %d is neither GDN_BF16 (0) nor GDN_F32 (1)", fn,
+                dtype);
+  return GDN_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, bool required) {
+  if (!p) {
+    if (required) return fail(GDN_ERR_ARG, "%s: %s is NULL", fn, name);
+    return GDN_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(GDN_ERR_ARG, "%s: %s is not 16-byte aligned", fn, name);
+  return GDN_OK;
+}
+
+int check_ptr4(const char* fn, const char* name, const void* p, bool required) {
+  if (!p) {
+    if (required) return fail(GDN_ERR_ARG, "%s: %s is NULL", fn, name);
+    return GDN_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
+    return fail(GDN_ERR_ARG, "%s: %s is not 4-byte aligned", fn, name);
+  return GDN_OK;
+}
+
+int hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess)
+    return fail(GDN_ERR_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+#define GDN_TRY(expr)          \
+  do {                         \
+    const int _rc = (expr);    \
+    if (_rc != GDN_OK) return _rc; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return (0 << 16) | 1; }
+
+const char* gdn_last_error(void) { return g_error.c_str(); }
+
+size_t gdn_factor_bytes(int B, int N, int H, int dk, int dv, int qkv_dtype) {
+  if (!sizes_ok(B, N, H, dk, dv) || (qkv_dtype != GDN_BF16 && qkv_dtype != GDN_F32)) return 0;
+  return gdn::record_layout(B, N, H, dk, dv, qkv_dtype).total;
+}
+
+int gdn_factor_layout(int B, int N, int H, int dk, int dv, int qkv_dtype, size_t offsets[5]) {
+  GDN_TRY(check_sizes("gdn_factor_layout", B, N, H, dk, dv));
+  GDN_TRY(check_dtype("gdn_factor_layout", qkv_dtype));
+  if (!offsets) return fail(GDN_ERR_ARG, "gdn_factor_layout: offsets is NULL");
+  const gdn::RecordLayout L = gdn::record_layout(B, N, H, dk, dv, qkv_dtype);
+  for (int i = 0; i < 5; ++i) offsets[i] = L.off[i];
+  return ok();
+}
+
+size_t gdn_workspace_bytes(int B, int N, int H, int dk, int dv) {
+  (void)B; (void)N; (void)H; (void)dk; (void)dv;
+  return 0;  // the fused tree kernel keeps all per-head factors in LDS
+}
+
+int gdn_tree_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const float* S0,
+                    const int32_t* parents, const void* q, const void* k, const void* v,
+                    const float* beta, const float* g, float scale, float* out, void* factors,
+                    void* workspace, uint64_t* mask_out, int32_t* dev_status, void* stream) {
+  const char* fn = "gdn_tree_verify";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (!std::isfinite(scale)) return fail(GDN_ERR_ARG, "%s: scale is not finite", fn);
+  if (B == 0 || N == 0) return ok();
+  GDN_TRY(check_ptr(fn, "S0", S0, true));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr(fn, "out", out, true));
+  GDN_TRY(check_ptr(fn, "factors", factors, true));
+  GDN_TRY(check_ptr(fn, "workspace", workspace, false));
+  GDN_TRY(check_ptr(fn, "mask_out", mask_out, false));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  return hip_status(fn, gdn::launch_tree_verify(B, N, H, dk, dv, qkv_dtype, S0, parents, q, k,
+                                                v, beta, g, scale, out, factors, workspace,
+                                                mask_out, dev_status,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int gdn_chain_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const float* S0,
+                     const void* q, const void* k, const void* v, const float* beta,
+                     const float* g, float scale, float* out, void* factors, void* stream) {
+  const char* fn = "gdn_chain_verify";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (!std::isfinite(scale)) return fail(GDN_ERR_ARG, "%s: scale is not finite", fn);
+  if (B == 0 || N == 0) return ok();
+  GDN_TRY(check_ptr(fn, "S0", S0, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr(fn, "out", out, true));
+  GDN_TRY(check_ptr(fn, "factors", factors, true));
+  return hip_status(fn, gdn::launch_chain_verify(B, N, H, dk, dv, qkv_dtype, S0, q, k, v, beta,
+                                                 g, scale, out, factors,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int gdn_commit_path(int B, int N, int H, int dk, int dv, int qkv_dtype, float* S,
+                    const void* factors, const int32_t* last_accepted, int32_t* path_out,
+                    int32_t* path_len_out, int32_t* dev_status, void* stream) {
+  const char* fn = "gdn_commit_path";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (B == 0) return ok();
+  GDN_TRY(check_ptr4(fn, "last_accepted", last_accepted, true));
+  GDN_TRY(check_ptr4(fn, "path_len_out", path_len_out, false));
+  GDN_TRY(check_ptr4(fn, "path_out", path_out, false));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  if (N == 0) return ok();  // only last_accepted = -1 is possible: nothing to apply
+  GDN_TRY(check_ptr(fn, "S", S, true));
+  GDN_TRY(check_ptr(fn, "factors", factors, true));
+  return hip_status(fn, gdn::launch_commit(B, N, H, dk, dv, qkv_dtype, S, factors,
+                                           last_accepted, path_out, path_len_out, dev_status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

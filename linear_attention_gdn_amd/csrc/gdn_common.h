@@ -1,0 +1,178 @@
+// Shared host/device definitions for libgdnspec (gfx950 / CDNA4).
+//
+// Factor-record layout, bf16 helpers and the MFMA fragment
+// conventions used by the verification and commit kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdnspec.h"
+
+namespace gdn {
+
+constexpr int kMaxNodes = 64;  // one wave64 lane / one uint64 mask bit per node
+constexpr int kMaxDim = 256;
+constexpr size_t kAlign = 256;
+
+__host__ __device__ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline size_t elem_bytes(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+// Factor record: [u' f32 B*H*N*dv | G f32 B*H*N | K B*H*N*dk | parents i32 B*N | mask u64 B*N]
+struct RecordLayout {
+  size_t off[5];
+  size_t total;
+};
+
+inline RecordLayout record_layout(int B, int N, int H, int dk, int dv, int dtype) {
+  RecordLayout L;
+  const size_t bhn = (size_t)B * H * N;
+  size_t o = 0;
+  L.off[0] = o;
+  o = align_up(o + bhn * dv * 4);
+  L.off[1] = o;
+  o = align_up(o + bhn * 4);
+  L.off[2] = o;
+  o = align_up(o + bhn * dk * elem_bytes(dtype));
+  L.off[3] = o;
+  o = align_up(o + (size_t)B * N * 4);
+  L.off[4] = o;
+  o = align_up(o + (size_t)B * N * 8);
+  L.total = o;
+  return L;
+}
+
+// Device views of a factor record.
+template <typename KT>
+struct Record {
+  float* up;         // [B][H][N][dv]
+  float* G;          // [B][H][N]
+  KT* K;             // [B][H][N][dk]
+  int32_t* parents;  // [B][N]
+  uint64_t* mask;    // [B][N]
+};
+
+template <typename KT>
+inline Record<KT> record_views(void* base, const RecordLayout& L) {
+  char* p = static_cast<char*>(base);
+  Record<KT> r;
+  r.up = reinterpret_cast<float*>(p + L.off[0]);
+  r.G = reinterpret_cast<float*>(p + L.off[1]);
+  r.K = reinterpret_cast<KT*>(p + L.off[2]);
+  r.parents = reinterpret_cast<int32_t*>(p + L.off[3]);
+  r.mask = reinterpret_cast<uint64_t*>(p + L.off[4]);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// element types
+// ---------------------------------------------------------------------------
+
+typedef uint16_t bf16_t;  // bfloat16 storage bits
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+__device__ inline float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Load 4 consecutive elements as float.
+__device__ inline f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ inline f32x4 load4(const bf16_t* p) {
+  u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  f32x4 r;
+  r.x = __uint_as_float(w.x << 16);
+  r.y = __uint_as_float(w.x & 0xffff0000u);
+  r.z = __uint_as_float(w.y << 16);
+  r.w = __uint_as_float(w.y & 0xffff0000u);
+  return r;
+}
+
+// Raw 4-element vectors: kept as loaded (bf16 bits or FP32) so that the load
+// is not consumed (and waited for) before it is needed; widen4 converts.
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<float> {
+  using type = f32x4;
+};
+template <>
+struct Raw4<bf16_t> {
+  using type = u32x2;
+};
+template <typename T>
+__device__ inline typename Raw4<T>::type raw4(const T* p) {
+  return *reinterpret_cast<const typename Raw4<T>::type*>(p);
+}
+__device__ inline f32x4 widen4(const f32x4& x) { return x; }
+__device__ inline f32x4 widen4(const u32x2& w) {
+  f32x4 r;
+  r.x = __uint_as_float(w.x << 16);
+  r.y = __uint_as_float(w.x & 0xffff0000u);
+  r.z = __uint_as_float(w.y << 16);
+  r.w = __uint_as_float(w.y & 0xffff0000u);
+  return r;
+}
+__device__ inline float widen1(float x) { return x; }
+__device__ inline float widen1(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Split 8 floats into bf16 hi + lo with x = hi + lo + r, |r| <= 2^-16 |x|
+// (both roundings to nearest even; x - hi is exact in fp32).
+__device__ inline void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+  float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h = (__bf16)x[e];
+    hi[e] = h;
+    lo[e] = (__bf16)(x[e] - (float)h);
+  }
+}
+
+// Loads are issued unconditionally from a clamped (always valid) address and
+// masked afterwards: a load under a branch makes the compiler wait for it
+// before the branch joins, which serialises memory round trips.
+__device__ inline int clampi(int x, int hi) { return x < hi ? x : hi; }
+__device__ inline f32x4 mask4(const f32x4& x, bool ok) {
+  return ok ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// 8 bf16 values already in bf16: reinterpret a 16-byte load.
+__device__ inline bf16x8 load_bf16x8(const bf16_t* p) {
+  u32x4 w = *reinterpret_cast<const u32x4*>(p);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ inline bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+// Sum over each row of 16 lanes with DPP (VALU-speed cross-lane moves inside
+// a row): rotate-by-8 and rotate-by-4 fold the row to four partial sums,
+// two quad permutations finish it.  Every lane of the row ends with the sum.
+template <int CTRL>
+__device__ inline float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float row16_sum(float x) {
+  x += dpp_f32<0x128>(x);  // row_ror:8
+  x += dpp_f32<0x124>(x);  // row_ror:4
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  return x;
+}
+
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
+// Fragment convention (lane l of a wave64):
+//   A: row i = l % 16, k = 8 * (l / 16) + e, e = 0..7
+//   B: col j = l % 16, k = 8 * (l / 16) + e
+//   D: row i = 4 * (l / 16) + r, col j = l % 16, r = 0..3
+__device__ inline f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace gdn

@@ -1,0 +1,548 @@
+// Tree-masked factorized verification (gfx950).
+//
+// SpecLA review, "Core claim" and "What carries the argument" (paper
+// Section 4.2): the draft-tree topology is inserted into the delta-rule UT
+// factorization as a mask, so every node's output comes from the committed
+// state S0 in one pass while updates flow only along ancestor paths.  With
+// M the ancestor mask, G_t the path-cumulative log decay, and the pages'
+// garbled symbols read as
+//     A[t,j]    = beta_t e^{G_t - G_j} (k_t . k_j)      j strict ancestor of t
+//     T         = (I + A)^{-1}                          (the "solve_tril" step)
+//     Attn[t,j] = e^{G_t - G_j} (q_t . k_j)             j ancestor-or-self of t
+// the outputs are
+//     U' = T (diag(beta) V - diag(beta e^G) K S0^T)     (factor record)
+//     O  = scale (diag(e^G) Q S0^T + Attn U')
+// i.e. O = bQ S0^T - Attn (W S0^T) + Attn U with W = T diag(beta e^G) K,
+// U = T diag(beta) V, bQ = diag(e^G) Q.  Reassociating
+// W S0^T = T diag(beta e^G) (K S0^T) keeps the large contraction on the raw
+// bf16 keys instead of an FP32 matrix W.
+//
+// One kernel, one workgroup (4 waves) per (sequence, head, tile of BV state
+// rows).  Each workgroup:
+//   0. issues one round of loads: Q and K of its head first (staged in LDS as
+//      bf16, rows padded against bank conflicts), then parents / g / beta,
+//      then its S0 tile (straight into MFMA B-fragment registers) and V tile,
+//      so the per-head work below overlaps the state tile's arrival;
+//   1. validates the parents and builds ancestor bitmasks and the
+//      path-cumulative G by pointer jumping (one lane per node);
+//   2. forms the Gram blocks Q K^T and K K^T on bf16 MFMA (lower triangle);
+//   3. solves row t of T on t's root path only (rows of T vanish off the
+//      path): one lane per node, the path held in registers; Attn is masked
+//      in place;
+//   4. runs the dense contraction Y = [Q; K] S0_tile^T on bf16 MFMA with the
+//      FP32 state split into bf16 hi + lo (bf16 q, k make every product
+//      exact; only the 2^-16 split residue is lost);
+//   5. forms R = beta (V - e^G Y_k) from the accumulators, then U' = T R and
+//      O = scale e^G Y_q + Attn U' as two dense MFMA products whose FP32
+//      operands are split into bf16 hi + lo (three passes: hi*hi, hi*lo,
+//      lo*hi).  Masked-out entries are exact zeros, so non-ancestors never
+//      contribute.
+// The per-head steps 1-3 are repeated by each of the head's tiles; they run
+// while the state tile is still in flight.
+#include <type_traits>
+
+#include "gdn_common.h"
+
+namespace gdn {
+
+__device__ inline void copy4e(float* d, const float* s) {
+  *reinterpret_cast<f32x4*>(d) = *reinterpret_cast<const f32x4*>(s);
+}
+
+// 8-element k-slice of a global row as MFMA operand(s): FP32 input is split
+// into bf16 hi + lo (used only on the FP32-input path).
+__device__ inline void frag_global(const float* p, bool ok, bf16x8& hi, bf16x8& lo) {
+  f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+    a = load4(p);
+    b = load4(p + 4);
+  }
+  split8(a, b, hi, lo);
+}
+
+// 8 consecutive FP32 values from LDS, split into bf16 hi + lo fragments.
+__device__ inline void frag_lds_split(const float* p, bf16x8& hi, bf16x8& lo) {
+  split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), hi, lo);
+}
+
+constexpr int kLd = kMaxNodes + 4;        // row stride of N x N float matrices (16B rows)
+constexpr int kQKRows = 2 * kMaxNodes;    // Q rows then K rows
+constexpr int kQKStride = kMaxDim + 8;    // bf16 elements per staged row
+constexpr int kQKBytes = kQKRows * kQKStride * 2;
+constexpr int kPathMax = 16;              // register-resident path solve up to this depth
+
+template <int BV>
+struct TreeLds {
+  static constexpr int kBVT = ((BV + 15) / 16) * 16;               // padded tile width
+  static constexpr int kMat = kMaxNodes * kLd * 4;                  // one N x N (float)
+  static constexpr int kRT = kBVT * kLd * 4;                        // R^T or U'^T
+  static constexpr int kRegionA = kQKBytes > 2 * kRT ? kQKBytes : 2 * kRT;  // Q/K, then R^T, U'^T
+  static constexpr int kOffKK = kRegionA;
+  static constexpr int kOffQK = kOffKK + kMat;  // Q K^T, then Attn in place
+  static constexpr int kOffT = kOffQK + kMat;
+  static constexpr int kBytes = kOffT + kMat;
+};
+
+// Row t of T on t's root path p_0..p_{d-1} = t, for d <= kPathMax:
+//   x_{d-1} = 1,  x_b = -sum_{a > b} x_a beta_{p_a} (prod_{i=b+1..a} alpha_{p_i}) (k_{p_a} . k_{p_b})
+// solves x^T (I + A)|_path = e_t^T (the decay e^{G_{p_a} - G_{p_b}} is the
+// product of the path's alphas, each <= 1).  Writes T[t][p_b] = x_b.
+__device__ inline void path_solve_registers(int t, uint64_t m, int d, const float* KK,
+                                            const float* salpha, const float* sbeta,
+                                            float* Trow) {
+  int p[kPathMax];
+  float al[kPathMax], be[kPathMax];
+  uint64_t mm = m;
+#pragma unroll
+  for (int a = 0; a < kPathMax; ++a) {
+    p[a] = mm ? __builtin_ctzll(mm) : t;
+    mm &= mm - 1ull;
+  }
+#pragma unroll
+  for (int a = 0; a < kPathMax; ++a) {
+    al[a] = salpha[p[a]];
+    be[a] = sbeta[p[a]];
+  }
+  float x[kPathMax];
+#pragma unroll
+  for (int a = 0; a < kPathMax; ++a) x[a] = (a == d - 1) ? 1.f : 0.f;
+#pragma unroll
+  for (int b = kPathMax - 2; b >= 0; --b) {
+    if (b < d - 1) {
+      float acc = 0.f;
+      float dec = 1.f;  // prod_{i=b+1..a} alpha_{p_i}
+#pragma unroll
+      for (int a = b + 1; a < kPathMax; ++a) {
+        dec *= al[a];
+        if (a < d) acc = fmaf(x[a] * be[a] * dec, KK[p[a] * kLd + p[b]], acc);
+      }
+      x[b] = -acc;
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < kPathMax; ++a)
+    if (a < d) Trow[p[a]] = x[a];
+}
+
+// The same for any depth, reading and writing the row in LDS (slower).
+__device__ inline void path_solve_lds(int t, uint64_t m, const float* KK, const float* sG,
+                                      const float* sbeta, float* Trow) {
+  Trow[t] = 1.f;
+  for (uint64_t rest = m & ~(1ull << t); rest;) {
+    const int j = 63 - __builtin_clzll(rest);
+    rest &= ~(1ull << j);
+    const float Gj = sG[j];
+    float acc = 0.f;
+    for (uint64_t above = m & ~((2ull << j) - 1ull); above; above &= above - 1ull) {
+      const int i = __builtin_ctzll(above);
+      acc = fmaf(Trow[i] * sbeta[i] * __expf(sG[i] - Gj), KK[i * kLd + j], acc);
+    }
+    Trow[j] = -acc;
+  }
+}
+
+template <typename T, int BV>
+__global__ __launch_bounds__(256) void tree_verify_kernel(
+    int N, int H, int dk, int dv, int ntiles, const float* __restrict__ S0,
+    const int32_t* __restrict__ parents, const T* __restrict__ q, const T* __restrict__ k,
+    const T* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ g,
+    float scale, float* __restrict__ out, Record<T> rec, uint64_t* __restrict__ mask_out,
+    int32_t* __restrict__ dev_status) {
+  using L = TreeLds<BV>;
+  constexpr bool kStaged = std::is_same<T, bf16_t>::value;  // Q/K staged in LDS as bf16
+  constexpr int NCT = (BV + 15) / 16;                        // MFMA column tiles
+  constexpr int WC = NCT < 4 ? NCT : 4;                      // waves along columns
+  constexpr int WR = 4 / WC;                                 // waves along rows
+  constexpr int MAXRT = (2 * kMaxNodes / 16 + WR - 1) / WR;  // Y row tiles per wave
+  constexpr int MAXNB = (kMaxNodes / 16 + WR - 1) / WR;      // node blocks per wave
+
+  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
+  __shared__ uint64_t smask[kMaxNodes];
+  __shared__ float sG[kMaxNodes], seG[kMaxNodes], sbeta[kMaxNodes], salpha[kMaxNodes];
+  __shared__ int sbad;
+  bf16_t* QKs = reinterpret_cast<bf16_t*>(smem);
+  float* RT = reinterpret_cast<float*>(smem);               // [kBVT][kLd]: R^T
+  float* UT = reinterpret_cast<float*>(smem + L::kRT);      // [kBVT][kLd]: U'^T
+  float* KK = reinterpret_cast<float*>(smem + L::kOffKK);
+  float* QK = reinterpret_cast<float*>(smem + L::kOffQK);   // then Attn
+  float* Tl = reinterpret_cast<float*>(smem + L::kOffT);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int koff = 8 * lg;
+  const int tile = blockIdx.x % ntiles;
+  const int bh = blockIdx.x / ntiles;
+  const int b = bh / H;
+  const int h = bh % H;
+  const int r0 = tile * BV;
+  const int Np = (N + 15) & ~15;
+  const int NQT = Np / 16;        // node blocks (row tiles of Q, and of K)
+  const int NK = (Np + 31) & ~31; // k extent of the N x N products
+  const int nrt = 2 * NQT;
+  const int nks = (dk + 31) / 32;
+  const int cj = wave % WC;       // this wave's column tile
+  const int rb = wave / WC;       // first row tile / node block of this wave
+  const int ccol = 16 * cj + l16; // column within the tile (B fragments, D columns)
+  const int srow = r0 + ccol;     // state row of this lane's column
+  const bool sok = ccol < BV && srow < dv;
+
+  // ---- 0. one round of loads, Q/K first (unconditional, clamped, masked).
+  // Consuming a load waits for every load issued before it, so the state
+  // tile is issued after what the per-head steps need.
+  constexpr int QKB = (kQKRows * kMaxDim / 8) / 256;  // 16-byte chunks per thread
+  const int qk_cpr = 4 * nks;                         // chunks per staged row
+  const int qk_total = 2 * Np * qk_cpr;
+  u32x4 qkw[kStaged ? QKB : 1];
+  if (kStaged) {
+    const bf16_t* qb = reinterpret_cast<const bf16_t*>(static_cast<const void*>(q));
+    const bf16_t* kb = reinterpret_cast<const bf16_t*>(static_cast<const void*>(k));
+#pragma unroll
+    for (int x = 0; x < QKB; ++x) {
+      const int idx = clampi(tid + 256 * x, qk_total - 1);
+      const int r = idx / qk_cpr;
+      const bool isq = r < Np;
+      const int t = clampi(isq ? r : r - Np, N - 1);
+      const int c8 = clampi(8 * (idx % qk_cpr), dk - 8);
+      qkw[x] = *reinterpret_cast<const u32x4*>((isq ? qb : kb) +
+                                               (((size_t)b * N + t) * H + h) * dk + c8);
+    }
+  }
+  const int tn = clampi(lane, N - 1);
+  const int pl = parents[(size_t)b * N + tn];
+  const float gl = g[((size_t)b * N + tn) * H + h];
+  const float bl = beta[((size_t)b * N + tn) * H + h];
+  const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
+  f32x4 Sraw[kMaxDim / 32][2];
+#pragma unroll
+  for (int ks = 0; ks < kMaxDim / 32; ++ks) {
+    const int kk = clampi(32 * ks + koff, dk - 8);
+    Sraw[ks][0] = load4(sptr + kk);
+    Sraw[ks][1] = load4(sptr + kk + 4);
+  }
+  // V for the K row tiles this wave turns into R: its j-th K tile is row tile
+  // rt = rb + WR*(iK0 + j) >= NQT, node block rt - NQT (D layout: node
+  // 16*nb + 4*lg + r, column ccol).
+  const int iK0 = NQT > rb ? (NQT - rb + WR - 1) / WR : 0;
+  T vreg[MAXNB][4];
+#pragma unroll
+  for (int j = 0; j < MAXNB; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int nb = rb + WR * (iK0 + j) - NQT;
+      const int t = clampi(16 * nb + 4 * lg + r, N - 1);
+      vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
+    }
+
+  if (kStaged) {
+#pragma unroll
+    for (int x = 0; x < QKB; ++x) {
+      const int idx = tid + 256 * x;
+      if (idx < qk_total) {
+        const int r = idx / qk_cpr;
+        const int t = r < Np ? r : r - Np;
+        const int c8 = 8 * (idx % qk_cpr);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
+      }
+    }
+  }
+  for (int idx = tid; idx < kMaxNodes * kLd; idx += 256) Tl[idx] = 0.f;
+
+  // ---- 1. parents -> validation, ancestor-or-self masks and G (pointer jumping)
+  if (wave == 0) {
+    const int t = lane;
+    const int p = t < N ? pl : -1;
+    const bool bad = t < N && (p < -1 || p >= t);
+    const uint64_t anybad = __ballot(bad);
+    uint64_t m = t < N ? (1ull << t) : 0ull;
+    float G = t < N ? gl : 0.f;
+    int a = (t < N && !bad) ? p : -1;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {  // 2^6 = 64 >= path length
+      const int src = a >= 0 ? a : t;
+      const uint64_t ma = __shfl(m, src);
+      const float Ga = __shfl(G, src);
+      const int aa = __shfl(a, src);
+      if (a >= 0) {
+        m |= ma;
+        G += Ga;
+        a = aa;
+      }
+    }
+    if (anybad) m = 0ull;
+    smask[t] = m;
+    sG[t] = G;
+    seG[t] = expf(G);
+    salpha[t] = t < N ? expf(gl) : 0.f;
+    sbeta[t] = t < N ? bl : 0.f;
+    if (t == 0) sbad = anybad != 0ull;
+    if (tile == 0 && t < N) {
+      rec.G[(size_t)bh * N + t] = anybad ? 0.f : G;
+      if (h == 0) {
+        rec.parents[(size_t)b * N + t] = pl;
+        rec.mask[(size_t)b * N + t] = m;
+        if (mask_out) mask_out[(size_t)b * N + t] = m;
+      }
+    }
+    if (tile == 0 && t == 0 && h == 0 && dev_status)
+      dev_status[b] = anybad ? GDN_ERR_TOPOLOGY : GDN_OK;
+  }
+  __syncthreads();
+
+  const bool bad = sbad != 0;
+  if (tile == 0) {  // factor record: copy of k for this head
+    const int cpr = dk / 4;
+    for (int idx = tid; idx < N * cpr; idx += 256) {
+      const int t = idx / cpr;
+      const int cc = 4 * (idx % cpr);
+      T* dst = rec.K + ((size_t)bh * N + t) * dk + cc;
+      if (kStaged)  // the staged K rows in LDS hold exactly these bits
+        *reinterpret_cast<u32x2*>(dst) =
+            *reinterpret_cast<const u32x2*>(QKs + (Np + t) * kQKStride + cc);
+      else
+        copy4e(reinterpret_cast<float*>(dst),
+               reinterpret_cast<const float*>(k) + (((size_t)b * N + t) * H + h) * dk + cc);
+    }
+  }
+  if (bad) {  // uniform: zero this tile's outputs
+    const int c = tid % BV;
+    for (int t = tid / BV; t < N; t += 256 / BV)
+      if (r0 + c < dv) {
+        out[(((size_t)b * N + t) * H + h) * dv + r0 + c] = 0.f;
+        rec.up[((size_t)bh * N + t) * dv + r0 + c] = 0.f;
+      }
+    return;
+  }
+
+  // ---- 2. Gram blocks C = [Q; K] K^T on MFMA (tiles with j <= t only)
+  for (int tileid = wave; tileid < nrt * NQT; tileid += 4) {
+    const int rt = tileid / NQT;
+    const int ct = tileid % NQT;
+    const bool isq = rt < NQT;
+    const int rtl = isq ? rt : rt - NQT;
+    if (ct > rtl) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (kStaged) {
+      const bf16_t* arow = QKs + (16 * rt + l16) * kQKStride + koff;
+      const bf16_t* brow = QKs + (Np + 16 * ct + l16) * kQKStride + koff;
+      for (int ks = 0; ks < nks; ++ks) {
+        const bf16x8 a8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * ks));
+        const bf16x8 b8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(brow + 32 * ks));
+        acc = mfma16x16x32(a8, b8, acc);
+      }
+    } else {
+      const int ti = 16 * rtl + l16;
+      const int tj = 16 * ct + l16;
+      const float* arow = reinterpret_cast<const float*>(isq ? (const void*)q : (const void*)k) +
+                          (((size_t)b * N + (ti < N ? ti : 0)) * H + h) * dk;
+      const float* brow = reinterpret_cast<const float*>(k) +
+                          (((size_t)b * N + (tj < N ? tj : 0)) * H + h) * dk;
+      for (int ks = 0; ks < nks; ++ks) {
+        const int kk = 32 * ks + koff;
+        bf16x8 ah, al, bh8, bl8;
+        frag_global(arow + kk, ti < N && kk < dk, ah, al);
+        frag_global(brow + kk, tj < N && kk < dk, bh8, bl8);
+        acc = mfma16x16x32(ah, bh8, acc);
+        acc = mfma16x16x32(ah, bl8, acc);
+        acc = mfma16x16x32(al, bh8, acc);
+      }
+    }
+    float* dst = isq ? QK : KK;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(16 * rtl + 4 * lg + r) * kLd + 16 * ct + l16] = acc[r];
+  }
+  __syncthreads();
+
+  // ---- 3. rows of T on root paths; Attn masked to ancestors-or-self in place
+  if (tid < Np) {
+    const int t = tid;
+    const uint64_t m = t < N ? smask[t] : 0ull;
+    const int d = __popcll(m);
+    if (t < N) {
+      if (d <= kPathMax)
+        path_solve_registers(t, m, d, KK, salpha, sbeta, Tl + t * kLd);
+      else
+        path_solve_lds(t, m, KK, sG, sbeta, Tl + t * kLd);
+    }
+    const float Gt = sG[t];
+    float* At = QK + t * kLd;
+    for (int j = 0; j < NK; ++j)
+      At[j] = ((m >> j) & 1ull) ? scale * expf(Gt - sG[j]) * At[j] : 0.f;
+  }
+
+  // ---- 4. Y = [Q; K] S0_tile^T (this wave: column tile cj, row tiles rb + WR*i)
+  f32x4 yacc[MAXRT];
+#pragma unroll
+  for (int i = 0; i < MAXRT; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < kMaxDim / 32; ++ks) {
+    if (ks < nks) {
+      bf16x8 bhi, blo;
+      const bool okk = sok && 32 * ks + koff < dk;
+      split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi, blo);
+#pragma unroll
+      for (int i = 0; i < MAXRT; ++i) {
+        const int rt = rb + WR * i;
+        if (rt < nrt) {
+          if (kStaged) {
+            const bf16x8 a8 = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(QKs + (16 * rt + l16) * kQKStride + 32 * ks + koff));
+            yacc[i] = mfma16x16x32(a8, bhi, yacc[i]);
+            yacc[i] = mfma16x16x32(a8, blo, yacc[i]);
+          } else {
+            const bool isq = rt < NQT;
+            const int t = 16 * (isq ? rt : rt - NQT) + l16;
+            const float* arow = reinterpret_cast<const float*>(isq ? (const void*)q : (const void*)k) +
+                                (((size_t)b * N + (t < N ? t : 0)) * H + h) * dk;
+            const int kk = 32 * ks + koff;
+            bf16x8 ah, al;
+            frag_global(arow + kk, t < N && kk < dk, ah, al);
+            yacc[i] = mfma16x16x32(ah, bhi, yacc[i]);
+            yacc[i] = mfma16x16x32(ah, blo, yacc[i]);
+            yacc[i] = mfma16x16x32(al, bhi, yacc[i]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();  // Q/K reads, solves and Attn done: region A becomes R^T, U'^T
+
+  // ---- 5. epilogue
+  // zero the k-padding columns [Np, NK) of R^T and U'^T (read by the products)
+  for (int idx = tid; idx < L::kBVT * (NK - Np); idx += 256) {
+    const int off = (idx / (NK - Np)) * kLd + Np + idx % (NK - Np);
+    RT[off] = 0.f;
+    UT[off] = 0.f;
+  }
+  // R = diag(beta) (V - diag(e^G) K S0^T) from the K-row accumulators, stored transposed
+#pragma unroll
+  for (int i = 0; i < MAXRT; ++i) {
+    const int rt = rb + WR * i;
+    if (rt >= NQT && rt < nrt) {
+      const int nb = rt - NQT;
+      const int j = i - iK0;  // this wave's j-th K tile: see the vreg loads
+      f32x4 rv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * nb + 4 * lg + r;
+        float vv = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < MAXNB; ++jj)
+          if (jj == j) vv = widen1(vreg[jj][r]);
+        rv[r] = sbeta[t] * ((sok ? vv : 0.f) - seG[t] * yacc[i][r]);
+      }
+      *reinterpret_cast<f32x4*>(RT + ccol * kLd + 16 * nb + 4 * lg) = rv;
+    }
+  }
+  __syncthreads();
+  // U' = T R  (A = T rows, B = R^T rows, split hi/lo, three passes)
+#pragma unroll
+  for (int j = 0; j < MAXNB; ++j) {
+    const int nb = rb + WR * j;
+    if (nb < NQT) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < NK / 32; ++ks) {
+        bf16x8 ah, al, bh8, bl8;
+        frag_lds_split(Tl + (16 * nb + l16) * kLd + 32 * ks + koff, ah, al);
+        frag_lds_split(RT + ccol * kLd + 32 * ks + koff, bh8, bl8);
+        acc = mfma16x16x32(ah, bh8, acc);
+        acc = mfma16x16x32(ah, bl8, acc);
+        acc = mfma16x16x32(al, bh8, acc);
+      }
+      *reinterpret_cast<f32x4*>(UT + ccol * kLd + 16 * nb + 4 * lg) = acc;
+      if (sok) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * nb + 4 * lg + r;
+          if (t < N) rec.up[((size_t)bh * N + t) * dv + srow] = acc[r];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // O = scale e^G Y_q + Attn U'   (Attn carries the scale).  Node block nb of
+  // this wave is Q row tile rt = nb = rb + WR*j, whose Y accumulator is yacc[j].
+#pragma unroll
+  for (int j = 0; j < MAXNB; ++j) {
+    const int nb = rb + WR * j;
+    if (nb < NQT) {
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = scale * seG[16 * nb + 4 * lg + r] * yacc[j][r];
+      for (int ks = 0; ks < NK / 32; ++ks) {
+        bf16x8 ah, al, bh8, bl8;
+        frag_lds_split(QK + (16 * nb + l16) * kLd + 32 * ks + koff, ah, al);
+        frag_lds_split(UT + ccol * kLd + 32 * ks + koff, bh8, bl8);
+        acc = mfma16x16x32(ah, bh8, acc);
+        acc = mfma16x16x32(ah, bl8, acc);
+        acc = mfma16x16x32(al, bh8, acc);
+      }
+      if (sok) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * nb + 4 * lg + r;
+          if (t < N) out[(((size_t)b * N + t) * H + h) * dv + srow] = acc[r];
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int BV>
+hipError_t launch_bv(int B, int N, int H, int dk, int dv, const float* S0, const int32_t* parents,
+                     const T* q, const T* k, const T* v, const float* beta, const float* g,
+                     float scale, float* out, const Record<T>& rec, uint64_t* mask_out,
+                     int32_t* dev_status, hipStream_t stream) {
+  const int ntiles = (dv + BV - 1) / BV;
+  const long grid = (long)B * H * ntiles;
+  hipLaunchKernelGGL((tree_verify_kernel<T, BV>), dim3((unsigned)grid), dim3(256), 0, stream, N,
+                     H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out, rec, mask_out,
+                     dev_status);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_tree_verify_t(int B, int N, int H, int dk, int dv, const float* S0,
+                                const int32_t* parents, const T* q, const T* k, const T* v,
+                                const float* beta, const float* g, float scale, float* out,
+                                void* factors, uint64_t* mask_out, int32_t* dev_status,
+                                hipStream_t stream, int dtype) {
+  const RecordLayout L = record_layout(B, N, H, dk, dv, dtype);
+  Record<T> rec = record_views<T>(factors, L);
+  // Tile width: the widest of 64/32/16/8 state rows that still gives one
+  // workgroup per compute unit (256), else the narrowest.
+  const long heads = (long)B * H;
+  if (heads * ((dv + 63) / 64) >= 256)
+    return launch_bv<T, 64>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, stream);
+  if (heads * ((dv + 31) / 32) >= 256)
+    return launch_bv<T, 32>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, stream);
+  if (heads * ((dv + 15) / 16) >= 256)
+    return launch_bv<T, 16>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, stream);
+  return launch_bv<T, 8>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                         mask_out, dev_status, stream);
+}
+
+hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
+                              const int32_t* parents, const void* q, const void* k,
+                              const void* v, const float* beta, const float* g, float scale,
+                              float* out, void* factors, void* workspace, uint64_t* mask_out,
+                              int32_t* dev_status, hipStream_t stream) {
+  (void)workspace;
+  if (dtype == GDN_BF16)
+    return launch_tree_verify_t<bf16_t>(
+        B, N, H, dk, dv, S0, parents, static_cast<const bf16_t*>(q),
+        static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), beta, g, scale, out,
+        factors, mask_out, dev_status, stream, dtype);
+  return launch_tree_verify_t<float>(B, N, H, dk, dv, S0, parents, static_cast<const float*>(q),
+                                     static_cast<const float*>(k), static_cast<const float*>(v),
+                                     beta, g, scale, out, factors, mask_out, dev_status, stream,
+                                     dtype);
+}
+
+}  // namespace gdn

@@ -1,0 +1,255 @@
+"""ctypes binding of libgdnspec (``include/gdnspec.h``), with the same names.
+
+Argument marshalling only: every step of verification and commit runs in the
+HIP kernels of ``libgdnspec.so``.  PyTorch supplies device memory and the
+current HIP stream.  There is no fallback: if the library is missing the
+calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdnspec.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "gdnspec.h")
+
+GDN_OK = 0
+GDN_ERR_ARG = -1
+GDN_ERR_SHAPE = -2
+GDN_ERR_TOPOLOGY = -3
+GDN_ERR_UNSUPPORTED = -4
+GDN_ERR_HIP = -5
+GDN_BF16 = 0
+GDN_F32 = 1
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdnspec.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m linear_attention_gdn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        I, P, F, S = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+        L.gdn_version.argtypes = []
+        L.gdn_version.restype = I
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_factor_bytes.argtypes = [I, I, I, I, I, I]
+        L.gdn_factor_bytes.restype = S
+        L.gdn_factor_layout.argtypes = [I, I, I, I, I, I, ctypes.POINTER(S)]
+        L.gdn_factor_layout.restype = I
+        L.gdn_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.gdn_workspace_bytes.restype = S
+        L.gdn_tree_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, P, P, P, P]
+        L.gdn_tree_verify.restype = I
+        L.gdn_chain_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P]
+        L.gdn_chain_verify.restype = I
+        L.gdn_commit_path.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
+        L.gdn_commit_path.restype = I
+        _lib = L
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions ``include/gdnspec.h`` declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+def gdn_version() -> int:
+    return int(lib().gdn_version())
+
+
+def gdn_last_error() -> str:
+    return lib().gdn_last_error().decode()
+
+
+def _raise_on(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, gdn_last_error())
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return GDN_BF16
+    if t == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t}")
+
+
+def torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == GDN_BF16 else torch.float32
+
+
+def gdn_factor_bytes(B, N, H, dk, dv, qkv_dtype) -> int:
+    return int(lib().gdn_factor_bytes(B, N, H, dk, dv, qkv_dtype))
+
+
+def gdn_factor_layout(B, N, H, dk, dv, qkv_dtype) -> tuple:
+    off = (ctypes.c_size_t * 5)()
+    _raise_on(lib().gdn_factor_layout(B, N, H, dk, dv, qkv_dtype, off))
+    return tuple(int(x) for x in off)
+
+
+def gdn_workspace_bytes(B, N, H, dk, dv) -> int:
+    return int(lib().gdn_workspace_bytes(B, N, H, dk, dv))
+
+
+@dataclass
+class FactorRecord:
+    """Device buffer holding one verification's factor record, plus its sizes."""
+
+    buf: torch.Tensor  # uint8, gdn_factor_bytes(...)
+    B: int
+    N: int
+    H: int
+    dk: int
+    dv: int
+    qkv_dtype: int
+
+    @classmethod
+    def empty(cls, B, N, H, dk, dv, qkv_dtype, device="cuda") -> "FactorRecord":
+        n = gdn_factor_bytes(B, N, H, dk, dv, qkv_dtype)
+        if n == 0:
+            raise GdnError(GDN_ERR_SHAPE, f"unsupported sizes B={B} N={N} H={H} dk={dk} dv={dv}")
+        return cls(torch.empty(n, dtype=torch.uint8, device=device), B, N, H, dk, dv, qkv_dtype)
+
+    def _section(self, i, dtype, shape):
+        off = gdn_factor_layout(self.B, self.N, self.H, self.dk, self.dv, self.qkv_dtype)[i]
+        count = 1
+        for s in shape:
+            count *= s
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return self.buf[off:off + nbytes].view(dtype).view(shape)
+
+    @property
+    def uprime(self):
+        return self._section(0, torch.float32, (self.B, self.H, self.N, self.dv))
+
+    @property
+    def G(self):
+        return self._section(1, torch.float32, (self.B, self.H, self.N))
+
+    @property
+    def K(self):
+        return self._section(2, torch_dtype(self.qkv_dtype), (self.B, self.H, self.N, self.dk))
+
+    @property
+    def parents(self):
+        return self._section(3, torch.int32, (self.B, self.N))
+
+    @property
+    def mask(self):
+        return self._section(4, torch.int64, (self.B, self.N))
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(name, t, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_draft(S0, q, k, v, beta, g):
+    if S0.dim() != 4:
+        raise ValueError("S0 must be [B][H][dv][dk]")
+    B, H, dv, dk = S0.shape
+    if q.dim() != 4:
+        raise ValueError("q must be [B][N][H][dk]")
+    N = q.shape[1]
+    dt = q.dtype
+    _need("S0", S0, (B, H, dv, dk), torch.float32)
+    _need("q", q, (B, N, H, dk), dt)
+    _need("k", k, (B, N, H, dk), dt)
+    _need("v", v, (B, N, H, dv), dt)
+    _need("beta", beta, (B, N, H), torch.float32)
+    _need("g", g, (B, N, H), torch.float32)
+    return B, N, H, dk, dv, dtype_code(dt)
+
+
+def _check_record(rec: FactorRecord, B, N, H, dk, dv, code):
+    if (rec.B, rec.N, rec.H, rec.dk, rec.dv, rec.qkv_dtype) != (B, N, H, dk, dv, code):
+        raise ValueError("factor record sizes do not match the call")
+
+
+def gdn_tree_verify(S0, parents, q, k, v, beta, g, out, factors: FactorRecord,
+                    workspace: Optional[torch.Tensor] = None, scale: float = 1.0,
+                    mask_out=None, dev_status=None, stream=None) -> None:
+    """Tree-masked factorized verification; see ``gdn_tree_verify`` in gdnspec.h."""
+    B, N, H, dk, dv, code = _check_draft(S0, q, k, v, beta, g)
+    _need("parents", parents, (B, N), torch.int32)
+    _need("out", out, (B, N, H, dv), torch.float32)
+    _check_record(factors, B, N, H, dk, dv, code)
+    need = gdn_workspace_bytes(B, N, H, dk, dv)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        raise ValueError("workspace is smaller than gdn_workspace_bytes()")
+    if mask_out is not None:
+        _need("mask_out", mask_out, (B, N), torch.int64)
+    if dev_status is not None:
+        _need("dev_status", dev_status, (B,), torch.int32)
+    _raise_on(lib().gdn_tree_verify(B, N, H, dk, dv, code, _p(S0), _p(parents), _p(q), _p(k),
+                                    _p(v), _p(beta), _p(g), float(scale), _p(out),
+                                    _p(factors.buf), _p(workspace), _p(mask_out),
+                                    _p(dev_status), _stream(stream)))
+
+
+def gdn_chain_verify(S0, q, k, v, beta, g, out, factors: FactorRecord, scale: float = 1.0,
+                     stream=None) -> None:
+    """Serial V-tiled chain verification; see ``gdn_chain_verify`` in gdnspec.h."""
+    B, N, H, dk, dv, code = _check_draft(S0, q, k, v, beta, g)
+    _need("out", out, (B, N, H, dv), torch.float32)
+    _check_record(factors, B, N, H, dk, dv, code)
+    _raise_on(lib().gdn_chain_verify(B, N, H, dk, dv, code, _p(S0), _p(q), _p(k), _p(v),
+                                     _p(beta), _p(g), float(scale), _p(out), _p(factors.buf),
+                                     _stream(stream)))
+
+
+def gdn_commit_path(S, factors: FactorRecord, last_accepted, path_out=None, path_len_out=None,
+                    dev_status=None, stream=None) -> None:
+    """Apply the accepted path's buffered factors to S in place; see gdnspec.h."""
+    B, N, H, dk, dv = factors.B, factors.N, factors.H, factors.dk, factors.dv
+    _need("S", S, (B, H, dv, dk), torch.float32)
+    _need("last_accepted", last_accepted, (B,), torch.int32)
+    if path_out is not None:
+        _need("path_out", path_out, (B, N), torch.int32)
+    if path_len_out is not None:
+        _need("path_len_out", path_len_out, (B,), torch.int32)
+    if dev_status is not None:
+        _need("dev_status", dev_status, (B,), torch.int32)
+    _raise_on(lib().gdn_commit_path(B, N, H, dk, dv, factors.qkv_dtype, _p(S), _p(factors.buf),
+                                    _p(last_accepted), _p(path_out), _p(path_len_out),
+                                    _p(dev_status), _stream(stream)))

@@ -1,0 +1,98 @@
+"""Host-side checks of libgdnspec: it loads, exports what gdnspec.h declares,
+computes layouts, and rejects bad arguments before touching the GPU."""
+
+import ctypes
+
+import pytest
+
+from linear_attention_gdn_amd import gdnspec as G
+
+
+def test_library_exports_every_declared_function():
+    names = G.declared_functions()
+    assert {"gdn_tree_verify", "gdn_chain_verify", "gdn_commit_path", "gdn_factor_bytes",
+            "gdn_factor_layout", "gdn_workspace_bytes", "gdn_last_error",
+            "gdn_version"} <= set(names)
+    L = G.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert G.gdn_version() >= 1
+
+
+def test_factor_layout_sections():
+    B, N, H, dk, dv = 8, 64, 8, 256, 256
+    for code, esize in ((G.GDN_BF16, 2), (G.GDN_F32, 4)):
+        off = G.gdn_factor_layout(B, N, H, dk, dv, code)
+        sizes = [B * H * N * dv * 4, B * H * N * 4, B * H * N * dk * esize, B * N * 4, B * N * 8]
+        assert off[0] == 0
+        for i in range(5):
+            assert off[i] % 256 == 0
+            end = off[i] + sizes[i]
+            nxt = off[i + 1] if i < 4 else G.gdn_factor_bytes(B, N, H, dk, dv, code)
+            assert end <= nxt < end + 256
+    assert G.gdn_workspace_bytes(B, N, H, dk, dv) == 0  # no scratch in this version
+
+
+@pytest.mark.parametrize("sizes", [(1, 65, 8, 256, 256), (1, 8, 8, 12, 256), (1, 8, 8, 256, 6),
+                                   (1, 8, 0, 256, 256), (-1, 8, 8, 256, 256),
+                                   (1, 8, 8, 264, 256), (1, 8, 8, 256, 260)])
+def test_bad_sizes_rejected(sizes):
+    assert G.gdn_factor_bytes(*sizes, G.GDN_BF16) == 0
+    P = ctypes.c_void_p(4096)
+    rc = G.lib().gdn_tree_verify(*sizes, G.GDN_BF16, P, P, P, P, P, P, P, 1.0, P, P, P, None,
+                                 None, None)
+    assert rc == G.GDN_ERR_SHAPE
+    assert "unsupported sizes" in G.gdn_last_error()
+    rc = G.lib().gdn_chain_verify(*sizes, G.GDN_BF16, P, P, P, P, P, P, 1.0, P, P, None)
+    assert rc == G.GDN_ERR_SHAPE
+    rc = G.lib().gdn_commit_path(*sizes, G.GDN_BF16, P, P, P, None, None, None, None)
+    assert rc == G.GDN_ERR_SHAPE
+
+
+def test_bad_pointers_and_dtype_rejected():
+    L = G.lib()
+    P = ctypes.c_void_p(4096)
+    odd = ctypes.c_void_p(4096 + 8)
+    sz = (1, 8, 8, 256, 256)
+    assert L.gdn_tree_verify(*sz, 7, P, P, P, P, P, P, P, 1.0, P, P, P, None, None,
+                             None) == G.GDN_ERR_ARG
+    assert "qkv_dtype" in G.gdn_last_error()
+    assert L.gdn_tree_verify(*sz, 0, None, P, P, P, P, P, P, 1.0, P, P, P, None, None,
+                             None) == G.GDN_ERR_ARG
+    assert "S0 is NULL" in G.gdn_last_error()
+    assert L.gdn_tree_verify(*sz, 0, odd, P, P, P, P, P, P, 1.0, P, P, P, None, None,
+                             None) == G.GDN_ERR_ARG
+    assert "aligned" in G.gdn_last_error()
+    assert L.gdn_tree_verify(*sz, 0, P, P, P, P, P, P, P, float("nan"), P, P, P, None, None,
+                             None) == G.GDN_ERR_ARG
+    assert L.gdn_chain_verify(*sz, 0, P, P, P, P, P, P, 1.0, P, None, None) == G.GDN_ERR_ARG
+    assert "factors is NULL" in G.gdn_last_error()
+    assert L.gdn_commit_path(*sz, 0, P, P, None, None, None, None, None) == G.GDN_ERR_ARG
+    assert "last_accepted is NULL" in G.gdn_last_error()
+
+
+def test_empty_problems_are_noops():
+    L = G.lib()
+    assert L.gdn_tree_verify(0, 8, 8, 256, 256, 0, None, None, None, None, None, None, None,
+                             1.0, None, None, None, None, None, None) == G.GDN_OK
+    assert L.gdn_chain_verify(1, 0, 8, 256, 256, 0, None, None, None, None, None, None, 1.0,
+                              None, None, None) == G.GDN_OK
+    assert L.gdn_commit_path(0, 8, 8, 256, 256, 0, None, None, None, None, None, None,
+                             None) == G.GDN_OK
+    assert G.gdn_last_error() == ""
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    S0 = torch.zeros(1, 1, 16, 16)
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        G.gdn_chain_verify(S0, q, q, q, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1),
+                           torch.zeros(1, 4, 1, 16), None)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(G, "_lib", None)
+    monkeypatch.setattr(G, "LIB_PATH", "/nonexistent/libgdnspec.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        G.lib()
