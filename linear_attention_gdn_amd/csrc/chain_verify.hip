@@ -7,114 +7,115 @@
 // independently under the recurrence, so each workgroup owns a tile of rows
 // for the whole chain and never writes S0 back.
 //
-// One wave64 per workgroup.  16 lanes cover one state row (lane s holds
-// columns 64*m + 4*s + e, m < dk/64, e < 4, so each 16-lane group reads
-// 256 contiguous bytes per load and dot products reduce across 16 lanes);
-// four rows are in flight per wave and RPL row groups per lane.  Everything
-// the serial loop needs (k, q as FP32, v for the tile's rows, beta, alpha) is
-// staged in LDS with one round of loads that overlaps the state-tile load,
-// so the N serial steps touch only registers and LDS.
+// Per step t and state row r (alpha_t = e^{g_t}):
+//     y_k = S_r . k_t,  y_q = S_r . q_t,  u'_t[r] = beta_t (v_t[r] - alpha_t y_k)
+//     o_t[r] = scale (alpha_t y_q + (k_t . q_t) u'_t[r])
+//     S_r <- alpha_t S_r + u'_t[r] k_t
+//
+// Mapping: 256 threads = 4 waves; each half-wave (32 lanes) owns one state row
+// and lane s of it holds columns 128*m + 4*s + e (m < dk/128, e < 4), so a row
+// is read as 512-byte coalesced runs and dot products reduce over 32 lanes
+// with DPP row rotations plus one v_permlane16_swap.  A workgroup owns 8 rows,
+// one per SIMD pair of half-waves, so all four SIMDs of a CU run the serial
+// loop.  Everything the loop needs (k, q as loaded, v of the 8 rows, alpha,
+// beta) is staged in LDS by one round of loads that overlaps the state-tile
+// load; the loop then touches only registers and LDS, reading the next
+// step's k and q while the current step computes.
 #include "gdn_common.h"
 
 namespace gdn {
 
-template <typename T, int RPL>
-__global__ __launch_bounds__(64) void chain_verify_kernel(
+constexpr int kChainRows = 8;  // state rows per workgroup (one per half-wave)
+
+template <typename T>
+__global__ __launch_bounds__(256) void chain_verify_kernel(
     int N, int H, int dk, int dv, int ntiles, const float* __restrict__ S0,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ g, float scale,
     float* __restrict__ out, Record<T> rec) {
-  constexpr int MC = kMaxDim / 64;
-  constexpr int ROWS = 4 * RPL;
-  // dynamic LDS: k, q as loaded [N][dk], v [N][ROWS], alpha, beta, g [N]
+  constexpr int MC = kMaxDim / 128;  // float4 chunks per lane
   using R4 = typename Raw4<T>::type;
+  // dynamic LDS: k, q as loaded [N][dk], v [N][8], alpha, beta, g [N]
   extern __shared__ f32x4 lds4[];
   const int cpr = dk / 4;
   R4* sk = reinterpret_cast<R4*>(lds4);
   R4* sq = sk + N * cpr;
   float* sv = reinterpret_cast<float*>(sq + N * cpr);
-  float* salpha = sv + N * ROWS;
+  float* salpha = sv + N * kChainRows;
   float* sbeta = salpha + N;
   float* sG = sbeta + N;
 
-  const int lane = threadIdx.x;
-  const int rw = lane >> 4;
-  const int s = lane & 15;
+  const int tid = threadIdx.x;
+  const int s = tid & 31;             // lane within the row's half-wave
+  const int rl = tid >> 5;            // row within the tile (0..7)
   const int tile = blockIdx.x % ntiles;
   const int bh = blockIdx.x / ntiles;
   const int h = bh % H;
   const int b = bh / H;
-  const int r0 = tile * ROWS;
+  const int r0 = tile * kChainRows;
+  const int row = r0 + rl;
+  const bool rok = row < dv;
 
-  // ---- every global load first (unconditional, clamped), then the LDS writes:
-  // a consumer of any load waits for all loads issued before it.
-  constexpr int BATCH = 8;
-  constexpr int VB = kMaxNodes * ROWS / 64;
-  const size_t nhl = ((size_t)b * N + clampi(lane, N - 1)) * H + h;
+  // ---- every global load first (unconditional, clamped), then the LDS writes
+  const size_t nhl = ((size_t)b * N + clampi(tid, N - 1)) * H + h;
   const float gl = g[nhl];
   const float bl = beta[nhl];
+  constexpr int VB = kMaxNodes * kChainRows / 256;  // v values per thread, at most
   T vb[VB];
 #pragma unroll
   for (int x = 0; x < VB; ++x) {
-    const int idx = clampi(lane + 64 * x, N * ROWS - 1);
-    const int r = clampi(r0 + idx % ROWS, dv - 1);
-    vb[x] = v[(((size_t)b * N + idx / ROWS) * H + h) * dv + r];
+    const int idx = clampi(tid + 256 * x, N * kChainRows - 1);
+    const int r = clampi(r0 + idx % kChainRows, dv - 1);
+    vb[x] = v[(((size_t)b * N + idx / kChainRows) * H + h) * dv + r];
   }
-  int row[RPL];
-  bool rok[RPL];
-  f32x4 Sx[RPL][MC];
+  f32x4 Sx[MC];
+  {
+    const float* rp = S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk;
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) {
-    row[i] = r0 + 4 * i + rw;
-    rok[i] = row[i] < dv;
-    const float* rp = S0 + ((size_t)bh * dv + clampi(row[i], dv - 1)) * dk;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) Sx[i][m] = load4(rp + clampi(64 * m + 4 * s, dk - 4));
+    for (int m = 0; m < MC; ++m) Sx[m] = load4(rp + clampi(128 * m + 4 * s, dk - 4));
   }
-  // k and q rows: the first batch is straight-line code (a loop here would make
-  // the compiler drain every outstanding load at its header); larger drafts
-  // continue in a loop.
+  // k and q rows: the first batch is straight-line code (a loop here would
+  // drain every outstanding load at its header); larger drafts loop.
+  constexpr int BATCH = 4;
   auto stage = [&](int base) {
     R4 kb[BATCH], qb[BATCH];
 #pragma unroll
     for (int x = 0; x < BATCH; ++x) {
-      const int idx = clampi(base + 64 * x, N * cpr - 1);
+      const int idx = clampi(base + 256 * x, N * cpr - 1);
       const size_t off = (((size_t)b * N + idx / cpr) * H + h) * dk + 4 * (idx % cpr);
       kb[x] = raw4(k + off);
       qb[x] = raw4(q + off);
     }
 #pragma unroll
     for (int x = 0; x < BATCH; ++x) {
-      const int idx = base + 64 * x;
+      const int idx = base + 256 * x;
       if (idx < N * cpr) {
         sk[idx] = kb[x];
         sq[idx] = qb[x];
       }
     }
   };
-  stage(lane);
-  for (int base = lane + 64 * BATCH; base < N * cpr; base += 64 * BATCH) stage(base);
+  stage(tid);
+  for (int base = tid + 256 * BATCH; base < N * cpr; base += 256 * BATCH) stage(base);
 #pragma unroll
   for (int x = 0; x < VB; ++x) {
-    const int idx = lane + 64 * x;
-    if (idx < N * ROWS) sv[idx] = (r0 + idx % ROWS < dv) ? widen1(vb[x]) : 0.f;
+    const int idx = tid + 256 * x;
+    if (idx < N * kChainRows) sv[idx] = (r0 + idx % kChainRows < dv) ? widen1(vb[x]) : 0.f;
   }
-  if (lane < N) {
-    salpha[lane] = expf(gl);
-    sbeta[lane] = bl;
-    sG[lane] = gl;
+  if (tid < N) {
+    salpha[tid] = expf(gl);
+    sbeta[tid] = bl;
+    sG[tid] = gl;
   }
-  float S[RPL][MC][4];
+  float S[MC][4];
 #pragma unroll
-  for (int i = 0; i < RPL; ++i)
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      const f32x4 x = mask4(Sx[i][m], rok[i] && 64 * m + 4 * s < dk);
-      S[i][m][0] = x.x;
-      S[i][m][1] = x.y;
-      S[i][m][2] = x.z;
-      S[i][m][3] = x.w;
-    }
+  for (int m = 0; m < MC; ++m) {
+    const f32x4 x = mask4(Sx[m], rok && 128 * m + 4 * s < dk);
+    S[m][0] = x.x;
+    S[m][1] = x.y;
+    S[m][2] = x.z;
+    S[m][3] = x.w;
+  }
   __syncthreads();
 
   // k_t, q_t (widened) for step t; the next step's are read from LDS while
@@ -122,8 +123,8 @@ __global__ __launch_bounds__(64) void chain_verify_kernel(
   auto fetch = [&](int t, float (&kf)[MC][4], float (&qf)[MC][4]) {
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
-      const int cidx = t * cpr + clampi(16 * m + s, cpr - 1);
-      const bool okc = 64 * m + 4 * s < dk;
+      const int cidx = t * cpr + clampi(32 * m + s, cpr - 1);
+      const bool okc = 128 * m + 4 * s < dk;
       const f32x4 kx = mask4(widen4(sk[cidx]), okc);
       const f32x4 qx = mask4(widen4(sq[cidx]), okc);
       kf[m][0] = kx.x; kf[m][1] = kx.y; kf[m][2] = kx.z; kf[m][3] = kx.w;
@@ -132,49 +133,40 @@ __global__ __launch_bounds__(64) void chain_verify_kernel(
   };
   float kf[MC][4], qf[MC][4];
   fetch(0, kf, qf);
+  const size_t obase = (size_t)b * N * H * dv + (size_t)h * dv + row;
+  const size_t ubase = (size_t)bh * N * dv + row;
   for (int t = 0; t < N; ++t) {
     float kn[MC][4], qn[MC][4];
     fetch(clampi(t + 1, N - 1), kn, qn);
     const float be = sbeta[t];
     const float al = salpha[t];
-    float vt[RPL];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) vt[i] = sv[t * ROWS + 4 * i + rw];
+    const float vt = sv[t * kChainRows + rl];
 
-    // partial dot products, two accumulators per value for a shorter chain:
-    // red[0] = k.q, red[1+2i] = S_i.k, red[2+2i] = S_i.q
-    float red[1 + 2 * RPL], red2[1 + 2 * RPL];
-#pragma unroll
-    for (int x = 0; x < 1 + 2 * RPL; ++x) red[x] = red2[x] = 0.f;
+    float kq = 0.f, yk = 0.f, yq = 0.f, kq2 = 0.f, yk2 = 0.f, yq2 = 0.f;
 #pragma unroll
     for (int m = 0; m < MC; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float* r = (e & 1) ? red2 : red;
-        r[0] = fmaf(kf[m][e], qf[m][e], r[0]);
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-          r[1 + 2 * i] = fmaf(S[i][m][e], kf[m][e], r[1 + 2 * i]);
-          r[2 + 2 * i] = fmaf(S[i][m][e], qf[m][e], r[2 + 2 * i]);
-        }
+      for (int e = 0; e < 4; e += 2) {
+        kq = fmaf(kf[m][e], qf[m][e], kq);
+        yk = fmaf(S[m][e], kf[m][e], yk);
+        yq = fmaf(S[m][e], qf[m][e], yq);
+        kq2 = fmaf(kf[m][e + 1], qf[m][e + 1], kq2);
+        yk2 = fmaf(S[m][e + 1], kf[m][e + 1], yk2);
+        yq2 = fmaf(S[m][e + 1], qf[m][e + 1], yq2);
       }
-#pragma unroll
-    for (int x = 0; x < 1 + 2 * RPL; ++x) red[x] = row16_sum(red[x] + red2[x]);
-    const float kq = red[0];
+    kq = half32_sum(kq + kq2);
+    yk = half32_sum(yk + yk2);
+    yq = half32_sum(yq + yq2);
 
+    const float u = be * (vt - al * yk);
+    const float o = scale * fmaf(kq, u, al * yq);
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      const float u = be * (vt[i] - al * red[1 + 2 * i]);
-      const float o = scale * fmaf(kq, u, al * red[2 + 2 * i]);
+    for (int m = 0; m < MC; ++m)
 #pragma unroll
-      for (int m = 0; m < MC; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) S[i][m][e] = fmaf(u, kf[m][e], al * S[i][m][e]);
-      if (s == 0 && rok[i]) {
-        const size_t nh = ((size_t)b * N + t) * H + h;
-        out[nh * dv + row[i]] = o;
-        rec.up[((size_t)bh * N + t) * dv + row[i]] = u;
-      }
+      for (int e = 0; e < 4; ++e) S[m][e] = fmaf(u, kf[m][e], al * S[m][e]);
+    if (s == 0 && rok) {
+      out[obase + (size_t)t * H * dv] = o;
+      rec.up[ubase + (size_t)t * dv] = u;
     }
 #pragma unroll
     for (int m = 0; m < MC; ++m)
@@ -187,18 +179,18 @@ __global__ __launch_bounds__(64) void chain_verify_kernel(
 
   // factor record: G (chain prefix sums), k copy, parents, masks
   if (tile == 0) {
-    if (lane == 0) {
+    if (tid == 0) {
       float G = 0.f;
       for (int t = 0; t < N; ++t) {
         G += sG[t];
         rec.G[(size_t)bh * N + t] = G;
       }
     }
-    for (int idx = lane; idx < N * cpr; idx += 64)  // from the staged rows in LDS
+    for (int idx = tid; idx < N * cpr; idx += 256)  // from the staged rows in LDS
       *reinterpret_cast<R4*>(rec.K + ((size_t)bh * N + idx / cpr) * dk + 4 * (idx % cpr)) = sk[idx];
-    if (h == 0 && lane < N) {
-      rec.parents[(size_t)b * N + lane] = lane - 1;
-      rec.mask[(size_t)b * N + lane] = lane >= 63 ? ~0ull : ((1ull << (lane + 1)) - 1ull);
+    if (h == 0 && tid < N) {
+      rec.parents[(size_t)b * N + tid] = tid - 1;
+      rec.mask[(size_t)b * N + tid] = tid >= 63 ? ~0ull : ((1ull << (tid + 1)) - 1ull);
     }
   }
 }
@@ -209,15 +201,13 @@ hipError_t launch_chain_verify_t(int B, int N, int H, int dk, int dv, const floa
                                  const float* beta, const float* g, float scale, float* out,
                                  void* factors, const RecordLayout& L, hipStream_t stream) {
   Record<T> rec = record_views<T>(factors, L);
-  constexpr int RPL = 2;
-  const int rows = 4 * RPL;
-  const int ntiles = (dv + rows - 1) / rows;
+  const int ntiles = (dv + kChainRows - 1) / kChainRows;
   const long grid = (long)B * H * ntiles;
-  const size_t lds = (size_t)N * dk * sizeof(T) * 2 + (size_t)N * rows * 4 + (size_t)N * 4 * 3;
-  hipLaunchKernelGGL((chain_verify_kernel<T, RPL>), dim3((unsigned)grid), dim3(64), lds, stream,
-                     N, H, dk, dv, ntiles, S0, static_cast<const T*>(q),
-                     static_cast<const T*>(k), static_cast<const T*>(v), beta, g, scale, out,
-                     rec);
+  const size_t lds =
+      (size_t)N * dk * sizeof(T) * 2 + (size_t)N * kChainRows * 4 + (size_t)N * 4 * 3;
+  hipLaunchKernelGGL((chain_verify_kernel<T>), dim3((unsigned)grid), dim3(256), lds, stream, N,
+                     H, dk, dv, ntiles, S0, static_cast<const T*>(q), static_cast<const T*>(k),
+                     static_cast<const T*>(v), beta, g, scale, out, rec);
   return hipGetLastError();
 }
 

@@ -166,6 +166,14 @@ __device__ inline float row16_sum(float x) {
   return x;
 }
 
+// Sum over each half-wave (32 lanes): the 16-lane row sums, then one
+// ds_swizzle in bit mode (and 0x1F, xor 0x10) adds the other row of the half.
+__device__ inline float half32_sum(float x) {
+  x = row16_sum(x);
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
+                                                                   (0x10 << 10) | 0x1F));
+}
+
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
 // Fragment convention (lane l of a wave64):
 //   A: row i = l % 16, k = 8 * (l / 16) + e, e = 0..7

@@ -26,19 +26,20 @@
 //   1. validates the parents and builds ancestor bitmasks and the
 //      path-cumulative G by pointer jumping (one lane per node);
 //   2. forms the Gram blocks Q K^T and K K^T on bf16 MFMA (lower triangle);
-//   3. solves row t of T on t's root path only (rows of T vanish off the
-//      path): one lane per node, the path held in registers; Attn is masked
-//      in place;
+//   3. masks and scales them into A and Attn (all threads), then solves row t
+//      of T on t's root path (rows of T vanish off the path), one lane per
+//      node with the path in registers;
 //   4. runs the dense contraction Y = [Q; K] S0_tile^T on bf16 MFMA with the
 //      FP32 state split into bf16 hi + lo (bf16 q, k make every product
 //      exact; only the 2^-16 split residue is lost);
 //   5. forms R = beta (V - e^G Y_k) from the accumulators, then U' = T R and
-//      O = scale e^G Y_q + Attn U' as two dense MFMA products whose FP32
-//      operands are split into bf16 hi + lo (three passes: hi*hi, hi*lo,
-//      lo*hi).  Masked-out entries are exact zeros, so non-ancestors never
-//      contribute.
+//      O = scale e^G Y_q + Attn U' as two dense MFMA products.  Their FP32
+//      operands are stored in LDS already split into bf16 hi + lo and summed
+//      in three passes (hi*hi, hi*lo, lo*hi).  Masked-out entries are exact
+//      zeros, so non-ancestors never contribute.
 // The per-head steps 1-3 are repeated by each of the head's tiles; they run
-// while the state tile is still in flight.
+// while the state tile is still in flight.  Workgroups are numbered so that
+// the tiles of one head run on the same XCD and share its L2 for Q and K.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -60,88 +61,110 @@ __device__ inline void frag_global(const float* p, bool ok, bf16x8& hi, bf16x8& 
   split8(a, b, hi, lo);
 }
 
-// 8 consecutive FP32 values from LDS, split into bf16 hi + lo fragments.
-__device__ inline void frag_lds_split(const float* p, bf16x8& hi, bf16x8& lo) {
-  split8(*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4), hi, lo);
+__device__ inline bf16x8 lds_bf16x8(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-constexpr int kLd = kMaxNodes + 4;        // row stride of N x N float matrices (16B rows)
-constexpr int kQKRows = 2 * kMaxNodes;    // Q rows then K rows
-constexpr int kQKStride = kMaxDim + 8;    // bf16 elements per staged row
+// Store 4 floats as bf16 hi (at p) and lo (at p + lo_off), 8 bytes each.
+__device__ inline void store_split4(bf16_t* p, int lo_off, const f32x4& x) {
+  u32x2 hi, lo;
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 hb = (__bf16)x[e];
+    r[e] = x[e] - (float)hb;
+    reinterpret_cast<__bf16*>(&hi)[e] = hb;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) reinterpret_cast<__bf16*>(&lo)[e] = (__bf16)r[e];
+  *reinterpret_cast<u32x2*>(p) = hi;
+  *reinterpret_cast<u32x2*>(p + lo_off) = lo;
+}
+
+// Store one float as bf16 hi (at p) and lo (at p + lo_off).
+__device__ inline void store_split1(bf16_t* p, int lo_off, float x) {
+  const __bf16 hb = (__bf16)x;
+  reinterpret_cast<__bf16*>(p)[0] = hb;
+  reinterpret_cast<__bf16*>(p)[lo_off] = (__bf16)(x - (float)hb);
+}
+
+// Hardware dispatches workgroup ids round-robin over the 8 XCDs; renumber so
+// that consecutive logical ids (the tiles of one head) share an XCD.
+__device__ inline int xcd_logical_id(int bid, int nblocks) {
+  constexpr int kXcds = 8;
+  if (nblocks % kXcds) return bid;
+  return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
+}
+
+constexpr int kLd = kMaxNodes + 8;         // row stride (floats) of N x N matrices: 288 B
+constexpr int kLdH = kLd;                  // row stride (bf16) of split matrices: 144 B
+constexpr int kSplitLo = kMaxNodes * kLdH; // bf16 offset of the lo half of a split matrix
+constexpr int kQKRows = 2 * kMaxNodes;     // Q rows then K rows
+constexpr int kQKStride = kMaxDim + 8;     // bf16 elements per staged row
 constexpr int kQKBytes = kQKRows * kQKStride * 2;
-constexpr int kPathMax = 16;              // register-resident path solve up to this depth
+constexpr int kPathMax = 16;               // register-resident path solve up to this depth
 
 template <int BV>
 struct TreeLds {
-  static constexpr int kBVT = ((BV + 15) / 16) * 16;               // padded tile width
-  static constexpr int kMat = kMaxNodes * kLd * 4;                  // one N x N (float)
-  static constexpr int kRT = kBVT * kLd * 4;                        // R^T or U'^T
-  static constexpr int kRegionA = kQKBytes > 2 * kRT ? kQKBytes : 2 * kRT;  // Q/K, then R^T, U'^T
-  static constexpr int kOffKK = kRegionA;
-  static constexpr int kOffQK = kOffKK + kMat;  // Q K^T, then Attn in place
-  static constexpr int kOffT = kOffQK + kMat;
+  static constexpr int kBVT = ((BV + 15) / 16) * 16;            // padded tile width
+  static constexpr int kMat = kMaxNodes * kLd * 4;               // one N x N float matrix
+  static constexpr int kSplitT = kBVT * kLdH * 2 * 2;            // R^T or U'^T, hi + lo
+  static constexpr int kRegionA = kQKBytes > 2 * kSplitT ? kQKBytes : 2 * kSplitT;
+  static constexpr int kOffKK = kRegionA;        // K K^T -> A (FP32)
+  static constexpr int kOffQK = kOffKK + kMat;   // Q K^T -> Attn (bf16 hi + lo)
+  static constexpr int kOffT = kOffQK + kMat;    // T (FP32) -> T (bf16 hi + lo)
   static constexpr int kBytes = kOffT + kMat;
 };
 
 // Row t of T on t's root path p_0..p_{d-1} = t, for d <= kPathMax:
-//   x_{d-1} = 1,  x_b = -sum_{a > b} x_a beta_{p_a} (prod_{i=b+1..a} alpha_{p_i}) (k_{p_a} . k_{p_b})
-// solves x^T (I + A)|_path = e_t^T (the decay e^{G_{p_a} - G_{p_b}} is the
-// product of the path's alphas, each <= 1).  Writes T[t][p_b] = x_b.
-__device__ inline void path_solve_registers(int t, uint64_t m, int d, const float* KK,
-                                            const float* salpha, const float* sbeta,
+//   x_{d-1} = 1,  x_b = -sum_{a > b} x_a A[p_a][p_b]
+// solves x^T (I + A)|_path = e_t^T and T[t][p_b] = x_b.  Terms with a <= b or
+// a >= d vanish on their own (x_a not yet set, or the padding), so the sum is
+// unconditional and its LDS reads issue together.
+__device__ inline void path_solve_registers(int t, uint64_t m, int d, const float* A,
                                             float* Trow) {
   int p[kPathMax];
-  float al[kPathMax], be[kPathMax];
+  float x[kPathMax];
   uint64_t mm = m;
 #pragma unroll
   for (int a = 0; a < kPathMax; ++a) {
     p[a] = mm ? __builtin_ctzll(mm) : t;
     mm &= mm - 1ull;
+    x[a] = (a == d - 1) ? 1.f : 0.f;
   }
+  Trow[t] = 1.f;
+  for (int b = d - 2; b >= 0; --b) {
+    int pb = t;
 #pragma unroll
-  for (int a = 0; a < kPathMax; ++a) {
-    al[a] = salpha[p[a]];
-    be[a] = sbeta[p[a]];
+    for (int a = 0; a < kPathMax; ++a)
+      if (a == b) pb = p[a];
+    float acc = 0.f;
+#pragma unroll
+    for (int a = 0; a < kPathMax; ++a) acc = fmaf(x[a], A[p[a] * kLd + pb], acc);
+    const float xb = -acc;
+    Trow[pb] = xb;
+#pragma unroll
+    for (int a = 0; a < kPathMax; ++a)
+      if (a == b) x[a] = xb;
   }
-  float x[kPathMax];
-#pragma unroll
-  for (int a = 0; a < kPathMax; ++a) x[a] = (a == d - 1) ? 1.f : 0.f;
-#pragma unroll
-  for (int b = kPathMax - 2; b >= 0; --b) {
-    if (b < d - 1) {
-      float acc = 0.f;
-      float dec = 1.f;  // prod_{i=b+1..a} alpha_{p_i}
-#pragma unroll
-      for (int a = b + 1; a < kPathMax; ++a) {
-        dec *= al[a];
-        if (a < d) acc = fmaf(x[a] * be[a] * dec, KK[p[a] * kLd + p[b]], acc);
-      }
-      x[b] = -acc;
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < kPathMax; ++a)
-    if (a < d) Trow[p[a]] = x[a];
 }
 
-// The same for any depth, reading and writing the row in LDS (slower).
-__device__ inline void path_solve_lds(int t, uint64_t m, const float* KK, const float* sG,
-                                      const float* sbeta, float* Trow) {
+// The same for any depth, with the row in LDS (slower).
+__device__ inline void path_solve_lds(int t, uint64_t m, const float* A, float* Trow) {
   Trow[t] = 1.f;
   for (uint64_t rest = m & ~(1ull << t); rest;) {
     const int j = 63 - __builtin_clzll(rest);
     rest &= ~(1ull << j);
-    const float Gj = sG[j];
     float acc = 0.f;
     for (uint64_t above = m & ~((2ull << j) - 1ull); above; above &= above - 1ull) {
       const int i = __builtin_ctzll(above);
-      acc = fmaf(Trow[i] * sbeta[i] * __expf(sG[i] - Gj), KK[i * kLd + j], acc);
+      acc = fmaf(Trow[i], A[i * kLd + j], acc);
     }
     Trow[j] = -acc;
   }
 }
 
-template <typename T, int BV>
+template <typename T, int BV, int NQT>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     int N, int H, int dk, int dv, int ntiles, const float* __restrict__ S0,
     const int32_t* __restrict__ parents, const T* __restrict__ q, const T* __restrict__ k,
@@ -153,19 +176,28 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   constexpr int NCT = (BV + 15) / 16;                        // MFMA column tiles
   constexpr int WC = NCT < 4 ? NCT : 4;                      // waves along columns
   constexpr int WR = 4 / WC;                                 // waves along rows
-  constexpr int MAXRT = (2 * kMaxNodes / 16 + WR - 1) / WR;  // Y row tiles per wave
-  constexpr int MAXNB = (kMaxNodes / 16 + WR - 1) / WR;      // node blocks per wave
+  // NQT = number of 16-node blocks (N <= 16 * NQT): every loop bound below is
+  // a compile-time constant, so no MFMA sits under a runtime branch.
+  constexpr int Np = 16 * NQT;
+  constexpr int NK = 32 * ((NQT + 1) / 2);                   // k extent of N x N products
+  constexpr int nrt = 2 * NQT;                               // Y row tiles (Q then K)
+  constexpr int MAXRT = (nrt + WR - 1) / WR;                 // Y row tiles per wave
+  constexpr int MAXNB = (NQT + WR - 1) / WR;                 // node blocks per wave
+  constexpr int EPT = kMaxNodes * kMaxNodes / 256;           // N x N entries per thread
 
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
   __shared__ uint64_t smask[kMaxNodes];
-  __shared__ float sG[kMaxNodes], seG[kMaxNodes], sbeta[kMaxNodes], salpha[kMaxNodes];
+  __shared__ float sG[kMaxNodes], seG[kMaxNodes], sbeta[kMaxNodes];
   __shared__ int sbad;
   bf16_t* QKs = reinterpret_cast<bf16_t*>(smem);
-  float* RT = reinterpret_cast<float*>(smem);               // [kBVT][kLd]: R^T
-  float* UT = reinterpret_cast<float*>(smem + L::kRT);      // [kBVT][kLd]: U'^T
-  float* KK = reinterpret_cast<float*>(smem + L::kOffKK);
-  float* QK = reinterpret_cast<float*>(smem + L::kOffQK);   // then Attn
+  bf16_t* RTs = reinterpret_cast<bf16_t*>(smem);                 // R^T, split [kBVT][kLdH]
+  bf16_t* UTs = reinterpret_cast<bf16_t*>(smem + L::kSplitT);    // U'^T, split
+  constexpr int kRTLo = L::kBVT * kLdH;                          // lo offset in R^T / U'^T
+  float* KK = reinterpret_cast<float*>(smem + L::kOffKK);        // then A
+  float* QK = reinterpret_cast<float*>(smem + L::kOffQK);
+  bf16_t* Attn = reinterpret_cast<bf16_t*>(smem + L::kOffQK);    // split, after phase 3
   float* Tl = reinterpret_cast<float*>(smem + L::kOffT);
+  bf16_t* Ts = reinterpret_cast<bf16_t*>(smem + L::kOffT);       // split, after phase 4
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,16 +205,12 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   const int l16 = lane & 15;
   const int lg = lane >> 4;
   const int koff = 8 * lg;
-  const int tile = blockIdx.x % ntiles;
-  const int bh = blockIdx.x / ntiles;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tile = lid % ntiles;
+  const int bh = lid / ntiles;
   const int b = bh / H;
   const int h = bh % H;
   const int r0 = tile * BV;
-  const int Np = (N + 15) & ~15;
-  const int NQT = Np / 16;        // node blocks (row tiles of Q, and of K)
-  const int NK = (Np + 31) & ~31; // k extent of the N x N products
-  const int nrt = 2 * NQT;
-  const int nks = (dk + 31) / 32;
   const int cj = wave % WC;       // this wave's column tile
   const int rb = wave / WC;       // first row tile / node block of this wave
   const int ccol = 16 * cj + l16; // column within the tile (B fragments, D columns)
@@ -192,9 +220,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   // ---- 0. one round of loads, Q/K first (unconditional, clamped, masked).
   // Consuming a load waits for every load issued before it, so the state
   // tile is issued after what the per-head steps need.
-  constexpr int QKB = (kQKRows * kMaxDim / 8) / 256;  // 16-byte chunks per thread
-  const int qk_cpr = 4 * nks;                         // chunks per staged row
-  const int qk_total = 2 * Np * qk_cpr;
+  constexpr int qk_cpr = kMaxDim / 8;                 // chunks per staged row (zero past dk)
+  constexpr int qk_total = 2 * Np * qk_cpr;
+  constexpr int QKB = (qk_total + 255) / 256;         // 16-byte chunks per thread
   u32x4 qkw[kStaged ? QKB : 1];
   if (kStaged) {
     const bf16_t* qb = reinterpret_cast<const bf16_t*>(static_cast<const void*>(q));
@@ -276,7 +304,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     smask[t] = m;
     sG[t] = G;
     seG[t] = expf(G);
-    salpha[t] = t < N ? expf(gl) : 0.f;
     sbeta[t] = t < N ? bl : 0.f;
     if (t == 0) sbad = anybad != 0ull;
     if (tile == 0 && t < N) {
@@ -328,11 +355,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     if (kStaged) {
       const bf16_t* arow = QKs + (16 * rt + l16) * kQKStride + koff;
       const bf16_t* brow = QKs + (Np + 16 * ct + l16) * kQKStride + koff;
-      for (int ks = 0; ks < nks; ++ks) {
-        const bf16x8 a8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(arow + 32 * ks));
-        const bf16x8 b8 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(brow + 32 * ks));
-        acc = mfma16x16x32(a8, b8, acc);
-      }
+#pragma unroll
+      for (int ks = 0; ks < kMaxDim / 32; ++ks)  // columns past dk are zero
+        acc = mfma16x16x32(lds_bf16x8(arow + 32 * ks), lds_bf16x8(brow + 32 * ks), acc);
     } else {
       const int ti = 16 * rtl + l16;
       const int tj = 16 * ct + l16;
@@ -340,6 +365,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
                           (((size_t)b * N + (ti < N ? ti : 0)) * H + h) * dk;
       const float* brow = reinterpret_cast<const float*>(k) +
                           (((size_t)b * N + (tj < N ? tj : 0)) * H + h) * dk;
+      const int nks = (dk + 31) / 32;
       for (int ks = 0; ks < nks; ++ks) {
         const int kk = 32 * ks + koff;
         bf16x8 ah, al, bh8, bl8;
@@ -356,21 +382,36 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   }
   __syncthreads();
 
-  // ---- 3. rows of T on root paths; Attn masked to ancestors-or-self in place
-  if (tid < Np) {
+  // ---- 3. A (FP32, in place of K K^T) and Attn (split bf16, in place of
+  // Q K^T) over all N x N entries, exact zeros off the masks; then the rows
+  // of T on root paths (one lane per node).
+  float attn[EPT];
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    const int idx = tid + 256 * x;
+    const int t = idx / kMaxNodes;
+    const int j = idx % kMaxNodes;
+    const uint64_t m = smask[t];
+    const bool on = (m >> j) & 1ull;  // j on t's root path (t >= N: empty mask)
+    const float dec = __expf(sG[t] - sG[j]);
+    float* a = KK + t * kLd + j;
+    *a = (on && j != t) ? sbeta[t] * dec * *a : 0.f;
+    attn[x] = on ? scale * dec * QK[t * kLd + j] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    const int idx = tid + 256 * x;
+    store_split1(Attn + (idx / kMaxNodes) * kLdH + idx % kMaxNodes, kSplitLo, attn[x]);
+  }
+  if (tid < N) {
     const int t = tid;
-    const uint64_t m = t < N ? smask[t] : 0ull;
+    const uint64_t m = smask[t];
     const int d = __popcll(m);
-    if (t < N) {
-      if (d <= kPathMax)
-        path_solve_registers(t, m, d, KK, salpha, sbeta, Tl + t * kLd);
-      else
-        path_solve_lds(t, m, KK, sG, sbeta, Tl + t * kLd);
-    }
-    const float Gt = sG[t];
-    float* At = QK + t * kLd;
-    for (int j = 0; j < NK; ++j)
-      At[j] = ((m >> j) & 1ull) ? scale * expf(Gt - sG[j]) * At[j] : 0.f;
+    if (d <= kPathMax)
+      path_solve_registers(t, m, d, KK, Tl + t * kLd);
+    else
+      path_solve_lds(t, m, KK, Tl + t * kLd);
   }
 
   // ---- 4. Y = [Q; K] S0_tile^T (this wave: column tile cj, row tiles rb + WR*i)
@@ -378,81 +419,104 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
   for (int i = 0; i < MAXRT; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < kMaxDim / 32; ++ks) {
-    if (ks < nks) {
-      bf16x8 bhi, blo;
-      const bool okk = sok && 32 * ks + koff < dk;
-      split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi, blo);
+  for (int ks = 0; ks < kMaxDim / 32; ++ks) {  // zero-padded past dk: no branch
+    bf16x8 bhi, blo;
+    const bool okk = sok && 32 * ks + koff < dk;
+    split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi, blo);
 #pragma unroll
-      for (int i = 0; i < MAXRT; ++i) {
-        const int rt = rb + WR * i;
-        if (rt < nrt) {
-          if (kStaged) {
-            const bf16x8 a8 = __builtin_bit_cast(
-                bf16x8, *reinterpret_cast<const u32x4*>(QKs + (16 * rt + l16) * kQKStride + 32 * ks + koff));
-            yacc[i] = mfma16x16x32(a8, bhi, yacc[i]);
-            yacc[i] = mfma16x16x32(a8, blo, yacc[i]);
-          } else {
-            const bool isq = rt < NQT;
-            const int t = 16 * (isq ? rt : rt - NQT) + l16;
-            const float* arow = reinterpret_cast<const float*>(isq ? (const void*)q : (const void*)k) +
-                                (((size_t)b * N + (t < N ? t : 0)) * H + h) * dk;
-            const int kk = 32 * ks + koff;
-            bf16x8 ah, al;
-            frag_global(arow + kk, t < N && kk < dk, ah, al);
-            yacc[i] = mfma16x16x32(ah, bhi, yacc[i]);
-            yacc[i] = mfma16x16x32(ah, blo, yacc[i]);
-            yacc[i] = mfma16x16x32(al, bhi, yacc[i]);
-          }
+    for (int i = 0; i < MAXRT; ++i) {
+      const int rt = rb + WR * i;  // rb < WR, so rt < nrt except on the last i
+      if (WR * i + WR <= nrt || rt < nrt) {
+        if (kStaged) {
+          const bf16x8 a8 = lds_bf16x8(QKs + (16 * rt + l16) * kQKStride + 32 * ks + koff);
+          yacc[i] = mfma16x16x32(a8, bhi, yacc[i]);
+          yacc[i] = mfma16x16x32(a8, blo, yacc[i]);
+        } else {
+          const bool isq = rt < NQT;
+          const int t = 16 * (isq ? rt : rt - NQT) + l16;
+          const float* arow = reinterpret_cast<const float*>(isq ? (const void*)q : (const void*)k) +
+                              (((size_t)b * N + (t < N ? t : 0)) * H + h) * dk;
+          const int kk = 32 * ks + koff;
+          bf16x8 ah, al;
+          frag_global(arow + kk, t < N && kk < dk, ah, al);
+          yacc[i] = mfma16x16x32(ah, bhi, yacc[i]);
+          yacc[i] = mfma16x16x32(ah, blo, yacc[i]);
+          yacc[i] = mfma16x16x32(al, bhi, yacc[i]);
         }
       }
     }
   }
-  __syncthreads();  // Q/K reads, solves and Attn done: region A becomes R^T, U'^T
+  __syncthreads();  // Q/K reads and the solves are done: region A becomes R^T, U'^T
 
   // ---- 5. epilogue
-  // zero the k-padding columns [Np, NK) of R^T and U'^T (read by the products)
-  for (int idx = tid; idx < L::kBVT * (NK - Np); idx += 256) {
-    const int off = (idx / (NK - Np)) * kLd + Np + idx % (NK - Np);
-    RT[off] = 0.f;
-    UT[off] = 0.f;
+  // T rows (FP32) -> registers, split in place after the barrier
+  float trow[EPT];
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    const int idx = tid + 256 * x;
+    trow[x] = Tl[(idx / kMaxNodes) * kLd + idx % kMaxNodes];
   }
-  // R = diag(beta) (V - diag(e^G) K S0^T) from the K-row accumulators, stored transposed
+  // R = diag(beta) (V - diag(e^G) K S0^T) from the K-row accumulators
+  f32x4 rv[MAXNB];
+#pragma unroll
+  for (int j = 0; j < MAXNB; ++j) rv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < MAXRT; ++i) {
     const int rt = rb + WR * i;
     if (rt >= NQT && rt < nrt) {
       const int nb = rt - NQT;
       const int j = i - iK0;  // this wave's j-th K tile: see the vreg loads
-      f32x4 rv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * nb + 4 * lg + r;
-        float vv = 0.f;
+      for (int jj = 0; jj < MAXNB; ++jj)
+        if (jj == j) {
 #pragma unroll
-        for (int jj = 0; jj < MAXNB; ++jj)
-          if (jj == j) vv = widen1(vreg[jj][r]);
-        rv[r] = sbeta[t] * ((sok ? vv : 0.f) - seG[t] * yacc[i][r]);
-      }
-      *reinterpret_cast<f32x4*>(RT + ccol * kLd + 16 * nb + 4 * lg) = rv;
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * nb + 4 * lg + r;
+            const float vv = sok ? widen1(vreg[jj][r]) : 0.f;
+            rv[jj][r] = sbeta[t] * (vv - seG[t] * yacc[i][r]);
+          }
+        }
     }
   }
   __syncthreads();
-  // U' = T R  (A = T rows, B = R^T rows, split hi/lo, three passes)
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    const int idx = tid + 256 * x;
+    store_split1(Ts + (idx / kMaxNodes) * kLdH + idx % kMaxNodes, kSplitLo, trow[x]);
+  }
+#pragma unroll
+  for (int j = 0; j < MAXNB; ++j) {
+    const int nb = rb + WR * (iK0 + j) - NQT;
+    if (nb >= 0 && nb < NQT) store_split4(RTs + ccol * kLdH + 16 * nb + 4 * lg, kRTLo, rv[j]);
+  }
+  if (NK > Np) {  // zero the k padding [Np, NK) of R^T and U'^T
+    constexpr int PAD = NK > Np ? NK - Np : 1;
+    for (int idx = tid; idx < L::kBVT * PAD; idx += 256) {
+      const int o = (idx / PAD) * kLdH + Np + idx % PAD;
+      RTs[o] = 0;
+      RTs[kRTLo + o] = 0;
+      UTs[o] = 0;
+      UTs[kRTLo + o] = 0;
+    }
+  }
+  __syncthreads();
+  // U' = T R  (A = T rows, B = R^T rows; three passes)
 #pragma unroll
   for (int j = 0; j < MAXNB; ++j) {
     const int nb = rb + WR * j;
     if (nb < NQT) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
       for (int ks = 0; ks < NK / 32; ++ks) {
-        bf16x8 ah, al, bh8, bl8;
-        frag_lds_split(Tl + (16 * nb + l16) * kLd + 32 * ks + koff, ah, al);
-        frag_lds_split(RT + ccol * kLd + 32 * ks + koff, bh8, bl8);
+        const int ao = (16 * nb + l16) * kLdH + 32 * ks + koff;
+        const int bo = ccol * kLdH + 32 * ks + koff;
+        const bf16x8 ah = lds_bf16x8(Ts + ao), al = lds_bf16x8(Ts + kSplitLo + ao);
+        const bf16x8 bh8 = lds_bf16x8(RTs + bo), bl8 = lds_bf16x8(RTs + kRTLo + bo);
         acc = mfma16x16x32(ah, bh8, acc);
         acc = mfma16x16x32(ah, bl8, acc);
         acc = mfma16x16x32(al, bh8, acc);
       }
-      *reinterpret_cast<f32x4*>(UT + ccol * kLd + 16 * nb + 4 * lg) = acc;
+      store_split4(UTs + ccol * kLdH + 16 * nb + 4 * lg, kRTLo, acc);
       if (sok) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -472,10 +536,12 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
       f32x4 acc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = scale * seG[16 * nb + 4 * lg + r] * yacc[j][r];
+#pragma unroll
       for (int ks = 0; ks < NK / 32; ++ks) {
-        bf16x8 ah, al, bh8, bl8;
-        frag_lds_split(QK + (16 * nb + l16) * kLd + 32 * ks + koff, ah, al);
-        frag_lds_split(UT + ccol * kLd + 32 * ks + koff, bh8, bl8);
+        const int ao = (16 * nb + l16) * kLdH + 32 * ks + koff;
+        const int bo = ccol * kLdH + 32 * ks + koff;
+        const bf16x8 ah = lds_bf16x8(Attn + ao), al = lds_bf16x8(Attn + kSplitLo + ao);
+        const bf16x8 bh8 = lds_bf16x8(UTs + bo), bl8 = lds_bf16x8(UTs + kRTLo + bo);
         acc = mfma16x16x32(ah, bh8, acc);
         acc = mfma16x16x32(ah, bl8, acc);
         acc = mfma16x16x32(al, bh8, acc);
@@ -491,17 +557,38 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   }
 }
 
+template <typename T, int BV, int NQT>
+hipError_t launch_bvn(int B, int N, int H, int dk, int dv, const float* S0, const int32_t* parents,
+                      const T* q, const T* k, const T* v, const float* beta, const float* g,
+                      float scale, float* out, const Record<T>& rec, uint64_t* mask_out,
+                      int32_t* dev_status, hipStream_t stream) {
+  const int ntiles = (dv + BV - 1) / BV;
+  const long grid = (long)B * H * ntiles;
+  hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out, rec,
+                     mask_out, dev_status);
+  return hipGetLastError();
+}
+
 template <typename T, int BV>
 hipError_t launch_bv(int B, int N, int H, int dk, int dv, const float* S0, const int32_t* parents,
                      const T* q, const T* k, const T* v, const float* beta, const float* g,
                      float scale, float* out, const Record<T>& rec, uint64_t* mask_out,
                      int32_t* dev_status, hipStream_t stream) {
-  const int ntiles = (dv + BV - 1) / BV;
-  const long grid = (long)B * H * ntiles;
-  hipLaunchKernelGGL((tree_verify_kernel<T, BV>), dim3((unsigned)grid), dim3(256), 0, stream, N,
-                     H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out, rec, mask_out,
-                     dev_status);
-  return hipGetLastError();
+  switch ((N + 15) / 16) {
+    case 1:
+      return launch_bvn<T, BV, 1>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                                  mask_out, dev_status, stream);
+    case 2:
+      return launch_bvn<T, BV, 2>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                                  mask_out, dev_status, stream);
+    case 3:
+      return launch_bvn<T, BV, 3>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                                  mask_out, dev_status, stream);
+    default:
+      return launch_bvn<T, BV, 4>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                                  mask_out, dev_status, stream);
+  }
 }
 
 template <typename T>
