@@ -12,7 +12,8 @@ Prints one JSON line:
   value           verified draft nodes per second (B * N per step), measured on
                   a HIP-graph replay of K steps (no host launch overhead)
   roofline        dominant kernel: algorithmic bytes per launch / its average
-                  duration from HIP events around each launch, against 8 TB/s
+                  duration (events around a HIP-graph replay of back-to-back
+                  launches of that kernel alone), against 8 TB/s
   cpu_baseline    the CPU oracle (per-path fp64 replay + commit replay) on a
                   bounded number of steps of the same workload
 """
@@ -34,6 +35,52 @@ from linear_attention_gdn_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+CSRC = os.path.join(ROOT, "linear_attention_gdn_amd", "csrc")
+KERNEL_SOURCES = {"gdn_chain_verify": "chain_verify.hip", "gdn_tree_verify": "tree_verify.hip",
+                  "gdn_commit_path": "commit.hip"}
+
+
+def source_digest(kernel: str) -> str:
+    """Short hash of a kernel's source (and the shared header) to tie counters to code."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "gdn_common.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current source of that kernel (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_digest") != source_digest(kernel):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib: int, iters: int) -> None:
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    n = (mib << 20) // 4
+    src = torch.rand(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(iters):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n * 4, "iters": iters}), flush=True)
 
 
 def bytes_verify(d: W.Draft, tree: bool) -> int:
@@ -110,7 +157,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 20)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -191,21 +243,45 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = B * N / (elapsed / args.steps)
 
-    # per-kernel durations: event pairs around each launch on the stream the
-    # library launches on (torch's current stream)
+    # Per-kernel durations: each kernel alone, `nper` back-to-back launches
+    # captured in a HIP graph, timed with events on the stream it runs on.
     nper = min(args.steps, 400)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * nper)]
-    for j in range(nper):
-        i = args.warmup + j
-        evs[4 * j].record(stream)
-        verify(i)
-        evs[4 * j + 1].record(stream)
-        evs[4 * j + 2].record(stream)
-        commit(i)
-        evs[4 * j + 3].record(stream)
-    torch.cuda.synchronize()
-    t_ver = np.array([evs[4 * j].elapsed_time(evs[4 * j + 1]) for j in range(nper)])
-    t_com = np.array([evs[4 * j + 2].elapsed_time(evs[4 * j + 3]) for j in range(nper)])
+
+    def graph_time(fn):
+        gph = torch.cuda.CUDAGraph()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(gph, stream=gs):
+                for j in range(nper):
+                    fn(args.warmup + j)
+        stream.wait_stream(gs)
+        gph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / nper
+
+    if args.no_graph:  # eager: event pairs around single launches
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * nper)]
+        for j in range(nper):
+            i = args.warmup + j
+            evs[4 * j].record(stream)
+            verify(i)
+            evs[4 * j + 1].record(stream)
+            evs[4 * j + 2].record(stream)
+            commit(i)
+            evs[4 * j + 3].record(stream)
+        torch.cuda.synchronize()
+        t_ver = np.array([evs[4 * j].elapsed_time(evs[4 * j + 1]) for j in range(nper)])
+        t_com = np.array([evs[4 * j + 2].elapsed_time(evs[4 * j + 3]) for j in range(nper)])
+    else:
+        t_ver = np.array([graph_time(verify)])
+        t_com = np.array([graph_time(commit)])
     plens = path_lengths(d, lasts_np[args.warmup:args.warmup + nper])
     b_ver = bytes_verify(d, not chain)
     b_com = np.mean([bytes_commit(d, p) for p in plens])
@@ -219,11 +295,12 @@ def main():
     if not chain:
         flops = 4.0 * B * H * N * dk * dv
         kernels["verify"]["fp32_equiv_tflops"] = float(flops / (t_ver.mean() * 1e-3) / 1e12)
-    dom = "verify" if t_ver.sum() >= t_com.sum() else "commit"
+    dom = "verify" if t_ver.mean() >= t_com.mean() else "commit"
     kd = kernels[dom]
     roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": kd["name"]}
+                "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(kd["name"], d.name), "kernel": kd["name"],
+                "algorithmic_bytes": kd["bytes"]}
 
     cpu = None
     if not args.no_cpu_baseline:
