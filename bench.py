@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 CSRC = os.path.join(ROOT, "linear_attention_gdn_amd", "csrc")
 KERNEL_SOURCES = {"gdn_chain_verify": "chain_verify.hip", "gdn_tree_verify": "tree_verify.hip",
-                  "gdn_commit_path": "commit.hip"}
+                  "gdn_commit_path": "commit.hip", "gdn_linear": "layer.hip"}
 
 
 def source_digest(kernel: str) -> str:
@@ -151,7 +151,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="chain8-b1-h8-d256", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--workload", default="chain8-b1-h8-d256",
+                    choices=sorted(W.WORKLOADS) + sorted(W.STACK_WORKLOADS))
     ap.add_argument("--rotate-mib", type=int, default=1024,
                     help="total size of the rotating layer states")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -170,6 +171,10 @@ def main():
               "(sequence, head, state-row tile) units with no exchange, so there is no "
               "multi-GPU step to time; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload in W.STACK_WORKLOADS:
+        bench_decode_loop(args)
+        return
 
     import torch
 
@@ -323,6 +328,210 @@ def main():
                    "qkv_dtype": d.dtype, "state_dtype": "f32", "rotating_states": R,
                    "timing": "eager" if args.no_graph else "hip_graph",
                    "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the decode loop over a stack of layers
+# ---------------------------------------------------------------------------
+
+
+def _graph_of(fn, count, stream):
+    """Capture `count` calls fn(0..count-1) in one HIP graph (uploaded by a
+    first replay)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for j in range(count):
+                fn(j)
+    stream.wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def _time_graph(g, stream, reps=1):
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3  # seconds
+
+
+def stack_cpu_baseline(shape, layers, S0, parents, lasts, x0_bits, budget_s):
+    """Oracle steps (24-layer verify + commit, fp64 with bf16 rounding at the
+    projection inputs and q/k/v) on the host for about `budget_s` seconds."""
+    from oracle import layer as LY
+    from oracle import oracle as O
+
+    threads = O.set_threads(0)
+    wide = lambda b: W.bf16_bits_to_f32(b).astype(np.float64)
+    wt = LY.StackWeights([wide(w) for w, _, _ in layers], [c for _, c, _ in layers],
+                         [wide(w) for _, _, w in layers], shape.H, shape.dk, shape.dv, bf16=True)
+    states = [S0[l][0].astype(np.float64) for l in range(shape.layers)]
+    hists = [np.zeros((3, shape.n_conv)) for _ in range(shape.layers)]
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        i = steps % len(lasts)
+        x, per_layer = LY.stack_spec_step(wt, wide(x0_bits[i]), parents[i], states, hists)
+        states, hists = LY.stack_commit(wt, parents[i], states, hists, per_layer, int(lasts[i]))
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    N = parents.shape[1]
+    return {"value": steps * N * shape.layers / el, "unit": "nodes/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} full {shape.layers}-layer verify+commit steps of {N}-node "
+                      f"trees (fp64, numpy BLAS + OpenMP C oracle) in {el:.1f} s; value counts "
+                      f"nodes x layers per second like the GPU value"}
+
+
+def bench_decode_loop(args):
+    import torch
+
+    from linear_attention_gdn_amd import gdnspec as G
+    from linear_attention_gdn_amd.stack import GdnStack
+
+    cfg = W.STACK_WORKLOADS[args.workload]
+    shape = W.StackShape(cfg["layers"], cfg["D"], cfg["H"], cfg["dk"], cfg["dv"])
+    N, L = cfg["N"], cfg["layers"]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(0)
+    layers = [W.stack_layer_weights(shape, rng) for _ in range(L)]
+    S0 = W.stack_states(shape, 1, rng)
+    st = GdnStack(shape, B=1, N=N, device=dev)
+    for l, (w_in, conv, w_o) in enumerate(layers):
+        st.load_layer(l, w_in, conv, w_o, S0=S0[l])
+
+    # per-step inputs: `chunk` distinct drafts captured in one graph
+    chunk = min(args.steps, 25)
+    slots = max(chunk, args.warmup)
+    parents_np, lasts_np = W.stack_drafts(rng, slots, N=N, accept_mean=cfg["accept_mean"])
+    x0_bits = np.stack([W.stack_inputs(rng, N, shape.D) for _ in range(slots)])
+    xt_bits = W.stack_inputs(rng, slots, shape.D)  # one token per autoregressive step
+    bfd = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    fd = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+    parents = torch.from_numpy(parents_np[:, None, :].copy()).to(dev)   # [slots][1][N]
+    lasts = torch.from_numpy(lasts_np[:, None].copy()).to(dev)          # [slots][1]
+    x0b = bfd(x0_bits)
+    x0f = fd(W.bf16_bits_to_f32(x0_bits))
+    xtb = bfd(xt_bits)
+    xtf = fd(W.bf16_bits_to_f32(xt_bits))
+
+    def spec_step(i):
+        st.set_inputs(x0f[i], x0b[i])
+        st.verify(parents[i])
+        st.commit(parents[i], lasts[i])
+
+    def ar_step(i):
+        st.ar_step(xtf[i:i + 1], xtb[i:i + 1])
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        spec_step(i % slots)
+        ar_step(i % slots)
+    torch.cuda.synchronize()
+    assert int(st.status[0]) == G.GDN_OK
+
+    def timed(step_fn):
+        reps, rem = divmod(args.steps, chunk)
+        el = _time_graph(_graph_of(step_fn, chunk, stream), stream, reps)
+        if rem:
+            el += _time_graph(_graph_of(step_fn, rem, stream), stream)
+        return el
+
+    t_spec = timed(spec_step)
+    t_ar = timed(ar_step)
+    ms_step = t_spec * 1e3 / args.steps
+    ms_tok = t_ar * 1e3 / args.steps
+    depth = np.stack([W.depths_of(p) for p in parents_np])
+    acc = np.array([0 if l < 0 else depth[i, l] for i, l in enumerate(lasts_np)])
+    reps, rem = divmod(args.steps, chunk)
+    acc_per_step = (reps * acc[:chunk].sum() + acc[:rem].sum()) / args.steps
+
+    # per-kernel durations: each kernel alone, back-to-back in a graph,
+    # rotating over the layers (the weights of 24 layers exceed the MALL)
+    nper = 4 * L
+    M, sh = N, shape
+    g0, g1 = st.gate_cols
+    P2 = lambda l: st.P[l].view(M, sh.n_in)
+    kern = {
+        "linear_in": (lambda j: G.gdn_linear(st.xb, st.W_in[j % L], C=P2(j % L)),
+                      sh.n_in * sh.D * 2 + M * sh.D * 2 + M * sh.n_in * 4),
+        "layer_prep": (lambda j: G.gdn_layer_prep(st.P[j % L], parents[0], st.conv_w[j % L],
+                                                  st.hist[j % L], st.q, st.k, st.v, st.beta,
+                                                  st.g), None),
+        "tree_verify": (lambda j: G.gdn_tree_verify(st.S[j % L], parents[0], st.q, st.k, st.v,
+                                                    st.beta, st.g, st.out, st.rec[j % L]), None),
+        "gate_merge": (lambda j: G.gdn_gate_merge(st.out.view(M, sh.H * sh.dv),
+                                                  P2(j % L)[:, g0:g1], st.Y), None),
+        "linear_out": (lambda j: G.gdn_linear(st.Y, st.W_o[j % L], C=st.x, R=st.x,
+                                              C_bf16=st.xb),
+                       sh.D * sh.H * sh.dv * 2 + M * sh.H * sh.dv * 2 + M * sh.D * 12),
+        "linear_in_m1": (lambda j: G.gdn_linear(st.x1b, st.W_in[j % L],
+                                                C=st.P1.view(1, sh.n_in)),
+                         sh.n_in * sh.D * 2 + sh.D * 2 + sh.n_in * 4),
+        "decode_step": (lambda j: G.gdn_decode_step(
+            st.S[j % L], st.q1.view(1, sh.H, sh.dk), st.k1.view(1, sh.H, sh.dk),
+            st.v1.view(1, sh.H, sh.dv), st.beta1.view(1, sh.H), st.g1.view(1, sh.H), st.out1),
+            2 * sh.H * sh.dv * sh.dk * 4),
+    }
+    kernels = {}
+    for name, (fn, nbytes) in kern.items():
+        us = _time_graph(_graph_of(fn, nper, stream), stream) * 1e6 / nper
+        kernels[name] = {"avg_us": round(us, 3)}
+        if nbytes:
+            kernels[name]["bytes"] = int(nbytes)
+            kernels[name]["gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    kd = kernels["linear_in"]
+    roofline = {"bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("gdn_linear", args.workload),
+                "kernel": "gdn_linear", "algorithmic_bytes": kd["bytes"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = stack_cpu_baseline(shape, layers, S0, parents_np, lasts_np, x0_bits,
+                                 args.cpu_seconds)
+    value = N * L / (ms_step * 1e-3)
+    line = {
+        "metric": "verified draft nodes/sec per GDN layer (h=8,d=256)",
+        "value": round(value, 1),
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layers": L, "hidden": shape.D, "B": 1, "N": N,
+                   "H": shape.H, "dk": shape.dk, "dv": shape.dv, "weights": "bf16",
+                   "state_dtype": "f32", "timing": "hip_graph", "parallelism": "single-gpu"},
+        "decode_loop": {
+            "stack_nodes_per_s": round(N / (ms_step * 1e-3), 1),
+            "mean_accepted_per_step": round(float(acc_per_step), 3),
+            "accepted_tokens_per_s": round(acc_per_step / (ms_step * 1e-3), 1),
+            "ar_ms_per_token": round(ms_tok, 6),
+            "ar_tokens_per_s": round(1e3 / ms_tok, 1),
+            "speedup_accepted_vs_ar": round(acc_per_step / (ms_step * 1e-3) / (1e3 / ms_tok), 3),
+        },
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,

@@ -8,6 +8,7 @@
 #include <string>
 
 #include "gdn_common.h"
+#include "../../include/gdnlayer.h"
 
 namespace gdn {
 hipError_t launch_chain_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
@@ -22,6 +23,20 @@ hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, co
 hipError_t launch_commit(int B, int N, int H, int dk, int dv, int dtype, float* S,
                          const void* factors, const int32_t* last, int32_t* path_out,
                          int32_t* path_len, int32_t* dev_status, hipStream_t stream);
+hipError_t launch_linear(int M, int Nc, int K, const void* A, const void* W, const float* R,
+                         float* C, void* Cb, hipStream_t stream);
+hipError_t launch_layer_prep(int B, int N, int H, int dk, int dv, const float* P,
+                             const int32_t* parents, const float* conv_w, const float* hist,
+                             float gate_shift, void* q, void* k, void* v, float* beta, float* g,
+                             hipStream_t stream);
+hipError_t launch_gate_merge(int M, int Cw, const float* o, const float* gate, int ldg, void* Y,
+                             hipStream_t stream);
+hipError_t launch_conv_commit(int B, int N, int Cc, const float* P, int ldP,
+                              const int32_t* parents, const int32_t* last, float* hist,
+                              int32_t* dev_status, hipStream_t stream);
+hipError_t launch_decode_step(int B, int H, int dk, int dv, int dtype, float* S, const void* q,
+                              const void* k, const void* v, const float* beta, const float* g,
+                              float scale, float* out, hipStream_t stream);
 }  // namespace gdn
 
 namespace {
@@ -190,6 +205,103 @@ int gdn_commit_path(int B, int N, int H, int dk, int dv, int qkv_dtype, float* S
   return hip_status(fn, gdn::launch_commit(B, N, H, dk, dv, qkv_dtype, S, factors,
                                            last_accepted, path_out, path_len_out, dev_status,
                                            static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// layer scaffold (gdnlayer.h)
+// ---------------------------------------------------------------------------
+
+int gdn_linear(int M, int Nc, int K, const void* A, const void* W, const float* R, float* C,
+               void* C_bf16, void* stream) {
+  const char* fn = "gdn_linear";
+  if (M < 0 || M > 64 || Nc < 0 || Nc % 16 != 0 || K < 512 || K > 65536 || K % 512 != 0)
+    return fail(GDN_ERR_SHAPE,
+                "%s: unsupported sizes M=%d Nc=%d K=%d (need 0<=M<=64, Nc%%16==0, "
+                "512<=K<=65536 with K%%512==0)",
+                fn, M, Nc, K);
+  if (!C && !C_bf16) return fail(GDN_ERR_ARG, "%s: C and C_bf16 are both NULL", fn);
+  if (M == 0 || Nc == 0) return ok();
+  GDN_TRY(check_ptr(fn, "A", A, true));
+  GDN_TRY(check_ptr(fn, "W", W, true));
+  GDN_TRY(check_ptr(fn, "R", R, false));
+  GDN_TRY(check_ptr(fn, "C", C, false));
+  GDN_TRY(check_ptr(fn, "C_bf16", C_bf16, false));
+  return hip_status(fn, gdn::launch_linear(M, Nc, K, A, W, R, C, C_bf16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int gdn_layer_prep(int B, int N, int H, int dk, int dv, const float* P, const int32_t* parents,
+                   const float* conv_w, const float* hist, float gate_shift, void* q, void* k,
+                   void* v, float* beta, float* g, void* stream) {
+  const char* fn = "gdn_layer_prep";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  if (!std::isfinite(gate_shift)) return fail(GDN_ERR_ARG, "%s: gate_shift is not finite", fn);
+  if (B == 0 || N == 0) return ok();
+  GDN_TRY(check_ptr(fn, "P", P, true));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "conv_w", conv_w, true));
+  GDN_TRY(check_ptr(fn, "hist", hist, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  return hip_status(fn, gdn::launch_layer_prep(B, N, H, dk, dv, P, parents, conv_w, hist,
+                                               gate_shift, q, k, v, beta, g,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int gdn_gate_merge(int M, int Cw, const float* o, const float* gate, int ldg, void* Y,
+                   void* stream) {
+  const char* fn = "gdn_gate_merge";
+  if (M < 0 || Cw < 0 || Cw % 4 != 0 || ldg < Cw || ldg % 4 != 0 ||
+      (long long)M * ldg >= (1ll << 40))
+    return fail(GDN_ERR_SHAPE, "%s: unsupported sizes M=%d Cw=%d ldg=%d (need Cw%%4==0, "
+                "ldg>=Cw, ldg%%4==0)", fn, M, Cw, ldg);
+  if (M == 0 || Cw == 0) return ok();
+  GDN_TRY(check_ptr(fn, "o", o, true));
+  GDN_TRY(check_ptr(fn, "gate", gate, true));
+  GDN_TRY(check_ptr(fn, "Y", Y, true));
+  return hip_status(fn, gdn::launch_gate_merge(M, Cw, o, gate, ldg, Y,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int gdn_conv_commit(int B, int N, int Cc, const float* P, int ldP, const int32_t* parents,
+                    const int32_t* last_accepted, float* hist, int32_t* dev_status,
+                    void* stream) {
+  const char* fn = "gdn_conv_commit";
+  if (B < 0 || N < 0 || N > gdn::kMaxNodes || Cc < 4 || Cc % 4 != 0 || ldP < Cc ||
+      ldP % 4 != 0 || B > 65535)
+    return fail(GDN_ERR_SHAPE, "%s: unsupported sizes B=%d N=%d Cc=%d ldP=%d (need "
+                "0<=B<=65535, 0<=N<=64, Cc%%4==0, ldP>=Cc, ldP%%4==0)", fn, B, N, Cc, ldP);
+  if (B == 0) return ok();
+  GDN_TRY(check_ptr4(fn, "last_accepted", last_accepted, true));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  if (N == 0) return ok();  // only last_accepted = -1 is possible: nothing to apply
+  GDN_TRY(check_ptr(fn, "P", P, true));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "hist", hist, true));
+  return hip_status(fn, gdn::launch_conv_commit(B, N, Cc, P, ldP, parents, last_accepted, hist,
+                                                dev_status, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_decode_step(int B, int H, int dk, int dv, int qkv_dtype, float* S, const void* q,
+                    const void* k, const void* v, const float* beta, const float* g,
+                    float scale, float* out, void* stream) {
+  const char* fn = "gdn_decode_step";
+  GDN_TRY(check_sizes(fn, B, 1, H, dk, dv));
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (!std::isfinite(scale)) return fail(GDN_ERR_ARG, "%s: scale is not finite", fn);
+  if (B == 0) return ok();
+  GDN_TRY(check_ptr(fn, "S", S, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr4(fn, "out", out, true));
+  return hip_status(fn, gdn::launch_decode_step(B, H, dk, dv, qkv_dtype, S, q, k, v, beta, g,
+                                                scale, out, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

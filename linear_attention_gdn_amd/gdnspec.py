@@ -1,7 +1,8 @@
-"""ctypes binding of libgdnspec (``include/gdnspec.h``), with the same names.
+"""ctypes binding of libgdnspec (``include/gdnspec.h``, ``include/gdnlayer.h``),
+with the same names.
 
-Argument marshalling only: every step of verification and commit runs in the
-HIP kernels of ``libgdnspec.so``.  PyTorch supplies device memory and the
+Argument marshalling only: every step of verification, commit and the layer
+scaffold runs in the HIP kernels of ``libgdnspec.so``.  PyTorch supplies device memory and the
 current HIP stream.  There is no fallback: if the library is missing the
 calls raise.
 """
@@ -18,7 +19,8 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdnspec.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "gdnspec.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADERS = [os.path.join(INCLUDE, "gdnspec.h"), os.path.join(INCLUDE, "gdnlayer.h")]
 
 GDN_OK = 0
 GDN_ERR_ARG = -1
@@ -63,16 +65,29 @@ def lib() -> ctypes.CDLL:
         L.gdn_chain_verify.restype = I
         L.gdn_commit_path.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
         L.gdn_commit_path.restype = I
+        L.gdn_linear.argtypes = [I, I, I, P, P, P, P, P, P]
+        L.gdn_linear.restype = I
+        L.gdn_layer_prep.argtypes = [I, I, I, I, I, P, P, P, P, F, P, P, P, P, P, P]
+        L.gdn_layer_prep.restype = I
+        L.gdn_gate_merge.argtypes = [I, I, P, P, I, P, P]
+        L.gdn_gate_merge.restype = I
+        L.gdn_conv_commit.argtypes = [I, I, I, P, I, P, P, P, P, P]
+        L.gdn_conv_commit.restype = I
+        L.gdn_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, F, P, P]
+        L.gdn_decode_step.restype = I
         _lib = L
     return _lib
 
 
 def declared_functions() -> list:
-    """Names of the functions ``include/gdnspec.h`` declares."""
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    """Names of the functions the headers under ``include/`` declare."""
+    names = set()
+    for path in HEADERS:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def gdn_version() -> int:
@@ -253,3 +268,104 @@ def gdn_commit_path(S, factors: FactorRecord, last_accepted, path_out=None, path
     _raise_on(lib().gdn_commit_path(B, N, H, dk, dv, factors.qkv_dtype, _p(S), _p(factors.buf),
                                     _p(last_accepted), _p(path_out), _p(path_len_out),
                                     _p(dev_status), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# layer scaffold (gdnlayer.h)
+# ---------------------------------------------------------------------------
+
+def _need_rows(name, t, dtype):
+    """A 2-D (or more) tensor on the GPU whose rows are contiguous; returns (rows, cols, ld)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def gdn_linear(A, W, C=None, R=None, C_bf16=None, stream=None) -> None:
+    """C = A W^T (+ R); see ``gdn_linear`` in gdnlayer.h.  A [M][K] and W [Nc][K] bf16."""
+    M, K = A.shape
+    Nc = W.shape[0]
+    _need("A", A, (M, K), torch.bfloat16)
+    _need("W", W, (Nc, K), torch.bfloat16)
+    if R is not None:
+        _need("R", R, (M, Nc), torch.float32)
+    if C is not None:
+        _need("C", C, (M, Nc), torch.float32)
+    if C_bf16 is not None:
+        _need("C_bf16", C_bf16, (M, Nc), torch.bfloat16)
+    _raise_on(lib().gdn_linear(M, Nc, K, _p(A), _p(W), _p(R), _p(C), _p(C_bf16),
+                               _stream(stream)))
+
+
+def gdn_layer_prep(P, parents, conv_w, hist, q, k, v, beta, g, gate_shift: float = 2.0,
+                   stream=None) -> None:
+    """Convolution along root paths, SiLU, L2 norm, beta and g; see gdnlayer.h."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][N][H][dk]")
+    B, N, H, dk = q.shape
+    dv = v.shape[-1]
+    Cc = H * (2 * dk + dv)
+    ldP = 2 * H * dk + 2 * H * dv + 2 * H
+    _need("P", P, (B, N, ldP), torch.float32)
+    _need("parents", parents, (B, N), torch.int32)
+    _need("conv_w", conv_w, (Cc, 4), torch.float32)
+    _need("hist", hist, (B, 3, Cc), torch.float32)
+    _need("q", q, (B, N, H, dk), torch.bfloat16)
+    _need("k", k, (B, N, H, dk), torch.bfloat16)
+    _need("v", v, (B, N, H, dv), torch.bfloat16)
+    _need("beta", beta, (B, N, H), torch.float32)
+    _need("g", g, (B, N, H), torch.float32)
+    _raise_on(lib().gdn_layer_prep(B, N, H, dk, dv, _p(P), _p(parents), _p(conv_w), _p(hist),
+                                   float(gate_shift), _p(q), _p(k), _p(v), _p(beta), _p(g),
+                                   _stream(stream)))
+
+
+def gdn_gate_merge(o, gate, Y, stream=None) -> None:
+    """Y = bf16(o * SiLU(gate)); o [M][Cw] FP32, gate a row-strided [M][Cw] FP32 view."""
+    M, Cw = o.shape
+    _need("o", o, (M, Cw), torch.float32)
+    _need("Y", Y, (M, Cw), torch.bfloat16)
+    gm, gc, ldg = _need_rows("gate", gate, torch.float32)
+    if (gm, gc) != (M, Cw):
+        raise ValueError(f"gate has shape {(gm, gc)}, expected {(M, Cw)}")
+    _raise_on(lib().gdn_gate_merge(M, Cw, _p(o), _p(gate), ldg, _p(Y), _stream(stream)))
+
+
+def gdn_conv_commit(P, parents, last_accepted, hist, dev_status=None, stream=None) -> None:
+    """Shift the accepted path's convolution inputs into hist; see gdnlayer.h."""
+    B, N = parents.shape
+    Cc = hist.shape[-1]
+    _need("parents", parents, (B, N), torch.int32)
+    _need("last_accepted", last_accepted, (B,), torch.int32)
+    _need("hist", hist, (B, 3, Cc), torch.float32)
+    if P.dim() != 3 or tuple(P.shape[:2]) != (B, N) or not P.is_contiguous():
+        raise ValueError("P must be a contiguous [B][N][ldP] tensor")
+    if P.dtype != torch.float32 or P.device.type != "cuda":
+        raise TypeError("P must be a float32 GPU tensor")
+    if dev_status is not None:
+        _need("dev_status", dev_status, (B,), torch.int32)
+    _raise_on(lib().gdn_conv_commit(B, N, Cc, _p(P), P.shape[2], _p(parents), _p(last_accepted),
+                                    _p(hist), _p(dev_status), _stream(stream)))
+
+
+def gdn_decode_step(S, q, k, v, beta, g, out, scale: float = 1.0, stream=None) -> None:
+    """One token of the recurrence, S updated in place; see ``gdn_decode_step``."""
+    if S.dim() != 4:
+        raise ValueError("S must be [B][H][dv][dk]")
+    B, H, dv, dk = S.shape
+    dt = q.dtype
+    _need("S", S, (B, H, dv, dk), torch.float32)
+    _need("q", q, (B, H, dk), dt)
+    _need("k", k, (B, H, dk), dt)
+    _need("v", v, (B, H, dv), dt)
+    _need("beta", beta, (B, H), torch.float32)
+    _need("g", g, (B, H), torch.float32)
+    _need("out", out, (B, H, dv), torch.float32)
+    _raise_on(lib().gdn_decode_step(B, H, dk, dv, dtype_code(dt), _p(S), _p(q), _p(k), _p(v),
+                                    _p(beta), _p(g), float(scale), _p(out), _stream(stream)))

@@ -1,0 +1,155 @@
+"""Speculative and autoregressive decoding through a stack of GDN layers.
+
+Sequencing and device buffers only: every arithmetic step is a libgdnspec
+call (``gdnspec.py``).  Verification is layer-major (the Pith review's axiom
+ledger, paper Section 4.1): all N draft nodes of a step go through layer l
+before layer l + 1, so each layer's weights are read once per step instead
+of once per node.  Per layer and step:
+
+    gdn_linear       P = bf16(x) W_in^T
+    gdn_layer_prep   conv along ancestor paths + SiLU + L2 norm; beta, g
+    gdn_tree_verify  every node's output from the committed state
+    gdn_gate_merge   bf16(o * SiLU(gate))
+    gdn_linear       x <- x + (...) W_o^T   (FP32 residual, bf16 copy for the next layer)
+
+and once the accepted node is known, per layer: gdn_commit_path (state) and
+gdn_conv_commit (convolution history).  The autoregressive baseline runs one
+token per step through the same layers with gdn_decode_step in place of
+verify + commit.
+"""
+
+from __future__ import annotations
+
+from typing import List
+
+import numpy as np
+import torch
+
+from . import gdnspec as G
+from .workloads import StackShape
+
+
+def _bf16(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(
+        torch.bfloat16)
+
+
+def _f32(x: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(device)
+
+
+class GdnStack:
+    """Device weights, per-layer states and histories, and work buffers for
+    B sequences verifying N-node drafts."""
+
+    def __init__(self, shape: StackShape, B: int = 1, N: int = 32, device="cuda",
+                 gate_shift: float = 2.0):
+        if B * N > 64:
+            raise ValueError("B * N must be at most 64 (rows of one projection)")
+        self.shape, self.B, self.N, self.device = shape, B, N, device
+        self.gate_shift = float(gate_shift)
+        L, D, H, dk, dv = shape.layers, shape.D, shape.H, shape.dk, shape.dv
+        bf, f32 = torch.bfloat16, torch.float32
+        e = lambda *s, dt=f32: torch.empty(*s, dtype=dt, device=device)
+        self.W_in = e(L, shape.n_in, D, dt=bf)
+        self.W_o = e(L, D, H * dv, dt=bf)
+        self.conv_w = e(L, shape.n_conv, 4)
+        self.S = torch.zeros(L, B, H, dv, dk, dtype=f32, device=device)
+        self.hist = torch.zeros(L, B, 3, shape.n_conv, dtype=f32, device=device)
+        # speculative step buffers (M = B * N rows)
+        M = B * N
+        self.x = e(M, D)
+        self.xb = e(M, D, dt=bf)
+        self.P = e(L, B, N, shape.n_in)
+        self.q = e(B, N, H, dk, dt=bf)
+        self.k = e(B, N, H, dk, dt=bf)
+        self.v = e(B, N, H, dv, dt=bf)
+        self.beta = e(B, N, H)
+        self.g = e(B, N, H)
+        self.out = e(B, N, H, dv)
+        self.Y = e(M, H * dv, dt=bf)
+        self.rec: List[G.FactorRecord] = [
+            G.FactorRecord.empty(B, N, H, dk, dv, G.GDN_BF16, device=device) for _ in range(L)]
+        self.status = torch.zeros(B, dtype=torch.int32, device=device)
+        # autoregressive step buffers (one token per sequence)
+        self.x1 = e(B, D)
+        self.x1b = e(B, D, dt=bf)
+        self.P1 = e(B, 1, shape.n_in)
+        self.q1 = e(B, 1, H, dk, dt=bf)
+        self.k1 = e(B, 1, H, dk, dt=bf)
+        self.v1 = e(B, 1, H, dv, dt=bf)
+        self.beta1 = e(B, 1, H)
+        self.g1 = e(B, 1, H)
+        self.out1 = e(B, H, dv)
+        self.Y1 = e(B, H * dv, dt=bf)
+        self.root1 = torch.full((B, 1), -1, dtype=torch.int32, device=device)
+        self.zero1 = torch.zeros(B, dtype=torch.int32, device=device)
+
+    # ------------------------------------------------------------------ setup
+    def load_layer(self, layer: int, w_in_bits, conv_w, w_o_bits, S0=None):
+        self.W_in[layer].copy_(_bf16(w_in_bits, self.device))
+        self.conv_w[layer].copy_(_f32(conv_w, self.device))
+        self.W_o[layer].copy_(_bf16(w_o_bits, self.device))
+        if S0 is not None:
+            self.S[layer].copy_(_f32(S0, self.device))
+
+    @property
+    def gate_cols(self):
+        sh = self.shape
+        return sh.n_conv, sh.n_conv + sh.H * sh.dv
+
+    # ------------------------------------------------------- speculative step
+    def set_inputs(self, x: torch.Tensor, x_bf16: torch.Tensor):
+        """Layer-0 input rows [B*N][D]: the FP32 residual stream and its bf16
+        projection input (the same values, bf16-representable)."""
+        self.x.copy_(x)
+        self.xb.copy_(x_bf16)
+
+    def verify(self, parents: torch.Tensor, stream=None):
+        """All layers, layer-major, for the draft tree `parents` [B][N]; the final
+        hidden rows are left in self.x (FP32) and self.xb (bf16)."""
+        sh = self.shape
+        g0, g1 = self.gate_cols
+        M = self.B * self.N
+        for l in range(sh.layers):
+            P = self.P[l]
+            G.gdn_linear(self.xb, self.W_in[l], C=P.view(M, sh.n_in), stream=stream)
+            G.gdn_layer_prep(P, parents, self.conv_w[l], self.hist[l], self.q, self.k, self.v,
+                             self.beta, self.g, gate_shift=self.gate_shift, stream=stream)
+            G.gdn_tree_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
+                              self.out, self.rec[l], dev_status=self.status, stream=stream)
+            G.gdn_gate_merge(self.out.view(M, sh.H * sh.dv), P.view(M, sh.n_in)[:, g0:g1],
+                             self.Y, stream=stream)
+            G.gdn_linear(self.Y, self.W_o[l], C=self.x, R=self.x, C_bf16=self.xb,
+                         stream=stream)
+
+    def commit(self, parents: torch.Tensor, last: torch.Tensor, stream=None):
+        """Apply the accepted path (deepest node `last` [B], -1 = none) in every layer."""
+        for l in range(self.shape.layers):
+            G.gdn_commit_path(self.S[l], self.rec[l], last, stream=stream)
+            G.gdn_conv_commit(self.P[l], parents, last, self.hist[l], stream=stream)
+
+    # ------------------------------------------------ autoregressive baseline
+    def ar_step(self, x: torch.Tensor, x_bf16: torch.Tensor, stream=None):
+        """One token per sequence ([B][D], FP32 and its bf16 copy) through every
+        layer, committing state and history as it goes; the output rows are
+        left in self.x1."""
+        sh = self.shape
+        g0, g1 = self.gate_cols
+        B = self.B
+        self.x1.copy_(x)
+        self.x1b.copy_(x_bf16)
+        for l in range(sh.layers):
+            P1 = self.P1
+            G.gdn_linear(self.x1b, self.W_in[l], C=P1.view(B, sh.n_in), stream=stream)
+            G.gdn_layer_prep(P1, self.root1, self.conv_w[l], self.hist[l], self.q1, self.k1,
+                             self.v1, self.beta1, self.g1, gate_shift=self.gate_shift,
+                             stream=stream)
+            G.gdn_conv_commit(P1, self.root1, self.zero1, self.hist[l], stream=stream)
+            G.gdn_decode_step(self.S[l], self.q1.view(B, sh.H, sh.dk), self.k1.view(B, sh.H, sh.dk),
+                              self.v1.view(B, sh.H, sh.dv), self.beta1.view(B, sh.H),
+                              self.g1.view(B, sh.H), self.out1, stream=stream)
+            G.gdn_gate_merge(self.out1.view(B, sh.H * sh.dv), P1.view(B, sh.n_in)[:, g0:g1],
+                             self.Y1, stream=stream)
+            G.gdn_linear(self.Y1, self.W_o[l], C=self.x1, R=self.x1, C_bf16=self.x1b,
+                         stream=stream)

@@ -335,3 +335,68 @@ WORKLOADS = {
     "tree32-b1-h8-d256": tree32_layer,
     "tree64-b8-h8-d256": tree64_batch8,
 }
+
+
+# --------------------------------------------------------------------------
+# the decode loop over a stack of GDN layers
+# --------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class StackShape:
+    """Sizes of a stack of GDN layers with hidden width D and H heads."""
+
+    layers: int
+    D: int = 2048
+    H: int = 8
+    dk: int = 256
+    dv: int = 256
+
+    @property
+    def n_conv(self) -> int:  # channels of the depthwise convolution (q^, k^, v^)
+        return self.H * (2 * self.dk + self.dv)
+
+    @property
+    def n_in(self) -> int:  # input projection columns: q^ k^ v^ gate alpha beta
+        return 2 * self.H * self.dk + 2 * self.H * self.dv + 2 * self.H
+
+
+def stack_layer_weights(shape: StackShape, rng: np.random.Generator):
+    """One layer's weights: W_in bf16 bits [n_in][D] ~ N(0, 1/D), conv_w f32
+    [n_conv][4] ~ N(0, 1/4), W_o bf16 bits [D][H*dv] ~ N(0, 1/(H*dv))."""
+    D, Hv = shape.D, shape.H * shape.dv
+    w_in = rng.standard_normal((shape.n_in, D), dtype=np.float32) * np.float32(D ** -0.5)
+    conv = (0.5 * rng.standard_normal((shape.n_conv, 4))).astype(np.float32)
+    w_o = rng.standard_normal((D, Hv), dtype=np.float32) * np.float32(Hv ** -0.5)
+    return f32_to_bf16_bits(w_in), conv, f32_to_bf16_bits(w_o)
+
+
+def stack_states(shape: StackShape, B: int, rng: np.random.Generator, state_std: float = 0.02):
+    """Per-layer FP32 states [layers][B][H][dv][dk] ~ N(0, state_std^2)."""
+    S = rng.standard_normal((shape.layers, B, shape.H, shape.dv, shape.dk), dtype=np.float32)
+    return S * np.float32(state_std)
+
+
+def stack_inputs(rng: np.random.Generator, rows: int, D: int) -> np.ndarray:
+    """Layer-0 inputs: bf16 bits [rows][D] of N(0, 1) values (no vocabulary)."""
+    return f32_to_bf16_bits(rng.standard_normal((rows, D), dtype=np.float32))
+
+
+def stack_drafts(rng: np.random.Generator, steps: int, N: int = 32, accept_mean: float = 3.0):
+    """Per step a window tree (parent among the previous 4 nodes, depth <= 8)
+    and the deepest accepted node: a uniform leaf's path cut to a
+    geometric(accept_mean) length.  Returns parents [steps][N], last [steps]."""
+    parents = np.empty((steps, N), np.int32)
+    last = np.empty(steps, np.int32)
+    for s in range(steps):
+        parents[s] = window_tree_parents(N, rng)
+        last[s] = accept_leaf_geometric(parents[s], rng, accept_mean)
+    return parents, last
+
+
+# The decode loop over 24 layers: hidden 2048, h=8, d=256, 32-node window
+# trees, geometric(3) acceptance, compared with one-token decoding.
+STACK_WORKLOADS = {
+    "decode24-b1-h8-d256": dict(layers=24, D=2048, H=8, dk=256, dv=256, N=32, accept_mean=3.0),
+}
+

@@ -22,6 +22,12 @@ The rest of the layer follows the plainest GDN reading:
 The committed conv history holds the 3 most recent pre-conv inputs of the
 accepted path, most recent first; a commit of the root path p_1..p_n shifts
 in P_conv(p_n), ..., P_conv(p_1) ahead of the old history.
+
+Precision: the workload fixes bf16 for the projections and for q, k, v.  With
+``bf16=True`` the layer rounds to bf16 exactly there (the input of each
+projection, and q, k, v after normalisation) and computes everything else in
+float64; with ``bf16=False`` nothing is rounded (the pure algebra, used by
+the exactness pins).
 """
 
 from __future__ import annotations
@@ -41,6 +47,15 @@ def sigmoid(x):
 
 def softplus(x):
     return np.logaddexp(0.0, x)
+
+
+def round_bf16(x):
+    """Nearest bfloat16 value (8 significant bits, ties to even), from float64.
+
+    x = m 2^e with 1/2 <= |m| < 1; keeping 8 bits means rounding m 2^8 to an
+    integer (np.rint rounds halves to even).  Finite, normal-range inputs."""
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.rint(m * 256.0), e - 8)
 
 
 def root_path(parents, t):
@@ -127,9 +142,10 @@ def commit_history(Pc, parents, hist, last):
 class StackWeights:
     """Per-layer weights: W_in [C_in][D], conv_w [3*H*d][taps], W_o [D][H*dv]."""
 
-    def __init__(self, W_in, conv_w, W_o, H, dk, dv, gate_shift=2.0):
+    def __init__(self, W_in, conv_w, W_o, H, dk, dv, gate_shift=2.0, bf16=False):
         self.W_in, self.conv_w, self.W_o = W_in, conv_w, W_o
         self.H, self.dk, self.dv, self.gate_shift = H, dk, dv, gate_shift
+        self.bf16 = bf16
 
     @property
     def layers(self):
@@ -142,13 +158,15 @@ def layer_forward(wt, layer, x, parents, S0, hist):
     what the commit needs (the verify's u' and G plus k, v, beta, g)."""
     from oracle import oracle as O
     H, dk, dv = wt.H, wt.dk, wt.dv
-    P = linear(x, wt.W_in[layer])
+    rnd = round_bf16 if wt.bf16 else (lambda a: a)
+    P = linear(rnd(x), wt.W_in[layer])
     q, k, v, beta, g, gate = layer_prep(P, parents, wt.conv_w[layer], hist, H, dk, dv,
                                         wt.gate_shift)
+    q, k, v = rnd(q), rnd(k), rnd(v)
     par = np.asarray(parents, np.int32)[None, :]
     o, up, G = O.tree_verify(np.asarray(S0)[None], par, q[None], k[None], v[None], beta[None],
                              g[None])
-    y = linear(gate_merge(o[0], gate), wt.W_o[layer], resid=x)
+    y = linear(rnd(gate_merge(o[0], gate)), wt.W_o[layer], resid=x)
     return y, o[0], P, dict(k=k, v=v, beta=beta, g=g)
 
 

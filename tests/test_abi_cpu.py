@@ -96,3 +96,66 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(G, "LIB_PATH", "/nonexistent/libgdnspec.so")
     with pytest.raises(RuntimeError, match="missing"):
         G.lib()
+
+
+def test_layer_scaffold_exports():
+    assert {"gdn_linear", "gdn_layer_prep", "gdn_gate_merge", "gdn_conv_commit",
+            "gdn_decode_step"} <= set(G.declared_functions())
+
+
+@pytest.mark.parametrize("mnk", [(65, 16, 512), (4, 24, 512), (4, 16, 384), (4, 16, 256),
+                                 (-1, 16, 512), (4, 16, 131072)])
+def test_linear_bad_sizes_rejected(mnk):
+    P = ctypes.c_void_p(4096)
+    assert G.lib().gdn_linear(*mnk, P, P, None, P, None, None) == G.GDN_ERR_SHAPE
+    assert "unsupported sizes" in G.gdn_last_error()
+
+
+def test_layer_scaffold_bad_arguments_rejected():
+    L = G.lib()
+    P = ctypes.c_void_p(4096)
+    odd = ctypes.c_void_p(4096 + 4)
+    assert L.gdn_linear(4, 16, 512, P, P, None, None, None, None) == G.GDN_ERR_ARG
+    assert "both NULL" in G.gdn_last_error()
+    assert L.gdn_linear(4, 16, 512, None, P, None, P, None, None) == G.GDN_ERR_ARG
+    assert L.gdn_linear(4, 16, 512, P, odd, None, P, None, None) == G.GDN_ERR_ARG
+    assert L.gdn_linear(0, 16, 512, None, None, None, P, None, None) == G.GDN_OK
+    # prep: sizes follow the verifier's limits; gate_shift must be finite
+    assert L.gdn_layer_prep(1, 65, 8, 256, 256, P, P, P, P, 2.0, P, P, P, P, P,
+                            None) == G.GDN_ERR_SHAPE
+    assert L.gdn_layer_prep(1, 8, 8, 256, 256, P, P, P, P, float("inf"), P, P, P, P, P,
+                            None) == G.GDN_ERR_ARG
+    assert L.gdn_layer_prep(1, 8, 8, 256, 256, P, P, None, P, 2.0, P, P, P, P, P,
+                            None) == G.GDN_ERR_ARG
+    assert "conv_w is NULL" in G.gdn_last_error()
+    assert L.gdn_layer_prep(0, 8, 8, 256, 256, None, None, None, None, 2.0, None, None, None,
+                            None, None, None) == G.GDN_OK
+    # gate merge
+    assert L.gdn_gate_merge(4, 6, P, P, 8, P, None) == G.GDN_ERR_SHAPE
+    assert L.gdn_gate_merge(4, 8, P, P, 4, P, None) == G.GDN_ERR_SHAPE
+    assert L.gdn_gate_merge(4, 8, P, P, 8, None, None) == G.GDN_ERR_ARG
+    assert L.gdn_gate_merge(0, 8, None, None, 8, None, None) == G.GDN_OK
+    # conv commit
+    assert L.gdn_conv_commit(1, 65, 16, P, 16, P, P, P, None, None) == G.GDN_ERR_SHAPE
+    assert L.gdn_conv_commit(1, 8, 18, P, 20, P, P, P, None, None) == G.GDN_ERR_SHAPE
+    assert L.gdn_conv_commit(1, 8, 16, P, 12, P, P, P, None, None) == G.GDN_ERR_SHAPE
+    assert L.gdn_conv_commit(1, 8, 16, P, 16, P, None, P, None, None) == G.GDN_ERR_ARG
+    assert L.gdn_conv_commit(0, 8, 16, None, 16, None, None, None, None, None) == G.GDN_OK
+    # decode step
+    assert L.gdn_decode_step(1, 8, 12, 256, 0, P, P, P, P, P, P, 1.0, P,
+                             None) == G.GDN_ERR_SHAPE
+    assert L.gdn_decode_step(1, 8, 256, 256, 5, P, P, P, P, P, P, 1.0, P,
+                             None) == G.GDN_ERR_ARG
+    assert L.gdn_decode_step(1, 8, 256, 256, 0, P, P, P, P, P, P, 1.0, None,
+                             None) == G.GDN_ERR_ARG
+    assert "out is NULL" in G.gdn_last_error()
+    assert L.gdn_decode_step(0, 8, 256, 256, 0, None, None, None, None, None, None, 1.0, None,
+                             None) == G.GDN_OK
+
+
+def test_layer_bindings_refuse_host_tensors():
+    import torch
+    A = torch.zeros(4, 512, dtype=torch.bfloat16)
+    W = torch.zeros(16, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        G.gdn_linear(A, W, C=torch.zeros(4, 16))

@@ -1,0 +1,311 @@
+"""GPU parity of the layer scaffold (include/gdnlayer.h) against the oracle in
+oracle/layer.py, through the C ABI, on seeded inputs: each stage alone, one
+speculative step of the full 24-layer stack at its real sizes, and the
+chain-verify == token-by-token decode property of the stack on the GPU."""
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_gdn_amd import gdnspec as G
+from linear_attention_gdn_amd import workloads as W
+from linear_attention_gdn_amd.stack import GdnStack
+from oracle import layer as LY
+from oracle import oracle as O
+
+from _gpu import TOL_OUT, TOL_STATE, dev_tensors, slice_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+U_BF16 = 2.0 ** -8  # bf16 rounding: |round(x) - x| <= 2^-8 |x|
+
+# Stacked layers re-round every layer's inputs to bf16.  Two correct
+# implementations that differ only in FP32-vs-FP64 rounding then round some
+# inputs one bf16 step apart, each such flip moves every projection output of
+# its node slightly, and later layers flip more inputs: past the first layer
+# the two agree to a few bf16 units, not to FP32 precision.  The oracle shows
+# the same spread against itself when its values are perturbed by 2^-24 before
+# rounding (24 layers, six perturbations: state max error up to 1.3e-2 = 3.3
+# units, RMS up to 4.9e-3 = 1.25 units; outputs 2.4e-4 to 2.9e-4).  States of
+# layers past the first are therefore gated at 8 units (max) and 2 units (RMS
+# per head); layer 0, whose inputs are identical on both sides, and the layer
+# outputs keep the verifier's own bounds.
+STACK_STATE_MAX = 8 * U_BF16
+STACK_STATE_RMS = 2 * U_BF16
+
+
+def bf(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).to(DEV).view(
+        torch.bfloat16)
+
+
+def f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(DEV)
+
+
+def i32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.int32)).to(DEV)
+
+
+def wide(bits):
+    return W.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def bits_of(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def rel(gpu, ref):
+    return np.abs(np.asarray(gpu, np.float64) - ref).max() / np.abs(ref).max()
+
+
+def assert_bf16_close(gpu_bits, ref, slack):
+    """Each bf16 value is within one rounding of the exact value, plus `slack`
+    (relative to the largest |ref|) for the FP32 arithmetic before rounding."""
+    g = wide(gpu_bits)
+    bound = U_BF16 * np.abs(ref) + slack * np.abs(ref).max()
+    bad = np.abs(g - ref) > bound
+    assert not bad.any(), f"{bad.sum()} values off; worst {np.abs(g - ref).max():.3e}"
+
+
+# ---------------------------------------------------------------------------
+# gdn_linear
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,Nc,K", [(1, 16, 512), (5, 48, 512), (16, 64, 1024), (33, 80, 512),
+                                    (64, 32, 1536), (32, 2048, 2048), (32, 8208, 2048),
+                                    (1, 8208, 2048)])
+@pytest.mark.parametrize("resid", [False, True])
+def test_linear_matches_oracle(M, Nc, K, resid):
+    rng = np.random.default_rng(M * 100003 + Nc * 7 + K + resid)
+    A = W.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    Wt = W.f32_to_bf16_bits(rng.standard_normal((Nc, K), dtype=np.float32) * np.float32(K ** -0.5))
+    R = rng.standard_normal((M, Nc)).astype(np.float32) if resid else None
+    ref = LY.linear(wide(A), wide(Wt), resid=R)
+    C = torch.full((M, Nc), float("nan"), device=DEV)
+    Cb = torch.empty((M, Nc), dtype=torch.bfloat16, device=DEV)
+    G.gdn_linear(bf(A), bf(Wt), C=C, R=f32(R) if resid else None, C_bf16=Cb)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy()
+    assert rel(c, ref) <= 1e-5
+    # the bf16 copy is C rounded to nearest even
+    np.testing.assert_array_equal(bits_of(Cb), W.f32_to_bf16_bits(c))
+    assert_bf16_close(bits_of(Cb), ref, 1e-5)
+
+
+def test_linear_in_place_residual_and_bitwise_repeat():
+    rng = np.random.default_rng(5)
+    M, Nc, K = 32, 2048, 2048
+    A = W.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    Wt = W.f32_to_bf16_bits(rng.standard_normal((Nc, K), dtype=np.float32) * np.float32(K ** -0.5))
+    R = rng.standard_normal((M, Nc)).astype(np.float32)
+    ref = LY.linear(wide(A), wide(Wt), resid=R)
+    X = f32(R)
+    G.gdn_linear(bf(A), bf(Wt), C=X, R=X)
+    Y = torch.empty_like(X)
+    G.gdn_linear(bf(A), bf(Wt), C=Y, R=f32(R))
+    torch.cuda.synchronize()
+    assert rel(X.cpu().numpy(), ref) <= 1e-5
+    assert torch.equal(X, Y)
+
+
+# ---------------------------------------------------------------------------
+# gdn_layer_prep
+# ---------------------------------------------------------------------------
+
+def _topology(kind, N, rng):
+    return {"window": lambda: W.window_tree_parents(N, rng),
+            "branching": lambda: W.branching_tree_parents(N, rng),
+            "random": lambda: W.random_parents(N, rng),
+            "chain": lambda: W.chain_parents(N)}[kind]()
+
+
+@pytest.mark.parametrize("B,N,H,dk,dv,topo", [(1, 32, 8, 256, 256, "window"),
+                                              (2, 64, 2, 64, 32, "branching"),
+                                              (2, 7, 3, 40, 24, "random"),
+                                              (3, 1, 2, 16, 8, "chain"),
+                                              (1, 12, 1, 256, 256, "chain")])
+def test_layer_prep_matches_oracle(B, N, H, dk, dv, topo):
+    rng = np.random.default_rng(B * 1000 + N * 10 + H)
+    ldP = 2 * H * dk + 2 * H * dv + 2 * H
+    Cc = H * (2 * dk + dv)
+    P = rng.standard_normal((B, N, ldP)).astype(np.float32)
+    parents = np.stack([_topology(topo, N, rng) for _ in range(B)]).astype(np.int32)
+    conv_w = (0.5 * rng.standard_normal((Cc, 4))).astype(np.float32)
+    hist = rng.standard_normal((B, 3, Cc)).astype(np.float32)
+    q = torch.empty((B, N, H, dk), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty_like(q)
+    v = torch.empty((B, N, H, dv), dtype=torch.bfloat16, device=DEV)
+    beta = torch.full((B, N, H), float("nan"), device=DEV)
+    g = torch.full((B, N, H), float("nan"), device=DEV)
+    G.gdn_layer_prep(f32(P), i32(parents), f32(conv_w), f32(hist), q, k, v, beta, g,
+                     gate_shift=2.0)
+    torch.cuda.synchronize()
+    for b in range(B):
+        rq, rk, rv, rb, rg, _ = LY.layer_prep(P[b], parents[b], conv_w, hist[b], H, dk, dv, 2.0)
+        assert_bf16_close(bits_of(q[b]), rq, 2e-6)
+        assert_bf16_close(bits_of(k[b]), rk, 2e-6)
+        assert_bf16_close(bits_of(v[b]), rv, 2e-6)
+        np.testing.assert_allclose(beta[b].cpu().numpy(), rb, rtol=4e-6, atol=0)
+        np.testing.assert_allclose(g[b].cpu().numpy(), rg, rtol=4e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# gdn_gate_merge, gdn_conv_commit
+# ---------------------------------------------------------------------------
+
+def test_gate_merge_matches_oracle():
+    rng = np.random.default_rng(9)
+    M, Cw, ldg, off = 37, 2048, 8208, 6144
+    o = rng.standard_normal((M, Cw)).astype(np.float32)
+    P = (2.0 * rng.standard_normal((M, ldg))).astype(np.float32)
+    Pt = f32(P)
+    Y = torch.empty((M, Cw), dtype=torch.bfloat16, device=DEV)
+    G.gdn_gate_merge(f32(o), Pt[:, off:off + Cw], Y)
+    torch.cuda.synchronize()
+    ref = LY.gate_merge(o.reshape(M, 1, Cw), P[:, off:off + Cw])
+    assert_bf16_close(bits_of(Y), ref, 1e-6)
+
+
+def test_conv_commit_is_exact():
+    rng = np.random.default_rng(13)
+    B, N, Cc, ldP = 3, 20, 1000, 1100
+    parents = np.stack([W.window_tree_parents(N, rng) for _ in range(B)]).astype(np.int32)
+    P = rng.standard_normal((B, N, ldP)).astype(np.float32)
+    hist0 = rng.standard_normal((B, 3, Cc)).astype(np.float32)
+    for lasts in ([-1, 0, 5], [N - 1, 3, 2], [N, -2, 1], [7, 11, -1]):
+        h = f32(hist0)
+        st = torch.full((B,), 77, dtype=torch.int32, device=DEV)
+        G.gdn_conv_commit(f32(P), i32(parents), i32(lasts), h, dev_status=st)
+        torch.cuda.synchronize()
+        got = h.cpu().numpy()
+        for b, last in enumerate(lasts):
+            if -1 <= last < N:
+                assert int(st[b]) == G.GDN_OK
+                ref = LY.commit_history(P[b][:, :Cc], parents[b], hist0[b], last)
+                np.testing.assert_array_equal(got[b].astype(np.float64), ref)
+            else:
+                assert int(st[b]) == G.GDN_ERR_TOPOLOGY
+                np.testing.assert_array_equal(got[b], hist0[b])
+
+
+# ---------------------------------------------------------------------------
+# gdn_decode_step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,H,dk,dv", [("bf16", 8, 256, 256), ("f32", 2, 64, 32),
+                                           ("bf16", 3, 40, 24)])
+def test_decode_step_matches_oracle(dtype, H, dk, dv):
+    B = 2
+    d = W.make_draft(B, 1, H, dk, dv, topology="chain", accept="full", dtype=dtype, seed=3)
+    ref_out, _, _ = O.draft_verify(d)        # [B][1][H][dv]
+    ref_S, _, _ = O.draft_commit(d)          # [B][H][dv][dk]
+    t = dev_tensors(d)
+    S = t["S0"].clone()
+    out = torch.full((B, H, dv), float("nan"), device=DEV)
+    G.gdn_decode_step(S, t["q"].view(B, H, dk), t["k"].view(B, H, dk), t["v"].view(B, H, dv),
+                      t["beta"].view(B, H), t["g"].view(B, H), out, scale=d.scale)
+    torch.cuda.synchronize()
+    assert slice_rel_err(out.cpu().numpy()[:, :, None, :],
+                         ref_out.transpose(0, 2, 1, 3)) <= TOL_OUT
+    assert slice_rel_err(S.cpu().numpy(), ref_S) <= TOL_STATE
+
+
+# ---------------------------------------------------------------------------
+# the stack
+# ---------------------------------------------------------------------------
+
+def rms_rel_err(gpu, ref):
+    """Largest per-head ||gpu - ref||_F / ||ref||_F; inputs shaped [H][...]."""
+    return max(np.linalg.norm(np.asarray(gpu[h], np.float64) - ref[h]) / np.linalg.norm(ref[h])
+               for h in range(ref.shape[0]))
+
+
+def _stack_case(shape, B, N, seed):
+    rng = np.random.default_rng(seed)
+    layers = [W.stack_layer_weights(shape, rng) for _ in range(shape.layers)]
+    S0 = W.stack_states(shape, B, rng)
+    return rng, layers, S0
+
+
+def _load(shape, layers, S0, B, N):
+    st = GdnStack(shape, B=B, N=N)
+    for l, (w_in, conv, w_o) in enumerate(layers):
+        st.load_layer(l, w_in, conv, w_o, S0=S0[l])
+    return st
+
+
+def test_stack_spec_step_matches_oracle_24_layers():
+    """One verify + commit step of the 24-layer stack (hidden 2048, h=8,
+    d=256, a 32-node window tree) against the oracle run with bf16 rounding
+    at the same points, free-running from the same seeded inputs (bounds:
+    see STACK_STATE_MAX)."""
+    shape = W.StackShape(layers=24)
+    N = 32
+    rng, layers, S0 = _stack_case(shape, 1, N, seed=21)
+    parents, last = W.stack_drafts(rng, 1, N=N)
+    x0 = W.stack_inputs(rng, N, shape.D)
+    st = _load(shape, layers, S0, 1, N)
+    st.set_inputs(f32(wide(x0)), bf(x0))
+    par_t, last_t = i32(parents), i32(last)
+    st.verify(par_t)
+    st.commit(par_t, last_t)
+    torch.cuda.synchronize()
+    assert int(st.status[0]) == G.GDN_OK
+
+    wt = LY.StackWeights([wide(w) for w, _, _ in layers], [c for _, c, _ in layers],
+                         [wide(w) for _, _, w in layers], shape.H, shape.dk, shape.dv, bf16=True)
+    zeros = [np.zeros((3, shape.n_conv)) for _ in range(shape.layers)]
+    states = [S0[l][0].astype(np.float64) for l in range(shape.layers)]
+    x_ref, per_layer = LY.stack_spec_step(wt, wide(x0), parents[0], states, zeros)
+    S_ref, h_ref = LY.stack_commit(wt, parents[0], states, zeros, per_layer, int(last[0]))
+    S_gpu = st.S.cpu().numpy()
+    h_gpu = st.hist.cpu().numpy()
+    e_x = rel(st.x.cpu().numpy(), x_ref)
+    e_S = [slice_rel_err(S_gpu[l], S_ref[l][None]) for l in range(shape.layers)]
+    e_R = [rms_rel_err(S_gpu[l, 0], S_ref[l]) for l in range(shape.layers)]
+    e_h = [rel(h_gpu[l, 0], h_ref[l]) for l in range(shape.layers)]
+    print(f"\n24-layer step: output {e_x:.2e}; layer-0 state {e_S[0]:.2e}; states max "
+          f"{max(e_S):.2e}, rms {max(e_R):.2e}; history {max(e_h):.2e}")
+    assert e_x <= TOL_OUT
+    assert e_S[0] <= TOL_STATE
+    assert max(e_S) <= STACK_STATE_MAX, e_S
+    assert max(e_R) <= STACK_STATE_RMS, e_R
+    assert max(e_h) <= TOL_OUT, e_h
+
+
+def test_stack_chain_verify_equals_token_by_token_decode():
+    """The stack's layer-major verification of an 8-node chain, then the
+    commit of all 8 nodes, gives the same outputs, states and histories as
+    8 one-token decode steps (both on the GPU)."""
+    shape = W.StackShape(layers=3, D=512, H=8, dk=64, dv=64)
+    N = 8
+    rng, layers, S0 = _stack_case(shape, 1, N, seed=4)
+    x0 = W.stack_inputs(rng, N, shape.D)
+    spec = _load(shape, layers, S0, 1, N)
+    spec.set_inputs(f32(wide(x0)), bf(x0))
+    par = i32(W.chain_parents(N)[None])
+    spec.verify(par)
+    spec.commit(par, i32([N - 1]))
+    ar = _load(shape, layers, S0, 1, N)
+    outs = []
+    for t in range(N):
+        ar.ar_step(f32(wide(x0[t:t + 1])), bf(x0[t:t + 1]))
+        outs.append(ar.x1.clone())
+    torch.cuda.synchronize()
+    x_ar = torch.cat(outs).cpu().numpy().astype(np.float64)
+    e_x = rel(spec.x.cpu().numpy(), x_ar)
+    S_ar = ar.S.cpu().numpy().astype(np.float64)
+    S_sp = spec.S.cpu().numpy()
+    e_S = [slice_rel_err(S_sp[l], S_ar[l]) for l in range(shape.layers)]
+    e_R = [rms_rel_err(S_sp[l, 0], S_ar[l, 0]) for l in range(shape.layers)]
+    e_h = [rel(spec.hist[l].cpu().numpy(), ar.hist[l].cpu().numpy().astype(np.float64))
+           for l in range(shape.layers)]
+    print(f"\nchain vs token-by-token: output {e_x:.2e}; layer-0 state {e_S[0]:.2e}; "
+          f"states max {max(e_S):.2e}, rms {max(e_R):.2e}; history {max(e_h):.2e}")
+    assert e_x <= TOL_OUT
+    assert e_S[0] <= TOL_STATE
+    assert max(e_S) <= STACK_STATE_MAX and max(e_R) <= STACK_STATE_RMS
+    assert max(e_h) <= TOL_OUT
+    # layer 0 sees identical inputs on both routes: its projection rows match bitwise
+    assert torch.equal(spec.hist[0], ar.hist[0])

@@ -115,3 +115,23 @@ def test_spec_step_on_a_tree_matches_each_path_decoded_alone():
         path = W.root_path(par, t)
         x_path, _ = LY.stack_spec_step(wt, x0[path], W.chain_parents(len(path)), states, hists)
         np.testing.assert_allclose(x_path[-1], x_spec[t], rtol=1e-10, atol=1e-12)
+
+
+def test_round_bf16_ties_and_cases():
+    r = LY.round_bf16
+    assert r(1.0) == 1.0
+    assert r(1 + 2.0 ** -8) == 1.0                      # tie -> even (mantissa 0)
+    assert r(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6        # tie -> even (mantissa 2)
+    assert r(1 + 2.0 ** -8 + 2.0 ** -20) == 1 + 2.0 ** -7  # above the tie
+    assert r(-(1 + 3 * 2.0 ** -8)) == -(1 + 2.0 ** -6)
+    assert r(0.0) == 0.0
+    assert r(3.0 * 2.0 ** -130) == 3.0 * 2.0 ** -130    # few bits: exact
+    assert r(255.5) == 256.0 and r(254.5) == 254.0      # spacing 1 in [128, 256)
+
+
+def test_round_bf16_matches_float32_bit_rounding():
+    """Against the generator's independent rule (RNE on float32 bit patterns)."""
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    ref = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)).astype(np.float64)
+    np.testing.assert_array_equal(LY.round_bf16(x.astype(np.float64)), ref)
