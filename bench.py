@@ -467,24 +467,30 @@ def bench_decode_loop(args):
     # rotating over the layers (the weights of 24 layers exceed the MALL)
     nper = 4 * L
     M, sh = N, shape
+    npj = sh.n_proj
+    PK = G.GDN_W_PACKED
     g0, g1 = st.gate_cols
-    P2 = lambda l: st.P[l].view(M, sh.n_in)
+    P2 = lambda l: st.P[l].view(M, npj)
+    xb3 = st.xb.view(1, N, sh.D)
     kern = {
-        "linear_in": (lambda j: G.gdn_linear(st.xb, st.W_in[j % L], C=P2(j % L)),
-                      sh.n_in * sh.D * 2 + M * sh.D * 2 + M * sh.n_in * 4),
-        "layer_prep": (lambda j: G.gdn_layer_prep(st.P[j % L], parents[0], st.conv_w[j % L],
-                                                  st.hist[j % L], st.q, st.k, st.v, st.beta,
-                                                  st.g), None),
+        "linear_in": (lambda j: G.gdn_linear(st.xb, st.W_in[j % L], C=P2(j % L), w_layout=PK),
+                      npj * sh.D * 2 + M * sh.D * 2 + M * npj * 4),
+        "layer_prep": (lambda j: G.gdn_layer_prep(st.P[j % L], xb3, st.W_ab[j % L],
+                                                  parents[0], st.conv_w[j % L], st.hist[j % L],
+                                                  st.q, st.k, st.v, st.beta, st.g), None),
         "tree_verify": (lambda j: G.gdn_tree_verify(st.S[j % L], parents[0], st.q, st.k, st.v,
                                                     st.beta, st.g, st.out, st.rec[j % L]), None),
         "gate_merge": (lambda j: G.gdn_gate_merge(st.out.view(M, sh.H * sh.dv),
                                                   P2(j % L)[:, g0:g1], st.Y), None),
         "linear_out": (lambda j: G.gdn_linear(st.Y, st.W_o[j % L], C=st.x, R=st.x,
-                                              C_bf16=st.xb),
-                       sh.D * sh.H * sh.dv * 2 + M * sh.H * sh.dv * 2 + M * sh.D * 12),
+                                              C_bf16=st.xb, w_layout=PK),
+                       sh.D * sh.H * sh.dv * 2 + M * sh.H * sh.dv * 2 + M * sh.D * 10),
+        "commit_path": (lambda j: G.gdn_commit_path(st.S[j % L], st.rec[j % L], lasts[0]), None),
+        "conv_commit": (lambda j: G.gdn_conv_commit(st.P[j % L], parents[0], lasts[0],
+                                                    st.hist[j % L]), None),
         "linear_in_m1": (lambda j: G.gdn_linear(st.x1b, st.W_in[j % L],
-                                                C=st.P1.view(1, sh.n_in)),
-                         sh.n_in * sh.D * 2 + sh.D * 2 + sh.n_in * 4),
+                                                C=st.P1.view(1, npj), w_layout=PK),
+                         npj * sh.D * 2 + sh.D * 2 + npj * 4),
         "decode_step": (lambda j: G.gdn_decode_step(
             st.S[j % L], st.q1.view(1, sh.H, sh.dk), st.k1.view(1, sh.H, sh.dk),
             st.v1.view(1, sh.H, sh.dv), st.beta1.view(1, sh.H), st.g1.view(1, sh.H), st.out1),

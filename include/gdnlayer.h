@@ -14,12 +14,16 @@
  * gives what token-by-token decoding gives.  The rest of the layer follows
  * the usual GDN block:
  *
- *   P        = x W_in^T         columns q^ | k^ | v^ | gate | alpha logit | beta logit
+ *   P        = x W_in^T         columns q^ | k^ | v^ | gate
  *   q, k, v  = SiLU(conv4(q^, k^, v^)) along each node's root path, then
  *              q and k L2-normalised per head and rounded to bfloat16
- *   beta     = sigmoid(beta logit),  g = -softplus(alpha logit + gate_shift)
+ *   beta     = sigmoid(x . w_beta),  g = -softplus(x . w_alpha + gate_shift)
  *   o        = gdn_tree_verify(...)            (gdnspec.h)
  *   x_next   = x + (o * SiLU(gate)) W_o^T
+ *
+ * The 2H rows of the input projection that give the alpha and beta logits
+ * are applied inside gdn_layer_prep (two dot products per node and head), so
+ * the large projection has exactly 2H(dk + dv) columns.
  *
  * Conventions: the ones of gdnspec.h (status codes, 16-byte aligned device
  * pointers, caller-owned memory, work only enqueued on `stream`), plus:
@@ -39,30 +43,53 @@
 extern "C" {
 #endif
 
+/* Weight layouts for gdn_linear. */
+typedef enum {
+  GDN_W_ROWS = 0,   /* bf16 [Nc][K], one output column per row (as in a linear layer) */
+  GDN_W_PACKED = 1  /* the same values in MFMA fragment order, from gdn_pack_weights */
+} gdn_wlayout_t;
+
 /*
  * gdn_linear: C[m][n] = sum_k A[m][k] W[n][k] (+ R[m][n])  -- the block's
  * input and output projections (bf16 weights, FP32 accumulation).
  *   M      rows, 1 <= M <= 64 (the draft nodes of one sequence, or one token)
  *   Nc     output columns, Nc % 16 == 0
- *   K      reduction length, K % 512 == 0, 512 <= K <= 65536
+ *   K      reduction length, K % 256 == 0, 256 <= K <= 65536
  *   A      bf16 [M][K]
- *   W      bf16 [Nc][K] (one output column per row, as in a linear layer)
+ *   W      bf16 weights in layout w_layout (GDN_W_ROWS or GDN_W_PACKED)
  *   R      optional FP32 [M][Nc] residual added to the product, or NULL
  *   C      optional FP32 [M][Nc] output, or NULL; may be the same buffer as R
  *          (each element is read before it is written by the same thread)
  *   C_bf16 optional bf16 [M][Nc] copy of C rounded to nearest even, or NULL
- * The sum order is fixed, so results are bitwise reproducible.  M = 0 or
- * Nc = 0 is a no-op.  Errors: GDN_ERR_SHAPE for sizes out of range,
- * GDN_ERR_ARG for a NULL A or W, or when C and C_bf16 are both NULL.
+ * The sum order is fixed, so results are bitwise reproducible and identical
+ * for both layouts.  M = 0 or Nc = 0 is a no-op.  Errors: GDN_ERR_SHAPE for
+ * sizes out of range, GDN_ERR_ARG for a NULL A or W, an unknown layout, or
+ * when C and C_bf16 are both NULL.
  */
-int gdn_linear(int M, int Nc, int K, const void* A, const void* W, const float* R, float* C,
-               void* C_bf16, void* stream);
+int gdn_linear(int M, int Nc, int K, const void* A, const void* W, int w_layout, const float* R,
+               float* C, void* C_bf16, void* stream);
+
+/*
+ * gdn_pack_weights: reorder W (bf16 [Nc][K]) into GDN_W_PACKED, the order in
+ * which gdn_linear's matrix-core fragments read it: for each 16-column tile
+ * and 32-wide k step, 64 lanes x 8 consecutive k values, lane l holding
+ * column l % 16 and k offset 8 * (l / 16).  Each wave load is then one
+ * contiguous kilobyte, which streams from HBM at the full rate (row-major
+ * fragments touch 16 rows per load).  Done once per weight matrix.
+ *   W_packed  bf16, Nc * K elements, must not overlap W
+ * Same size limits as gdn_linear.
+ */
+int gdn_pack_weights(int Nc, int K, const void* W, void* W_packed, void* stream);
 
 /*
  * gdn_layer_prep: the per-node inputs of the verifier from the projection
- * output P, for B sequences of N draft nodes and H heads.
- *   P       FP32 [B][N][ldP], ldP = 2*H*dk + 2*H*dv + 2*H; column blocks
- *           q^ [H*dk] | k^ [H*dk] | v^ [H*dv] | gate [H*dv] | alpha [H] | beta [H]
+ * output P and the layer input x, for B sequences of N draft nodes, H heads
+ * and hidden width D.
+ *   P       FP32 [B][N][ldP], ldP = 2*H*(dk + dv); column blocks
+ *           q^ [H*dk] | k^ [H*dk] | v^ [H*dv] | gate [H*dv]
+ *   x       bf16 [B][N][D], the rows the projection consumed
+ *   W_ab    bf16 [2H][D]: the input-projection rows of the alpha logits
+ *           (heads 0..H-1) then of the beta logits
  *   parents int32 [B][N], -1 <= parents[t] < t (an entry outside that range
  *           is read as -1; gdn_tree_verify reports such a draft)
  *   conv_w  FP32 [Cc][4], Cc = H*(2*dk + dv): tap 0 multiplies the node's own
@@ -74,13 +101,15 @@ int gdn_linear(int M, int Nc, int K, const void* A, const void* W, const float* 
  *           else hist[i - depth(t)]
  *   q, k    bf16 [B][N][H][dk]:  SiLU(conv) normalised to unit L2 norm per head
  *   v       bf16 [B][N][H][dv]:  SiLU(conv)
- *   beta, g FP32 [B][N][H]: sigmoid(beta logit), -softplus(alpha logit + gate_shift)
- * Sizes as in gdnspec.h (N <= 64, dk, dv <= 256).  Errors: GDN_ERR_SHAPE,
- * GDN_ERR_ARG (NULL pointer, misalignment, non-finite gate_shift).
+ *   beta, g FP32 [B][N][H]: sigmoid(x . W_ab[H + h]), -softplus(x . W_ab[h] + gate_shift)
+ * Sizes as in gdnspec.h (N <= 64, dk, dv <= 256); 8 <= D <= 65536, D % 8 == 0.
+ * Errors: GDN_ERR_SHAPE, GDN_ERR_ARG (NULL pointer, misalignment, non-finite
+ * gate_shift).
  */
-int gdn_layer_prep(int B, int N, int H, int dk, int dv, const float* P, const int32_t* parents,
-                   const float* conv_w, const float* hist, float gate_shift, void* q, void* k,
-                   void* v, float* beta, float* g, void* stream);
+int gdn_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P, const void* x,
+                   const void* W_ab, const int32_t* parents, const float* conv_w,
+                   const float* hist, float gate_shift, void* q, void* k, void* v, float* beta,
+                   float* g, void* stream);
 
 /*
  * gdn_gate_merge: Y[m][c] = bf16(o[m][c] * SiLU(gate[m][c])), the SiLU output

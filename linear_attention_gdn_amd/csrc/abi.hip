@@ -23,12 +23,13 @@ hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, co
 hipError_t launch_commit(int B, int N, int H, int dk, int dv, int dtype, float* S,
                          const void* factors, const int32_t* last, int32_t* path_out,
                          int32_t* path_len, int32_t* dev_status, hipStream_t stream);
-hipError_t launch_linear(int M, int Nc, int K, const void* A, const void* W, const float* R,
-                         float* C, void* Cb, hipStream_t stream);
-hipError_t launch_layer_prep(int B, int N, int H, int dk, int dv, const float* P,
-                             const int32_t* parents, const float* conv_w, const float* hist,
-                             float gate_shift, void* q, void* k, void* v, float* beta, float* g,
-                             hipStream_t stream);
+hipError_t launch_linear(int M, int Nc, int K, const void* A, const void* W, int layout,
+                         const float* R, float* C, void* Cb, hipStream_t stream);
+hipError_t launch_pack_weights(int Nc, int K, const void* W, void* Wp, hipStream_t stream);
+hipError_t launch_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P,
+                             const void* x, const void* W_ab, const int32_t* parents,
+                             const float* conv_w, const float* hist, float gate_shift, void* q,
+                             void* k, void* v, float* beta, float* g, hipStream_t stream);
 hipError_t launch_gate_merge(int M, int Cw, const float* o, const float* gate, int ldg, void* Y,
                              hipStream_t stream);
 hipError_t launch_conv_commit(int B, int N, int Cc, const float* P, int ldP,
@@ -211,14 +212,22 @@ int gdn_commit_path(int B, int N, int H, int dk, int dv, int qkv_dtype, float* S
 // layer scaffold (gdnlayer.h)
 // ---------------------------------------------------------------------------
 
-int gdn_linear(int M, int Nc, int K, const void* A, const void* W, const float* R, float* C,
-               void* C_bf16, void* stream) {
-  const char* fn = "gdn_linear";
-  if (M < 0 || M > 64 || Nc < 0 || Nc % 16 != 0 || K < 512 || K > 65536 || K % 512 != 0)
+static int linear_sizes_ok(const char* fn, int M, int Nc, int K) {
+  if (M < 0 || M > 64 || Nc < 0 || Nc % 16 != 0 || K < 256 || K > 65536 || K % 256 != 0)
     return fail(GDN_ERR_SHAPE,
                 "%s: unsupported sizes M=%d Nc=%d K=%d (need 0<=M<=64, Nc%%16==0, "
-                "512<=K<=65536 with K%%512==0)",
+                "256<=K<=65536 with K%%256==0)",
                 fn, M, Nc, K);
+  return GDN_OK;
+}
+
+int gdn_linear(int M, int Nc, int K, const void* A, const void* W, int w_layout, const float* R,
+               float* C, void* C_bf16, void* stream) {
+  const char* fn = "gdn_linear";
+  GDN_TRY(linear_sizes_ok(fn, M, Nc, K));
+  if (w_layout != GDN_W_ROWS && w_layout != GDN_W_PACKED)
+    return fail(GDN_ERR_ARG, "%s: w_layout %d is neither GDN_W_ROWS (0) nor GDN_W_PACKED (1)",
+                fn, w_layout);
   if (!C && !C_bf16) return fail(GDN_ERR_ARG, "%s: C and C_bf16 are both NULL", fn);
   if (M == 0 || Nc == 0) return ok();
   GDN_TRY(check_ptr(fn, "A", A, true));
@@ -226,18 +235,38 @@ int gdn_linear(int M, int Nc, int K, const void* A, const void* W, const float* 
   GDN_TRY(check_ptr(fn, "R", R, false));
   GDN_TRY(check_ptr(fn, "C", C, false));
   GDN_TRY(check_ptr(fn, "C_bf16", C_bf16, false));
-  return hip_status(fn, gdn::launch_linear(M, Nc, K, A, W, R, C, C_bf16,
+  return hip_status(fn, gdn::launch_linear(M, Nc, K, A, W, w_layout, R, C, C_bf16,
                                            static_cast<hipStream_t>(stream)));
 }
 
-int gdn_layer_prep(int B, int N, int H, int dk, int dv, const float* P, const int32_t* parents,
-                   const float* conv_w, const float* hist, float gate_shift, void* q, void* k,
-                   void* v, float* beta, float* g, void* stream) {
+int gdn_pack_weights(int Nc, int K, const void* W, void* W_packed, void* stream) {
+  const char* fn = "gdn_pack_weights";
+  GDN_TRY(linear_sizes_ok(fn, 1, Nc, K));
+  if (Nc == 0) return ok();
+  GDN_TRY(check_ptr(fn, "W", W, true));
+  GDN_TRY(check_ptr(fn, "W_packed", W_packed, true));
+  const char* w0 = static_cast<const char*>(W);
+  const char* p0 = static_cast<const char*>(W_packed);
+  const size_t n = (size_t)Nc * K * 2;
+  if (w0 < p0 + n && p0 < w0 + n) return fail(GDN_ERR_ARG, "%s: W and W_packed overlap", fn);
+  return hip_status(fn, gdn::launch_pack_weights(Nc, K, W, W_packed,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int gdn_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P, const void* x,
+                   const void* W_ab, const int32_t* parents, const float* conv_w,
+                   const float* hist, float gate_shift, void* q, void* k, void* v, float* beta,
+                   float* g, void* stream) {
   const char* fn = "gdn_layer_prep";
   GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  if (D < 8 || D > 65536 || D % 8 != 0)
+    return fail(GDN_ERR_SHAPE, "%s: unsupported hidden width D=%d (need 8<=D<=65536, D%%8==0)",
+                fn, D);
   if (!std::isfinite(gate_shift)) return fail(GDN_ERR_ARG, "%s: gate_shift is not finite", fn);
   if (B == 0 || N == 0) return ok();
   GDN_TRY(check_ptr(fn, "P", P, true));
+  GDN_TRY(check_ptr(fn, "x", x, true));
+  GDN_TRY(check_ptr(fn, "W_ab", W_ab, true));
   GDN_TRY(check_ptr4(fn, "parents", parents, true));
   GDN_TRY(check_ptr(fn, "conv_w", conv_w, true));
   GDN_TRY(check_ptr(fn, "hist", hist, true));
@@ -246,8 +275,8 @@ int gdn_layer_prep(int B, int N, int H, int dk, int dv, const float* P, const in
   GDN_TRY(check_ptr(fn, "v", v, true));
   GDN_TRY(check_ptr4(fn, "beta", beta, true));
   GDN_TRY(check_ptr4(fn, "g", g, true));
-  return hip_status(fn, gdn::launch_layer_prep(B, N, H, dk, dv, P, parents, conv_w, hist,
-                                               gate_shift, q, k, v, beta, g,
+  return hip_status(fn, gdn::launch_layer_prep(B, N, H, dk, dv, D, P, x, W_ab, parents, conv_w,
+                                               hist, gate_shift, q, k, v, beta, g,
                                                static_cast<hipStream_t>(stream)));
 }
 

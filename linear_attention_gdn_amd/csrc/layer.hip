@@ -13,6 +13,7 @@
 // the projection kernel is built as a streaming kernel that happens to use
 // MFMA for its arithmetic.
 #include "gdn_common.h"
+#include "../../include/gdnlayer.h"
 
 namespace gdn {
 
@@ -58,14 +59,113 @@ __device__ inline u32x4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-template <int MT, int NT>
+// Sum of the per-wave partial tiles in LDS (fixed wave order) plus residual,
+// written as FP32 and/or bf16.
+template <int MT, int NT, int WAVES>
+__device__ inline void linear_epilogue(const float (&red)[WAVES][MT * 16][NT * 16 + 4], int tid,
+                                       int nthreads, int M, int Nc, int n0, const float* R,
+                                       float* C, bf16_t* Cb) {
+  constexpr int C4 = NT * 4;  // float4 columns per tile row
+  for (int idx = tid; idx < MT * 16 * C4; idx += nthreads) {
+    const int m = idx / C4;
+    const int c = 4 * (idx % C4);
+    const int n = n0 + c;
+    if (m >= M || n >= Nc) continue;
+    f32x4 v = *reinterpret_cast<const f32x4*>(&red[0][m][c]);
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const f32x4*>(&red[w][m][c]);
+    const size_t o = (size_t)m * Nc + n;
+    if (R) v += load4(R + o);
+    if (C) *reinterpret_cast<f32x4*>(C + o) = v;
+    if (Cb) *reinterpret_cast<u32x2*>(Cb + o) = pack_bf16x4(v);
+  }
+}
+
+// D fragment of wave w's tile (mt, nt) into LDS: row 4 * (l / 16) + r, column l % 16.
+template <int MT, int NT, int WAVES>
+__device__ inline void linear_stash(float (&red)[WAVES][MT * 16][NT * 16 + 4], int w, int li,
+                                    int lg, const f32x4 (&acc)[MT][NT]) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      red[w][16 * mt + 4 * lg + 0][16 * nt + li] = acc[mt][nt].x;
+      red[w][16 * mt + 4 * lg + 1][16 * nt + li] = acc[mt][nt].y;
+      red[w][16 * mt + 4 * lg + 2][16 * nt + li] = acc[mt][nt].z;
+      red[w][16 * mt + 4 * lg + 3][16 * nt + li] = acc[mt][nt].w;
+    }
+}
+
+// Main form: 8 waves split K into eighths of KS k-steps each, and every load
+// of a wave's slice is issued before its first MFMA (KS * (MT + NT) loads of
+// 16 bytes per lane, all in flight at once), so a workgroup pays one memory
+// round trip for its whole tile.  Used for K = 256 * KS, KS in {1, 2, 4, 8}.
+// Byte offset, within a workgroup's weight range, of lane (li, lg)'s B
+// fragment for local column tile nt and k-step ks.  Row-major: 16 rows x 64
+// bytes per wave load.  Packed: tile (nt, ks) is one contiguous kilobyte.
+template <bool PK>
+__device__ inline int wfrag_off(int nt, int ks, int li, int lg, int K) {
+  if (PK) return ((nt * (K >> 5) + ks) * 64 + 16 * lg + li) * 16;
+  return ((16 * nt + li) * K + 32 * ks + 8 * lg) * 2;
+}
+
+template <int MT, int NT, int KS, bool PK>
+__global__ __launch_bounds__(512) void linear_w8_kernel(int M, int Nc, int K,
+                                                        const bf16_t* __restrict__ A,
+                                                        const bf16_t* __restrict__ W,
+                                                        const float* R, float* C,
+                                                        bf16_t* __restrict__ Cb) {
+  __shared__ float red[8][MT * 16][NT * 16 + 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int li = lane & 15;
+  const int lg = lane >> 4;
+  const int n0 = blockIdx.x * (16 * NT);
+  const int kw = K >> 3;
+  const int wrows = Nc - n0 < 16 * NT ? Nc - n0 : 16 * NT;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc(W + (size_t)n0 * K, (uint32_t)wrows * K * 2);
+
+  u32x4 a[KS][MT], b[KS][NT];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      b[s][nt] = bload16(rW, wfrag_off<PK>(nt, w * KS + s, li, lg, K));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      a[s][mt] = bload16(rA, ((16 * mt + li) * K + w * kw + 8 * lg) * 2 + 64 * s);
+  }
+  // Keep every load above this point: the scheduler would otherwise sink
+  // them next to their MFMAs and serialise the memory round trips.
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[mt][nt] = mfma16x16x32(__builtin_bit_cast(bf16x8, a[s][mt]),
+                                   __builtin_bit_cast(bf16x8, b[s][nt]), acc[mt][nt]);
+  linear_stash<MT, NT, 8>(red, w, li, lg, acc);
+  __syncthreads();
+  linear_epilogue<MT, NT, 8>(red, tid, 512, M, Nc, n0, R, C, Cb);
+}
+
+// General form for other K: 4 waves split K into quarters and run a loop
+// whose loads stay one batch of KB k-steps ahead of the MFMAs.
+template <int MT, int NT, int KB, bool PK>
 __global__ __launch_bounds__(256) void linear_kernel(int M, int Nc, int K,
                                                      const bf16_t* __restrict__ A,
                                                      const bf16_t* __restrict__ W, const float* R,
                                                      float* C, bf16_t* __restrict__ Cb) {
-  constexpr int KB = (MT + NT <= 4) ? 4 : 2;  // k-steps per load batch
-  constexpr int LDR = NT * 16 + 4;            // LDS row stride (floats)
-  __shared__ float red[4][MT * 16][LDR];
+  __shared__ float red[4][MT * 16][NT * 16 + 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -79,20 +179,22 @@ __global__ __launch_bounds__(256) void linear_kernel(int M, int Nc, int K,
 
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(A, (uint32_t)M * K * 2);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc(W + (size_t)n0 * K, (uint32_t)wrows * K * 2);
-  int offA[MT], offW[NT];  // byte offsets of this lane's fragment at k-step 0
+  const int ks0 = w * (kq >> 5);  // first k-step of this wave
+  int offA[MT], offW[NT];         // byte offsets of this lane's fragments at k-step ks0
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) offA[mt] = ((16 * mt + li) * K + w * kq + 8 * lg) * 2;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) offW[nt] = ((16 * nt + li) * K + w * kq + 8 * lg) * 2;
+  for (int nt = 0; nt < NT; ++nt) offW[nt] = wfrag_off<PK>(nt, ks0, li, lg, K);
+  constexpr int kWStep = PK ? 1024 : 64;  // bytes between consecutive k-steps of a fragment
 
   auto load = [&](int bi, u32x4 (&a)[KB][MT], u32x4 (&b)[KB][NT]) {
 #pragma unroll
     for (int s = 0; s < KB; ++s) {
-      const int koff = (bi * KB + s) * 64;
+      const int ks = bi * KB + s;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) b[s][nt] = bload16(rW, offW[nt] + koff);
+      for (int nt = 0; nt < NT; ++nt) b[s][nt] = bload16(rW, offW[nt] + kWStep * ks);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) a[s][mt] = bload16(rA, offA[mt] + koff);
+      for (int mt = 0; mt < MT; ++mt) a[s][mt] = bload16(rA, offA[mt] + 64 * ks);
     }
   };
 
@@ -125,61 +227,87 @@ __global__ __launch_bounds__(256) void linear_kernel(int M, int Nc, int K,
   }
   if (bi < nb) compute(a0, b0);
 
-  // D fragment: row 4 * (l / 16) + r, column l % 16
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      red[w][16 * mt + 4 * lg + 0][16 * nt + li] = acc[mt][nt].x;
-      red[w][16 * mt + 4 * lg + 1][16 * nt + li] = acc[mt][nt].y;
-      red[w][16 * mt + 4 * lg + 2][16 * nt + li] = acc[mt][nt].z;
-      red[w][16 * mt + 4 * lg + 3][16 * nt + li] = acc[mt][nt].w;
-    }
+  linear_stash<MT, NT, 4>(red, w, li, lg, acc);
   __syncthreads();
-  constexpr int C4 = NT * 4;  // float4 columns per tile row
-  for (int idx = tid; idx < MT * 16 * C4; idx += 256) {
-    const int m = idx / C4;
-    const int c = 4 * (idx % C4);
-    const int n = n0 + c;
-    if (m >= M || n >= Nc) continue;
-    f32x4 v = *reinterpret_cast<const f32x4*>(&red[0][m][c]);
-    v += *reinterpret_cast<const f32x4*>(&red[1][m][c]);
-    v += *reinterpret_cast<const f32x4*>(&red[2][m][c]);
-    v += *reinterpret_cast<const f32x4*>(&red[3][m][c]);
-    const size_t o = (size_t)m * Nc + n;
-    if (R) v += load4(R + o);
-    if (C) *reinterpret_cast<f32x4*>(C + o) = v;
-    if (Cb) *reinterpret_cast<u32x2*>(Cb + o) = pack_bf16x4(v);
-  }
+  linear_epilogue<MT, NT, 4>(red, tid, 256, M, Nc, n0, R, C, Cb);
 }
 
-template <int MT>
-hipError_t launch_linear_mt(int M, int Nc, int K, const bf16_t* A, const bf16_t* W,
+template <int MT, int NT, bool PK>
+hipError_t launch_linear_mn(int M, int Nc, int K, const bf16_t* A, const bf16_t* W,
                             const float* R, float* C, bf16_t* Cb, hipStream_t stream) {
-  // Two column tiles per workgroup when that still gives >= 256 workgroups.
-  if (Nc / 32 >= 256) {
-    const int grid = (Nc + 31) / 32;
-    hipLaunchKernelGGL((linear_kernel<MT, 2>), dim3(grid), dim3(256), 0, stream, M, Nc, K, A, W,
-                       R, C, Cb);
+  const int grid = (Nc + 16 * NT - 1) / (16 * NT);
+  const int ks = K / 256;
+  if (ks * (MT + NT) <= 48 && (ks == 1 || ks == 2 || ks == 4 || ks == 8)) {
+    switch (ks) {
+      case 1: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 1, PK>), dim3(grid), dim3(512), 0,
+                                 stream, M, Nc, K, A, W, R, C, Cb); break;
+      case 2: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 2, PK>), dim3(grid), dim3(512), 0,
+                                 stream, M, Nc, K, A, W, R, C, Cb); break;
+      case 4: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 4, PK>), dim3(grid), dim3(512), 0,
+                                 stream, M, Nc, K, A, W, R, C, Cb); break;
+      default: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 8, PK>), dim3(grid), dim3(512), 0,
+                                  stream, M, Nc, K, A, W, R, C, Cb); break;
+    }
+  } else if ((K / 128) % 4 == 0 && MT + NT <= 4) {
+    hipLaunchKernelGGL((linear_kernel<MT, NT, 4, PK>), dim3(grid), dim3(256), 0, stream, M, Nc,
+                       K, A, W, R, C, Cb);
   } else {
-    const int grid = Nc / 16;
-    hipLaunchKernelGGL((linear_kernel<MT, 1>), dim3(grid), dim3(256), 0, stream, M, Nc, K, A, W,
-                       R, C, Cb);
+    hipLaunchKernelGGL((linear_kernel<MT, NT, 2, PK>), dim3(grid), dim3(256), 0, stream, M, Nc,
+                       K, A, W, R, C, Cb);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_linear(int M, int Nc, int K, const void* A, const void* W, const float* R,
-                         float* C, void* Cb, hipStream_t stream) {
+template <int MT, bool PK>
+hipError_t launch_linear_mt(int M, int Nc, int K, const bf16_t* A, const bf16_t* W,
+                            const float* R, float* C, bf16_t* Cb, hipStream_t stream) {
+  // Two column tiles per workgroup when that still gives >= 256 workgroups.
+  if (Nc / 32 >= 256) return launch_linear_mn<MT, 2, PK>(M, Nc, K, A, W, R, C, Cb, stream);
+  return launch_linear_mn<MT, 1, PK>(M, Nc, K, A, W, R, C, Cb, stream);
+}
+
+template <bool PK>
+hipError_t launch_linear_pk(int M, int Nc, int K, const bf16_t* a, const bf16_t* w,
+                            const float* R, float* C, bf16_t* cb, hipStream_t stream) {
+  switch ((M + 15) / 16) {
+    case 1: return launch_linear_mt<1, PK>(M, Nc, K, a, w, R, C, cb, stream);
+    case 2: return launch_linear_mt<2, PK>(M, Nc, K, a, w, R, C, cb, stream);
+    case 3: return launch_linear_mt<3, PK>(M, Nc, K, a, w, R, C, cb, stream);
+    default: return launch_linear_mt<4, PK>(M, Nc, K, a, w, R, C, cb, stream);
+  }
+}
+
+hipError_t launch_linear(int M, int Nc, int K, const void* A, const void* W, int layout,
+                         const float* R, float* C, void* Cb, hipStream_t stream) {
   const bf16_t* a = static_cast<const bf16_t*>(A);
   const bf16_t* w = static_cast<const bf16_t*>(W);
   bf16_t* cb = static_cast<bf16_t*>(Cb);
-  switch ((M + 15) / 16) {
-    case 1: return launch_linear_mt<1>(M, Nc, K, a, w, R, C, cb, stream);
-    case 2: return launch_linear_mt<2>(M, Nc, K, a, w, R, C, cb, stream);
-    case 3: return launch_linear_mt<3>(M, Nc, K, a, w, R, C, cb, stream);
-    default: return launch_linear_mt<4>(M, Nc, K, a, w, R, C, cb, stream);
-  }
+  if (layout == GDN_W_PACKED) return launch_linear_pk<true>(M, Nc, K, a, w, R, C, cb, stream);
+  return launch_linear_pk<false>(M, Nc, K, a, w, R, C, cb, stream);
+}
+
+// gdn_pack_weights: thread i writes packed 16-byte chunk i (coalesced) from
+// row 16 * tile + lane % 16, k = 32 * kstep + 8 * (lane / 16) of W.
+__global__ __launch_bounds__(256) void pack_weights_kernel(int K, long nchunks,
+                                                           const bf16_t* __restrict__ W,
+                                                           bf16_t* __restrict__ Wp) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nchunks) return;
+  const int lane = (int)(i & 63);
+  const long ks_all = i >> 6;
+  const int nks = K >> 5;
+  const long ct = ks_all / nks;
+  const int ks = (int)(ks_all % nks);
+  const size_t src = (size_t)(16 * ct + (lane & 15)) * K + 32 * ks + 8 * (lane >> 4);
+  *reinterpret_cast<u32x4*>(Wp + 8 * (size_t)i) = *reinterpret_cast<const u32x4*>(W + src);
+}
+
+hipError_t launch_pack_weights(int Nc, int K, const void* W, void* Wp, hipStream_t stream) {
+  const long nchunks = (long)Nc * K / 8;
+  const long grid = (nchunks + 255) / 256;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)grid), dim3(256), 0, stream, K, nchunks,
+                     static_cast<const bf16_t*>(W), static_cast<bf16_t*>(Wp));
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -187,13 +315,26 @@ hipError_t launch_linear(int M, int Nc, int K, const void* A, const void* W, con
 // channel i of that head's q, k and v blocks.  The node's three nearest
 // ancestors come from the parent array held one entry per lane (a single
 // load) and read back with readlane, so the walk costs no extra round trip.
-// Past the root the committed history supplies the inputs.
+// Past the root the committed history supplies the inputs.  The head's alpha
+// and beta logits are two length-D dot products of the node's input row with
+// the matching rows of the input projection, reduced together with the q and
+// k norms.
 // ---------------------------------------------------------------------------
 
 __device__ inline int checked_parent(int p, int cur) { return (p >= -1 && p < cur) ? p : -1; }
 
-__global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv, int ldP,
+__device__ inline float dot8_bf16(const u32x4& x, const u32x4& w, float acc) {
+  const bf16x8 xv = __builtin_bit_cast(bf16x8, x);
+  const bf16x8 wv = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf((float)xv[e], (float)wv[e], acc);
+  return acc;
+}
+
+__global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv, int D,
                                                    const float* __restrict__ P,
+                                                   const bf16_t* __restrict__ x,
+                                                   const bf16_t* __restrict__ W_ab,
                                                    const int32_t* __restrict__ parents,
                                                    const float* __restrict__ conv_w,
                                                    const float* __restrict__ hist,
@@ -202,7 +343,7 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
                                                    bf16_t* __restrict__ vo,
                                                    float* __restrict__ beta,
                                                    float* __restrict__ g) {
-  __shared__ float wsum[4][2];
+  __shared__ float wsum[4][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int h = blockIdx.x % H;
@@ -210,14 +351,20 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
   const int t = bt % N;
   const int b = bt / N;
   const int Cc = H * (2 * dk + dv);
+  const int ldP = 2 * H * (dk + dv);
 
   // ---- every global load first
   const int mypar = parents[(size_t)b * N + clampi(lane, N - 1)];
   const float* Pb = P + (size_t)b * N * ldP;
   const float* hb = hist + (size_t)b * 3 * Cc;
-  const int oa = 2 * H * dk + 2 * H * dv;
-  const float alog = Pb[(size_t)t * ldP + oa + h];
-  const float blog = Pb[(size_t)t * ldP + oa + H + h];
+  // first D-chunk of the logit dot products (later chunks loop below)
+  const bf16_t* xr = x + ((size_t)b * N + t) * D;
+  const bf16_t* wa = W_ab + (size_t)h * D;
+  const bf16_t* wb = W_ab + (size_t)(H + h) * D;
+  const int c0 = clampi(8 * tid, D - 8);
+  const u32x4 xv0 = *reinterpret_cast<const u32x4*>(xr + c0);
+  const u32x4 av0 = *reinterpret_cast<const u32x4*>(wa + c0);
+  const u32x4 bv0 = *reinterpret_cast<const u32x4*>(wb + c0);
   // channels of this thread in the q, k, v blocks (clamped, results masked)
   const int cq = h * dk + clampi(tid, dk - 1);
   const int ck = H * dk + cq;
@@ -247,6 +394,16 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
     xv[j] = pr[cv];
   }
 
+  // ---- alpha / beta logits
+  const bool on0 = 8 * tid < D;
+  float la = on0 ? dot8_bf16(xv0, av0, 0.f) : 0.f;
+  float lb = on0 ? dot8_bf16(xv0, bv0, 0.f) : 0.f;
+  for (int c = 8 * tid + 2048; c < D; c += 2048) {
+    const u32x4 xv1 = *reinterpret_cast<const u32x4*>(xr + c);
+    la = dot8_bf16(xv1, *reinterpret_cast<const u32x4*>(wa + c), la);
+    lb = dot8_bf16(xv1, *reinterpret_cast<const u32x4*>(wb + c), lb);
+  }
+
   // ---- taps past the root come from the history (most recent first)
 #pragma unroll
   for (int j = 1; j < 4; ++j) {
@@ -256,34 +413,34 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
       xv[j] = hv[j - navail];
     }
   }
-  auto conv = [](const f32x4& w4, const float (&x)[4]) {
-    float c = w4.x * x[0];
-    c = fmaf(w4.y, x[1], c);
-    c = fmaf(w4.z, x[2], c);
-    return fmaf(w4.w, x[3], c);
+  auto conv = [](const f32x4& w4, const float (&xs)[4]) {
+    float c = w4.x * xs[0];
+    c = fmaf(w4.y, xs[1], c);
+    c = fmaf(w4.z, xs[2], c);
+    return fmaf(w4.w, xs[3], c);
   };
   const float sq = tid < dk ? silu(conv(wq, xq)) : 0.f;
   const float sk = tid < dk ? silu(conv(wk, xk)) : 0.f;
   const float sv = silu(conv(wv, xv));
 
-  // ---- per-head L2 norms of q and k
-  float nq = sq * sq;
-  float nk = sk * sk;
-  nq = row16_sum(nq);
-  nk = row16_sum(nk);
-  nq += __shfl_xor(nq, 16);
-  nk += __shfl_xor(nk, 16);
-  nq += __shfl_xor(nq, 32);
-  nk += __shfl_xor(nk, 32);
+  // ---- per-head L2 norms of q and k, and the logits, reduced together
+  float red[4] = {sq * sq, sk * sk, la, lb};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    red[i] = row16_sum(red[i]);
+    red[i] += __shfl_xor(red[i], 16);
+    red[i] += __shfl_xor(red[i], 32);
+  }
   if (lane == 0) {
-    wsum[tid >> 6][0] = nq;
-    wsum[tid >> 6][1] = nk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wsum[tid >> 6][i] = red[i];
   }
   __syncthreads();
-  const float tq = ((wsum[0][0] + wsum[1][0]) + wsum[2][0]) + wsum[3][0];
-  const float tk = ((wsum[0][1] + wsum[1][1]) + wsum[2][1]) + wsum[3][1];
-  const float iq = 1.0f / sqrtf(fmaxf(tq, 1e-30f));
-  const float ik = 1.0f / sqrtf(fmaxf(tk, 1e-30f));
+  float tot[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tot[i] = ((wsum[0][i] + wsum[1][i]) + wsum[2][i]) + wsum[3][i];
+  const float iq = 1.0f / sqrtf(fmaxf(tot[0], 1e-30f));
+  const float ik = 1.0f / sqrtf(fmaxf(tot[1], 1e-30f));
 
   const size_t node = ((size_t)b * N + t) * H + h;
   if (tid < dk) {
@@ -292,9 +449,9 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
   }
   if (tid < dv) vo[node * dv + tid] = to_bf16(sv);
   if (tid == 0) {
-    beta[node] = 1.0f / (1.0f + expf(-blog));
-    const float x = alog + gate_shift;
-    const float sp = x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+    beta[node] = 1.0f / (1.0f + expf(-tot[3]));
+    const float xa = tot[2] + gate_shift;
+    const float sp = xa > 0.f ? xa + log1pf(expf(-xa)) : log1pf(expf(xa));
     g[node] = -sp;
   }
 }
@@ -440,15 +597,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(int H, int dk, int dv,
 // launchers
 // ---------------------------------------------------------------------------
 
-hipError_t launch_layer_prep(int B, int N, int H, int dk, int dv, const float* P,
-                             const int32_t* parents, const float* conv_w, const float* hist,
-                             float gate_shift, void* q, void* k, void* v, float* beta, float* g,
-                             hipStream_t stream) {
-  const int ldP = 2 * H * dk + 2 * H * dv + 2 * H;
+hipError_t launch_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P,
+                             const void* x, const void* W_ab, const int32_t* parents,
+                             const float* conv_w, const float* hist, float gate_shift, void* q,
+                             void* k, void* v, float* beta, float* g, hipStream_t stream) {
   const long grid = (long)B * N * H;
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(256), 0, stream, N, H, dk, dv, ldP,
-                     P, parents, conv_w, hist, gate_shift, static_cast<bf16_t*>(q),
-                     static_cast<bf16_t*>(k), static_cast<bf16_t*>(v), beta, g);
+  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(256), 0, stream, N, H, dk, dv, D, P,
+                     static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W_ab), parents,
+                     conv_w, hist, gate_shift, static_cast<bf16_t*>(q), static_cast<bf16_t*>(k),
+                     static_cast<bf16_t*>(v), beta, g);
   return hipGetLastError();
 }
 

@@ -30,6 +30,8 @@ GDN_ERR_UNSUPPORTED = -4
 GDN_ERR_HIP = -5
 GDN_BF16 = 0
 GDN_F32 = 1
+GDN_W_ROWS = 0
+GDN_W_PACKED = 1
 
 _lib = None
 
@@ -65,9 +67,11 @@ def lib() -> ctypes.CDLL:
         L.gdn_chain_verify.restype = I
         L.gdn_commit_path.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
         L.gdn_commit_path.restype = I
-        L.gdn_linear.argtypes = [I, I, I, P, P, P, P, P, P]
+        L.gdn_linear.argtypes = [I, I, I, P, P, I, P, P, P, P]
         L.gdn_linear.restype = I
-        L.gdn_layer_prep.argtypes = [I, I, I, I, I, P, P, P, P, F, P, P, P, P, P, P]
+        L.gdn_pack_weights.argtypes = [I, I, P, P, P]
+        L.gdn_pack_weights.restype = I
+        L.gdn_layer_prep.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, P]
         L.gdn_layer_prep.restype = I
         L.gdn_gate_merge.argtypes = [I, I, P, P, I, P, P]
         L.gdn_gate_merge.restype = I
@@ -287,8 +291,10 @@ def _need_rows(name, t, dtype):
     return t.shape[0], t.shape[1], t.stride(0)
 
 
-def gdn_linear(A, W, C=None, R=None, C_bf16=None, stream=None) -> None:
-    """C = A W^T (+ R); see ``gdn_linear`` in gdnlayer.h.  A [M][K] and W [Nc][K] bf16."""
+def gdn_linear(A, W, C=None, R=None, C_bf16=None, w_layout: int = GDN_W_ROWS,
+               stream=None) -> None:
+    """C = A W^T (+ R); see ``gdn_linear`` in gdnlayer.h.  A [M][K] bf16; W bf16
+    [Nc][K] (GDN_W_ROWS) or its gdn_pack_weights image (GDN_W_PACKED, same shape)."""
     M, K = A.shape
     Nc = W.shape[0]
     _need("A", A, (M, K), torch.bfloat16)
@@ -299,20 +305,31 @@ def gdn_linear(A, W, C=None, R=None, C_bf16=None, stream=None) -> None:
         _need("C", C, (M, Nc), torch.float32)
     if C_bf16 is not None:
         _need("C_bf16", C_bf16, (M, Nc), torch.bfloat16)
-    _raise_on(lib().gdn_linear(M, Nc, K, _p(A), _p(W), _p(R), _p(C), _p(C_bf16),
-                               _stream(stream)))
+    _raise_on(lib().gdn_linear(M, Nc, K, _p(A), _p(W), int(w_layout), _p(R), _p(C),
+                               _p(C_bf16), _stream(stream)))
 
 
-def gdn_layer_prep(P, parents, conv_w, hist, q, k, v, beta, g, gate_shift: float = 2.0,
-                   stream=None) -> None:
-    """Convolution along root paths, SiLU, L2 norm, beta and g; see gdnlayer.h."""
+def gdn_pack_weights(W, W_packed, stream=None) -> None:
+    """Reorder bf16 W [Nc][K] into the GDN_W_PACKED layout (same shape, other buffer)."""
+    Nc, K = W.shape
+    _need("W", W, (Nc, K), torch.bfloat16)
+    _need("W_packed", W_packed, (Nc, K), torch.bfloat16)
+    _raise_on(lib().gdn_pack_weights(Nc, K, _p(W), _p(W_packed), _stream(stream)))
+
+
+def gdn_layer_prep(P, x, W_ab, parents, conv_w, hist, q, k, v, beta, g,
+                   gate_shift: float = 2.0, stream=None) -> None:
+    """Convolution along root paths, SiLU, L2 norm, beta and g; see gdnlayer.h.
+    P [B][N][2H(dk+dv)] FP32, x [B][N][D] bf16, W_ab [2H][D] bf16."""
     if q.dim() != 4:
         raise ValueError("q must be [B][N][H][dk]")
     B, N, H, dk = q.shape
     dv = v.shape[-1]
+    D = x.shape[-1]
     Cc = H * (2 * dk + dv)
-    ldP = 2 * H * dk + 2 * H * dv + 2 * H
-    _need("P", P, (B, N, ldP), torch.float32)
+    _need("P", P, (B, N, 2 * H * (dk + dv)), torch.float32)
+    _need("x", x, (B, N, D), torch.bfloat16)
+    _need("W_ab", W_ab, (2 * H, D), torch.bfloat16)
     _need("parents", parents, (B, N), torch.int32)
     _need("conv_w", conv_w, (Cc, 4), torch.float32)
     _need("hist", hist, (B, 3, Cc), torch.float32)
@@ -321,9 +338,9 @@ def gdn_layer_prep(P, parents, conv_w, hist, q, k, v, beta, g, gate_shift: float
     _need("v", v, (B, N, H, dv), torch.bfloat16)
     _need("beta", beta, (B, N, H), torch.float32)
     _need("g", g, (B, N, H), torch.float32)
-    _raise_on(lib().gdn_layer_prep(B, N, H, dk, dv, _p(P), _p(parents), _p(conv_w), _p(hist),
-                                   float(gate_shift), _p(q), _p(k), _p(v), _p(beta), _p(g),
-                                   _stream(stream)))
+    _raise_on(lib().gdn_layer_prep(B, N, H, dk, dv, D, _p(P), _p(x), _p(W_ab), _p(parents),
+                                   _p(conv_w), _p(hist), float(gate_shift), _p(q), _p(k), _p(v),
+                                   _p(beta), _p(g), _stream(stream)))
 
 
 def gdn_gate_merge(o, gate, Y, stream=None) -> None:

@@ -6,8 +6,9 @@ ledger, paper Section 4.1): all N draft nodes of a step go through layer l
 before layer l + 1, so each layer's weights are read once per step instead
 of once per node.  Per layer and step:
 
-    gdn_linear       P = bf16(x) W_in^T
-    gdn_layer_prep   conv along ancestor paths + SiLU + L2 norm; beta, g
+    gdn_linear       P = bf16(x) W_in^T   (q^ k^ v^ gate columns)
+    gdn_layer_prep   conv along ancestor paths + SiLU + L2 norm; beta, g from
+                     the last 2H rows of W_in
     gdn_tree_verify  every node's output from the committed state
     gdn_gate_merge   bf16(o * SiLU(gate))
     gdn_linear       x <- x + (...) W_o^T   (FP32 residual, bf16 copy for the next layer)
@@ -27,6 +28,8 @@ import torch
 
 from . import gdnspec as G
 from .workloads import StackShape
+
+PK = G.GDN_W_PACKED
 
 
 def _bf16(bits: np.ndarray, device) -> torch.Tensor:
@@ -51,7 +54,10 @@ class GdnStack:
         L, D, H, dk, dv = shape.layers, shape.D, shape.H, shape.dk, shape.dv
         bf, f32 = torch.bfloat16, torch.float32
         e = lambda *s, dt=f32: torch.empty(*s, dtype=dt, device=device)
-        self.W_in = e(L, shape.n_in, D, dt=bf)
+        # projection weights in the packed fragment layout; the 2H logit rows of
+        # the input projection stay row-major for gdn_layer_prep
+        self.W_in = e(L, shape.n_proj, D, dt=bf)
+        self.W_ab = e(L, 2 * H, D, dt=bf)
         self.W_o = e(L, D, H * dv, dt=bf)
         self.conv_w = e(L, shape.n_conv, 4)
         self.S = torch.zeros(L, B, H, dv, dk, dtype=f32, device=device)
@@ -60,7 +66,7 @@ class GdnStack:
         M = B * N
         self.x = e(M, D)
         self.xb = e(M, D, dt=bf)
-        self.P = e(L, B, N, shape.n_in)
+        self.P = e(L, B, N, shape.n_proj)
         self.q = e(B, N, H, dk, dt=bf)
         self.k = e(B, N, H, dk, dt=bf)
         self.v = e(B, N, H, dv, dt=bf)
@@ -74,7 +80,7 @@ class GdnStack:
         # autoregressive step buffers (one token per sequence)
         self.x1 = e(B, D)
         self.x1b = e(B, D, dt=bf)
-        self.P1 = e(B, 1, shape.n_in)
+        self.P1 = e(B, 1, shape.n_proj)
         self.q1 = e(B, 1, H, dk, dt=bf)
         self.k1 = e(B, 1, H, dk, dt=bf)
         self.v1 = e(B, 1, H, dv, dt=bf)
@@ -87,9 +93,13 @@ class GdnStack:
 
     # ------------------------------------------------------------------ setup
     def load_layer(self, layer: int, w_in_bits, conv_w, w_o_bits, S0=None):
-        self.W_in[layer].copy_(_bf16(w_in_bits, self.device))
+        """Weights as bf16 bits: w_in [n_in][D] (q^ k^ v^ gate rows, then alpha
+        and beta rows), w_o [D][H*dv]; conv_w FP32 [n_conv][4]."""
+        npj = self.shape.n_proj
+        G.gdn_pack_weights(_bf16(w_in_bits[:npj], self.device), self.W_in[layer])
+        self.W_ab[layer].copy_(_bf16(w_in_bits[npj:], self.device))
+        G.gdn_pack_weights(_bf16(w_o_bits, self.device), self.W_o[layer])
         self.conv_w[layer].copy_(_f32(conv_w, self.device))
-        self.W_o[layer].copy_(_bf16(w_o_bits, self.device))
         if S0 is not None:
             self.S[layer].copy_(_f32(S0, self.device))
 
@@ -111,16 +121,19 @@ class GdnStack:
         sh = self.shape
         g0, g1 = self.gate_cols
         M = self.B * self.N
+        npj = sh.n_proj
+        xb3 = self.xb.view(self.B, self.N, sh.D)
         for l in range(sh.layers):
             P = self.P[l]
-            G.gdn_linear(self.xb, self.W_in[l], C=P.view(M, sh.n_in), stream=stream)
-            G.gdn_layer_prep(P, parents, self.conv_w[l], self.hist[l], self.q, self.k, self.v,
-                             self.beta, self.g, gate_shift=self.gate_shift, stream=stream)
+            G.gdn_linear(self.xb, self.W_in[l], C=P.view(M, npj), w_layout=PK, stream=stream)
+            G.gdn_layer_prep(P, xb3, self.W_ab[l], parents, self.conv_w[l], self.hist[l],
+                             self.q, self.k, self.v, self.beta, self.g,
+                             gate_shift=self.gate_shift, stream=stream)
             G.gdn_tree_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
                               self.out, self.rec[l], dev_status=self.status, stream=stream)
-            G.gdn_gate_merge(self.out.view(M, sh.H * sh.dv), P.view(M, sh.n_in)[:, g0:g1],
+            G.gdn_gate_merge(self.out.view(M, sh.H * sh.dv), P.view(M, npj)[:, g0:g1],
                              self.Y, stream=stream)
-            G.gdn_linear(self.Y, self.W_o[l], C=self.x, R=self.x, C_bf16=self.xb,
+            G.gdn_linear(self.Y, self.W_o[l], C=self.x, R=self.x, C_bf16=self.xb, w_layout=PK,
                          stream=stream)
 
     def commit(self, parents: torch.Tensor, last: torch.Tensor, stream=None):
@@ -139,17 +152,19 @@ class GdnStack:
         B = self.B
         self.x1.copy_(x)
         self.x1b.copy_(x_bf16)
+        npj = sh.n_proj
+        xb3 = self.x1b.view(B, 1, sh.D)
         for l in range(sh.layers):
             P1 = self.P1
-            G.gdn_linear(self.x1b, self.W_in[l], C=P1.view(B, sh.n_in), stream=stream)
-            G.gdn_layer_prep(P1, self.root1, self.conv_w[l], self.hist[l], self.q1, self.k1,
-                             self.v1, self.beta1, self.g1, gate_shift=self.gate_shift,
-                             stream=stream)
+            G.gdn_linear(self.x1b, self.W_in[l], C=P1.view(B, npj), w_layout=PK, stream=stream)
+            G.gdn_layer_prep(P1, xb3, self.W_ab[l], self.root1, self.conv_w[l],
+                             self.hist[l], self.q1, self.k1, self.v1, self.beta1, self.g1,
+                             gate_shift=self.gate_shift, stream=stream)
             G.gdn_conv_commit(P1, self.root1, self.zero1, self.hist[l], stream=stream)
             G.gdn_decode_step(self.S[l], self.q1.view(B, sh.H, sh.dk), self.k1.view(B, sh.H, sh.dk),
                               self.v1.view(B, sh.H, sh.dv), self.beta1.view(B, sh.H),
                               self.g1.view(B, sh.H), self.out1, stream=stream)
-            G.gdn_gate_merge(self.out1.view(B, sh.H * sh.dv), P1.view(B, sh.n_in)[:, g0:g1],
+            G.gdn_gate_merge(self.out1.view(B, sh.H * sh.dv), P1.view(B, npj)[:, g0:g1],
                              self.Y1, stream=stream)
             G.gdn_linear(self.Y1, self.W_o[l], C=self.x1, R=self.x1, C_bf16=self.x1b,
-                         stream=stream)
+                         w_layout=PK, stream=stream)

@@ -357,8 +357,12 @@ class StackShape:
         return self.H * (2 * self.dk + self.dv)
 
     @property
-    def n_in(self) -> int:  # input projection columns: q^ k^ v^ gate alpha beta
-        return 2 * self.H * self.dk + 2 * self.H * self.dv + 2 * self.H
+    def n_proj(self) -> int:  # input projection columns q^ k^ v^ gate
+        return 2 * self.H * (self.dk + self.dv)
+
+    @property
+    def n_in(self) -> int:  # all input projection rows: q^ k^ v^ gate, then alpha, beta
+        return self.n_proj + 2 * self.H
 
 
 def stack_layer_weights(shape: StackShape, rng: np.random.Generator):

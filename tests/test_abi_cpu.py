@@ -99,15 +99,15 @@ def test_missing_library_fails_loudly(monkeypatch):
 
 
 def test_layer_scaffold_exports():
-    assert {"gdn_linear", "gdn_layer_prep", "gdn_gate_merge", "gdn_conv_commit",
-            "gdn_decode_step"} <= set(G.declared_functions())
+    assert {"gdn_linear", "gdn_pack_weights", "gdn_layer_prep", "gdn_gate_merge",
+            "gdn_conv_commit", "gdn_decode_step"} <= set(G.declared_functions())
 
 
-@pytest.mark.parametrize("mnk", [(65, 16, 512), (4, 24, 512), (4, 16, 384), (4, 16, 256),
+@pytest.mark.parametrize("mnk", [(65, 16, 512), (4, 24, 512), (4, 16, 384), (4, 16, 128),
                                  (-1, 16, 512), (4, 16, 131072)])
 def test_linear_bad_sizes_rejected(mnk):
     P = ctypes.c_void_p(4096)
-    assert G.lib().gdn_linear(*mnk, P, P, None, P, None, None) == G.GDN_ERR_SHAPE
+    assert G.lib().gdn_linear(*mnk, P, P, 0, None, P, None, None) == G.GDN_ERR_SHAPE
     assert "unsupported sizes" in G.gdn_last_error()
 
 
@@ -115,21 +115,32 @@ def test_layer_scaffold_bad_arguments_rejected():
     L = G.lib()
     P = ctypes.c_void_p(4096)
     odd = ctypes.c_void_p(4096 + 4)
-    assert L.gdn_linear(4, 16, 512, P, P, None, None, None, None) == G.GDN_ERR_ARG
+    assert L.gdn_linear(4, 16, 512, P, P, 0, None, None, None, None) == G.GDN_ERR_ARG
     assert "both NULL" in G.gdn_last_error()
-    assert L.gdn_linear(4, 16, 512, None, P, None, P, None, None) == G.GDN_ERR_ARG
-    assert L.gdn_linear(4, 16, 512, P, odd, None, P, None, None) == G.GDN_ERR_ARG
-    assert L.gdn_linear(0, 16, 512, None, None, None, P, None, None) == G.GDN_OK
-    # prep: sizes follow the verifier's limits; gate_shift must be finite
-    assert L.gdn_layer_prep(1, 65, 8, 256, 256, P, P, P, P, 2.0, P, P, P, P, P,
+    assert L.gdn_linear(4, 16, 512, None, P, 0, None, P, None, None) == G.GDN_ERR_ARG
+    assert L.gdn_linear(4, 16, 512, P, odd, 0, None, P, None, None) == G.GDN_ERR_ARG
+    assert L.gdn_linear(4, 16, 512, P, P, 2, None, P, None, None) == G.GDN_ERR_ARG
+    assert "w_layout" in G.gdn_last_error()
+    assert L.gdn_linear(0, 16, 512, None, None, 1, None, P, None, None) == G.GDN_OK
+    assert L.gdn_pack_weights(24, 512, P, P, None) == G.GDN_ERR_SHAPE
+    assert L.gdn_pack_weights(16, 512, P, ctypes.c_void_p(4096 + 1024), None) == G.GDN_ERR_ARG
+    assert "overlap" in G.gdn_last_error()
+    # prep: sizes follow the verifier's limits; D % 8 == 0; gate_shift must be finite
+    assert L.gdn_layer_prep(1, 65, 8, 256, 256, 2048, P, P, P, P, P, P, 2.0, P, P, P, P, P,
                             None) == G.GDN_ERR_SHAPE
-    assert L.gdn_layer_prep(1, 8, 8, 256, 256, P, P, P, P, float("inf"), P, P, P, P, P,
-                            None) == G.GDN_ERR_ARG
-    assert L.gdn_layer_prep(1, 8, 8, 256, 256, P, P, None, P, 2.0, P, P, P, P, P,
+    assert L.gdn_layer_prep(1, 8, 8, 256, 256, 2044, P, P, P, P, P, P, 2.0, P, P, P, P, P,
+                            None) == G.GDN_ERR_SHAPE
+    assert "hidden width" in G.gdn_last_error()
+    assert L.gdn_layer_prep(1, 8, 8, 256, 256, 2048, P, P, P, P, P, P, float("inf"), P, P, P,
+                            P, P, None) == G.GDN_ERR_ARG
+    assert L.gdn_layer_prep(1, 8, 8, 256, 256, 2048, P, P, P, P, None, P, 2.0, P, P, P, P, P,
                             None) == G.GDN_ERR_ARG
     assert "conv_w is NULL" in G.gdn_last_error()
-    assert L.gdn_layer_prep(0, 8, 8, 256, 256, None, None, None, None, 2.0, None, None, None,
-                            None, None, None) == G.GDN_OK
+    assert L.gdn_layer_prep(1, 8, 8, 256, 256, 2048, P, P, None, P, P, P, 2.0, P, P, P, P, P,
+                            None) == G.GDN_ERR_ARG
+    assert "W_ab is NULL" in G.gdn_last_error()
+    assert L.gdn_layer_prep(0, 8, 8, 256, 256, 2048, None, None, None, None, None, None, 2.0,
+                            None, None, None, None, None, None) == G.GDN_OK
     # gate merge
     assert L.gdn_gate_merge(4, 6, P, P, 8, P, None) == G.GDN_ERR_SHAPE
     assert L.gdn_gate_merge(4, 8, P, P, 4, P, None) == G.GDN_ERR_SHAPE

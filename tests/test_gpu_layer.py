@@ -72,25 +72,51 @@ def assert_bf16_close(gpu_bits, ref, slack):
 # gdn_linear
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M,Nc,K", [(1, 16, 512), (5, 48, 512), (16, 64, 1024), (33, 80, 512),
-                                    (64, 32, 1536), (32, 2048, 2048), (32, 8208, 2048),
-                                    (1, 8208, 2048)])
+@pytest.mark.parametrize("M,Nc,K", [(1, 16, 512), (5, 48, 512), (16, 64, 1024), (33, 80, 256),
+                                    (64, 32, 1536), (32, 2048, 2048), (32, 8192, 2048),
+                                    (1, 8192, 2048), (7, 8208, 2048), (40, 96, 4096)])
 @pytest.mark.parametrize("resid", [False, True])
 def test_linear_matches_oracle(M, Nc, K, resid):
+    """Both weight layouts, every kernel form (all-in-flight for K = 256,
+    512, 1024, 2048; the pipelined loop for 1536 and 4096), ragged M and Nc."""
     rng = np.random.default_rng(M * 100003 + Nc * 7 + K + resid)
     A = W.f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
     Wt = W.f32_to_bf16_bits(rng.standard_normal((Nc, K), dtype=np.float32) * np.float32(K ** -0.5))
     R = rng.standard_normal((M, Nc)).astype(np.float32) if resid else None
     ref = LY.linear(wide(A), wide(Wt), resid=R)
-    C = torch.full((M, Nc), float("nan"), device=DEV)
-    Cb = torch.empty((M, Nc), dtype=torch.bfloat16, device=DEV)
-    G.gdn_linear(bf(A), bf(Wt), C=C, R=f32(R) if resid else None, C_bf16=Cb)
+    Wd = bf(Wt)
+    Wp = torch.empty_like(Wd)
+    G.gdn_pack_weights(Wd, Wp)
+    outs = []
+    for Wx, layout in ((Wd, G.GDN_W_ROWS), (Wp, G.GDN_W_PACKED)):
+        C = torch.full((M, Nc), float("nan"), device=DEV)
+        Cb = torch.empty((M, Nc), dtype=torch.bfloat16, device=DEV)
+        G.gdn_linear(bf(A), Wx, C=C, R=f32(R) if resid else None, C_bf16=Cb, w_layout=layout)
+        outs.append((C, Cb))
     torch.cuda.synchronize()
-    c = C.cpu().numpy()
+    c = outs[0][0].cpu().numpy()
     assert rel(c, ref) <= 1e-5
     # the bf16 copy is C rounded to nearest even
-    np.testing.assert_array_equal(bits_of(Cb), W.f32_to_bf16_bits(c))
-    assert_bf16_close(bits_of(Cb), ref, 1e-5)
+    np.testing.assert_array_equal(bits_of(outs[0][1]), W.f32_to_bf16_bits(c))
+    assert_bf16_close(bits_of(outs[0][1]), ref, 1e-5)
+    # the packed layout gives bitwise the same results
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_pack_weights_layout():
+    """Packed chunk (tile t, k-step s, lane l) holds W[16 t + l % 16][32 s + 8 (l // 16) + e]."""
+    rng = np.random.default_rng(17)
+    Nc, K = 48, 512
+    Wt = rng.integers(0, 1 << 16, size=(Nc, K), dtype=np.uint16)
+    Wp = torch.empty((Nc, K), dtype=torch.bfloat16, device=DEV)
+    G.gdn_pack_weights(bf(Wt), Wp)
+    torch.cuda.synchronize()
+    got = bits_of(Wp).reshape(Nc // 16, K // 32, 64, 8)
+    l = np.arange(64)
+    for t in range(Nc // 16):
+        for s_ in range(K // 32):
+            want = np.stack([Wt[16 * t + l % 16, 32 * s_ + 8 * (l // 16) + e] for e in range(8)], 1)
+            np.testing.assert_array_equal(got[t, s_], want)
 
 
 def test_linear_in_place_residual_and_bitwise_repeat():
@@ -120,16 +146,19 @@ def _topology(kind, N, rng):
             "chain": lambda: W.chain_parents(N)}[kind]()
 
 
-@pytest.mark.parametrize("B,N,H,dk,dv,topo", [(1, 32, 8, 256, 256, "window"),
-                                              (2, 64, 2, 64, 32, "branching"),
-                                              (2, 7, 3, 40, 24, "random"),
-                                              (3, 1, 2, 16, 8, "chain"),
-                                              (1, 12, 1, 256, 256, "chain")])
-def test_layer_prep_matches_oracle(B, N, H, dk, dv, topo):
+@pytest.mark.parametrize("B,N,H,dk,dv,D,topo", [(1, 32, 8, 256, 256, 2048, "window"),
+                                                (2, 64, 2, 64, 32, 72, "branching"),
+                                                (2, 7, 3, 40, 24, 4104, "random"),
+                                                (3, 1, 2, 16, 8, 8, "chain"),
+                                                (1, 12, 1, 256, 256, 512, "chain")])
+def test_layer_prep_matches_oracle(B, N, H, dk, dv, D, topo):
     rng = np.random.default_rng(B * 1000 + N * 10 + H)
-    ldP = 2 * H * dk + 2 * H * dv + 2 * H
+    npj = 2 * H * (dk + dv)
     Cc = H * (2 * dk + dv)
-    P = rng.standard_normal((B, N, ldP)).astype(np.float32)
+    P = rng.standard_normal((B, N, npj)).astype(np.float32)
+    x = W.f32_to_bf16_bits(rng.standard_normal((B, N, D), dtype=np.float32))
+    W_ab = W.f32_to_bf16_bits(rng.standard_normal((2 * H, D), dtype=np.float32) *
+                              np.float32(D ** -0.5))
     parents = np.stack([_topology(topo, N, rng) for _ in range(B)]).astype(np.int32)
     conv_w = (0.5 * rng.standard_normal((Cc, 4))).astype(np.float32)
     hist = rng.standard_normal((B, 3, Cc)).astype(np.float32)
@@ -138,16 +167,19 @@ def test_layer_prep_matches_oracle(B, N, H, dk, dv, topo):
     v = torch.empty((B, N, H, dv), dtype=torch.bfloat16, device=DEV)
     beta = torch.full((B, N, H), float("nan"), device=DEV)
     g = torch.full((B, N, H), float("nan"), device=DEV)
-    G.gdn_layer_prep(f32(P), i32(parents), f32(conv_w), f32(hist), q, k, v, beta, g,
-                     gate_shift=2.0)
+    G.gdn_layer_prep(f32(P), bf(x), bf(W_ab), i32(parents), f32(conv_w), f32(hist), q, k, v,
+                     beta, g, gate_shift=2.0)
     torch.cuda.synchronize()
     for b in range(B):
-        rq, rk, rv, rb, rg, _ = LY.layer_prep(P[b], parents[b], conv_w, hist[b], H, dk, dv, 2.0)
+        # the oracle's projection output: the given columns, then the logits x . W_ab
+        P_full = np.concatenate([P[b].astype(np.float64), LY.linear(wide(x[b]), wide(W_ab))], 1)
+        rq, rk, rv, rb, rg, _ = LY.layer_prep(P_full, parents[b], conv_w, hist[b], H, dk, dv, 2.0)
         assert_bf16_close(bits_of(q[b]), rq, 2e-6)
         assert_bf16_close(bits_of(k[b]), rk, 2e-6)
         assert_bf16_close(bits_of(v[b]), rv, 2e-6)
-        np.testing.assert_allclose(beta[b].cpu().numpy(), rb, rtol=4e-6, atol=0)
-        np.testing.assert_allclose(g[b].cpu().numpy(), rg, rtol=4e-6, atol=1e-7)
+        # FP32 dot products of length D feed the logits
+        np.testing.assert_allclose(beta[b].cpu().numpy(), rb, rtol=2e-5, atol=1e-6)
+        np.testing.assert_allclose(g[b].cpu().numpy(), rg, rtol=2e-5, atol=1e-6)
 
 
 # ---------------------------------------------------------------------------
