@@ -37,7 +37,8 @@ HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 CSRC = os.path.join(ROOT, "linear_attention_gdn_amd", "csrc")
 KERNEL_SOURCES = {"gdn_chain_verify": "chain_verify.hip", "gdn_tree_verify": "tree_verify.hip",
-                  "gdn_commit_path": "commit.hip", "gdn_linear": "layer.hip"}
+                  "gdn_commit_path": "commit.hip", "gdn_linear": "layer.hip",
+                  "gdn_chain_verify_delayed": "chain_verify.hip"}
 
 
 def source_digest(kernel: str) -> str:
@@ -109,6 +110,20 @@ def bytes_commit(d: W.Draft, plens: np.ndarray) -> float:
     return tot + B * 4
 
 
+def bytes_delayed(d: W.Draft, plens: np.ndarray) -> float:
+    """Algorithmic bytes of one delayed-commit verification: the verification's
+    own bytes, plus, for every sequence with a non-empty accepted path, the
+    state written back once and the path's u', k and G read from the previous
+    record (the state read is shared with the verification)."""
+    es = 2 if d.dtype == "bf16" else 4
+    B, N, H, dk, dv = d.B, d.N, d.H, d.dk, d.dv
+    tot = float(bytes_verify(d, False)) + B * N * 8 + B * 4
+    for n in plens:
+        if n > 0:
+            tot += H * dv * dk * 4 + H * n * (dv * 4 + dk * es + 4)
+    return tot
+
+
 def draw_lasts(d: W.Draft, rng, count: int, chain: bool) -> np.ndarray:
     out = np.empty((count, d.B), dtype=np.int32)
     for i in range(count):
@@ -158,6 +173,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--separate-commit", action="store_true",
+                    help="chain workloads: verify and commit as two launches per step instead "
+                         "of the delayed commit fused into the next verification")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -213,10 +231,33 @@ def main():
     def commit(i):
         G.gdn_commit_path(states[i % R], rec, lasts[i])
 
+    # Delayed commit (chain workloads): step i commits, on state i % R, the
+    # draft that state verified on its previous visit (accepted node
+    # lasts[i]) and verifies the new draft, in one launch.  Each state keeps
+    # two record slots used alternately.
+    delayed = chain and not args.separate_commit
+    if delayed:
+        recs = [[G.FactorRecord.empty(B, N, H, dk, dv, code, device=dev) for _ in range(2)]
+                for _ in range(R)]
+        for j in range(R):  # every state's "previous visit": a plain verify
+            G.gdn_chain_verify(states[j], q, k, v, beta, g, out, recs[j][1])
+        torch.cuda.synchronize()
+
+    def fused(i):
+        j, vis = i % R, i // R
+        G.gdn_chain_verify_delayed(states[j], recs[j][(vis + 1) % 2], lasts[i], q, k, v, beta, g,
+                                   out, recs[j][vis % 2])
+
+    def step(i):
+        if delayed:
+            fused(i)
+        else:
+            verify(i)
+            commit(i)
+
     # warmup (eager)
     for i in range(args.warmup):
-        verify(i)
-        commit(i)
+        step(i)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -225,8 +266,7 @@ def main():
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in timed:
-            verify(i)
-            commit(i)
+            step(i)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     else:
@@ -236,8 +276,7 @@ def main():
         with torch.cuda.stream(s):
             with torch.cuda.graph(graph, stream=s):
                 for i in timed:
-                    verify(i)
-                    commit(i)
+                    step(i)
         stream.wait_stream(s)
         graph.replay()  # first replay uploads the graph; not timed
         torch.cuda.synchronize()
@@ -301,6 +340,13 @@ def main():
         flops = 4.0 * B * H * N * dk * dv
         kernels["verify"]["fp32_equiv_tflops"] = float(flops / (t_ver.mean() * 1e-3) / 1e12)
     dom = "verify" if t_ver.mean() >= t_com.mean() else "commit"
+    if delayed:
+        t_fus = graph_time(fused)
+        b_fus = np.mean([bytes_delayed(d, p) for p in plens])
+        kernels["verify_delayed"] = {"name": "gdn_chain_verify_delayed",
+                                     "avg_us": float(t_fus * 1e3), "bytes": float(b_fus),
+                                     "gbs": float(b_fus / (t_fus * 1e-3) / 1e9)}
+        dom = "verify_delayed"  # the only kernel of the timed step
     kd = kernels[dom]
     roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
@@ -327,6 +373,8 @@ def main():
         "config": {"workload": d.name, "B": B, "N": N, "H": H, "dk": dk, "dv": dv,
                    "qkv_dtype": d.dtype, "state_dtype": "f32", "rotating_states": R,
                    "timing": "eager" if args.no_graph else "hip_graph",
+                   "commit": "delayed, fused into the next verification" if delayed
+                             else "separate launch after each verification",
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "kernels": kernels,

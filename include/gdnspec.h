@@ -170,6 +170,39 @@ int gdn_commit_path(int B, int N, int H, int dk, int dv, int qkv_dtype, float* S
                     const void* factors, const int32_t* last_accepted, int32_t* path_out,
                     int32_t* path_len_out, int32_t* dev_status, void* stream);
 
+/*
+ * gdn_chain_verify_delayed - the delayed commit fused into the next
+ * verification (review: Referee Report summary, mechanism (ii); Figures,
+ * Figure 7 caption, right side; paper Section 5): the accepted-factor buffer
+ * of the previous draft is applied inside the next verification kernel, on
+ * the state tiles it loads anyway, so the commit costs no state round trip of
+ * its own.  Equivalent to
+ *     gdn_commit_path(B, N_prev, H, dk, dv, qkv_dtype, S, prev_factors,
+ *                     last_accepted, NULL, NULL, dev_status, stream);
+ *     gdn_chain_verify(B, N, H, dk, dv, qkv_dtype, S, q, k, v, beta, g,
+ *                      scale, out, factors, stream);
+ * and bitwise identical to them: each workgroup reads its state tile once,
+ * applies the accepted path in the commit's operation order, writes the tile
+ * back and verifies the new chain from registers.
+ *   S             [B][H][dv][dk] float32, in place: on entry the state the
+ *                 previous verification started from; on return the state
+ *                 after its accepted path
+ *   prev_factors  the previous verification's record, written with
+ *                 (B, N_prev, H, dk, dv, qkv_dtype), 1 <= N_prev <= 64
+ *   last_accepted [B] int32, -1 <= last < N_prev (-1: nothing to commit)
+ *   dev_status    optional [B] int32: GDN_OK, or GDN_ERR_TOPOLOGY when
+ *                 last_accepted is out of range or the previous record's
+ *                 topology was rejected; that sequence's state is then left
+ *                 as it was and the new chain is verified from it
+ *   factors       the new record; must not overlap prev_factors
+ *   other arguments as for gdn_chain_verify
+ */
+int gdn_chain_verify_delayed(int B, int N_prev, int N, int H, int dk, int dv, int qkv_dtype,
+                             float* S, const void* prev_factors, const int32_t* last_accepted,
+                             int32_t* dev_status, const void* q, const void* k, const void* v,
+                             const float* beta, const float* g, float scale, float* out,
+                             void* factors, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

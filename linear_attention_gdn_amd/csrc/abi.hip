@@ -11,10 +11,11 @@
 #include "../../include/gdnlayer.h"
 
 namespace gdn {
-hipError_t launch_chain_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
+hipError_t launch_chain_verify(int B, int N, int H, int dk, int dv, int dtype, float* S0,
                                const void* q, const void* k, const void* v, const float* beta,
                                const float* g, float scale, float* out, void* factors,
-                               hipStream_t stream);
+                               const void* prev_factors, int Np, const int32_t* last,
+                               int32_t* dev_status, hipStream_t stream);
 hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
                               const int32_t* parents, const void* q, const void* k,
                               const void* v, const float* beta, const float* g, float scale,
@@ -184,8 +185,46 @@ int gdn_chain_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const f
   GDN_TRY(check_ptr4(fn, "g", g, true));
   GDN_TRY(check_ptr(fn, "out", out, true));
   GDN_TRY(check_ptr(fn, "factors", factors, true));
-  return hip_status(fn, gdn::launch_chain_verify(B, N, H, dk, dv, qkv_dtype, S0, q, k, v, beta,
-                                                 g, scale, out, factors,
+  return hip_status(fn, gdn::launch_chain_verify(B, N, H, dk, dv, qkv_dtype,
+                                                 const_cast<float*>(S0), q, k, v, beta, g,
+                                                 scale, out, factors, nullptr, 0, nullptr,
+                                                 nullptr, static_cast<hipStream_t>(stream)));
+}
+
+int gdn_chain_verify_delayed(int B, int N_prev, int N, int H, int dk, int dv, int qkv_dtype,
+                             float* S, const void* prev_factors, const int32_t* last_accepted,
+                             int32_t* dev_status, const void* q, const void* k, const void* v,
+                             const float* beta, const float* g, float scale, float* out,
+                             void* factors, void* stream) {
+  const char* fn = "gdn_chain_verify_delayed";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  if (N_prev < 1 || N_prev > gdn::kMaxNodes)
+    return fail(GDN_ERR_SHAPE, "%s: N_prev=%d outside 1..64", fn, N_prev);
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (!std::isfinite(scale)) return fail(GDN_ERR_ARG, "%s: scale is not finite", fn);
+  if (B == 0) return ok();
+  if (N == 0)
+    return fail(GDN_ERR_SHAPE, "%s: N=0; use gdn_commit_path to commit without verifying", fn);
+  GDN_TRY(check_ptr(fn, "S", S, true));
+  GDN_TRY(check_ptr(fn, "prev_factors", prev_factors, true));
+  GDN_TRY(check_ptr4(fn, "last_accepted", last_accepted, true));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr(fn, "out", out, true));
+  GDN_TRY(check_ptr(fn, "factors", factors, true));
+  const char* a0 = static_cast<const char*>(prev_factors);
+  const char* b0 = static_cast<const char*>(factors);
+  const size_t na = gdn::record_layout(B, N_prev, H, dk, dv, qkv_dtype).total;
+  const size_t nb = gdn::record_layout(B, N, H, dk, dv, qkv_dtype).total;
+  if (a0 < b0 + nb && b0 < a0 + na)
+    return fail(GDN_ERR_ARG, "%s: factors and prev_factors overlap", fn);
+  return hip_status(fn, gdn::launch_chain_verify(B, N, H, dk, dv, qkv_dtype, S, q, k, v, beta, g,
+                                                 scale, out, factors, prev_factors, N_prev,
+                                                 last_accepted, dev_status,
                                                  static_cast<hipStream_t>(stream)));
 }
 

@@ -21,29 +21,44 @@
 // beta) is staged in LDS by one round of loads that overlaps the state-tile
 // load; the loop then touches only registers and LDS, reading the next
 // step's k and q while the current step computes.
+//
+// Delayed commit (review: Referee Report summary, mechanism (ii); Figure 7
+// caption, right side): with DLY the same workgroup first applies the
+// previous draft's accepted path to its state tile, using the previous factor
+// record staged in LDS in the same round of loads, writes the tile back, and
+// then verifies the new chain from the updated registers.  The update repeats
+// the commit kernel's operations in the same order (scale by e^{G_last}, then
+// one fused multiply-add per path node in node order), so the result is
+// bitwise that of commit followed by verify.
 #include "gdn_common.h"
 
 namespace gdn {
 
 constexpr int kChainRows = 8;  // state rows per workgroup (one per half-wave)
 
-template <typename T>
+template <typename T, bool DLY>
 __global__ __launch_bounds__(256) void chain_verify_kernel(
-    int N, int H, int dk, int dv, int ntiles, const float* __restrict__ S0,
+    int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ g, float scale,
-    float* __restrict__ out, Record<T> rec) {
+    float* __restrict__ out, Record<T> rec, Record<T> prev, int Np,
+    const int32_t* __restrict__ last_acc, int32_t* __restrict__ dev_status) {
   constexpr int MC = kMaxDim / 128;  // float4 chunks per lane
   using R4 = typename Raw4<T>::type;
-  // dynamic LDS: k, q as loaded [N][dk], v [N][8], alpha, beta, g [N]
+  // dynamic LDS: k, q as loaded [N][dk], v [N][8], alpha, beta, g [N];
+  // with DLY also the previous record's k [Np][dk], u' of the tile's rows
+  // [Np][8] and the commit coefficients e^{G_last - G_i} [Np]
   extern __shared__ f32x4 lds4[];
   const int cpr = dk / 4;
   R4* sk = reinterpret_cast<R4*>(lds4);
   R4* sq = sk + N * cpr;
-  float* sv = reinterpret_cast<float*>(sq + N * cpr);
+  R4* skp = sq + N * cpr;
+  float* sv = reinterpret_cast<float*>(skp + (DLY ? Np * cpr : 0));
   float* salpha = sv + N * kChainRows;
   float* sbeta = salpha + N;
   float* sG = sbeta + N;
+  float* sup = sG + N;
+  float* sGp = sup + (DLY ? Np * kChainRows : 0);
 
   const int tid = threadIdx.x;
   const int s = tid & 31;             // lane within the row's half-wave
@@ -74,9 +89,37 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
 #pragma unroll
     for (int m = 0; m < MC; ++m) Sx[m] = load4(rp + clampi(128 * m + 4 * s, dk - 4));
   }
+  // the previous draft's record (delayed commit): masks, G, u' of this tile's
+  // rows and the k rows, none of which depends on last_accepted
+  constexpr int BATCH = 4;
+  int last = -1;
+  uint64_t mlp = 0;
+  float glp = 0.f;
+  float upb[DLY ? VB : 1];
+  R4 kpb[DLY ? BATCH : 1];
+  auto prevk_off = [&](int idx) {
+    idx = clampi(idx, Np * cpr - 1);
+    return ((size_t)bh * Np + idx / cpr) * dk + 4 * (idx % cpr);
+  };
+  int last_v = -1;
+  uint64_t pm_r = 0;   // accepted path of the previous draft (bit i: node i)
+  float Glast_r = 0.f;
+  if (DLY) {
+    last_v = last_acc[b];  // a vector load: it joins this round instead of a later scalar one
+    const int tcp = clampi(tid & 63, Np - 1);  // every wave holds node j's mask and G in lane j
+    mlp = prev.mask[(size_t)b * Np + tcp];
+    glp = prev.G[(size_t)bh * Np + tcp];
+#pragma unroll
+    for (int x = 0; x < VB; ++x) {
+      const int idx = clampi(tid + 256 * x, Np * kChainRows - 1);
+      const int r = clampi(r0 + idx % kChainRows, dv - 1);
+      upb[x] = prev.up[((size_t)bh * Np + idx / kChainRows) * dv + r];
+    }
+#pragma unroll
+    for (int x = 0; x < BATCH; ++x) kpb[x] = raw4(prev.K + prevk_off(tid + 256 * x));
+  }
   // k and q rows: the first batch is straight-line code (a loop here would
   // drain every outstanding load at its header); larger drafts loop.
-  constexpr int BATCH = 4;
   auto stage = [&](int base) {
     R4 kb[BATCH], qb[BATCH];
 #pragma unroll
@@ -97,6 +140,19 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
   };
   stage(tid);
   for (int base = tid + 256 * BATCH; base < N * cpr; base += 256 * BATCH) stage(base);
+  if (DLY) {
+#pragma unroll
+    for (int x = 0; x < BATCH; ++x)
+      if (tid + 256 * x < Np * cpr) skp[tid + 256 * x] = kpb[x];
+    for (int base = tid + 256 * BATCH; base < Np * cpr; base += 256 * BATCH) {
+      R4 kb[BATCH];
+#pragma unroll
+      for (int x = 0; x < BATCH; ++x) kb[x] = raw4(prev.K + prevk_off(base + 256 * x));
+#pragma unroll
+      for (int x = 0; x < BATCH; ++x)
+        if (base + 256 * x < Np * cpr) skp[base + 256 * x] = kb[x];
+    }
+  }
 #pragma unroll
   for (int x = 0; x < VB; ++x) {
     const int idx = tid + 256 * x;
@@ -106,6 +162,24 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
     salpha[tid] = expf(gl);
     sbeta[tid] = bl;
     sG[tid] = gl;
+  }
+  if (DLY) {
+    // the accepted path and each node's coefficient e^{G_last - G_i}, one lane
+    // per node (the same expression the commit kernel evaluates)
+    last = __builtin_amdgcn_readfirstlane(last_v);
+    const bool in_rng = last >= 0 && last < Np;
+    const int lc = in_rng ? last : 0;
+    const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)mlp, lc);
+    const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(mlp >> 32), lc);
+    const uint64_t valid = Np >= 64 ? ~0ull : ((1ull << Np) - 1ull);
+    pm_r = in_rng ? ((((uint64_t)mhi << 32) | mlo) & valid) : 0ull;
+    Glast_r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, glp), lc));
+    if (tid < Np) sGp[tid] = ((pm_r >> tid) & 1ull) ? expf(Glast_r - glp) : 0.f;
+#pragma unroll
+    for (int x = 0; x < VB; ++x) {
+      const int idx = tid + 256 * x;
+      if (idx < Np * kChainRows) sup[idx] = (r0 + idx % kChainRows < dv) ? upb[x] : 0.f;
+    }
   }
   float S[MC][4];
 #pragma unroll
@@ -117,6 +191,41 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
     S[m][3] = x.w;
   }
   __syncthreads();
+
+  if (DLY) {
+    // ---- the previous draft's accepted path: S <- e^{G_last} S + sum c_i u'_i k_i^T
+    const uint64_t pm = pm_r;
+    const bool okp = last >= 0 && last < Np && ((pm >> last) & 1ull);
+    if (dev_status && tile == 0 && h == 0 && tid == 0)
+      dev_status[b] = (last == -1 || okp) ? GDN_OK : GDN_ERR_TOPOLOGY;
+    if (okp) {  // uniform
+      const float s0 = expf(Glast_r);
+#pragma unroll
+      for (int m = 0; m < MC; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[m][e] = S[m][e] * s0;
+      for (int i = 0; i <= last; ++i) {
+        if (((pm >> i) & 1ull) == 0ull) continue;  // uniform
+        const float c = sGp[i] * sup[i * kChainRows + rl];
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+          const f32x4 kc = widen4(skp[i * cpr + clampi(32 * m + s, cpr - 1)]);
+          S[m][0] = fmaf(c, kc.x, S[m][0]);
+          S[m][1] = fmaf(c, kc.y, S[m][1]);
+          S[m][2] = fmaf(c, kc.z, S[m][2]);
+          S[m][3] = fmaf(c, kc.w, S[m][3]);
+        }
+      }
+      if (rok) {
+        float* wp = S0 + ((size_t)bh * dv + row) * dk;
+#pragma unroll
+        for (int m = 0; m < MC; ++m)
+          if (128 * m + 4 * s < dk)
+            *reinterpret_cast<f32x4*>(wp + 128 * m + 4 * s) =
+                f32x4{S[m][0], S[m][1], S[m][2], S[m][3]};
+      }
+    }
+  }
 
   // k_t, q_t (widened) for step t; the next step's are read from LDS while
   // the current step computes.
@@ -196,31 +305,44 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
 }
 
 template <typename T>
-hipError_t launch_chain_verify_t(int B, int N, int H, int dk, int dv, const float* S0,
-                                 const void* q, const void* k, const void* v,
-                                 const float* beta, const float* g, float scale, float* out,
-                                 void* factors, const RecordLayout& L, hipStream_t stream) {
+hipError_t launch_chain_verify_t(int B, int N, int H, int dk, int dv, float* S0, const void* q,
+                                 const void* k, const void* v, const float* beta,
+                                 const float* g, float scale, float* out, void* factors,
+                                 const RecordLayout& L, const void* prev_factors, int Np,
+                                 const int32_t* last, int32_t* dev_status, hipStream_t stream) {
   Record<T> rec = record_views<T>(factors, L);
   const int ntiles = (dv + kChainRows - 1) / kChainRows;
   const long grid = (long)B * H * ntiles;
-  const size_t lds =
+  size_t lds =
       (size_t)N * dk * sizeof(T) * 2 + (size_t)N * kChainRows * 4 + (size_t)N * 4 * 3;
-  hipLaunchKernelGGL((chain_verify_kernel<T>), dim3((unsigned)grid), dim3(256), lds, stream, N,
-                     H, dk, dv, ntiles, S0, static_cast<const T*>(q), static_cast<const T*>(k),
-                     static_cast<const T*>(v), beta, g, scale, out, rec);
+  if (prev_factors) {
+    const RecordLayout Lp = record_layout(B, Np, H, dk, dv, sizeof(T) == 2 ? GDN_BF16 : GDN_F32);
+    Record<T> prev = record_views<T>(const_cast<void*>(prev_factors), Lp);
+    lds += (size_t)Np * dk * sizeof(T) + (size_t)Np * kChainRows * 4 + (size_t)Np * 4;
+    hipLaunchKernelGGL((chain_verify_kernel<T, true>), dim3((unsigned)grid), dim3(256), lds,
+                       stream, N, H, dk, dv, ntiles, S0, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), beta, g, scale, out,
+                       rec, prev, Np, last, dev_status);
+  } else {
+    hipLaunchKernelGGL((chain_verify_kernel<T, false>), dim3((unsigned)grid), dim3(256), lds,
+                       stream, N, H, dk, dv, ntiles, S0, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), beta, g, scale, out,
+                       rec, Record<T>{}, 0, nullptr, nullptr);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_chain_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
+hipError_t launch_chain_verify(int B, int N, int H, int dk, int dv, int dtype, float* S0,
                                const void* q, const void* k, const void* v, const float* beta,
                                const float* g, float scale, float* out, void* factors,
-                               hipStream_t stream) {
+                               const void* prev_factors, int Np, const int32_t* last,
+                               int32_t* dev_status, hipStream_t stream) {
   const RecordLayout L = record_layout(B, N, H, dk, dv, dtype);
   if (dtype == GDN_BF16)
     return launch_chain_verify_t<bf16_t>(B, N, H, dk, dv, S0, q, k, v, beta, g, scale, out,
-                                         factors, L, stream);
+                                         factors, L, prev_factors, Np, last, dev_status, stream);
   return launch_chain_verify_t<float>(B, N, H, dk, dv, S0, q, k, v, beta, g, scale, out,
-                                      factors, L, stream);
+                                      factors, L, prev_factors, Np, last, dev_status, stream);
 }
 
 }  // namespace gdn

@@ -1,0 +1,98 @@
+"""GPU checks of the delayed commit fused into the next verification
+(gdn_chain_verify_delayed): bitwise equal to gdn_commit_path followed by the
+plain verification, for previous records written from chains and from
+trees, and close to the oracle's commit-then-verify."""
+
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_gdn_amd import gdnspec as G
+from linear_attention_gdn_amd import workloads as W
+from oracle import oracle as O
+
+from _gpu import TOL_OUT, TOL_STATE, code_of, dev_tensors, run_chain, run_tree, slice_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _lasts(prev: W.Draft, rng):
+    B, Np = prev.B, prev.N
+    cases = [np.full(B, -1), np.full(B, Np - 1), prev.last_accepted.copy()]
+    cases.append(np.array([int(rng.integers(-1, Np)) for _ in range(B)]))
+    bad = prev.last_accepted.copy()
+    bad[0] = Np  # out of range: that sequence is not committed
+    cases.append(bad)
+    return [c.astype(np.int32) for c in cases]
+
+
+@pytest.mark.parametrize("dtype,B,Np,N,H,dk,dv,prev_topo", [
+    ("bf16", 1, 8, 8, 8, 256, 256, "chain"),
+    ("bf16", 2, 12, 5, 3, 64, 24, "random"),
+    ("f32", 2, 7, 9, 2, 40, 32, "chain"),
+    ("bf16", 3, 64, 16, 2, 256, 64, "branching"),
+    ("bf16", 1, 1, 3, 1, 16, 8, "chain"),
+])
+def test_delayed_chain_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo):
+    seed = B * 100 + Np + N
+    accept = "uniform" if prev_topo == "chain" else "leaf_geometric"
+    prev = W.make_draft(B, Np, H, dk, dv, topology=prev_topo, accept=accept, dtype=dtype,
+                        seed=seed)
+    new = W.make_draft(B, N, H, dk, dv, topology="chain", accept="none", dtype=dtype,
+                       seed=seed + 1)
+    if prev_topo == "chain":
+        _, rec_prev, tp = run_chain(prev)
+    else:
+        _, rec_prev, _, st, tp = run_tree(prev)
+        assert (st.cpu().numpy() == G.GDN_OK).all()
+    tn = dev_tensors(new)
+    rng = np.random.default_rng(seed)
+    for last in _lasts(prev, rng):
+        last_t = torch.from_numpy(last).cuda()
+        # two calls
+        S_a = tp["S0"].clone()
+        st_a = torch.full((B,), 77, dtype=torch.int32, device="cuda")
+        G.gdn_commit_path(S_a, rec_prev, last_t, dev_status=st_a)
+        out_a = torch.full((B, N, H, dv), float("nan"), device="cuda")
+        rec_a = G.FactorRecord.empty(B, N, H, dk, dv, code_of(new))
+        rec_a.buf.zero_()
+        G.gdn_chain_verify(S_a, tn["q"], tn["k"], tn["v"], tn["beta"], tn["g"], out_a, rec_a)
+        # one fused call
+        S_b = tp["S0"].clone()
+        st_b = torch.full((B,), 77, dtype=torch.int32, device="cuda")
+        out_b = torch.full((B, N, H, dv), float("nan"), device="cuda")
+        rec_b = G.FactorRecord.empty(B, N, H, dk, dv, code_of(new))
+        rec_b.buf.zero_()
+        G.gdn_chain_verify_delayed(S_b, rec_prev, last_t, tn["q"], tn["k"], tn["v"], tn["beta"],
+                                   tn["g"], out_b, rec_b, dev_status=st_b)
+        torch.cuda.synchronize()
+        assert torch.equal(st_a, st_b), (last, st_a, st_b)
+        assert torch.equal(S_a, S_b), last
+        assert torch.equal(out_a, out_b), last
+        assert torch.equal(rec_a.buf, rec_b.buf), last
+        for b in range(B):
+            ok = -1 <= last[b] < Np
+            assert int(st_b[b]) == (G.GDN_OK if ok else G.GDN_ERR_TOPOLOGY)
+
+
+def test_delayed_chain_verify_matches_oracle():
+    """Commit of a tree path then a chain verification, against the oracle's
+    replay of the same two steps."""
+    prev = W.make_draft(2, 32, 8, 256, 256, topology="window", accept="leaf_geometric",
+                        dtype="bf16", seed=31)
+    new = W.make_draft(2, 8, 8, 256, 256, topology="chain", accept="none", dtype="bf16",
+                       seed=32)
+    _, rec_prev, _, _, tp = run_tree(prev)
+    tn = dev_tensors(new)
+    S = tp["S0"].clone()
+    out = torch.empty(2, 8, 8, 256, device="cuda")
+    rec = G.FactorRecord.empty(2, 8, 8, 256, 256, G.GDN_BF16)
+    G.gdn_chain_verify_delayed(S, rec_prev, tp["last"], tn["q"], tn["k"], tn["v"], tn["beta"],
+                               tn["g"], out, rec)
+    torch.cuda.synchronize()
+    S_ref, _, _ = O.draft_commit(prev)
+    out_ref, _, _ = O.tree_verify(S_ref, new.parents, new.q64(), new.k64(), new.v64(), new.beta,
+                                  new.g, new.scale)
+    assert slice_rel_err(S.cpu().numpy(), S_ref) <= TOL_STATE
+    assert slice_rel_err(out.cpu().numpy().transpose(0, 2, 1, 3),
+                         out_ref.transpose(0, 2, 1, 3)) <= TOL_OUT
