@@ -2,7 +2,7 @@
 
 ``python -m linear_attention_gdn_amd.build`` compiles every ``csrc/*.hip``
 into ``linear_attention_gdn_amd/libgdnspec.so``.  All device code is built
-with packed-FP32 instructions disabled.
+with packed-FP32 instructions disabled and kernel-argument preloading on.
 """
 
 from __future__ import annotations
@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 16 dwords of kernel arguments arrive in SGPRs at wave launch
+    # instead of through a scalar load the first global loads would wait for
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -15,12 +15,16 @@
 // Mapping: 256 threads = 4 waves; each half-wave (32 lanes) owns one state row
 // and lane s of it holds columns 128*m + 4*s + e (m < dk/128, e < 4), so a row
 // is read as 512-byte coalesced runs and dot products reduce over 32 lanes
-// with DPP row rotations plus one v_permlane16_swap.  A workgroup owns 8 rows,
+// with DPP row rotations plus one v_permlane16_swap (or, for y_q, which only
+// the storing lane needs, one DPP row broadcast).  A workgroup owns 8 rows,
 // one per SIMD pair of half-waves, so all four SIMDs of a CU run the serial
-// loop.  Everything the loop needs (k, q as loaded, v of the 8 rows, alpha,
-// beta) is staged in LDS by one round of loads that overlaps the state-tile
-// load; the loop then touches only registers and LDS, reading the next
-// step's k and q while the current step computes.
+// loop.  Everything the loop needs (k, q, v of the 8 rows, alpha, beta) is
+// staged in LDS by one round of loads that overlaps the state-tile load.
+// The loop is bound by VALU issue (one wave per SIMD), so work that does not
+// depend on the row leaves it: k and q are widened to FP32 once while staging
+// (drafts of up to 32 nodes), k_t . q_t is computed once per step for the
+// whole workgroup before the loop, and column masks exist only for d_k < 256.
+// Each step reads the next step's operands from LDS while it computes.
 //
 // Delayed commit (review: Referee Report summary, mechanism (ii); Figure 7
 // caption, right side): with DLY the same workgroup first applies the
@@ -30,13 +34,31 @@
 // the commit kernel's operations in the same order (scale by e^{G_last}, then
 // one fused multiply-add per path node in node order), so the result is
 // bitwise that of commit followed by verify.
+#include <type_traits>
+
 #include "gdn_common.h"
 
 namespace gdn {
 
 constexpr int kChainRows = 8;  // state rows per workgroup (one per half-wave)
 
-template <typename T, bool DLY>
+// Stored form of staged k/q rows: FP32 (QF) or as loaded.
+template <typename T, bool QF>
+struct Staged {
+  using type = typename std::conditional<QF, f32x4, typename Raw4<T>::type>::type;
+};
+__device__ inline f32x4 stage_cvt(const f32x4& x, f32x4*) { return x; }
+__device__ inline f32x4 stage_cvt(const u32x2& x, f32x4*) { return widen4(x); }
+__device__ inline u32x2 stage_cvt(const u32x2& x, u32x2*) { return x; }
+// back to the element type (exact: the values came from T)
+__device__ inline f32x4 unstage(const f32x4& x, float*) { return x; }
+__device__ inline u32x2 unstage(const f32x4& x, bf16_t*) {
+  return u32x2{(__float_as_uint(x.x) >> 16) | (__float_as_uint(x.y) & 0xffff0000u),
+               (__float_as_uint(x.z) >> 16) | (__float_as_uint(x.w) & 0xffff0000u)};
+}
+__device__ inline u32x2 unstage(const u32x2& x, bf16_t*) { return x; }
+
+template <typename T, bool DLY, bool QF, bool FULL>
 __global__ __launch_bounds__(256) void chain_verify_kernel(
     int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -45,19 +67,21 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
     const int32_t* __restrict__ last_acc, int32_t* __restrict__ dev_status) {
   constexpr int MC = kMaxDim / 128;  // float4 chunks per lane
   using R4 = typename Raw4<T>::type;
-  // dynamic LDS: k, q as loaded [N][dk], v [N][8], alpha, beta, g [N];
-  // with DLY also the previous record's k [Np][dk], u' of the tile's rows
-  // [Np][8] and the commit coefficients e^{G_last - G_i} [Np]
+  using SK = typename Staged<T, QF>::type;
+  // dynamic LDS: k, q [N][dk] (staged form), v [N][8], alpha, beta, g, k.q [N];
+  // with DLY also the previous record's k [Np][dk] (as loaded), u' of the
+  // tile's rows [Np][8] and the commit coefficients e^{G_last - G_i} [Np]
   extern __shared__ f32x4 lds4[];
   const int cpr = dk / 4;
-  R4* sk = reinterpret_cast<R4*>(lds4);
-  R4* sq = sk + N * cpr;
-  R4* skp = sq + N * cpr;
+  SK* sk = reinterpret_cast<SK*>(lds4);
+  SK* sq = sk + N * cpr;
+  R4* skp = reinterpret_cast<R4*>(sq + N * cpr);
   float* sv = reinterpret_cast<float*>(skp + (DLY ? Np * cpr : 0));
   float* salpha = sv + N * kChainRows;
   float* sbeta = salpha + N;
   float* sG = sbeta + N;
-  float* sup = sG + N;
+  float* skq = sG + N;
+  float* sup = skq + N;
   float* sGp = sup + (DLY ? Np * kChainRows : 0);
 
   const int tid = threadIdx.x;
@@ -70,6 +94,7 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
   const int r0 = tile * kChainRows;
   const int row = r0 + rl;
   const bool rok = row < dv;
+  auto colok = [&](int m) { return FULL || 128 * m + 4 * s < dk; };
 
   // ---- every global load first (unconditional, clamped), then the LDS writes
   const size_t nhl = ((size_t)b * N + clampi(tid, N - 1)) * H + h;
@@ -93,6 +118,7 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
   // rows and the k rows, none of which depends on last_accepted
   constexpr int BATCH = 4;
   int last = -1;
+  int last_v = -1;
   uint64_t mlp = 0;
   float glp = 0.f;
   float upb[DLY ? VB : 1];
@@ -101,7 +127,6 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
     idx = clampi(idx, Np * cpr - 1);
     return ((size_t)bh * Np + idx / cpr) * dk + 4 * (idx % cpr);
   };
-  int last_v = -1;
   uint64_t pm_r = 0;   // accepted path of the previous draft (bit i: node i)
   float Glast_r = 0.f;
   if (DLY) {
@@ -133,8 +158,8 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
     for (int x = 0; x < BATCH; ++x) {
       const int idx = base + 256 * x;
       if (idx < N * cpr) {
-        sk[idx] = kb[x];
-        sq[idx] = qb[x];
+        sk[idx] = stage_cvt(kb[x], (SK*)nullptr);
+        sq[idx] = stage_cvt(qb[x], (SK*)nullptr);
       }
     }
   };
@@ -184,13 +209,33 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
   float S[MC][4];
 #pragma unroll
   for (int m = 0; m < MC; ++m) {
-    const f32x4 x = mask4(Sx[m], rok && 128 * m + 4 * s < dk);
+    const f32x4 x = mask4(Sx[m], rok && colok(m));
     S[m][0] = x.x;
     S[m][1] = x.y;
     S[m][2] = x.z;
     S[m][3] = x.w;
   }
   __syncthreads();
+
+  // ---- k_t . q_t, the same for every row: half-wave rl takes nodes rl, rl + 8, ...
+  auto kchunk = [&](const SK* base, int t, int m) {
+    return mask4(widen4(base[t * cpr + (FULL ? 32 * m + s : clampi(32 * m + s, cpr - 1))]),
+                 colok(m));
+  };
+  for (int t = rl; t < N; t += kChainRows) {
+    float a = 0.f, a2 = 0.f;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      const f32x4 kx = kchunk(sk, t, m);
+      const f32x4 qx = kchunk(sq, t, m);
+      a = fmaf(kx.x, qx.x, a);
+      a2 = fmaf(kx.y, qx.y, a2);
+      a = fmaf(kx.z, qx.z, a);
+      a2 = fmaf(kx.w, qx.w, a2);
+    }
+    a = half32_sum(a + a2);
+    if (s == 0) skq[t] = a;
+  }
 
   if (DLY) {
     // ---- the previous draft's accepted path: S <- e^{G_last} S + sum c_i u'_i k_i^T
@@ -204,86 +249,114 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
       for (int m = 0; m < MC; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[m][e] = S[m][e] * s0;
-      for (int i = 0; i <= last; ++i) {
-        if (((pm >> i) & 1ull) == 0ull) continue;  // uniform
-        const float c = sGp[i] * sup[i * kChainRows + rl];
+      // path nodes in increasing order, four at a time: the LDS reads of a
+      // group are issued before its multiply-adds
+      for (int i0 = 0; i0 <= last; i0 += 4) {
+        float c[4];
+        f32x4 kc[4][MC];
 #pragma unroll
-        for (int m = 0; m < MC; ++m) {
-          const f32x4 kc = widen4(skp[i * cpr + clampi(32 * m + s, cpr - 1)]);
-          S[m][0] = fmaf(c, kc.x, S[m][0]);
-          S[m][1] = fmaf(c, kc.y, S[m][1]);
-          S[m][2] = fmaf(c, kc.z, S[m][2]);
-          S[m][3] = fmaf(c, kc.w, S[m][3]);
+        for (int u = 0; u < 4; ++u) {
+          const int i = clampi(i0 + u, Np - 1);
+          c[u] = sGp[i] * sup[i * kChainRows + rl];
+#pragma unroll
+          for (int m = 0; m < MC; ++m) kc[u][m] = widen4(skp[i * cpr + clampi(32 * m + s, cpr - 1)]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (i0 + u > last || ((pm >> (i0 + u)) & 1ull) == 0ull) continue;  // uniform
+#pragma unroll
+          for (int m = 0; m < MC; ++m) {
+            S[m][0] = fmaf(c[u], kc[u][m].x, S[m][0]);
+            S[m][1] = fmaf(c[u], kc[u][m].y, S[m][1]);
+            S[m][2] = fmaf(c[u], kc[u][m].z, S[m][2]);
+            S[m][3] = fmaf(c[u], kc[u][m].w, S[m][3]);
+          }
         }
       }
       if (rok) {
         float* wp = S0 + ((size_t)bh * dv + row) * dk;
 #pragma unroll
         for (int m = 0; m < MC; ++m)
-          if (128 * m + 4 * s < dk)
+          if (colok(m))
             *reinterpret_cast<f32x4*>(wp + 128 * m + 4 * s) =
                 f32x4{S[m][0], S[m][1], S[m][2], S[m][3]};
       }
     }
   }
+  __syncthreads();  // k.q of every node is in LDS
 
-  // k_t, q_t (widened) for step t; the next step's are read from LDS while
-  // the current step computes.
-  auto fetch = [&](int t, float (&kf)[MC][4], float (&qf)[MC][4]) {
+  // ---- the recurrence.  Operands of step t (k_t, q_t chunks; alpha, beta,
+  // v, k.q) are read from LDS during step t - 1; two register sets alternate.
+  struct Ops {
+    f32x4 kc[MC], qc[MC];
+    float al, be, vt, kq;
+  };
+  auto fetch = [&](int t, Ops& o) {
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
-      const int cidx = t * cpr + clampi(32 * m + s, cpr - 1);
-      const bool okc = 128 * m + 4 * s < dk;
-      const f32x4 kx = mask4(widen4(sk[cidx]), okc);
-      const f32x4 qx = mask4(widen4(sq[cidx]), okc);
-      kf[m][0] = kx.x; kf[m][1] = kx.y; kf[m][2] = kx.z; kf[m][3] = kx.w;
-      qf[m][0] = qx.x; qf[m][1] = qx.y; qf[m][2] = qx.z; qf[m][3] = qx.w;
+      o.kc[m] = kchunk(sk, t, m);
+      o.qc[m] = kchunk(sq, t, m);
     }
+    o.al = salpha[t];
+    o.be = sbeta[t];
+    o.vt = sv[t * kChainRows + rl];
+    o.kq = skq[t];
   };
-  float kf[MC][4], qf[MC][4];
-  fetch(0, kf, qf);
   const size_t obase = (size_t)b * N * H * dv + (size_t)h * dv + row;
   const size_t ubase = (size_t)bh * N * dv + row;
-  for (int t = 0; t < N; ++t) {
-    float kn[MC][4], qn[MC][4];
-    fetch(clampi(t + 1, N - 1), kn, qn);
-    const float be = sbeta[t];
-    const float al = salpha[t];
-    const float vt = sv[t * kChainRows + rl];
-
-    float kq = 0.f, yk = 0.f, yq = 0.f, kq2 = 0.f, yk2 = 0.f, yq2 = 0.f;
+  auto run = [&](int t, const Ops& o) {
+    float yk = 0.f, yq = 0.f, yk2 = 0.f, yq2 = 0.f;
 #pragma unroll
-    for (int m = 0; m < MC; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        kq = fmaf(kf[m][e], qf[m][e], kq);
-        yk = fmaf(S[m][e], kf[m][e], yk);
-        yq = fmaf(S[m][e], qf[m][e], yq);
-        kq2 = fmaf(kf[m][e + 1], qf[m][e + 1], kq2);
-        yk2 = fmaf(S[m][e + 1], kf[m][e + 1], yk2);
-        yq2 = fmaf(S[m][e + 1], qf[m][e + 1], yq2);
-      }
-    kq = half32_sum(kq + kq2);
+    for (int m = 0; m < MC; ++m) {
+      yk = fmaf(S[m][0], o.kc[m].x, yk);
+      yq = fmaf(S[m][0], o.qc[m].x, yq);
+      yk2 = fmaf(S[m][1], o.kc[m].y, yk2);
+      yq2 = fmaf(S[m][1], o.qc[m].y, yq2);
+      yk = fmaf(S[m][2], o.kc[m].z, yk);
+      yq = fmaf(S[m][2], o.qc[m].z, yq);
+      yk2 = fmaf(S[m][3], o.kc[m].w, yk2);
+      yq2 = fmaf(S[m][3], o.qc[m].w, yq2);
+    }
     yk = half32_sum(yk + yk2);
-    yq = half32_sum(yq + yq2);
-
-    const float u = be * (vt - al * yk);
-    const float o = scale * fmaf(kq, u, al * yq);
+    yq = half32_sum_hi(yq + yq2);  // complete in lanes 16..31 of the half-wave only
+    const float u = o.be * (o.vt - o.al * yk);
+    const float ov = scale * fmaf(o.kq, u, o.al * yq);
 #pragma unroll
-    for (int m = 0; m < MC; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[m][e] = fmaf(u, kf[m][e], al * S[m][e]);
-    if (s == 0 && rok) {
-      out[obase + (size_t)t * H * dv] = o;
+    for (int m = 0; m < MC; ++m) {
+      S[m][0] = fmaf(u, o.kc[m].x, o.al * S[m][0]);
+      S[m][1] = fmaf(u, o.kc[m].y, o.al * S[m][1]);
+      S[m][2] = fmaf(u, o.kc[m].z, o.al * S[m][2]);
+      S[m][3] = fmaf(u, o.kc[m].w, o.al * S[m][3]);
+    }
+    if (s == 16 && rok) {
+      out[obase + (size_t)t * H * dv] = ov;
       rec.up[ubase + (size_t)t * dv] = u;
     }
+  };
+  // The prefetched operands pass through an empty asm after the step that
+  // overlaps their reads: the values carried around the loop are then not
+  // loads, which the optimiser would otherwise re-issue at the top of the
+  // next step (folding a phi of loads into a load) and wait for at once.
+  auto opaque = [](Ops& o) {
 #pragma unroll
-    for (int m = 0; m < MC; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[m][e] = kn[m][e];
-        qf[m][e] = qn[m][e];
-      }
+    for (int m = 0; m < MC; ++m) {
+      asm volatile("" : "+v"(o.kc[m]));
+      asm volatile("" : "+v"(o.qc[m]));
+    }
+    asm volatile("" : "+v"(o.al), "+v"(o.be), "+v"(o.vt), "+v"(o.kq));
+  };
+  Ops A, Bo;
+  fetch(0, A);
+  opaque(A);
+  for (int t = 0; t < N; t += 2) {
+    fetch(clampi(t + 1, N - 1), Bo);
+    run(t, A);
+    opaque(Bo);
+    if (t + 1 < N) {  // uniform
+      fetch(clampi(t + 2, N - 1), A);
+      run(t + 1, Bo);
+      opaque(A);
+    }
   }
 
   // factor record: G (chain prefix sums), k copy, parents, masks
@@ -296,12 +369,29 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
       }
     }
     for (int idx = tid; idx < N * cpr; idx += 256)  // from the staged rows in LDS
-      *reinterpret_cast<R4*>(rec.K + ((size_t)bh * N + idx / cpr) * dk + 4 * (idx % cpr)) = sk[idx];
+      *reinterpret_cast<R4*>(rec.K + ((size_t)bh * N + idx / cpr) * dk + 4 * (idx % cpr)) =
+          unstage(sk[idx], (T*)nullptr);
     if (h == 0 && tid < N) {
       rec.parents[(size_t)b * N + tid] = tid - 1;
       rec.mask[(size_t)b * N + tid] = tid >= 63 ? ~0ull : ((1ull << (tid + 1)) - 1ull);
     }
   }
+}
+
+template <typename T, bool DLY, bool QF>
+void launch_chain_qf(bool full, long grid, size_t lds, hipStream_t stream, int N, int H, int dk,
+                     int dv, int ntiles, float* S0, const T* q, const T* k, const T* v,
+                     const float* beta, const float* g, float scale, float* out,
+                     const Record<T>& rec, const Record<T>& prev, int Np, const int32_t* last,
+                     int32_t* dev_status) {
+  if (full)
+    hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, true>), dim3((unsigned)grid), dim3(256),
+                       lds, stream, N, H, dk, dv, ntiles, S0, q, k, v, beta, g, scale, out, rec,
+                       prev, Np, last, dev_status);
+  else
+    hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, false>), dim3((unsigned)grid), dim3(256),
+                       lds, stream, N, H, dk, dv, ntiles, S0, q, k, v, beta, g, scale, out, rec,
+                       prev, Np, last, dev_status);
 }
 
 template <typename T>
@@ -311,23 +401,39 @@ hipError_t launch_chain_verify_t(int B, int N, int H, int dk, int dv, float* S0,
                                  const RecordLayout& L, const void* prev_factors, int Np,
                                  const int32_t* last, int32_t* dev_status, hipStream_t stream) {
   Record<T> rec = record_views<T>(factors, L);
+  Record<T> prev{};
+  const bool dly = prev_factors != nullptr;
+  if (dly) {
+    const RecordLayout Lp = record_layout(B, Np, H, dk, dv, sizeof(T) == 2 ? GDN_BF16 : GDN_F32);
+    prev = record_views<T>(const_cast<void*>(prev_factors), Lp);
+  } else {
+    Np = 0;
+  }
+  // k, q staged as FP32 for drafts of up to 32 nodes (bf16 beyond, to bound LDS)
+  const bool qf = sizeof(T) == 4 || N <= 32;
+  const bool full = dk == kMaxDim;
   const int ntiles = (dv + kChainRows - 1) / kChainRows;
   const long grid = (long)B * H * ntiles;
-  size_t lds =
-      (size_t)N * dk * sizeof(T) * 2 + (size_t)N * kChainRows * 4 + (size_t)N * 4 * 3;
-  if (prev_factors) {
-    const RecordLayout Lp = record_layout(B, Np, H, dk, dv, sizeof(T) == 2 ? GDN_BF16 : GDN_F32);
-    Record<T> prev = record_views<T>(const_cast<void*>(prev_factors), Lp);
-    lds += (size_t)Np * dk * sizeof(T) + (size_t)Np * kChainRows * 4 + (size_t)Np * 4;
-    hipLaunchKernelGGL((chain_verify_kernel<T, true>), dim3((unsigned)grid), dim3(256), lds,
-                       stream, N, H, dk, dv, ntiles, S0, static_cast<const T*>(q),
-                       static_cast<const T*>(k), static_cast<const T*>(v), beta, g, scale, out,
-                       rec, prev, Np, last, dev_status);
+  const size_t lds = (size_t)N * dk * (qf ? 4 : sizeof(T)) * 2 + (size_t)N * kChainRows * 4 +
+                     (size_t)N * 4 * 4 + (size_t)Np * dk * sizeof(T) +
+                     (size_t)Np * kChainRows * 4 + (size_t)Np * 4;
+  const T* qq = static_cast<const T*>(q);
+  const T* kk = static_cast<const T*>(k);
+  const T* vv = static_cast<const T*>(v);
+  if (dly) {
+    if (qf)
+      launch_chain_qf<T, true, true>(full, grid, lds, stream, N, H, dk, dv, ntiles, S0, qq, kk,
+                                     vv, beta, g, scale, out, rec, prev, Np, last, dev_status);
+    else
+      launch_chain_qf<T, true, false>(full, grid, lds, stream, N, H, dk, dv, ntiles, S0, qq, kk,
+                                      vv, beta, g, scale, out, rec, prev, Np, last, dev_status);
   } else {
-    hipLaunchKernelGGL((chain_verify_kernel<T, false>), dim3((unsigned)grid), dim3(256), lds,
-                       stream, N, H, dk, dv, ntiles, S0, static_cast<const T*>(q),
-                       static_cast<const T*>(k), static_cast<const T*>(v), beta, g, scale, out,
-                       rec, Record<T>{}, 0, nullptr, nullptr);
+    if (qf)
+      launch_chain_qf<T, false, true>(full, grid, lds, stream, N, H, dk, dv, ntiles, S0, qq, kk,
+                                      vv, beta, g, scale, out, rec, prev, 0, nullptr, nullptr);
+    else
+      launch_chain_qf<T, false, false>(full, grid, lds, stream, N, H, dk, dv, ntiles, S0, qq, kk,
+                                       vv, beta, g, scale, out, rec, prev, 0, nullptr, nullptr);
   }
   return hipGetLastError();
 }

@@ -153,10 +153,13 @@ __device__ inline bf16x8 zero_bf16x8() {
 // Sum over each row of 16 lanes with DPP (VALU-speed cross-lane moves inside
 // a row): rotate-by-8 and rotate-by-4 fold the row to four partial sums,
 // two quad permutations finish it.  Every lane of the row ends with the sum.
+// These patterns never read outside the row, so bound_ctrl may be set, which
+// lets the compiler fuse each move into its add (one v_add_f32 with a DPP
+// source per stage).
 template <int CTRL>
 __device__ inline float dpp_f32(float x) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 __device__ inline float row16_sum(float x) {
   x += dpp_f32<0x128>(x);  // row_ror:8
@@ -166,12 +169,29 @@ __device__ inline float row16_sum(float x) {
   return x;
 }
 
-// Sum over each half-wave (32 lanes): the 16-lane row sums, then one
-// ds_swizzle in bit mode (and 0x1F, xor 0x10) adds the other row of the half.
+// Sum over each half-wave (32 lanes): the 16-lane row sums, then
+// v_permlane16_swap exchanges the two rows of each half on the VALU (no LDS
+// round trip), so every lane of the half ends with the total.  The empty asm
+// copy keeps the swap's two operands distinct to the compiler, which otherwise
+// folds a swap of a value with itself.
 __device__ inline float half32_sum(float x) {
   x = row16_sum(x);
-  return x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
-                                                                   (0x10 << 10) | 0x1F));
+  const unsigned a = __builtin_bit_cast(unsigned, x);
+  unsigned b;
+  asm("" : "=v"(b) : "0"(a));
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Sum over each half-wave delivered only to its upper 16 lanes (rows 1 and 3
+// of the wave): the row sums, then DPP row_bcast:15 adds the lower row's sum
+// into the upper row (GFX9 DPP; rows 0 and 2 keep their own row sum).  One
+// DPP step instead of a row exchange, for values only the upper row consumes.
+__device__ inline float half32_sum_hi(float x) {
+  x = row16_sum(x);
+  const float lo = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+  return x + lo;
 }
 
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
