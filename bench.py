@@ -35,10 +35,12 @@ from linear_attention_gdn_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "linear_attention_gdn_amd", "csrc")
 KERNEL_SOURCES = {"gdn_chain_verify": "chain_verify.hip", "gdn_tree_verify": "tree_verify.hip",
                   "gdn_commit_path": "commit.hip", "gdn_linear": "layer.hip",
-                  "gdn_chain_verify_delayed": "chain_verify.hip"}
+                  "gdn_chain_verify_delayed": "chain_verify.hip",
+                  "gdn_tree_verify_delayed": "tree_verify.hip"}
 
 
 def source_digest(kernel: str) -> str:
@@ -110,14 +112,14 @@ def bytes_commit(d: W.Draft, plens: np.ndarray) -> float:
     return tot + B * 4
 
 
-def bytes_delayed(d: W.Draft, plens: np.ndarray) -> float:
+def bytes_delayed(d: W.Draft, plens: np.ndarray, tree: bool) -> float:
     """Algorithmic bytes of one delayed-commit verification: the verification's
     own bytes, plus, for every sequence with a non-empty accepted path, the
     state written back once and the path's u', k and G read from the previous
     record (the state read is shared with the verification)."""
     es = 2 if d.dtype == "bf16" else 4
     B, N, H, dk, dv = d.B, d.N, d.H, d.dk, d.dv
-    tot = float(bytes_verify(d, False)) + B * N * 8 + B * 4
+    tot = float(bytes_verify(d, tree)) + B * N * 8 + B * 4
     for n in plens:
         if n > 0:
             tot += H * dv * dk * 4 + H * n * (dv * 4 + dk * es + 4)
@@ -174,8 +176,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     ap.add_argument("--separate-commit", action="store_true",
-                    help="chain workloads: verify and commit as two launches per step instead "
-                         "of the delayed commit fused into the next verification")
+                    help="verify and commit as two launches per step instead of the delayed "
+                         "commit fused into the next verification")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -231,22 +233,29 @@ def main():
     def commit(i):
         G.gdn_commit_path(states[i % R], rec, lasts[i])
 
-    # Delayed commit (chain workloads): step i commits, on state i % R, the
-    # draft that state verified on its previous visit (accepted node
-    # lasts[i]) and verifies the new draft, in one launch.  Each state keeps
-    # two record slots used alternately.
-    delayed = chain and not args.separate_commit
+    # Delayed commit: step i commits, on state i % R, the draft that state
+    # verified on its previous visit (accepted node lasts[i]) and verifies
+    # the new draft, in one launch.  Each state keeps two record slots used
+    # alternately.
+    delayed = not args.separate_commit
     if delayed:
         recs = [[G.FactorRecord.empty(B, N, H, dk, dv, code, device=dev) for _ in range(2)]
                 for _ in range(R)]
         for j in range(R):  # every state's "previous visit": a plain verify
-            G.gdn_chain_verify(states[j], q, k, v, beta, g, out, recs[j][1])
+            if chain:
+                G.gdn_chain_verify(states[j], q, k, v, beta, g, out, recs[j][1])
+            else:
+                G.gdn_tree_verify(states[j], parents, q, k, v, beta, g, out, recs[j][1])
         torch.cuda.synchronize()
 
     def fused(i):
         j, vis = i % R, i // R
-        G.gdn_chain_verify_delayed(states[j], recs[j][(vis + 1) % 2], lasts[i], q, k, v, beta, g,
-                                   out, recs[j][vis % 2])
+        if chain:
+            G.gdn_chain_verify_delayed(states[j], recs[j][(vis + 1) % 2], lasts[i], q, k, v, beta,
+                                       g, out, recs[j][vis % 2])
+        else:
+            G.gdn_tree_verify_delayed(states[j], recs[j][(vis + 1) % 2], lasts[i], parents, q, k,
+                                      v, beta, g, out, recs[j][vis % 2])
 
     def step(i):
         if delayed:
@@ -342,16 +351,32 @@ def main():
     dom = "verify" if t_ver.mean() >= t_com.mean() else "commit"
     if delayed:
         t_fus = graph_time(fused)
-        b_fus = np.mean([bytes_delayed(d, p) for p in plens])
-        kernels["verify_delayed"] = {"name": "gdn_chain_verify_delayed",
+        b_fus = np.mean([bytes_delayed(d, p, not chain) for p in plens])
+        kernels["verify_delayed"] = {"name": "gdn_chain_verify_delayed" if chain
+                                     else "gdn_tree_verify_delayed",
                                      "avg_us": float(t_fus * 1e3), "bytes": float(b_fus),
                                      "gbs": float(b_fus / (t_fus * 1e-3) / 1e9)}
         dom = "verify_delayed"  # the only kernel of the timed step
     kd = kernels[dom]
-    roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(kd["name"], d.name), "kernel": kd["name"],
-                "algorithmic_bytes": kd["bytes"]}
+    if chain:  # the serial chain kernel streams the state: HBM roofline
+        roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(kd["name"], d.name), "kernel": kd["name"],
+                    "algorithmic_bytes": kd["bytes"]}
+    else:  # the tree kernel's S0 contraction, FP32-accurate on bf16 matrix cores
+        flops = 4.0 * B * H * N * dk * dv          # algorithmic (FP32-equivalent) per launch
+        t_s = kd["avg_us"] * 1e-6
+        tflops = flops / t_s / 1e12
+        issued = 2.0 * flops                        # hi + lo passes of the dominant product
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2),
+                    "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(kd["name"], d.name), "kernel": kd["name"],
+                    "algorithmic_flops": flops,
+                    "issued_bf16_tflops": round(issued / t_s / 1e12, 2),
+                    "issued_bf16_frac": round(issued / t_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "hbm_gbs": round(kd["gbs"], 2), "hbm_frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes": kd["bytes"]}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -203,6 +203,36 @@ int gdn_chain_verify_delayed(int B, int N_prev, int N, int H, int dk, int dv, in
                              const float* beta, const float* g, float scale, float* out,
                              void* factors, void* stream);
 
+/*
+ * gdn_tree_verify_delayed - the delayed commit fused into the next tree
+ * verification (same passages as gdn_chain_verify_delayed).  Equivalent to
+ *     gdn_commit_path(B, N_prev, H, dk, dv, qkv_dtype, S, prev_factors,
+ *                     last_accepted, NULL, NULL, commit_status, stream);
+ *     gdn_tree_verify(B, N, H, dk, dv, qkv_dtype, S, parents, q, k, v, beta,
+ *                     g, scale, out, factors, workspace, mask_out,
+ *                     dev_status, stream);
+ * with the committed state bitwise that of gdn_commit_path: each workgroup
+ * applies the previous accepted path to the state tile it loads for the
+ * verification, writes the tile back once and verifies from the registers.
+ * The commit takes place even when the new draft's topology is rejected.
+ *   S             in place, as for gdn_chain_verify_delayed
+ *   prev_factors, N_prev, last_accepted   as for gdn_chain_verify_delayed
+ *   commit_status optional [B] int32: GDN_OK, or GDN_ERR_TOPOLOGY when
+ *                 last_accepted is out of range or the previous record's
+ *                 topology was rejected (that sequence's state is then left
+ *                 as it was)
+ *   dev_status    optional [B] int32: the new draft's topology, as in
+ *                 gdn_tree_verify
+ *   factors       the new record; must not overlap prev_factors
+ *   other arguments as for gdn_tree_verify
+ */
+int gdn_tree_verify_delayed(int B, int N_prev, int N, int H, int dk, int dv, int qkv_dtype,
+                            float* S, const void* prev_factors, const int32_t* last_accepted,
+                            int32_t* commit_status, const int32_t* parents, const void* q,
+                            const void* k, const void* v, const float* beta, const float* g,
+                            float scale, float* out, void* factors, void* workspace,
+                            uint64_t* mask_out, int32_t* dev_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

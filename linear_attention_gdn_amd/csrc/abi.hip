@@ -16,11 +16,12 @@ hipError_t launch_chain_verify(int B, int N, int H, int dk, int dv, int dtype, f
                                const float* g, float scale, float* out, void* factors,
                                const void* prev_factors, int Np, const int32_t* last,
                                int32_t* dev_status, hipStream_t stream);
-hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
+hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, float* S0,
                               const int32_t* parents, const void* q, const void* k,
                               const void* v, const float* beta, const float* g, float scale,
                               float* out, void* factors, void* workspace, uint64_t* mask_out,
-                              int32_t* dev_status, hipStream_t stream);
+                              int32_t* dev_status, const void* prev_factors, int Np,
+                              const int32_t* last, int32_t* commit_status, hipStream_t stream);
 hipError_t launch_commit(int B, int N, int H, int dk, int dv, int dtype, float* S,
                          const void* factors, const int32_t* last, int32_t* path_out,
                          int32_t* path_len, int32_t* dev_status, hipStream_t stream);
@@ -163,9 +164,53 @@ int gdn_tree_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const fl
   GDN_TRY(check_ptr(fn, "workspace", workspace, false));
   GDN_TRY(check_ptr(fn, "mask_out", mask_out, false));
   GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
-  return hip_status(fn, gdn::launch_tree_verify(B, N, H, dk, dv, qkv_dtype, S0, parents, q, k,
-                                                v, beta, g, scale, out, factors, workspace,
-                                                mask_out, dev_status,
+  return hip_status(fn, gdn::launch_tree_verify(B, N, H, dk, dv, qkv_dtype,
+                                                const_cast<float*>(S0), parents, q, k, v, beta,
+                                                g, scale, out, factors, workspace, mask_out,
+                                                dev_status, nullptr, 0, nullptr, nullptr,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int gdn_tree_verify_delayed(int B, int N_prev, int N, int H, int dk, int dv, int qkv_dtype,
+                            float* S, const void* prev_factors, const int32_t* last_accepted,
+                            int32_t* commit_status, const int32_t* parents, const void* q,
+                            const void* k, const void* v, const float* beta, const float* g,
+                            float scale, float* out, void* factors, void* workspace,
+                            uint64_t* mask_out, int32_t* dev_status, void* stream) {
+  const char* fn = "gdn_tree_verify_delayed";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  if (N_prev < 1 || N_prev > gdn::kMaxNodes)
+    return fail(GDN_ERR_SHAPE, "%s: N_prev=%d outside 1..64", fn, N_prev);
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (!std::isfinite(scale)) return fail(GDN_ERR_ARG, "%s: scale is not finite", fn);
+  if (B == 0) return ok();
+  if (N == 0)
+    return fail(GDN_ERR_SHAPE, "%s: N=0; use gdn_commit_path to commit without verifying", fn);
+  GDN_TRY(check_ptr(fn, "S", S, true));
+  GDN_TRY(check_ptr(fn, "prev_factors", prev_factors, true));
+  GDN_TRY(check_ptr4(fn, "last_accepted", last_accepted, true));
+  GDN_TRY(check_ptr4(fn, "commit_status", commit_status, false));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr(fn, "out", out, true));
+  GDN_TRY(check_ptr(fn, "factors", factors, true));
+  GDN_TRY(check_ptr(fn, "workspace", workspace, false));
+  GDN_TRY(check_ptr(fn, "mask_out", mask_out, false));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  const char* a0 = static_cast<const char*>(prev_factors);
+  const char* b0 = static_cast<const char*>(factors);
+  const size_t na = gdn::record_layout(B, N_prev, H, dk, dv, qkv_dtype).total;
+  const size_t nb = gdn::record_layout(B, N, H, dk, dv, qkv_dtype).total;
+  if (a0 < b0 + nb && b0 < a0 + na)
+    return fail(GDN_ERR_ARG, "%s: factors and prev_factors overlap", fn);
+  return hip_status(fn, gdn::launch_tree_verify(B, N, H, dk, dv, qkv_dtype, S, parents, q, k, v,
+                                                beta, g, scale, out, factors, workspace,
+                                                mask_out, dev_status, prev_factors, N_prev,
+                                                last_accepted, commit_status,
                                                 static_cast<hipStream_t>(stream)));
 }
 

@@ -40,6 +40,15 @@
 // The per-head steps 1-3 are repeated by each of the head's tiles; they run
 // while the state tile is still in flight.  Workgroups are numbered so that
 // the tiles of one head run on the same XCD and share its L2 for Q and K.
+//
+// Delayed commit (review: Referee Report summary, mechanism (ii); Figure 7
+// caption, right side): with DLY the kernel also applies the previous draft's
+// accepted path to its register-resident state tile before step 4.  The
+// path (from the previous record's masks) is known after step 0; its k rows,
+// u' of the tile's rows and coefficients e^{G_last - G_i} are loaded during
+// step 1 and staged in LDS (16 path nodes at a time) while steps 2-3 run,
+// then applied in the commit kernel's operation order (so the committed
+// state is bitwise gdn_commit_path's) and the tile is written back once.
 #include <type_traits>
 
 #include "gdn_common.h"
@@ -164,13 +173,25 @@ __device__ inline void path_solve_lds(int t, uint64_t m, const float* A, float* 
   }
 }
 
-template <typename T, int BV, int NQT>
+constexpr int kDlyChunk = 16;  // path nodes staged per round for the delayed commit
+
+template <bool DLY, int BV>
+struct DelayLds {  // k rows (FP32), u' of the tile's rows, coefficients, node ids
+  static constexpr int kBVT = ((BV + 15) / 16) * 16;
+  float k[DLY ? kDlyChunk * kMaxDim : 1];
+  float u[DLY ? kDlyChunk * kBVT : 1];
+  float c[DLY ? kMaxNodes : 1];
+  int node[DLY ? kMaxNodes : 1];
+};
+
+template <typename T, int BV, int NQT, bool DLY>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
-    int N, int H, int dk, int dv, int ntiles, const float* __restrict__ S0,
+    int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
     const int32_t* __restrict__ parents, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ g,
     float scale, float* __restrict__ out, Record<T> rec, uint64_t* __restrict__ mask_out,
-    int32_t* __restrict__ dev_status) {
+    int32_t* __restrict__ dev_status, Record<T> prev, int Npv,
+    const int32_t* __restrict__ last_acc, int32_t* __restrict__ commit_status) {
   using L = TreeLds<BV>;
   constexpr bool kStaged = std::is_same<T, bf16_t>::value;  // Q/K staged in LDS as bf16
   constexpr int NCT = (BV + 15) / 16;                        // MFMA column tiles
@@ -189,6 +210,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   __shared__ uint64_t smask[kMaxNodes];
   __shared__ float sG[kMaxNodes], seG[kMaxNodes], sbeta[kMaxNodes];
   __shared__ int sbad;
+  __shared__ __attribute__((aligned(16))) DelayLds<DLY, BV> dly;
+  __shared__ int sdly_n;
+  __shared__ float sdly_s0;
   bf16_t* QKs = reinterpret_cast<bf16_t*>(smem);
   bf16_t* RTs = reinterpret_cast<bf16_t*>(smem);                 // R^T, split [kBVT][kLdH]
   bf16_t* UTs = reinterpret_cast<bf16_t*>(smem + L::kSplitT);    // U'^T, split
@@ -264,6 +288,18 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
       vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
     }
 
+  // delayed commit: the previous draft's last accepted node, and node j's
+  // mask and G in lane j of every wave
+  int last_v = -1;
+  uint64_t pmask_l = 0;
+  float pG_l = 0.f;
+  if (DLY) {
+    last_v = last_acc[b];
+    const int tj = clampi(lane, Npv - 1);
+    pmask_l = prev.mask[(size_t)b * Npv + tj];
+    pG_l = prev.G[(size_t)bh * Npv + tj];
+  }
+
   if (kStaged) {
 #pragma unroll
     for (int x = 0; x < QKB; ++x) {
@@ -316,8 +352,129 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     }
     if (tile == 0 && t == 0 && h == 0 && dev_status)
       dev_status[b] = anybad ? GDN_ERR_TOPOLOGY : GDN_OK;
+    if (DLY) {  // the accepted path, root first, and its coefficients
+      const int lst = __builtin_amdgcn_readfirstlane(last_v);
+      const bool in_rng = lst >= 0 && lst < Npv;
+      const int lc = in_rng ? lst : 0;
+      const uint64_t valid = Npv >= 64 ? ~0ull : ((1ull << Npv) - 1ull);
+      const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)pmask_l, lc);
+      const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(pmask_l >> 32), lc);
+      const uint64_t pm = in_rng ? ((((uint64_t)mhi << 32) | mlo) & valid) : 0ull;
+      const bool okp = in_rng && ((pm >> lst) & 1ull);
+      const float Glast =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pG_l), lc));
+      if (okp && ((pm >> t) & 1ull)) {
+        const int pos = __popcll(pm & ((1ull << t) - 1ull));
+        dly.node[pos] = t;
+        dly.c[pos] = expf(Glast - pG_l);
+      }
+      if (t == 0) {
+        sdly_n = okp ? __popcll(pm) : 0;
+        sdly_s0 = expf(Glast);
+        if (tile == 0 && h == 0 && commit_status)
+          commit_status[b] = (lst == -1 || okp) ? GDN_OK : GDN_ERR_TOPOLOGY;
+      }
+    }
   }
   __syncthreads();
+
+  // ---- delayed commit, staging: k rows and u' of path nodes [c0, c0 + 16)
+  const int dn = DLY ? sdly_n : 0;  // path length (0: nothing to commit)
+  constexpr int kTE = std::is_same<T, bf16_t>::value ? 8 : 4;  // elements per 16-byte chunk
+  constexpr int DKC = kDlyChunk * kMaxDim / kTE / 256;          // k chunks per thread
+  constexpr int DUC = (kDlyChunk * L::kBVT + 255) / 256;        // u' values per thread
+  using KChunk = typename std::conditional<std::is_same<T, bf16_t>::value, u32x4, f32x4>::type;
+  KChunk dkr[DLY ? DKC : 1];
+  float dur[DLY ? DUC : 1];
+  auto dly_load = [&](int c0) {
+#pragma unroll
+    for (int x = 0; x < DKC; ++x) {
+      const int idx = tid + 256 * x;                 // chunk of (node j, column)
+      const int j = idx / (kMaxDim / kTE);
+      const int col = clampi(kTE * (idx % (kMaxDim / kTE)), dk - kTE);
+      const int nd = dly.node[clampi(c0 + j, dn > 0 ? dn - 1 : 0)];
+      dkr[x] = *reinterpret_cast<const KChunk*>(prev.K + ((size_t)bh * Npv + nd) * dk + col);
+    }
+#pragma unroll
+    for (int x = 0; x < DUC; ++x) {
+      const int idx = clampi(tid + 256 * x, kDlyChunk * L::kBVT - 1);
+      const int j = idx / L::kBVT;
+      const int r = clampi(r0 + idx % L::kBVT, dv - 1);
+      const int nd = dly.node[clampi(c0 + j, dn > 0 ? dn - 1 : 0)];
+      dur[x] = prev.up[((size_t)bh * Npv + nd) * dv + r];
+    }
+  };
+  auto dly_store = [&]() {
+#pragma unroll
+    for (int x = 0; x < DKC; ++x) {
+      const int idx = tid + 256 * x;
+      const int j = idx / (kMaxDim / kTE);
+      const int col = kTE * (idx % (kMaxDim / kTE));
+      const f32x4 a = widen4(reinterpret_cast<const typename Raw4<T>::type*>(&dkr[x])[0]);
+      *reinterpret_cast<f32x4*>(&dly.k[j * kMaxDim + col]) = a;
+      if constexpr (kTE == 8) {
+        const f32x4 b8 = widen4(reinterpret_cast<const typename Raw4<T>::type*>(&dkr[x])[1]);
+        *reinterpret_cast<f32x4*>(&dly.k[j * kMaxDim + col + 4]) = b8;
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < DUC; ++x) {
+      const int idx = tid + 256 * x;
+      if (idx < kDlyChunk * L::kBVT) dly.u[idx] = dur[x];
+    }
+  };
+  // S_tile <- S_tile + sum over staged nodes [c0, c0 + nc) of c_i u'_i k_i^T, one
+  // multiply-add per node in node order (the commit kernel's order)
+  auto dly_apply = [&](int c0, int nc) {
+    for (int jj = 0; jj < nc; ++jj) {  // uniform
+      const float cu = dly.c[c0 + jj] * dly.u[jj * L::kBVT + (ccol < L::kBVT ? ccol : 0)];
+#pragma unroll
+      for (int ks = 0; ks < kMaxDim / 32; ++ks) {
+        const float* kr = &dly.k[jj * kMaxDim + 32 * ks + koff];
+        const f32x4 k0 = *reinterpret_cast<const f32x4*>(kr);
+        const f32x4 k1 = *reinterpret_cast<const f32x4*>(kr + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Sraw[ks][0][e] = fmaf(cu, k0[e], Sraw[ks][0][e]);
+          Sraw[ks][1][e] = fmaf(cu, k1[e], Sraw[ks][1][e]);
+        }
+      }
+    }
+  };
+  // the whole commit on the register tile, then its write-back (one wave per
+  // row set); `first_staged` says whether chunk 0 is already in LDS
+  auto dly_commit = [&](bool first_staged) {
+    if (dn == 0) return;  // uniform
+    const float s0 = sdly_s0;
+#pragma unroll
+    for (int ks = 0; ks < kMaxDim / 32; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Sraw[ks][0][e] = Sraw[ks][0][e] * s0;
+        Sraw[ks][1][e] = Sraw[ks][1][e] * s0;
+      }
+    for (int c0 = 0; c0 < dn; c0 += kDlyChunk) {  // uniform
+      if (c0 > 0 || !first_staged) {
+        __syncthreads();  // every wave is done with the previous chunk
+        dly_load(c0);
+        dly_store();
+        __syncthreads();
+      }
+      dly_apply(c0, dn - c0 < kDlyChunk ? dn - c0 : kDlyChunk);
+    }
+    if (rb == 0 && sok) {
+      float* wp = S0 + ((size_t)bh * dv + srow) * dk;
+#pragma unroll
+      for (int ks = 0; ks < kMaxDim / 32; ++ks) {
+        const int col = 32 * ks + koff;
+        if (col < dk) {
+          *reinterpret_cast<f32x4*>(wp + col) = Sraw[ks][0];
+          *reinterpret_cast<f32x4*>(wp + col + 4) = Sraw[ks][1];
+        }
+      }
+    }
+  };
+  if (DLY && dn > 0) dly_load(0);  // lands while steps 2-3 run
 
   const bool bad = sbad != 0;
   if (tile == 0) {  // factor record: copy of k for this head
@@ -334,7 +491,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
                reinterpret_cast<const float*>(k) + (((size_t)b * N + t) * H + h) * dk + cc);
     }
   }
-  if (bad) {  // uniform: zero this tile's outputs
+  if (bad) {  // uniform: zero this tile's outputs (a delayed commit still applies)
+    if (DLY) dly_commit(false);
     const int c = tid % BV;
     for (int t = tid / BV; t < N; t += 256 / BV)
       if (r0 + c < dv) {
@@ -380,6 +538,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[(16 * rtl + 4 * lg + r) * kLd + 16 * ct + l16] = acc[r];
   }
+  if (DLY && dn > 0) dly_store();  // the path loads issued after step 1
   __syncthreads();
 
   // ---- 3. A (FP32, in place of K K^T) and Attn (split bf16, in place of
@@ -413,6 +572,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     else
       path_solve_lds(t, m, KK, Tl + t * kLd);
   }
+
+  if (DLY) dly_commit(true);
 
   // ---- 4. Y = [Q; K] S0_tile^T (this wave: column tile cj, row tiles rb + WR*i)
   f32x4 yacc[MAXRT];
@@ -557,46 +718,61 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   }
 }
 
+struct DelayArgs {
+  const void* prev_factors;
+  int Np;
+  const int32_t* last;
+  int32_t* commit_status;
+};
+
 template <typename T, int BV, int NQT>
-hipError_t launch_bvn(int B, int N, int H, int dk, int dv, const float* S0, const int32_t* parents,
+hipError_t launch_bvn(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
                       const T* q, const T* k, const T* v, const float* beta, const float* g,
                       float scale, float* out, const Record<T>& rec, uint64_t* mask_out,
-                      int32_t* dev_status, hipStream_t stream) {
+                      int32_t* dev_status, const DelayArgs& da, int dtype, hipStream_t stream) {
   const int ntiles = (dv + BV - 1) / BV;
   const long grid = (long)B * H * ntiles;
-  hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out, rec,
-                     mask_out, dev_status);
+  if (da.prev_factors) {
+    const RecordLayout Lp = record_layout(B, da.Np, H, dk, dv, dtype);
+    const Record<T> prev = record_views<T>(const_cast<void*>(da.prev_factors), Lp);
+    hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT, true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out,
+                       rec, mask_out, dev_status, prev, da.Np, da.last, da.commit_status);
+  } else {
+    hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT, false>), dim3((unsigned)grid), dim3(256),
+                       0, stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale,
+                       out, rec, mask_out, dev_status, Record<T>{}, 1, nullptr, nullptr);
+  }
   return hipGetLastError();
 }
 
 template <typename T, int BV>
-hipError_t launch_bv(int B, int N, int H, int dk, int dv, const float* S0, const int32_t* parents,
+hipError_t launch_bv(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
                      const T* q, const T* k, const T* v, const float* beta, const float* g,
                      float scale, float* out, const Record<T>& rec, uint64_t* mask_out,
-                     int32_t* dev_status, hipStream_t stream) {
+                     int32_t* dev_status, const DelayArgs& da, int dtype, hipStream_t stream) {
   switch ((N + 15) / 16) {
     case 1:
       return launch_bvn<T, BV, 1>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                                  mask_out, dev_status, stream);
+                                  mask_out, dev_status, da, dtype, stream);
     case 2:
       return launch_bvn<T, BV, 2>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                                  mask_out, dev_status, stream);
+                                  mask_out, dev_status, da, dtype, stream);
     case 3:
       return launch_bvn<T, BV, 3>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                                  mask_out, dev_status, stream);
+                                  mask_out, dev_status, da, dtype, stream);
     default:
       return launch_bvn<T, BV, 4>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                                  mask_out, dev_status, stream);
+                                  mask_out, dev_status, da, dtype, stream);
   }
 }
 
 template <typename T>
-hipError_t launch_tree_verify_t(int B, int N, int H, int dk, int dv, const float* S0,
+hipError_t launch_tree_verify_t(int B, int N, int H, int dk, int dv, float* S0,
                                 const int32_t* parents, const T* q, const T* k, const T* v,
                                 const float* beta, const float* g, float scale, float* out,
                                 void* factors, uint64_t* mask_out, int32_t* dev_status,
-                                hipStream_t stream, int dtype) {
+                                const DelayArgs& da, hipStream_t stream, int dtype) {
   const RecordLayout L = record_layout(B, N, H, dk, dv, dtype);
   Record<T> rec = record_views<T>(factors, L);
   // Tile width: the widest of 64/32/16/8 state rows that still gives one
@@ -604,32 +780,34 @@ hipError_t launch_tree_verify_t(int B, int N, int H, int dk, int dv, const float
   const long heads = (long)B * H;
   if (heads * ((dv + 63) / 64) >= 256)
     return launch_bv<T, 64>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                            mask_out, dev_status, stream);
+                            mask_out, dev_status, da, dtype, stream);
   if (heads * ((dv + 31) / 32) >= 256)
     return launch_bv<T, 32>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                            mask_out, dev_status, stream);
+                            mask_out, dev_status, da, dtype, stream);
   if (heads * ((dv + 15) / 16) >= 256)
     return launch_bv<T, 16>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                            mask_out, dev_status, stream);
+                            mask_out, dev_status, da, dtype, stream);
   return launch_bv<T, 8>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                         mask_out, dev_status, stream);
+                         mask_out, dev_status, da, dtype, stream);
 }
 
-hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
+hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, float* S0,
                               const int32_t* parents, const void* q, const void* k,
                               const void* v, const float* beta, const float* g, float scale,
                               float* out, void* factors, void* workspace, uint64_t* mask_out,
-                              int32_t* dev_status, hipStream_t stream) {
+                              int32_t* dev_status, const void* prev_factors, int Np,
+                              const int32_t* last, int32_t* commit_status, hipStream_t stream) {
   (void)workspace;
+  const DelayArgs da{prev_factors, Np, last, commit_status};
   if (dtype == GDN_BF16)
     return launch_tree_verify_t<bf16_t>(
         B, N, H, dk, dv, S0, parents, static_cast<const bf16_t*>(q),
         static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(v), beta, g, scale, out,
-        factors, mask_out, dev_status, stream, dtype);
+        factors, mask_out, dev_status, da, stream, dtype);
   return launch_tree_verify_t<float>(B, N, H, dk, dv, S0, parents, static_cast<const float*>(q),
                                      static_cast<const float*>(k), static_cast<const float*>(v),
-                                     beta, g, scale, out, factors, mask_out, dev_status, stream,
-                                     dtype);
+                                     beta, g, scale, out, factors, mask_out, dev_status, da,
+                                     stream, dtype);
 }
 
 }  // namespace gdn

@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_chain_verify_delayed.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, F,
                                                P, P, P]
         L.gdn_chain_verify_delayed.restype = I
+        L.gdn_tree_verify_delayed.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
+                                              F, P, P, P, P, P, P]
+        L.gdn_tree_verify_delayed.restype = I
         L.gdn_linear.argtypes = [I, I, I, P, P, I, P, P, P, P]
         L.gdn_linear.restype = I
         L.gdn_pack_weights.argtypes = [I, I, P, P, P]
@@ -278,6 +281,32 @@ def gdn_chain_verify_delayed(S, prev_factors: FactorRecord, last_accepted, q, k,
                                              _p(last_accepted), _p(dev_status), _p(q), _p(k),
                                              _p(v), _p(beta), _p(g), float(scale), _p(out),
                                              _p(factors.buf), _stream(stream)))
+
+
+def gdn_tree_verify_delayed(S, prev_factors: FactorRecord, last_accepted, parents, q, k, v,
+                            beta, g, out, factors: FactorRecord, workspace=None,
+                            scale: float = 1.0, commit_status=None, mask_out=None,
+                            dev_status=None, stream=None) -> None:
+    """Apply the previous record's accepted path to S, then verify a new tree,
+    in one pass; see ``gdn_tree_verify_delayed`` in gdnspec.h."""
+    B, N, H, dk, dv, code = _check_draft(S, q, k, v, beta, g)
+    _need("parents", parents, (B, N), torch.int32)
+    _need("out", out, (B, N, H, dv), torch.float32)
+    _check_record(factors, B, N, H, dk, dv, code)
+    pf = prev_factors
+    if (pf.B, pf.H, pf.dk, pf.dv, pf.qkv_dtype) != (B, H, dk, dv, code):
+        raise ValueError("prev_factors sizes do not match the call")
+    _need("last_accepted", last_accepted, (B,), torch.int32)
+    for name, t in (("commit_status", commit_status), ("dev_status", dev_status)):
+        if t is not None:
+            _need(name, t, (B,), torch.int32)
+    if mask_out is not None:
+        _need("mask_out", mask_out, (B, N), torch.int64)
+    _raise_on(lib().gdn_tree_verify_delayed(B, pf.N, N, H, dk, dv, code, _p(S), _p(pf.buf),
+                                            _p(last_accepted), _p(commit_status), _p(parents),
+                                            _p(q), _p(k), _p(v), _p(beta), _p(g), float(scale),
+                                            _p(out), _p(factors.buf), _p(workspace),
+                                            _p(mask_out), _p(dev_status), _stream(stream)))
 
 
 def gdn_commit_path(S, factors: FactorRecord, last_accepted, path_out=None, path_len_out=None,

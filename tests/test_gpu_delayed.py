@@ -96,3 +96,76 @@ def test_delayed_chain_verify_matches_oracle():
     assert slice_rel_err(S.cpu().numpy(), S_ref) <= TOL_STATE
     assert slice_rel_err(out.cpu().numpy().transpose(0, 2, 1, 3),
                          out_ref.transpose(0, 2, 1, 3)) <= TOL_OUT
+
+
+def _prev_record(prev: W.Draft):
+    if (prev.parents == W.chain_parents(prev.N)[None]).all():
+        _, rec, tp = run_chain(prev)
+    else:
+        _, rec, _, st, tp = run_tree(prev)
+        assert (st.cpu().numpy() == G.GDN_OK).all()
+    return rec, tp
+
+
+@pytest.mark.parametrize("dtype,B,Np,N,H,dk,dv,prev_topo,new_topo", [
+    ("bf16", 1, 32, 32, 8, 256, 256, "window", "window"),      # BV = 8 tiles
+    ("bf16", 8, 64, 64, 8, 256, 256, "branching", "branching"),  # BV = 64 tiles
+    ("bf16", 2, 40, 12, 3, 64, 40, "chain", "random"),         # 40-node path: 3 chunks
+    ("f32", 2, 9, 17, 2, 40, 24, "random", "window"),
+    ("bf16", 1, 5, 1, 1, 16, 8, "binary", "chain"),
+])
+def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo,
+                                                   new_topo):
+    seed = 7 * B + Np + N
+    accept = "full" if prev_topo == "chain" else "leaf_geometric"
+    prev = W.make_draft(B, Np, H, dk, dv, topology=prev_topo, accept=accept, dtype=dtype,
+                        seed=seed)
+    new = W.make_draft(B, N, H, dk, dv, topology=new_topo, accept="none", dtype=dtype,
+                       seed=seed + 1)
+    rec_prev, tp = _prev_record(prev)
+    tn = dev_tensors(new)
+    rng = np.random.default_rng(seed)
+    for last in _lasts(prev, rng):
+        last_t = torch.from_numpy(last).cuda()
+        outs = []
+        for fused in (False, True):
+            S = tp["S0"].clone()
+            cst = torch.full((B,), 77, dtype=torch.int32, device="cuda")
+            dst = torch.full((B,), 77, dtype=torch.int32, device="cuda")
+            msk = torch.zeros((B, N), dtype=torch.int64, device="cuda")
+            out = torch.full((B, N, H, dv), float("nan"), device="cuda")
+            rec = G.FactorRecord.empty(B, N, H, dk, dv, code_of(new))
+            rec.buf.zero_()
+            if fused:
+                G.gdn_tree_verify_delayed(S, rec_prev, last_t, tn["parents"], tn["q"], tn["k"],
+                                          tn["v"], tn["beta"], tn["g"], out, rec,
+                                          commit_status=cst, mask_out=msk, dev_status=dst)
+            else:
+                G.gdn_commit_path(S, rec_prev, last_t, dev_status=cst)
+                G.gdn_tree_verify(S, tn["parents"], tn["q"], tn["k"], tn["v"], tn["beta"],
+                                  tn["g"], out, rec, mask_out=msk, dev_status=dst)
+            outs.append((S, out, rec.buf, cst, dst, msk))
+        torch.cuda.synchronize()
+        for a, b_ in zip(*outs):
+            assert torch.equal(a, b_), last
+
+
+def test_delayed_tree_commit_lands_when_new_topology_is_rejected():
+    prev = W.make_draft(2, 16, 2, 64, 32, topology="window", accept="leaf_geometric",
+                        dtype="bf16", seed=51)
+    new = W.make_draft(2, 8, 2, 64, 32, topology="chain", accept="none", dtype="bf16", seed=52)
+    rec_prev, tp = _prev_record(prev)
+    tn = dev_tensors(new)
+    tn["parents"][1, 5] = 6  # not topological: sequence 1's draft is rejected
+    S_a = tp["S0"].clone()
+    G.gdn_commit_path(S_a, rec_prev, tp["last"])
+    S_b = tp["S0"].clone()
+    out = torch.full((2, 8, 2, 32), float("nan"), device="cuda")
+    rec = G.FactorRecord.empty(2, 8, 2, 64, 32, G.GDN_BF16)
+    dst = torch.full((2,), 77, dtype=torch.int32, device="cuda")
+    G.gdn_tree_verify_delayed(S_b, rec_prev, tp["last"], tn["parents"], tn["q"], tn["k"],
+                              tn["v"], tn["beta"], tn["g"], out, rec, dev_status=dst)
+    torch.cuda.synchronize()
+    assert torch.equal(S_a, S_b)
+    assert dst.tolist() == [G.GDN_OK, G.GDN_ERR_TOPOLOGY]
+    assert (out[1] == 0).all() and torch.isfinite(out[0]).all()
