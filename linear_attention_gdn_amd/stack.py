@@ -14,9 +14,15 @@ of once per node.  Per layer and step:
     gdn_linear       x <- x + (...) W_o^T   (FP32 residual, bf16 copy for the next layer)
 
 and once the accepted node is known, per layer: gdn_commit_path (state) and
-gdn_conv_commit (convolution history).  The autoregressive baseline runs one
-token per step through the same layers with gdn_decode_step in place of
-verify + commit.
+gdn_conv_commit (convolution history).  With the delayed commit (the
+review's Figure 7 caption, right side), a step instead carries the previous
+step's accepted node into every layer: gdn_conv_commit shifts the previous
+path into the history before the layer's prep, and gdn_tree_verify_delayed
+applies it to the layer's state inside the verification; records and
+projection outputs alternate between two buffers per layer, and flush()
+applies the last pending commit.  The autoregressive baseline runs one token
+per step through the same layers with gdn_decode_step in place of verify +
+commit.
 """
 
 from __future__ import annotations
@@ -66,7 +72,7 @@ class GdnStack:
         M = B * N
         self.x = e(M, D)
         self.xb = e(M, D, dt=bf)
-        self.P = e(L, B, N, shape.n_proj)
+        self.P = e(2, L, B, N, shape.n_proj)  # two sets, used by alternate steps
         self.q = e(B, N, H, dk, dt=bf)
         self.k = e(B, N, H, dk, dt=bf)
         self.v = e(B, N, H, dv, dt=bf)
@@ -74,8 +80,11 @@ class GdnStack:
         self.g = e(B, N, H)
         self.out = e(B, N, H, dv)
         self.Y = e(M, H * dv, dt=bf)
-        self.rec: List[G.FactorRecord] = [
-            G.FactorRecord.empty(B, N, H, dk, dv, G.GDN_BF16, device=device) for _ in range(L)]
+        self.rec: List[List[G.FactorRecord]] = [
+            [G.FactorRecord.empty(B, N, H, dk, dv, G.GDN_BF16, device=device) for _ in range(L)]
+            for _ in range(2)]
+        self.cur = 0  # buffer set of the latest verification
+        self.pending = None  # (parents, last) of a verified step not yet committed
         self.status = torch.zeros(B, dtype=torch.int32, device=device)
         # autoregressive step buffers (one token per sequence)
         self.x1 = e(B, D)
@@ -117,30 +126,63 @@ class GdnStack:
 
     def verify(self, parents: torch.Tensor, stream=None):
         """All layers, layer-major, for the draft tree `parents` [B][N]; the final
-        hidden rows are left in self.x (FP32) and self.xb (bf16)."""
+        hidden rows are left in self.x (FP32) and self.xb (bf16).  A step
+        verified earlier and not yet committed (see step()) is committed first,
+        fused into each layer's verification."""
         sh = self.shape
         g0, g1 = self.gate_cols
         M = self.B * self.N
         npj = sh.n_proj
         xb3 = self.xb.view(self.B, self.N, sh.D)
+        prev, cur = self.cur, 1 - self.cur
+        pend = self.pending
         for l in range(sh.layers):
-            P = self.P[l]
+            P = self.P[cur, l]
+            if pend is not None:  # the previous path enters this layer's history
+                G.gdn_conv_commit(self.P[prev, l], pend[0], pend[1], self.hist[l], stream=stream)
             G.gdn_linear(self.xb, self.W_in[l], C=P.view(M, npj), w_layout=PK, stream=stream)
             G.gdn_layer_prep(P, xb3, self.W_ab[l], parents, self.conv_w[l], self.hist[l],
                              self.q, self.k, self.v, self.beta, self.g,
                              gate_shift=self.gate_shift, stream=stream)
-            G.gdn_tree_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
-                              self.out, self.rec[l], dev_status=self.status, stream=stream)
+            if pend is None:
+                G.gdn_tree_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
+                                  self.out, self.rec[cur][l], dev_status=self.status,
+                                  stream=stream)
+            else:
+                G.gdn_tree_verify_delayed(self.S[l], self.rec[prev][l], pend[1], parents, self.q,
+                                          self.k, self.v, self.beta, self.g, self.out,
+                                          self.rec[cur][l], dev_status=self.status,
+                                          stream=stream)
             G.gdn_gate_merge(self.out.view(M, sh.H * sh.dv), P.view(M, npj)[:, g0:g1],
                              self.Y, stream=stream)
             G.gdn_linear(self.Y, self.W_o[l], C=self.x, R=self.x, C_bf16=self.xb, w_layout=PK,
                          stream=stream)
+        self.cur = cur
+        self.pending = None
 
     def commit(self, parents: torch.Tensor, last: torch.Tensor, stream=None):
-        """Apply the accepted path (deepest node `last` [B], -1 = none) in every layer."""
+        """Apply the accepted path of the latest verification (deepest node `last`
+        [B], -1 = none) in every layer now."""
+        cur = self.cur
         for l in range(self.shape.layers):
-            G.gdn_commit_path(self.S[l], self.rec[l], last, stream=stream)
-            G.gdn_conv_commit(self.P[l], parents, last, self.hist[l], stream=stream)
+            G.gdn_commit_path(self.S[l], self.rec[cur][l], last, stream=stream)
+            G.gdn_conv_commit(self.P[cur, l], parents, last, self.hist[l], stream=stream)
+
+    def defer_commit(self, parents: torch.Tensor, last: torch.Tensor):
+        """Leave the latest verification's accepted path to the next verify()."""
+        self.pending = (parents, last)
+
+    def step(self, parents: torch.Tensor, last_prev=None, parents_prev=None, stream=None):
+        """One speculative step with the delayed commit: the previous step's
+        accepted node (last_prev, on its tree parents_prev) is committed inside
+        this step's verification."""
+        if last_prev is not None:
+            self.defer_commit(parents_prev, last_prev)
+        self.verify(parents, stream=stream)
+
+    def flush(self, parents: torch.Tensor, last: torch.Tensor, stream=None):
+        """Commit the latest verification's accepted path (end of a run)."""
+        self.commit(parents, last, stream=stream)
 
     # ------------------------------------------------ autoregressive baseline
     def ar_step(self, x: torch.Tensor, x_bf16: torch.Tensor, stream=None):

@@ -341,3 +341,35 @@ def test_stack_chain_verify_equals_token_by_token_decode():
     assert max(e_h) <= TOL_OUT
     # layer 0 sees identical inputs on both routes: its projection rows match bitwise
     assert torch.equal(spec.hist[0], ar.hist[0])
+
+
+def test_stack_delayed_commit_is_bitwise_the_two_step_path():
+    """Two speculative steps with the delayed commit (then a flush) leave the
+    stack bitwise where verify / commit / verify / commit leaves it."""
+    shape = W.StackShape(layers=3, D=512, H=8, dk=64, dv=64)
+    N = 16
+    rng, layers, S0 = _stack_case(shape, 1, N, seed=8)
+    parents, last = W.stack_drafts(rng, 2, N=N)
+    x0 = [W.stack_inputs(rng, N, shape.D) for _ in range(2)]
+    par = [i32(parents[s][None]) for s in range(2)]
+    lst = [i32(last[s:s + 1]) for s in range(2)]
+    a = _load(shape, layers, S0, 1, N)
+    b = _load(shape, layers, S0, 1, N)
+    outs_a, outs_b = [], []
+    for s_ in range(2):
+        a.set_inputs(f32(wide(x0[s_])), bf(x0[s_]))
+        a.verify(par[s_])
+        a.commit(par[s_], lst[s_])
+        outs_a.append(a.x.clone())
+        b.set_inputs(f32(wide(x0[s_])), bf(x0[s_]))
+        if s_ == 0:
+            b.verify(par[0])
+        else:
+            b.step(par[1], last_prev=lst[0], parents_prev=par[0])
+        outs_b.append(b.x.clone())
+    b.flush(par[1], lst[1])
+    torch.cuda.synchronize()
+    for xa, xb_ in zip(outs_a, outs_b):
+        assert torch.equal(xa, xb_)
+    assert torch.equal(a.S, b.S)
+    assert torch.equal(a.hist, b.hist)
