@@ -19,16 +19,17 @@
 //
 // One kernel, one workgroup (4 waves) per (sequence, head, tile of BV state
 // rows).  Each workgroup:
-//   0. issues one round of loads: Q and K of its head first (staged in LDS as
-//      bf16, rows padded against bank conflicts), then parents / g / beta,
-//      then its S0 tile (straight into MFMA B-fragment registers) and V tile,
-//      so the per-head work below overlaps the state tile's arrival;
+//   0. issues one round of loads: Q and K of its head (staged in LDS as bf16,
+//      rows padded against bank conflicts) and parents / g / beta; its S0 tile
+//      (straight into MFMA B-fragment registers) and V tile are requested
+//      right after step 1, so steps 2-3 overlap the state tile's arrival;
 //   1. validates the parents and builds ancestor bitmasks and the
 //      path-cumulative G by pointer jumping (one lane per node);
 //   2. forms the Gram blocks Q K^T and K K^T on bf16 MFMA (lower triangle);
-//   3. masks and scales them into A and Attn (all threads), then solves row t
-//      of T on t's root path (rows of T vanish off the path), one lane per
-//      node with the path in registers;
+//   3. masks and scales them into A and Attn (all threads, only the N x N
+//      block the products read), then solves row t of T on t's root path
+//      (rows of T vanish off the path), one lane per node with the path's
+//      block of A in registers;
 //   4. runs the dense contraction Y = [Q; K] S0_tile^T on bf16 MFMA with the
 //      FP32 state split into bf16 hi + lo (bf16 q, k make every product
 //      exact; only the 2^-16 split residue is lost);
@@ -158,6 +159,41 @@ __device__ inline void path_solve_registers(int t, uint64_t m, int d, const floa
   }
 }
 
+// The same for paths of at most 8 nodes with the path's 8 x 8 block of A read
+// into registers first (one round of LDS reads), then substituted in
+// registers: each step is a few FMAs instead of a wait on LDS.
+__device__ inline void path_solve_registers8(int t, uint64_t m, int d, const float* A,
+                                             float* Trow) {
+  constexpr int P = 8;
+  int p[P];
+  uint64_t mm = m;
+#pragma unroll
+  for (int a = 0; a < P; ++a) {
+    p[a] = mm ? __builtin_ctzll(mm) : t;
+    mm &= mm - 1ull;
+  }
+  float Ab[P][P];  // Ab[a][b] = A[p_a][p_b] for a > b (zero above the path)
+#pragma unroll
+  for (int a = 0; a < P; ++a)
+#pragma unroll
+    for (int b = 0; b < a; ++b) Ab[a][b] = A[p[a] * kLd + p[b]];
+  float x[P];
+#pragma unroll
+  for (int a = 0; a < P; ++a) x[a] = (a == d - 1) ? 1.f : 0.f;
+  // x_b = -sum_{a > b} x_a A[p_a][p_b], b = d-2 .. 0; entries a >= d have x_a = 0
+#pragma unroll
+  for (int b = P - 2; b >= 0; --b) {
+    float acc = 0.f;
+#pragma unroll
+    for (int a = b + 1; a < P; ++a) acc = fmaf(x[a], Ab[a][b], acc);
+    if (b < d - 1) x[b] = -acc;
+  }
+  Trow[t] = 1.f;
+#pragma unroll
+  for (int b = 0; b < P; ++b)
+    if (b < d - 1) Trow[p[b]] = x[b];
+}
+
 // The same for any depth, with the row in LDS (slower).
 __device__ inline void path_solve_lds(int t, uint64_t m, const float* A, float* Trow) {
   Trow[t] = 1.f;
@@ -204,7 +240,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   constexpr int nrt = 2 * NQT;                               // Y row tiles (Q then K)
   constexpr int MAXRT = (nrt + WR - 1) / WR;                 // Y row tiles per wave
   constexpr int MAXNB = (NQT + WR - 1) / WR;                 // node blocks per wave
-  constexpr int EPT = kMaxNodes * kMaxNodes / 256;           // N x N entries per thread
+  constexpr int EPT = Np * NK / 256;                         // Np x NK entries per thread
 
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
   __shared__ uint64_t smask[kMaxNodes];
@@ -266,27 +302,32 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   const int pl = parents[(size_t)b * N + tn];
   const float gl = g[((size_t)b * N + tn) * H + h];
   const float bl = beta[((size_t)b * N + tn) * H + h];
-  const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
+  // The state tile (straight into MFMA B-fragment order) and V are loaded
+  // after the topology step (load_state below): step 4 is the first to need
+  // them, and loads issued here would be waited for by the Q/K staging.
   f32x4 Sraw[kMaxDim / 32][2];
-#pragma unroll
-  for (int ks = 0; ks < kMaxDim / 32; ++ks) {
-    const int kk = clampi(32 * ks + koff, dk - 8);
-    Sraw[ks][0] = load4(sptr + kk);
-    Sraw[ks][1] = load4(sptr + kk + 4);
-  }
   // V for the K row tiles this wave turns into R: its j-th K tile is row tile
   // rt = rb + WR*(iK0 + j) >= NQT, node block rt - NQT (D layout: node
   // 16*nb + 4*lg + r, column ccol).
   const int iK0 = NQT > rb ? (NQT - rb + WR - 1) / WR : 0;
   T vreg[MAXNB][4];
+  auto load_state = [&]() {
+    const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
 #pragma unroll
-  for (int j = 0; j < MAXNB; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int nb = rb + WR * (iK0 + j) - NQT;
-      const int t = clampi(16 * nb + 4 * lg + r, N - 1);
-      vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
+    for (int ks = 0; ks < kMaxDim / 32; ++ks) {
+      const int kk = clampi(32 * ks + koff, dk - 8);
+      Sraw[ks][0] = load4(sptr + kk);
+      Sraw[ks][1] = load4(sptr + kk + 4);
     }
+#pragma unroll
+    for (int j = 0; j < MAXNB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int nb = rb + WR * (iK0 + j) - NQT;
+        const int t = clampi(16 * nb + 4 * lg + r, N - 1);
+        vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
+      }
+  };
 
   // delayed commit: the previous draft's last accepted node, and node j's
   // mask and G in lane j of every wave
@@ -313,7 +354,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
       }
     }
   }
-  for (int idx = tid; idx < kMaxNodes * kLd; idx += 256) Tl[idx] = 0.f;
+  for (int idx = tid; idx < Np * kLd; idx += 256) Tl[idx] = 0.f;
 
   // ---- 1. parents -> validation, ancestor-or-self masks and G (pointer jumping)
   if (wave == 0) {
@@ -423,36 +464,27 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
       if (idx < kDlyChunk * L::kBVT) dly.u[idx] = dur[x];
     }
   };
-  // S_tile <- S_tile + sum over staged nodes [c0, c0 + nc) of c_i u'_i k_i^T, one
-  // multiply-add per node in node order (the commit kernel's order)
-  auto dly_apply = [&](int c0, int nc) {
-    for (int jj = 0; jj < nc; ++jj) {  // uniform
-      const float cu = dly.c[c0 + jj] * dly.u[jj * L::kBVT + (ccol < L::kBVT ? ccol : 0)];
-#pragma unroll
-      for (int ks = 0; ks < kMaxDim / 32; ++ks) {
-        const float* kr = &dly.k[jj * kMaxDim + 32 * ks + koff];
-        const f32x4 k0 = *reinterpret_cast<const f32x4*>(kr);
-        const f32x4 k1 = *reinterpret_cast<const f32x4*>(kr + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Sraw[ks][0][e] = fmaf(cu, k0[e], Sraw[ks][0][e]);
-          Sraw[ks][1][e] = fmaf(cu, k1[e], Sraw[ks][1][e]);
-        }
-      }
-    }
-  };
-  // the whole commit on the register tile, then its write-back (one wave per
-  // row set); `first_staged` says whether chunk 0 is already in LDS
-  auto dly_commit = [&](bool first_staged) {
+  // the whole commit on the register tile, then its write-back; `first_staged`
+  // says whether chunk 0 is already in LDS.  With 16-row tiles or narrower
+  // all four waves hold the same rows (WR == 4), so each updates a quarter of
+  // the columns (ks chunks [KQ0, KQ1)), writes it back, and the committed
+  // quarters are exchanged through the N x N A block's LDS, free once the
+  // solves are done (`xchg`, which then costs two barriers).
+  constexpr bool kSplit = WR == 4;
+  constexpr int KQN = kSplit ? (kMaxDim / 32) / 4 : kMaxDim / 32;
+  const int KQ0 = kSplit ? rb * KQN : 0;
+  constexpr int kXLd = kMaxDim + 4;  // row stride (floats) of the exchanged tile
+  auto dly_commit = [&](bool first_staged, bool xchg) {
     if (dn == 0) return;  // uniform
     const float s0 = sdly_s0;
 #pragma unroll
     for (int ks = 0; ks < kMaxDim / 32; ++ks)
+      if (!kSplit || (ks >= KQ0 && ks < KQ0 + KQN))
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Sraw[ks][0][e] = Sraw[ks][0][e] * s0;
-        Sraw[ks][1][e] = Sraw[ks][1][e] * s0;
-      }
+        for (int e = 0; e < 4; ++e) {
+          Sraw[ks][0][e] = Sraw[ks][0][e] * s0;
+          Sraw[ks][1][e] = Sraw[ks][1][e] * s0;
+        }
     for (int c0 = 0; c0 < dn; c0 += kDlyChunk) {  // uniform
       if (c0 > 0 || !first_staged) {
         __syncthreads();  // every wave is done with the previous chunk
@@ -460,21 +492,54 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         dly_store();
         __syncthreads();
       }
-      dly_apply(c0, dn - c0 < kDlyChunk ? dn - c0 : kDlyChunk);
+      const int nc = dn - c0 < kDlyChunk ? dn - c0 : kDlyChunk;
+      for (int jj = 0; jj < nc; ++jj) {  // uniform; node order as in the commit kernel
+        const float cu = dly.c[c0 + jj] * dly.u[jj * L::kBVT + (ccol < L::kBVT ? ccol : 0)];
+#pragma unroll
+        for (int ks = 0; ks < kMaxDim / 32; ++ks) {
+          if (kSplit && (ks < KQ0 || ks >= KQ0 + KQN)) continue;
+          const float* kr = &dly.k[jj * kMaxDim + 32 * ks + koff];
+          const f32x4 k0 = *reinterpret_cast<const f32x4*>(kr);
+          const f32x4 k1 = *reinterpret_cast<const f32x4*>(kr + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            Sraw[ks][0][e] = fmaf(cu, k0[e], Sraw[ks][0][e]);
+            Sraw[ks][1][e] = fmaf(cu, k1[e], Sraw[ks][1][e]);
+          }
+        }
+      }
     }
-    if (rb == 0 && sok) {
+    if ((kSplit || rb == 0) && sok) {  // write-back: each element once
       float* wp = S0 + ((size_t)bh * dv + srow) * dk;
 #pragma unroll
       for (int ks = 0; ks < kMaxDim / 32; ++ks) {
         const int col = 32 * ks + koff;
-        if (col < dk) {
+        if ((!kSplit || (ks >= KQ0 && ks < KQ0 + KQN)) && col < dk) {
           *reinterpret_cast<f32x4*>(wp + col) = Sraw[ks][0];
           *reinterpret_cast<f32x4*>(wp + col + 4) = Sraw[ks][1];
         }
       }
     }
+    if (kSplit && xchg) {  // every wave needs the whole committed tile for step 4
+      float* X = KK;       // 16 rows x kXLd floats fit in the A block's space
+      __syncthreads();     // the solves (readers of A) are done
+#pragma unroll
+      for (int ks = 0; ks < kMaxDim / 32; ++ks)
+        if (ks >= KQ0 && ks < KQ0 + KQN) {
+          *reinterpret_cast<f32x4*>(X + l16 * kXLd + 32 * ks + koff) = Sraw[ks][0];
+          *reinterpret_cast<f32x4*>(X + l16 * kXLd + 32 * ks + koff + 4) = Sraw[ks][1];
+        }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < kMaxDim / 32; ++ks) {
+        Sraw[ks][0] = *reinterpret_cast<const f32x4*>(X + l16 * kXLd + 32 * ks + koff);
+        Sraw[ks][1] = *reinterpret_cast<const f32x4*>(X + l16 * kXLd + 32 * ks + koff + 4);
+      }
+    }
   };
+  static_assert(!kSplit || 16 * kXLd * 4 <= L::kMat, "exchange tile exceeds the A block");
   if (DLY && dn > 0) dly_load(0);  // lands while steps 2-3 run
+  load_state();                     // likewise: first needed by step 4
 
   const bool bad = sbad != 0;
   if (tile == 0) {  // factor record: copy of k for this head
@@ -492,7 +557,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     }
   }
   if (bad) {  // uniform: zero this tile's outputs (a delayed commit still applies)
-    if (DLY) dly_commit(false);
+    if (DLY) dly_commit(false, false);
     const int c = tid % BV;
     for (int t = tid / BV; t < N; t += 256 / BV)
       if (r0 + c < dv) {
@@ -548,8 +613,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
   for (int x = 0; x < EPT; ++x) {
     const int idx = tid + 256 * x;
-    const int t = idx / kMaxNodes;
-    const int j = idx % kMaxNodes;
+    const int t = idx / NK;
+    const int j = idx % NK;
     const uint64_t m = smask[t];
     const bool on = (m >> j) & 1ull;  // j on t's root path (t >= N: empty mask)
     const float dec = __expf(sG[t] - sG[j]);
@@ -561,19 +626,21 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
   for (int x = 0; x < EPT; ++x) {
     const int idx = tid + 256 * x;
-    store_split1(Attn + (idx / kMaxNodes) * kLdH + idx % kMaxNodes, kSplitLo, attn[x]);
+    store_split1(Attn + (idx / NK) * kLdH + idx % NK, kSplitLo, attn[x]);
   }
   if (tid < N) {
     const int t = tid;
     const uint64_t m = smask[t];
     const int d = __popcll(m);
-    if (d <= kPathMax)
+    if (d <= 8)
+      path_solve_registers8(t, m, d, KK, Tl + t * kLd);
+    else if (d <= kPathMax)
       path_solve_registers(t, m, d, KK, Tl + t * kLd);
     else
       path_solve_lds(t, m, KK, Tl + t * kLd);
   }
 
-  if (DLY) dly_commit(true);
+  if (DLY) dly_commit(true, true);
 
   // ---- 4. Y = [Q; K] S0_tile^T (this wave: column tile cj, row tiles rb + WR*i)
   f32x4 yacc[MAXRT];
@@ -615,7 +682,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
   for (int x = 0; x < EPT; ++x) {
     const int idx = tid + 256 * x;
-    trow[x] = Tl[(idx / kMaxNodes) * kLd + idx % kMaxNodes];
+    trow[x] = Tl[(idx / NK) * kLd + idx % NK];
   }
   // R = diag(beta) (V - diag(e^G) K S0^T) from the K-row accumulators
   f32x4 rv[MAXNB];
@@ -643,7 +710,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
   for (int x = 0; x < EPT; ++x) {
     const int idx = tid + 256 * x;
-    store_split1(Ts + (idx / kMaxNodes) * kLdH + idx % kMaxNodes, kSplitLo, trow[x]);
+    store_split1(Ts + (idx / NK) * kLdH + idx % NK, kSplitLo, trow[x]);
   }
 #pragma unroll
   for (int j = 0; j < MAXNB; ++j) {
