@@ -543,17 +543,32 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 
   const bool bad = sbad != 0;
   if (tile == 0) {  // factor record: copy of k for this head
-    const int cpr = dk / 4;
-    for (int idx = tid; idx < N * cpr; idx += 256) {
-      const int t = idx / cpr;
-      const int cc = 4 * (idx % cpr);
-      T* dst = rec.K + ((size_t)bh * N + t) * dk + cc;
-      if (kStaged)  // the staged K rows in LDS hold exactly these bits
-        *reinterpret_cast<u32x2*>(dst) =
-            *reinterpret_cast<const u32x2*>(QKs + (Np + t) * kQKStride + cc);
-      else
-        copy4e(reinterpret_cast<float*>(dst),
+    if constexpr (kStaged) {  // the staged K rows in LDS hold exactly these bits
+      constexpr int kC8 = kMaxDim / 8;              // 16-byte chunks per staged row
+      constexpr int RKC = Np * kC8 / 256;           // chunks per thread
+      u32x4 kc[RKC];
+#pragma unroll
+      for (int x = 0; x < RKC; ++x) {  // all reads first, then the stores
+        const int idx = tid + 256 * x;
+        kc[x] = *reinterpret_cast<const u32x4*>(QKs + (Np + idx / kC8) * kQKStride +
+                                                8 * (idx % kC8));
+      }
+#pragma unroll
+      for (int x = 0; x < RKC; ++x) {
+        const int idx = tid + 256 * x;
+        const int t = idx / kC8;
+        const int c8 = 8 * (idx % kC8);
+        if (t < N && c8 < dk)
+          *reinterpret_cast<u32x4*>(rec.K + ((size_t)bh * N + t) * dk + c8) = kc[x];
+      }
+    } else {
+      const int cpr = dk / 4;
+      for (int idx = tid; idx < N * cpr; idx += 256) {
+        const int t = idx / cpr;
+        const int cc = 4 * (idx % cpr);
+        copy4e(reinterpret_cast<float*>(rec.K + ((size_t)bh * N + t) * dk + cc),
                reinterpret_cast<const float*>(k) + (((size_t)b * N + t) * H + h) * dk + cc);
+      }
     }
   }
   if (bad) {  // uniform: zero this tile's outputs (a delayed commit still applies)
@@ -568,6 +583,56 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   }
 
   // ---- 2. Gram blocks C = [Q; K] K^T on MFMA (tiles with j <= t only)
+  if constexpr (kStaged) {
+    // The kGT lower-triangle tiles (Q rows, then K rows) go round-robin to
+    // the waves with no branch, so each tile's fragment reads can issue while
+    // the previous tile's MFMAs run.  A wave past the end recomputes the last
+    // tile and stores the same bits again.
+    constexpr int kTri = NQT * (NQT + 1) / 2;
+    constexpr int kGT = 2 * kTri;
+    constexpr int kGPW = (kGT + 3) / 4;
+    constexpr int KS = kMaxDim / 32;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    struct GTile {
+      bool isq;
+      int rtl, ct;
+    };
+    auto gtile = [&](int i) {
+      const int tau = wv + 4 * i < kGT ? wv + 4 * i : kGT - 1;
+      GTile g;
+      g.isq = tau < kTri;
+      const int tq = g.isq ? tau : tau - kTri;
+      g.rtl = 0;  // tq = rtl (rtl + 1) / 2 + ct with ct <= rtl
+#pragma unroll
+      for (int r = 1; r < NQT; ++r) g.rtl += tq >= r * (r + 1) / 2;
+      g.ct = tq - g.rtl * (g.rtl + 1) / 2;
+      return g;
+    };
+    bf16x8 af[2][KS], bfr[2][KS];  // fragments of tiles i (set i & 1) and i + 1
+    auto gload = [&](int i) {
+      const GTile g = gtile(i);
+      const bf16_t* arow = QKs + (16 * (g.isq ? g.rtl : NQT + g.rtl) + l16) * kQKStride + koff;
+      const bf16_t* brow = QKs + (Np + 16 * g.ct + l16) * kQKStride + koff;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {  // columns past dk are zero
+        af[i & 1][ks] = lds_bf16x8(arow + 32 * ks);
+        bfr[i & 1][ks] = lds_bf16x8(brow + 32 * ks);
+      }
+    };
+    gload(0);
+#pragma unroll
+    for (int i = 0; i < kGPW; ++i) {
+      if (i + 1 < kGPW) gload(i + 1);  // in flight while tile i multiplies
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(af[i & 1][ks], bfr[i & 1][ks], acc);
+      const GTile g = gtile(i);
+      float* dst = g.isq ? QK : KK;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * g.rtl + 4 * lg + r) * kLd + 16 * g.ct + l16] = acc[r];
+    }
+  } else {
   for (int tileid = wave; tileid < nrt * NQT; tileid += 4) {
     const int rt = tileid / NQT;
     const int ct = tileid % NQT;
@@ -575,13 +640,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int rtl = isq ? rt : rt - NQT;
     if (ct > rtl) continue;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (kStaged) {
-      const bf16_t* arow = QKs + (16 * rt + l16) * kQKStride + koff;
-      const bf16_t* brow = QKs + (Np + 16 * ct + l16) * kQKStride + koff;
-#pragma unroll
-      for (int ks = 0; ks < kMaxDim / 32; ++ks)  // columns past dk are zero
-        acc = mfma16x16x32(lds_bf16x8(arow + 32 * ks), lds_bf16x8(brow + 32 * ks), acc);
-    } else {
+    {
       const int ti = 16 * rtl + l16;
       const int tj = 16 * ct + l16;
       const float* arow = reinterpret_cast<const float*>(isq ? (const void*)q : (const void*)k) +
@@ -603,24 +662,39 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[(16 * rtl + 4 * lg + r) * kLd + 16 * ct + l16] = acc[r];
   }
+  }
   if (DLY && dn > 0) dly_store();  // the path loads issued after step 1
   __syncthreads();
 
   // ---- 3. A (FP32, in place of K K^T) and Attn (split bf16, in place of
   // Q K^T) over all N x N entries, exact zeros off the masks; then the rows
   // of T on root paths (one lane per node).
-  float attn[EPT];
+  // Every operand is read unconditionally first (all in bounds: t < Np,
+  // j < NK), so the reads issue together instead of one masked round trip
+  // per entry.
+  float attn[EPT], kkv[EPT], qkv[EPT], gt[EPT], gj[EPT], bt[EPT];
+  uint64_t mt[EPT];
 #pragma unroll
   for (int x = 0; x < EPT; ++x) {
     const int idx = tid + 256 * x;
     const int t = idx / NK;
     const int j = idx % NK;
-    const uint64_t m = smask[t];
-    const bool on = (m >> j) & 1ull;  // j on t's root path (t >= N: empty mask)
-    const float dec = __expf(sG[t] - sG[j]);
-    float* a = KK + t * kLd + j;
-    *a = (on && j != t) ? sbeta[t] * dec * *a : 0.f;
-    attn[x] = on ? scale * dec * QK[t * kLd + j] : 0.f;
+    mt[x] = smask[t];
+    gt[x] = sG[t];
+    gj[x] = sG[j];
+    bt[x] = sbeta[t];
+    kkv[x] = KK[t * kLd + j];
+    qkv[x] = QK[t * kLd + j];
+  }
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    const int idx = tid + 256 * x;
+    const int t = idx / NK;
+    const int j = idx % NK;
+    const bool on = (mt[x] >> j) & 1ull;  // j on t's root path (t >= N: empty mask)
+    const float dec = __expf(gt[x] - gj[x]);
+    KK[t * kLd + j] = (on && j != t) ? bt[x] * dec * kkv[x] : 0.f;
+    attn[x] = on ? scale * dec * qkv[x] : 0.f;
   }
   __syncthreads();
 #pragma unroll
