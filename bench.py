@@ -3,17 +3,26 @@
 
 A step is the whole hot path over one batch of synthetic drafts for one GDN
 layer (h = 8, d_k = d_v = 256, FP32 state): verification (chain kernel for
-chain workloads, tree-masked factorized kernels otherwise) followed by the
-accepted-path commit from the factor record.  Steps rotate over enough
-distinct layer states (default 1 GiB in total, several times the 256 MB
-Infinity Cache) that every state read comes from HBM.
+chain workloads, tree-masked factorized kernel otherwise) and the commit of
+an accepted path from a factor record.  By default the commit is delayed: the
+step's single launch first commits the accepted path of the draft that the
+same state verified on its previous visit, then verifies the new draft
+(bitwise the same as commit followed by verify); --separate-commit runs the
+plain verification and then gdn_commit_path as two launches.  Steps rotate
+over enough distinct layer states (default 1 GiB in total, several times the
+256 MB Infinity Cache) that every state read comes from HBM.  The
+decode24-b1-h8-d256 workload runs the 24-layer decode loop instead.
 
 Prints one JSON line:
   value           verified draft nodes per second (B * N per step), measured on
                   a HIP-graph replay of K steps (no host launch overhead)
-  roofline        dominant kernel: algorithmic bytes per launch / its average
-                  duration (events around a HIP-graph replay of back-to-back
-                  launches of that kernel alone), against 8 TB/s
+  roofline        dominant kernel, timed alone (events around a HIP-graph
+                  replay of back-to-back launches): for the chain kernel its
+                  algorithmic bytes per launch / duration against 8 TB/s; for
+                  the tree kernel its FP32-equivalent contraction flops per
+                  launch / duration against the 157.3 TFLOP/s FP32 peak (with
+                  the bf16 rate it issues and its HBM rate alongside);
+                  `traffic` from the rocprofv3 counter summaries in profiles/
   cpu_baseline    the CPU oracle (per-path fp64 replay + commit replay) on a
                   bounded number of steps of the same workload
 """
@@ -442,6 +451,20 @@ def _time_graph(g, stream, reps=1):
     return e0.elapsed_time(e1) * 1e-3  # seconds
 
 
+def _time_eager(fn, count, stream, reps=1):
+    """Seconds for reps * count direct calls fn(0..count-1) on `stream`."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        for j in range(count):
+            fn(j)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
 def stack_cpu_baseline(shape, layers, S0, parents, lasts, x0_bits, budget_s):
     """Oracle steps (24-layer verify + commit, fp64 with bf16 rounding at the
     projection inputs and q/k/v) on the host for about `budget_s` seconds."""
@@ -524,6 +547,8 @@ def bench_decode_loop(args):
 
     def timed(step_fn):
         reps, rem = divmod(args.steps, chunk)
+        if args.no_graph:
+            return _time_eager(step_fn, chunk, stream, reps) + _time_eager(step_fn, rem, stream)
         el = _time_graph(_graph_of(step_fn, chunk, stream), stream, reps)
         if rem:
             el += _time_graph(_graph_of(step_fn, rem, stream), stream)
@@ -578,7 +603,10 @@ def bench_decode_loop(args):
     }
     kernels = {}
     for name, (fn, nbytes) in kern.items():
-        us = _time_graph(_graph_of(fn, nper, stream), stream) * 1e6 / nper
+        if args.no_graph:
+            us = _time_eager(fn, nper, stream) * 1e6 / nper
+        else:
+            us = _time_graph(_graph_of(fn, nper, stream), stream) * 1e6 / nper
         kernels[name] = {"avg_us": round(us, 3)}
         if nbytes:
             kernels[name]["bytes"] = int(nbytes)
@@ -609,7 +637,8 @@ def bench_decode_loop(args):
         "data": "synthetic",
         "config": {"workload": args.workload, "layers": L, "hidden": shape.D, "B": 1, "N": N,
                    "H": shape.H, "dk": shape.dk, "dv": shape.dv, "weights": "bf16",
-                   "state_dtype": "f32", "timing": "hip_graph", "parallelism": "single-gpu"},
+                   "state_dtype": "f32", "timing": "eager" if args.no_graph else "hip_graph",
+                   "parallelism": "single-gpu"},
         "decode_loop": {
             "stack_nodes_per_s": round(N / (ms_step * 1e-3), 1),
             "mean_accepted_per_step": round(float(acc_per_step), 3),
