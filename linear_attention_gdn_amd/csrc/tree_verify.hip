@@ -302,9 +302,10 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   const int pl = parents[(size_t)b * N + tn];
   const float gl = g[((size_t)b * N + tn) * H + h];
   const float bl = beta[((size_t)b * N + tn) * H + h];
-  // The state tile (straight into MFMA B-fragment order) and V are loaded
-  // after the topology step (load_state below): step 4 is the first to need
-  // them, and loads issued here would be waited for by the Q/K staging.
+  // The state tile (straight into MFMA B-fragment order) and V are requested
+  // last in this round (load_state below): loads complete in issue order, so
+  // the Q/K staging and the topology step wait only for what was issued
+  // before them, while the state streams in behind steps 1-3.
   f32x4 Sraw[kMaxDim / 32][2];
   // V for the K row tiles this wave turns into R: its j-th K tile is row tile
   // rt = rb + WR*(iK0 + j) >= NQT, node block rt - NQT (D layout: node
@@ -340,18 +341,20 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     pmask_l = prev.mask[(size_t)b * Npv + tj];
     pG_l = prev.G[(size_t)bh * Npv + tj];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load above issued before the state's
+  load_state();
+  __builtin_amdgcn_sched_barrier(0);
 
   if (kStaged) {
+    static_assert(qk_total % 256 == 0, "every thread stages QKB chunks");
 #pragma unroll
-    for (int x = 0; x < QKB; ++x) {
+    for (int x = 0; x < QKB; ++x) {  // no branch: a load under one is waited for at once
       const int idx = tid + 256 * x;
-      if (idx < qk_total) {
-        const int r = idx / qk_cpr;
-        const int t = r < Np ? r : r - Np;
-        const int c8 = 8 * (idx % qk_cpr);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
-      }
+      const int r = idx / qk_cpr;
+      const int t = r < Np ? r : r - Np;
+      const int c8 = 8 * (idx % qk_cpr);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
     }
   }
   for (int idx = tid; idx < Np * kLd; idx += 256) Tl[idx] = 0.f;
@@ -476,6 +479,15 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   constexpr int kXLd = kMaxDim + 4;  // row stride (floats) of the exchanged tile
   auto dly_commit = [&](bool first_staged, bool xchg) {
     if (dn == 0) return;  // uniform
+    // Stores count in the same vector-memory counter as loads: every state
+    // and V register is consumed here, before the first write-back store, so
+    // no later wait for those loads also waits for the stores to drain.
+#pragma unroll
+    for (int ks = 0; ks < kMaxDim / 32; ++ks) asm volatile("" : "+v"(Sraw[ks][0]), "+v"(Sraw[ks][1]));
+#pragma unroll
+    for (int j = 0; j < MAXNB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) asm volatile("" : "+v"(vreg[j][r]));
     const float s0 = sdly_s0;
 #pragma unroll
     for (int ks = 0; ks < kMaxDim / 32; ++ks)
@@ -539,7 +551,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   };
   static_assert(!kSplit || 16 * kXLd * 4 <= L::kMat, "exchange tile exceeds the A block");
   if (DLY && dn > 0) dly_load(0);  // lands while steps 2-3 run
-  load_state();                     // likewise: first needed by step 4
 
   const bool bad = sbad != 0;
   if (tile == 0) {  // factor record: copy of k for this head

@@ -32,6 +32,7 @@ def _lasts(prev: W.Draft, rng):
     ("f32", 2, 7, 9, 2, 40, 32, "chain"),
     ("bf16", 3, 64, 16, 2, 256, 64, "branching"),
     ("bf16", 1, 1, 3, 1, 16, 8, "chain"),
+    ("bf16", 1, 64, 64, 2, 256, 16, "chain"),  # largest LDS footprint (~136 KB)
 ])
 def test_delayed_chain_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo):
     seed = B * 100 + Np + N
