@@ -108,12 +108,6 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
     const int r = clampi(r0 + idx % kChainRows, dv - 1);
     vb[x] = v[(((size_t)b * N + idx / kChainRows) * H + h) * dv + r];
   }
-  f32x4 Sx[MC];
-  {
-    const float* rp = S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) Sx[m] = load4(rp + clampi(128 * m + 4 * s, dk - 4));
-  }
   // the previous draft's record (delayed commit): masks, G, u' of this tile's
   // rows and the k rows, none of which depends on last_accepted
   constexpr int BATCH = 4;
@@ -145,8 +139,7 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
   }
   // k and q rows: the first batch is straight-line code (a loop here would
   // drain every outstanding load at its header); larger drafts loop.
-  auto stage = [&](int base) {
-    R4 kb[BATCH], qb[BATCH];
+  auto stage_load = [&](int base, R4 (&kb)[BATCH], R4 (&qb)[BATCH]) {
 #pragma unroll
     for (int x = 0; x < BATCH; ++x) {
       const int idx = clampi(base + 256 * x, N * cpr - 1);
@@ -154,17 +147,38 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
       kb[x] = raw4(k + off);
       qb[x] = raw4(q + off);
     }
+  };
+  // No branch around the stores (a load used only under one is sunk into it
+  // and waited for together with everything issued before): past the end a
+  // thread rewrites the clamped chunk with the bits it loaded for it, which
+  // are the owner's bits.
+  auto stage_store = [&](int base, const R4 (&kb)[BATCH], const R4 (&qb)[BATCH]) {
 #pragma unroll
     for (int x = 0; x < BATCH; ++x) {
-      const int idx = base + 256 * x;
-      if (idx < N * cpr) {
-        sk[idx] = stage_cvt(kb[x], (SK*)nullptr);
-        sq[idx] = stage_cvt(qb[x], (SK*)nullptr);
-      }
+      const int idx = clampi(base + 256 * x, N * cpr - 1);
+      sk[idx] = stage_cvt(kb[x], (SK*)nullptr);
+      sq[idx] = stage_cvt(qb[x], (SK*)nullptr);
     }
   };
-  stage(tid);
-  for (int base = tid + 256 * BATCH; base < N * cpr; base += 256 * BATCH) stage(base);
+  R4 kb0[BATCH], qb0[BATCH];
+  stage_load(tid, kb0, qb0);
+  // The state row is requested last: loads complete in issue order, so the
+  // staging below waits only for the loads above, and the state (from HBM)
+  // streams in while the staging and the k.q products run.
+  f32x4 Sx[MC];
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const float* rp = S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) Sx[m] = load4(rp + clampi(128 * m + 4 * s, dk - 4));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  stage_store(tid, kb0, qb0);
+  for (int base = tid + 256 * BATCH; base < N * cpr; base += 256 * BATCH) {
+    R4 kb[BATCH], qb[BATCH];
+    stage_load(base, kb, qb);
+    stage_store(base, kb, qb);
+  }
   if (DLY) {
 #pragma unroll
     for (int x = 0; x < BATCH; ++x)
@@ -206,15 +220,6 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
       if (idx < Np * kChainRows) sup[idx] = (r0 + idx % kChainRows < dv) ? upb[x] : 0.f;
     }
   }
-  float S[MC][4];
-#pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    const f32x4 x = mask4(Sx[m], rok && colok(m));
-    S[m][0] = x.x;
-    S[m][1] = x.y;
-    S[m][2] = x.z;
-    S[m][3] = x.w;
-  }
   __syncthreads();
 
   // ---- k_t . q_t, the same for every row: half-wave rl takes nodes rl, rl + 8, ...
@@ -235,6 +240,17 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
     }
     a = half32_sum(a + a2);
     if (s == 0) skq[t] = a;
+  }
+
+  // the state row (first needed here)
+  float S[MC][4];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    const f32x4 x = mask4(Sx[m], rok && colok(m));
+    S[m][0] = x.x;
+    S[m][1] = x.y;
+    S[m][2] = x.z;
+    S[m][3] = x.w;
   }
 
   if (DLY) {
