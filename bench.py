@@ -344,6 +344,18 @@ def main():
     else:
         t_ver = np.array([graph_time(verify)])
         t_com = np.array([graph_time(commit)])
+    # The latency floor of one step on this GPU, in the same harness: an empty
+    # kernel, and a plain device copy that reads one step's states (rotating
+    # like the steps, so from HBM) and writes as many bytes.
+    floor = None
+    if not args.no_graph:
+        scratch = torch.empty_like(states[0])
+        t_empty = graph_time(lambda i: torch.cuda._sleep(0))
+        t_copy = graph_time(lambda i: scratch.copy_(states[i % R]))
+        floor = {"empty_kernel_us": round(t_empty * 1e3, 3),
+                 "state_copy_us": round(t_copy * 1e3, 3),
+                 "state_copy_bytes": 2 * state_bytes,
+                 "state_copy_gbs": round(2 * state_bytes / (t_copy * 1e-3) / 1e9, 1)}
     plens = path_lengths(d, lasts_np[args.warmup:args.warmup + nper])
     b_ver = bytes_verify(d, not chain)
     b_com = np.mean([bytes_commit(d, p) for p in plens])
@@ -411,6 +423,7 @@ def main():
                              else "separate launch after each verification",
                    "parallelism": "single-gpu"},
         "roofline": roofline,
+        "latency_floor": floor,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }

@@ -504,19 +504,52 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         dly_store();
         __syncthreads();
       }
-      const int nc = dn - c0 < kDlyChunk ? dn - c0 : kDlyChunk;
-      for (int jj = 0; jj < nc; ++jj) {  // uniform; node order as in the commit kernel
-        const float cu = dly.c[c0 + jj] * dly.u[jj * L::kBVT + (ccol < L::kBVT ? ccol : 0)];
+      const int nc = __builtin_amdgcn_readfirstlane(dn - c0 < kDlyChunk ? dn - c0 : kDlyChunk);
+      // Narrow tiles: columns [32 K0, 32 (K0 + KQN)) of the tile, a compile-time
+      // range, so each node's LDS reads issue together with no branch between.
+      auto apply_nodes = [&](auto k0c) {
+        constexpr int K0 = decltype(k0c)::value;
+        for (int jj = 0; jj < nc; ++jj) {  // uniform; node order as in the commit kernel
+          const float cu = dly.c[c0 + jj] * dly.u[jj * L::kBVT + (ccol < L::kBVT ? ccol : 0)];
+          f32x4 kv[KQN][2];
 #pragma unroll
-        for (int ks = 0; ks < kMaxDim / 32; ++ks) {
-          if (kSplit && (ks < KQ0 || ks >= KQ0 + KQN)) continue;
-          const float* kr = &dly.k[jj * kMaxDim + 32 * ks + koff];
-          const f32x4 k0 = *reinterpret_cast<const f32x4*>(kr);
-          const f32x4 k1 = *reinterpret_cast<const f32x4*>(kr + 4);
+          for (int q = 0; q < KQN; ++q) {
+            const float* kr = &dly.k[jj * kMaxDim + 32 * (K0 + q) + koff];
+            kv[q][0] = *reinterpret_cast<const f32x4*>(kr);
+            kv[q][1] = *reinterpret_cast<const f32x4*>(kr + 4);
+          }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            Sraw[ks][0][e] = fmaf(cu, k0[e], Sraw[ks][0][e]);
-            Sraw[ks][1][e] = fmaf(cu, k1[e], Sraw[ks][1][e]);
+          for (int q = 0; q < KQN; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              Sraw[K0 + q][0][e] = fmaf(cu, kv[q][0][e], Sraw[K0 + q][0][e]);
+              Sraw[K0 + q][1][e] = fmaf(cu, kv[q][1][e], Sraw[K0 + q][1][e]);
+            }
+        }
+      };
+      if constexpr (kSplit) {
+        switch (__builtin_amdgcn_readfirstlane(rb)) {  // this wave's quarter of the columns
+          case 0: apply_nodes(std::integral_constant<int, 0 * KQN>{}); break;
+          case 1: apply_nodes(std::integral_constant<int, 1 * KQN>{}); break;
+          case 2: apply_nodes(std::integral_constant<int, 2 * KQN>{}); break;
+          default: apply_nodes(std::integral_constant<int, 3 * KQN>{}); break;
+        }
+      } else {
+        // wide tiles: every wave reads all of k per node, bounded by LDS
+        // bandwidth, where interleaving the reads with the multiply-adds is
+        // faster than issuing them together
+        for (int jj = 0; jj < nc; ++jj) {
+          const float cu = dly.c[c0 + jj] * dly.u[jj * L::kBVT + (ccol < L::kBVT ? ccol : 0)];
+#pragma unroll
+          for (int ks = 0; ks < kMaxDim / 32; ++ks) {
+            const float* kr = &dly.k[jj * kMaxDim + 32 * ks + koff];
+            const f32x4 k0 = *reinterpret_cast<const f32x4*>(kr);
+            const f32x4 k1 = *reinterpret_cast<const f32x4*>(kr + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              Sraw[ks][0][e] = fmaf(cu, k0[e], Sraw[ks][0][e]);
+              Sraw[ks][1][e] = fmaf(cu, k1[e], Sraw[ks][1][e]);
+            }
           }
         }
       }
