@@ -597,6 +597,10 @@ def bench_decode_loop(args):
         "tree_verify_delayed": (lambda j: G.gdn_tree_verify_delayed(
             st.S[j % L], st.rec[st.cur][j % L], lasts[0], parents[0], st.q, st.k, st.v, st.beta,
             st.g, st.out, st.rec[1 - st.cur][j % L]), None),
+        "layer_verify": (lambda j: G.gdn_layer_verify(
+            st.S[j % L], parents[0], st.q, st.k, st.v, st.beta, st.g, P2(j % L)[:, g0:g1], st.Y,
+            st.rec[1 - st.cur][j % L], prev_factors=st.rec[st.cur][j % L],
+            last_accepted=lasts[0]), None),
         "gate_merge": (lambda j: G.gdn_gate_merge(st.out.view(M, sh.H * sh.dv),
                                                   P2(j % L)[:, g0:g1], st.Y), None),
         "linear_out": (lambda j: G.gdn_linear(st.Y, st.W_o[j % L], C=st.x, R=st.x,

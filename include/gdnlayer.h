@@ -124,6 +124,32 @@ int gdn_gate_merge(int M, int Cw, const float* o, const float* gate, int ldg, vo
                    void* stream);
 
 /*
+ * gdn_layer_verify: the layer's tree verification with the SiLU output gate
+ * fused into its epilogue, for bf16 q, k, v.  With prev_factors != NULL it is
+ * gdn_tree_verify_delayed (the previous draft's accepted path is committed to
+ * S first; N_prev, last_accepted and commit_status as there), else
+ * gdn_tree_verify (S read only; N_prev, last_accepted ignored).  Instead of
+ * the FP32 output O it writes
+ *   Y  bf16 [B][N][H*dv]: Y[b][t][h*dv + c] = bf16(O[b][t][h][c] * SiLU(gate))
+ *      with gate = gate[(b*N + t)*ldg + h*dv + c] (the gate block of P,
+ *      ldg >= H*dv),
+ * bitwise equal to the verify call followed by gdn_gate_merge on O.  The
+ * factor record, S and the status words are exactly those of that verify call.
+ * It is the verifier (SpecLA review, "Core claim"; "What carries the
+ * argument") with the block's output gate (review: skeptic critique and
+ * Referee Report major comment 1, both on Section 7) folded in, so a
+ * layer's step saves the gate launch and the FP32 output round trip.
+ * Errors: as the verify call, plus GDN_ERR_SHAPE for ldg < H*dv and GDN_ERR_ARG
+ * for a NULL or misaligned gate or Y.
+ */
+int gdn_layer_verify(int B, int N_prev, int N, int H, int dk, int dv, float* S,
+                     const void* prev_factors, const int32_t* last_accepted,
+                     int32_t* commit_status, const int32_t* parents, const void* q,
+                     const void* k, const void* v, const float* beta, const float* g,
+                     float scale, const float* gate, int ldg, void* Y, void* factors,
+                     int32_t* dev_status, void* stream);
+
+/*
  * gdn_conv_commit: the convolution history after accepting the root path of
  * node last_accepted[b] (path p_1..p_n, root first): the new history is
  * P[p_n], P[p_{n-1}], ... followed by the old history, truncated to three

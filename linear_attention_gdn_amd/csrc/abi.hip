@@ -21,7 +21,8 @@ hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, fl
                               const void* v, const float* beta, const float* g, float scale,
                               float* out, void* factors, void* workspace, uint64_t* mask_out,
                               int32_t* dev_status, const void* prev_factors, int Np,
-                              const int32_t* last, int32_t* commit_status, hipStream_t stream);
+                              const int32_t* last, int32_t* commit_status, const float* gate,
+                              int ldg, void* Y, hipStream_t stream);
 hipError_t launch_commit(int B, int N, int H, int dk, int dv, int dtype, float* S,
                          const void* factors, const int32_t* last, int32_t* path_out,
                          int32_t* path_len, int32_t* dev_status, hipStream_t stream);
@@ -168,6 +169,7 @@ int gdn_tree_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const fl
                                                 const_cast<float*>(S0), parents, q, k, v, beta,
                                                 g, scale, out, factors, workspace, mask_out,
                                                 dev_status, nullptr, 0, nullptr, nullptr,
+                                                nullptr, 0, nullptr,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -210,8 +212,8 @@ int gdn_tree_verify_delayed(int B, int N_prev, int N, int H, int dk, int dv, int
   return hip_status(fn, gdn::launch_tree_verify(B, N, H, dk, dv, qkv_dtype, S, parents, q, k, v,
                                                 beta, g, scale, out, factors, workspace,
                                                 mask_out, dev_status, prev_factors, N_prev,
-                                                last_accepted, commit_status,
-                                                static_cast<hipStream_t>(stream)));
+                                                last_accepted, commit_status, nullptr, 0,
+                                                nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_chain_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const float* S0,
@@ -377,6 +379,48 @@ int gdn_gate_merge(int M, int Cw, const float* o, const float* gate, int ldg, vo
   GDN_TRY(check_ptr(fn, "Y", Y, true));
   return hip_status(fn, gdn::launch_gate_merge(M, Cw, o, gate, ldg, Y,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int gdn_layer_verify(int B, int N_prev, int N, int H, int dk, int dv, float* S,
+                     const void* prev_factors, const int32_t* last_accepted,
+                     int32_t* commit_status, const int32_t* parents, const void* q,
+                     const void* k, const void* v, const float* beta, const float* g,
+                     float scale, const float* gate, int ldg, void* Y, void* factors,
+                     int32_t* dev_status, void* stream) {
+  const char* fn = "gdn_layer_verify";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  const bool dly = prev_factors != nullptr;
+  if (dly && (N_prev < 1 || N_prev > gdn::kMaxNodes))
+    return fail(GDN_ERR_SHAPE, "%s: N_prev=%d outside 1..64", fn, N_prev);
+  if (!std::isfinite(scale)) return fail(GDN_ERR_ARG, "%s: scale is not finite", fn);
+  if (ldg < H * dv) return fail(GDN_ERR_SHAPE, "%s: ldg=%d below H*dv=%d", fn, ldg, H * dv);
+  if (B == 0 || N == 0) return ok();
+  GDN_TRY(check_ptr(fn, "S", S, true));
+  if (dly) GDN_TRY(check_ptr4(fn, "last_accepted", last_accepted, true));
+  GDN_TRY(check_ptr4(fn, "commit_status", commit_status, false));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr4(fn, "gate", gate, true));
+  GDN_TRY(check_ptr(fn, "Y", Y, true));
+  GDN_TRY(check_ptr(fn, "factors", factors, true));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  if (dly) {
+    const char* a0 = static_cast<const char*>(prev_factors);
+    const char* b0 = static_cast<const char*>(factors);
+    const size_t na = gdn::record_layout(B, N_prev, H, dk, dv, GDN_BF16).total;
+    const size_t nb = gdn::record_layout(B, N, H, dk, dv, GDN_BF16).total;
+    if (a0 < b0 + nb && b0 < a0 + na)
+      return fail(GDN_ERR_ARG, "%s: factors and prev_factors overlap", fn);
+  }
+  return hip_status(fn, gdn::launch_tree_verify(B, N, H, dk, dv, GDN_BF16, S, parents, q, k, v,
+                                                beta, g, scale, nullptr, factors, nullptr,
+                                                nullptr, dev_status, prev_factors,
+                                                dly ? N_prev : 0, last_accepted, commit_status,
+                                                gate, ldg, Y, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_conv_commit(int B, int N, int Cc, const float* P, int ldP, const int32_t* parents,

@@ -78,6 +78,10 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 __device__ inline float bf16_to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// FP32 -> bf16, round to nearest even
+__device__ inline bf16_t to_bf16(float x) { return __builtin_bit_cast(bf16_t, (__bf16)x); }
+// SiLU(x) = x sigmoid(x), as the output gate and the convolution use it
+__device__ inline float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // Load 4 consecutive elements as float.
 __device__ inline f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }

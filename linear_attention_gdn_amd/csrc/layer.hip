@@ -28,9 +28,6 @@ __device__ inline u32x2 pack_bf16x4(const f32x4& x) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-__device__ inline bf16_t to_bf16(float x) { return __builtin_bit_cast(bf16_t, (__bf16)x); }
-
-__device__ inline float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // ---------------------------------------------------------------------------
 // gdn_linear: C = A W^T (+ R), A bf16 [M][K], W bf16 [Nc][K]

@@ -114,6 +114,15 @@ constexpr int kQKStride = kMaxDim + 8;     // bf16 elements per staged row
 constexpr int kQKBytes = kQKRows * kQKStride * 2;
 constexpr int kPathMax = 16;               // register-resident path solve up to this depth
 
+// Optional SiLU output gate fused into the epilogue: Y = bf16(O * SiLU(gate))
+// with gate row t at gate + (b N + t) ldg + h dv (the gate block of the layer's
+// projection output); null `gate` and `Y` leave the epilogue as O only.
+struct GateArgs {
+  const float* gate;
+  int ldg;
+  bf16_t* Y;
+};
+
 template <int BV>
 struct TreeLds {
   static constexpr int kBVT = ((BV + 15) / 16) * 16;            // padded tile width
@@ -227,7 +236,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const T* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ g,
     float scale, float* __restrict__ out, Record<T> rec, uint64_t* __restrict__ mask_out,
     int32_t* __restrict__ dev_status, Record<T> prev, int Npv,
-    const int32_t* __restrict__ last_acc, int32_t* __restrict__ commit_status) {
+    const int32_t* __restrict__ last_acc, int32_t* __restrict__ commit_status, GateArgs ga) {
   using L = TreeLds<BV>;
   constexpr bool kStaged = std::is_same<T, bf16_t>::value;  // Q/K staged in LDS as bf16
   constexpr int NCT = (BV + 15) / 16;                        // MFMA column tiles
@@ -312,6 +321,10 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   // 16*nb + 4*lg + r, column ccol).
   const int iK0 = NQT > rb ? (NQT - rb + WR - 1) / WR : 0;
   T vreg[MAXNB][4];
+  // Output gate values for the rows this lane stores (node 16 nb + 4 lg + r of
+  // its node blocks nb = rb + WR j, column srow); without a gate the loads
+  // read one valid state element instead, so no load sits under a branch.
+  float gvr[MAXNB][4];
   auto load_state = [&]() {
     const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
 #pragma unroll
@@ -328,6 +341,13 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         const int t = clampi(16 * nb + 4 * lg + r, N - 1);
         vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
       }
+    const float* gp = ga.gate ? ga.gate + (size_t)b * N * ga.ldg + h * dv + clampi(srow, dv - 1)
+                              : S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
+    const size_t gs = ga.gate ? (size_t)ga.ldg : 0;
+#pragma unroll
+    for (int j = 0; j < MAXNB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gvr[j][r] = gp[clampi(16 * (rb + WR * j) + 4 * lg + r, N - 1) * gs];
   };
 
   // delayed commit: the previous draft's last accepted node, and node j's
@@ -896,7 +916,11 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * nb + 4 * lg + r;
-          if (t < N) out[(((size_t)b * N + t) * H + h) * dv + srow] = acc[r];
+          if (t < N) {
+            const size_t o = (((size_t)b * N + t) * H + h) * dv + srow;
+            if (out) out[o] = acc[r];
+            if (ga.Y) ga.Y[o] = to_bf16(acc[r] * silu(gvr[j][r]));  // gdn_gate_merge's arithmetic
+          }
         }
       }
     }
@@ -908,6 +932,7 @@ struct DelayArgs {
   int Np;
   const int32_t* last;
   int32_t* commit_status;
+  GateArgs gate;
 };
 
 template <typename T, int BV, int NQT>
@@ -922,11 +947,11 @@ hipError_t launch_bvn(int B, int N, int H, int dk, int dv, float* S0, const int3
     const Record<T> prev = record_views<T>(const_cast<void*>(da.prev_factors), Lp);
     hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT, true>), dim3((unsigned)grid), dim3(256), 0,
                        stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out,
-                       rec, mask_out, dev_status, prev, da.Np, da.last, da.commit_status);
+                       rec, mask_out, dev_status, prev, da.Np, da.last, da.commit_status, da.gate);
   } else {
     hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT, false>), dim3((unsigned)grid), dim3(256),
                        0, stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale,
-                       out, rec, mask_out, dev_status, Record<T>{}, 1, nullptr, nullptr);
+                       out, rec, mask_out, dev_status, Record<T>{}, 1, nullptr, nullptr, da.gate);
   }
   return hipGetLastError();
 }
@@ -981,9 +1006,11 @@ hipError_t launch_tree_verify(int B, int N, int H, int dk, int dv, int dtype, fl
                               const void* v, const float* beta, const float* g, float scale,
                               float* out, void* factors, void* workspace, uint64_t* mask_out,
                               int32_t* dev_status, const void* prev_factors, int Np,
-                              const int32_t* last, int32_t* commit_status, hipStream_t stream) {
+                              const int32_t* last, int32_t* commit_status, const float* gate,
+                              int ldg, void* Y, hipStream_t stream) {
   (void)workspace;
-  const DelayArgs da{prev_factors, Np, last, commit_status};
+  const DelayArgs da{prev_factors, Np, last, commit_status,
+                     GateArgs{gate, ldg, static_cast<bf16_t*>(Y)}};
   if (dtype == GDN_BF16)
     return launch_tree_verify_t<bf16_t>(
         B, N, H, dk, dv, S0, parents, static_cast<const bf16_t*>(q),

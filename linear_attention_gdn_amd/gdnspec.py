@@ -81,6 +81,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_layer_prep.restype = I
         L.gdn_gate_merge.argtypes = [I, I, P, P, I, P, P]
         L.gdn_gate_merge.restype = I
+        L.gdn_layer_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, F, P, I,
+                                       P, P, P, P]
+        L.gdn_layer_verify.restype = I
         L.gdn_conv_commit.argtypes = [I, I, I, P, I, P, P, P, P, P]
         L.gdn_conv_commit.restype = I
         L.gdn_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, F, P, P]
@@ -404,6 +407,37 @@ def gdn_gate_merge(o, gate, Y, stream=None) -> None:
     if (gm, gc) != (M, Cw):
         raise ValueError(f"gate has shape {(gm, gc)}, expected {(M, Cw)}")
     _raise_on(lib().gdn_gate_merge(M, Cw, _p(o), _p(gate), ldg, _p(Y), _stream(stream)))
+
+
+def gdn_layer_verify(S, parents, q, k, v, beta, g, gate, Y, factors: FactorRecord,
+                     prev_factors: FactorRecord = None, last_accepted=None, scale: float = 1.0,
+                     commit_status=None, dev_status=None, stream=None) -> None:
+    """Tree verification (delayed when prev_factors is given) writing
+    Y = bf16(O * SiLU(gate)) instead of O; see ``gdn_layer_verify`` in gdnlayer.h.
+    gate is a row-strided [B*N][H*dv] FP32 view (the gate block of P)."""
+    B, N, H, dk, dv, code = _check_draft(S, q, k, v, beta, g)
+    if code != GDN_BF16:
+        raise TypeError("gdn_layer_verify takes bf16 q, k, v")
+    _need("parents", parents, (B, N), torch.int32)
+    _need("Y", Y, (B * N, H * dv), torch.bfloat16)
+    gm, gc, ldg = _need_rows("gate", gate, torch.float32)
+    if (gm, gc) != (B * N, H * dv):
+        raise ValueError(f"gate has shape {(gm, gc)}, expected {(B * N, H * dv)}")
+    _check_record(factors, B, N, H, dk, dv, code)
+    n_prev = 0
+    if prev_factors is not None:
+        pf = prev_factors
+        if (pf.B, pf.H, pf.dk, pf.dv, pf.qkv_dtype) != (B, H, dk, dv, code):
+            raise ValueError("prev_factors sizes do not match the call")
+        _need("last_accepted", last_accepted, (B,), torch.int32)
+        n_prev = pf.N
+    for name, t in (("commit_status", commit_status), ("dev_status", dev_status)):
+        if t is not None:
+            _need(name, t, (B,), torch.int32)
+    _raise_on(lib().gdn_layer_verify(
+        B, n_prev, N, H, dk, dv, _p(S), _p(prev_factors.buf if prev_factors is not None else None),
+        _p(last_accepted), _p(commit_status), _p(parents), _p(q), _p(k), _p(v), _p(beta), _p(g),
+        float(scale), _p(gate), ldg, _p(Y), _p(factors.buf), _p(dev_status), _stream(stream)))
 
 
 def gdn_conv_commit(P, parents, last_accepted, hist, dev_status=None, stream=None) -> None:

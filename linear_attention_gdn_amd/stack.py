@@ -9,16 +9,17 @@ of once per node.  Per layer and step:
     gdn_linear       P = bf16(x) W_in^T   (q^ k^ v^ gate columns)
     gdn_layer_prep   conv along ancestor paths + SiLU + L2 norm; beta, g from
                      the last 2H rows of W_in
-    gdn_tree_verify  every node's output from the committed state
-    gdn_gate_merge   bf16(o * SiLU(gate))
+    gdn_layer_verify every node's output from the committed state (the tree
+                     verifier), gated in its epilogue: bf16(o * SiLU(gate))
     gdn_linear       x <- x + (...) W_o^T   (FP32 residual, bf16 copy for the next layer)
 
 and once the accepted node is known, per layer: gdn_commit_path (state) and
 gdn_conv_commit (convolution history).  With the delayed commit (the
 review's Figure 7 caption, right side), a step instead carries the previous
 step's accepted node into every layer: gdn_conv_commit shifts the previous
-path into the history before the layer's prep, and gdn_tree_verify_delayed
-applies it to the layer's state inside the verification; records and
+path into the history before the layer's prep, and gdn_layer_verify (as
+gdn_tree_verify_delayed) applies it to the layer's state inside the
+verification; records and
 projection outputs alternate between two buffers per layer, and flush()
 applies the last pending commit.  The autoregressive baseline runs one token
 per step through the same layers with gdn_decode_step in place of verify +
@@ -144,17 +145,11 @@ class GdnStack:
             G.gdn_layer_prep(P, xb3, self.W_ab[l], parents, self.conv_w[l], self.hist[l],
                              self.q, self.k, self.v, self.beta, self.g,
                              gate_shift=self.gate_shift, stream=stream)
-            if pend is None:
-                G.gdn_tree_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
-                                  self.out, self.rec[cur][l], dev_status=self.status,
-                                  stream=stream)
-            else:
-                G.gdn_tree_verify_delayed(self.S[l], self.rec[prev][l], pend[1], parents, self.q,
-                                          self.k, self.v, self.beta, self.g, self.out,
-                                          self.rec[cur][l], dev_status=self.status,
-                                          stream=stream)
-            G.gdn_gate_merge(self.out.view(M, sh.H * sh.dv), P.view(M, npj)[:, g0:g1],
-                             self.Y, stream=stream)
+            G.gdn_layer_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
+                               P.view(M, npj)[:, g0:g1], self.Y, self.rec[cur][l],
+                               prev_factors=None if pend is None else self.rec[prev][l],
+                               last_accepted=None if pend is None else pend[1],
+                               dev_status=self.status, stream=stream)
             G.gdn_linear(self.Y, self.W_o[l], C=self.x, R=self.x, C_bf16=self.xb, w_layout=PK,
                          stream=stream)
         self.cur = cur

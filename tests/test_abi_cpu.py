@@ -100,7 +100,7 @@ def test_missing_library_fails_loudly(monkeypatch):
 
 def test_layer_scaffold_exports():
     assert {"gdn_linear", "gdn_pack_weights", "gdn_layer_prep", "gdn_gate_merge",
-            "gdn_conv_commit", "gdn_decode_step"} <= set(G.declared_functions())
+            "gdn_conv_commit", "gdn_decode_step", "gdn_layer_verify"} <= set(G.declared_functions())
 
 
 @pytest.mark.parametrize("mnk", [(65, 16, 512), (4, 24, 512), (4, 16, 384), (4, 16, 128),
@@ -162,6 +162,20 @@ def test_layer_scaffold_bad_arguments_rejected():
     assert "out is NULL" in G.gdn_last_error()
     assert L.gdn_decode_step(0, 8, 256, 256, 0, None, None, None, None, None, None, 1.0, None,
                              None) == G.GDN_OK
+    # gated layer verify: gate row length, gate and Y required, N_prev when delayed
+    lv = lambda B, Np, N, prev, gate, ldg, Y: L.gdn_layer_verify(
+        B, Np, N, 8, 256, 256, P, prev, P, None, P, P, P, P, P, P, 1.0, gate, ldg, Y, P, None,
+        None)
+    assert lv(1, 32, 32, P, P, 2047, P) == G.GDN_ERR_SHAPE
+    assert "ldg" in G.gdn_last_error()
+    assert lv(1, 32, 32, P, P, 2048, None) == G.GDN_ERR_ARG
+    assert "Y is NULL" in G.gdn_last_error()
+    assert lv(1, 32, 32, P, None, 2048, P) == G.GDN_ERR_ARG
+    assert lv(1, 0, 32, P, P, 2048, P) == G.GDN_ERR_SHAPE
+    assert "N_prev" in G.gdn_last_error()
+    assert lv(1, 65, 32, P, P, 2048, P) == G.GDN_ERR_SHAPE
+    assert lv(1, 0, 65, None, P, 2048, P) == G.GDN_ERR_SHAPE
+    assert lv(0, 0, 32, None, None, 2048, None) == G.GDN_OK
 
 
 def test_layer_bindings_refuse_host_tensors():

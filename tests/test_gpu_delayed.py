@@ -170,3 +170,62 @@ def test_delayed_tree_commit_lands_when_new_topology_is_rejected():
     assert torch.equal(S_a, S_b)
     assert dst.tolist() == [G.GDN_OK, G.GDN_ERR_TOPOLOGY]
     assert (out[1] == 0).all() and torch.isfinite(out[0]).all()
+
+
+@pytest.mark.parametrize("B,Np,N,H,dk,dv,topo,delayed", [
+    (1, 32, 32, 8, 256, 256, "window", True),     # the 24-layer step's shape
+    (1, 32, 32, 8, 256, 256, "window", False),
+    (2, 9, 17, 3, 64, 40, "random", True),        # ragged: N and dv not multiples of 16
+    (8, 64, 64, 8, 256, 256, "branching", True),  # wide tiles
+])
+def test_layer_verify_is_verify_then_gate(B, Np, N, H, dk, dv, topo, delayed):
+    """gdn_layer_verify == the verify call followed by gdn_gate_merge, bitwise
+    (outputs through the gate, state, record, status words)."""
+    seed = 7000 + B * 100 + N
+    prev = W.make_draft(B, Np, H, dk, dv, topology=topo, accept="leaf_geometric",
+                        dtype="bf16", seed=seed)
+    new = W.make_draft(B, N, H, dk, dv, topology=topo, accept="none", dtype="bf16",
+                       seed=seed + 1)
+    _, rec_prev, _, st, tp = run_tree(prev)
+    assert (st.cpu().numpy() == G.GDN_OK).all()
+    tn = dev_tensors(new)
+    rng = np.random.default_rng(seed)
+    ldg = H * dv + 24  # the gate block sits inside wider rows, as in P
+    gate_rows = torch.from_numpy(rng.standard_normal((B * N, ldg)).astype(np.float32)).cuda()
+    gate = gate_rows[:, 8:8 + H * dv]
+    last_t = torch.from_numpy(prev.last_accepted.astype(np.int32)).cuda()
+    code = code_of(new)
+
+    S_a = tp["S0"].clone()
+    out_a = torch.empty((B, N, H, dv), device="cuda")
+    rec_a = G.FactorRecord.empty(B, N, H, dk, dv, code)
+    rec_a.buf.zero_()
+    st_a = torch.full((B,), 77, dtype=torch.int32, device="cuda")
+    cs_a = torch.full((B,), 77, dtype=torch.int32, device="cuda")
+    if delayed:
+        G.gdn_tree_verify_delayed(S_a, rec_prev, last_t, tn["parents"], tn["q"], tn["k"], tn["v"],
+                                  tn["beta"], tn["g"], out_a, rec_a, commit_status=cs_a,
+                                  dev_status=st_a)
+    else:
+        G.gdn_tree_verify(S_a, tn["parents"], tn["q"], tn["k"], tn["v"], tn["beta"], tn["g"],
+                          out_a, rec_a, dev_status=st_a)
+    Y_a = torch.empty((B * N, H * dv), dtype=torch.bfloat16, device="cuda")
+    G.gdn_gate_merge(out_a.view(B * N, H * dv), gate, Y_a)
+
+    S_b = tp["S0"].clone()
+    rec_b = G.FactorRecord.empty(B, N, H, dk, dv, code)
+    rec_b.buf.zero_()
+    st_b = torch.full((B,), 77, dtype=torch.int32, device="cuda")
+    cs_b = torch.full((B,), 77, dtype=torch.int32, device="cuda")
+    Y_b = torch.full((B * N, H * dv), float("nan"), dtype=torch.bfloat16, device="cuda")
+    G.gdn_layer_verify(S_b, tn["parents"], tn["q"], tn["k"], tn["v"], tn["beta"], tn["g"], gate,
+                       Y_b, rec_b, prev_factors=rec_prev if delayed else None,
+                       last_accepted=last_t if delayed else None,
+                       commit_status=cs_b if delayed else None, dev_status=st_b)
+    torch.cuda.synchronize()
+    assert torch.equal(Y_a.view(torch.int16), Y_b.view(torch.int16))
+    assert torch.equal(S_a, S_b)
+    assert torch.equal(rec_a.buf, rec_b.buf)
+    assert torch.equal(st_a, st_b)
+    if delayed:
+        assert torch.equal(cs_a, cs_b)
