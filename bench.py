@@ -591,6 +591,10 @@ def bench_decode_loop(args):
         "layer_prep": (lambda j: G.gdn_layer_prep(st.P[st.cur, j % L], xb3, st.W_ab[j % L],
                                                   parents[0], st.conv_w[j % L], st.hist[j % L],
                                                   st.q, st.k, st.v, st.beta, st.g), None),
+        "layer_prep_delayed": (lambda j: G.gdn_layer_prep_delayed(
+            st.P[st.cur, j % L], xb3, st.W_ab[j % L], parents[0], st.conv_w[j % L],
+            st.hists[st.hc, j % L], st.q, st.k, st.v, st.beta, st.g, st.P[1 - st.cur, j % L],
+            parents[0], lasts[0], st.hists[1 - st.hc, j % L]), None),
         "tree_verify": (lambda j: G.gdn_tree_verify(st.S[j % L], parents[0], st.q, st.k, st.v,
                                                     st.beta, st.g, st.out,
                                                     st.rec[st.cur][j % L]), None),

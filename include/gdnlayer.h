@@ -112,6 +112,35 @@ int gdn_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P, c
                    float* g, void* stream);
 
 /*
+ * gdn_layer_prep_delayed: gdn_conv_commit of the previous step's accepted path
+ * followed by gdn_layer_prep, in one launch, with the history double-buffered:
+ *   hist       FP32 [B][3][Cc], the history before the previous step's commit
+ *              (read only)
+ *   P_prev     FP32 [B][N_prev][ldP], the previous step's projection output
+ *   parents_prev int32 [B][N_prev], last_prev int32 [B] (-1: nothing accepted),
+ *              the previous draft and its deepest accepted node
+ *   hist_out   FP32 [B][3][Cc], written: the history after that commit,
+ *              bitwise gdn_conv_commit's result (hist itself when last_prev is
+ *              -1 or out of range); must not overlap hist
+ *   dev_status optional int32 [B]: GDN_OK, or GDN_ERR_TOPOLOGY when last_prev
+ *              is out of range
+ * The other arguments and all outputs are gdn_layer_prep's, computed from
+ * hist_out, bitwise equal to gdn_conv_commit(P_prev, ...) followed by
+ * gdn_layer_prep.  It is the history half of the delayed commit (SpecLA
+ * review, Figures, Figure 7 caption, right side) for the block's causal
+ * convolution (review: skeptic critique, on Section 7).  1 <= N_prev <= 64.
+ * Errors: as gdn_layer_prep, plus GDN_ERR_SHAPE for N_prev and GDN_ERR_ARG for
+ * overlapping histories or a NULL previous-step pointer.
+ */
+int gdn_layer_prep_delayed(int B, int N_prev, int N, int H, int dk, int dv, int D,
+                           const float* P, const void* x, const void* W_ab,
+                           const int32_t* parents, const float* conv_w, const float* hist,
+                           float gate_shift, void* q, void* k, void* v, float* beta, float* g,
+                           const float* P_prev, const int32_t* parents_prev,
+                           const int32_t* last_prev, float* hist_out, int32_t* dev_status,
+                           void* stream);
+
+/*
  * gdn_gate_merge: Y[m][c] = bf16(o[m][c] * SiLU(gate[m][c])), the SiLU output
  * gate in front of the output projection.
  *   M, Cw   rows and columns, Cw % 4 == 0

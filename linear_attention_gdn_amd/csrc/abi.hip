@@ -32,7 +32,9 @@ hipError_t launch_pack_weights(int Nc, int K, const void* W, void* Wp, hipStream
 hipError_t launch_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P,
                              const void* x, const void* W_ab, const int32_t* parents,
                              const float* conv_w, const float* hist, float gate_shift, void* q,
-                             void* k, void* v, float* beta, float* g, hipStream_t stream);
+                             void* k, void* v, float* beta, float* g, const float* P_prev,
+                             int Np, const int32_t* parents_prev, const int32_t* last_prev,
+                             float* hist_out, int32_t* dev_status, hipStream_t stream);
 hipError_t launch_gate_merge(int M, int Cw, const float* o, const float* gate, int ldg, void* Y,
                              hipStream_t stream);
 hipError_t launch_conv_commit(int B, int N, int Cc, const float* P, int ldP,
@@ -362,8 +364,53 @@ int gdn_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P, c
   GDN_TRY(check_ptr4(fn, "beta", beta, true));
   GDN_TRY(check_ptr4(fn, "g", g, true));
   return hip_status(fn, gdn::launch_layer_prep(B, N, H, dk, dv, D, P, x, W_ab, parents, conv_w,
-                                               hist, gate_shift, q, k, v, beta, g,
+                                               hist, gate_shift, q, k, v, beta, g, nullptr, 0,
+                                               nullptr, nullptr, nullptr, nullptr,
                                                static_cast<hipStream_t>(stream)));
+}
+
+int gdn_layer_prep_delayed(int B, int N_prev, int N, int H, int dk, int dv, int D,
+                           const float* P, const void* x, const void* W_ab,
+                           const int32_t* parents, const float* conv_w, const float* hist,
+                           float gate_shift, void* q, void* k, void* v, float* beta, float* g,
+                           const float* P_prev, const int32_t* parents_prev,
+                           const int32_t* last_prev, float* hist_out, int32_t* dev_status,
+                           void* stream) {
+  const char* fn = "gdn_layer_prep_delayed";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  if (N_prev < 1 || N_prev > gdn::kMaxNodes)
+    return fail(GDN_ERR_SHAPE, "%s: N_prev=%d outside 1..64", fn, N_prev);
+  if (D < 8 || D > 65536 || D % 8 != 0)
+    return fail(GDN_ERR_SHAPE, "%s: unsupported hidden width D=%d (need 8<=D<=65536, D%%8==0)",
+                fn, D);
+  if (!std::isfinite(gate_shift)) return fail(GDN_ERR_ARG, "%s: gate_shift is not finite", fn);
+  if (B == 0) return ok();
+  if (N == 0) return fail(GDN_ERR_SHAPE, "%s: N=0; use gdn_conv_commit alone", fn);
+  GDN_TRY(check_ptr(fn, "P", P, true));
+  GDN_TRY(check_ptr(fn, "x", x, true));
+  GDN_TRY(check_ptr(fn, "W_ab", W_ab, true));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "conv_w", conv_w, true));
+  GDN_TRY(check_ptr(fn, "hist", hist, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr(fn, "P_prev", P_prev, true));
+  GDN_TRY(check_ptr4(fn, "parents_prev", parents_prev, true));
+  GDN_TRY(check_ptr4(fn, "last_prev", last_prev, true));
+  GDN_TRY(check_ptr(fn, "hist_out", hist_out, true));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  const size_t hb = (size_t)B * 3 * H * (2 * dk + dv) * sizeof(float);
+  const char* h0 = reinterpret_cast<const char*>(hist);
+  const char* h1 = reinterpret_cast<const char*>(hist_out);
+  if (h0 < h1 + hb && h1 < h0 + hb)
+    return fail(GDN_ERR_ARG, "%s: hist and hist_out overlap", fn);
+  return hip_status(fn, gdn::launch_layer_prep(B, N, H, dk, dv, D, P, x, W_ab, parents, conv_w,
+                                               hist, gate_shift, q, k, v, beta, g, P_prev,
+                                               N_prev, parents_prev, last_prev, hist_out,
+                                               dev_status, static_cast<hipStream_t>(stream)));
 }
 
 int gdn_gate_merge(int M, int Cw, const float* o, const float* gate, int ldg, void* Y,

@@ -328,6 +328,11 @@ __device__ inline float dot8_bf16(const u32x4& x, const u32x4& w, float acc) {
   return acc;
 }
 
+// With DLY the history is first advanced by the previous step's accepted
+// path (node last_prev[b] of a draft of Np nodes whose projection output is
+// P_prev), as gdn_conv_commit would do it; the taps use the advanced history,
+// and the workgroups of node 0 write it to hist_out for their channels.
+template <bool DLY>
 __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv, int D,
                                                    const float* __restrict__ P,
                                                    const bf16_t* __restrict__ x,
@@ -339,7 +344,12 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
                                                    bf16_t* __restrict__ ko,
                                                    bf16_t* __restrict__ vo,
                                                    float* __restrict__ beta,
-                                                   float* __restrict__ g) {
+                                                   float* __restrict__ g,
+                                                   const float* __restrict__ P_prev, int Np,
+                                                   const int32_t* __restrict__ parents_prev,
+                                                   const int32_t* __restrict__ last_prev,
+                                                   float* __restrict__ hist_out,
+                                                   int32_t* __restrict__ dev_status) {
   __shared__ float wsum[4][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -352,6 +362,11 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
 
   // ---- every global load first
   const int mypar = parents[(size_t)b * N + clampi(lane, N - 1)];
+  int lastv = -1, myppar = -1;
+  if (DLY) {
+    lastv = last_prev[b];
+    myppar = parents_prev[(size_t)b * Np + clampi(lane, Np - 1)];
+  }
   const float* Pb = P + (size_t)b * N * ldP;
   const float* hb = hist + (size_t)b * 3 * Cc;
   // first D-chunk of the logit dot products (later chunks loop below)
@@ -376,6 +391,26 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
     hk[j] = hb[(size_t)j * Cc + ck];
     hv[j] = hb[(size_t)j * Cc + cv];
   }
+  // previous accepted path (uniform): node L and its nearest two ancestors
+  const int L = DLY ? __builtin_amdgcn_readfirstlane(lastv) : -1;
+  const bool pbad = DLY && (L < -1 || L >= Np);
+  const bool padv = DLY && L >= 0 && L < Np;
+  const int Lc = padv ? L : 0;
+  const int p1 = padv ? checked_parent(__builtin_amdgcn_readlane(myppar, Lc), Lc) : -1;
+  const int p2 = p1 >= 0 ? checked_parent(__builtin_amdgcn_readlane(myppar, p1), p1) : -1;
+  const int npath = p1 < 0 ? 1 : p2 < 0 ? 2 : 3;  // accepted-path rows available (<= 3 needed)
+  float pq[3] = {0.f, 0.f, 0.f}, pk[3] = {0.f, 0.f, 0.f}, pv[3] = {0.f, 0.f, 0.f};
+  if (DLY) {
+    const int prow[3] = {Lc, p1 < 0 ? Lc : p1, p2 < 0 ? Lc : p2};
+    const float* Ppb = P_prev + (size_t)b * Np * ldP;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const float* pr = Ppb + (size_t)prow[j] * ldP;
+      pq[j] = pr[cq];
+      pk[j] = pr[ck];
+      pv[j] = pr[cv];
+    }
+  }
   // ancestors a_1..a_3 (uniform): lane j of every wave holds parents[b][j]
   const int a1 = checked_parent(__builtin_amdgcn_readlane(mypar, t), t);
   const int a2 = a1 >= 0 ? checked_parent(__builtin_amdgcn_readlane(mypar, a1), a1) : -1;
@@ -399,6 +434,32 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
     const u32x4 xv1 = *reinterpret_cast<const u32x4*>(xr + c);
     la = dot8_bf16(xv1, *reinterpret_cast<const u32x4*>(wa + c), la);
     lb = dot8_bf16(xv1, *reinterpret_cast<const u32x4*>(wb + c), lb);
+  }
+
+  // ---- the history after the previous accepted path: its rows, most recent
+  // first, then the old history (gdn_conv_commit's update)
+  if (DLY && padv) {  // uniform
+    auto adv = [&](float (&hh)[3], const float (&pp)[3]) {
+      const float h0 = hh[0], h1 = hh[1];
+      hh[0] = pp[0];
+      hh[1] = npath >= 2 ? pp[1] : h0;
+      hh[2] = npath >= 3 ? pp[2] : (npath == 2 ? h0 : h1);
+    };
+    adv(hq, pq);
+    adv(hk, pk);
+    adv(hv, pv);
+  }
+  if (DLY && t == 0) {  // node 0's workgroups store the advanced history of their channels
+    float* ho = hist_out + (size_t)b * 3 * Cc;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (tid < dk) {
+        ho[(size_t)j * Cc + cq] = hq[j];
+        ho[(size_t)j * Cc + ck] = hk[j];
+      }
+      if (tid < dv) ho[(size_t)j * Cc + cv] = hv[j];
+    }
+    if (dev_status && h == 0 && tid == 0) dev_status[b] = pbad ? GDN_ERR_TOPOLOGY : GDN_OK;
   }
 
   // ---- taps past the root come from the history (most recent first)
@@ -597,12 +658,22 @@ __global__ __launch_bounds__(256) void decode_step_kernel(int H, int dk, int dv,
 hipError_t launch_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P,
                              const void* x, const void* W_ab, const int32_t* parents,
                              const float* conv_w, const float* hist, float gate_shift, void* q,
-                             void* k, void* v, float* beta, float* g, hipStream_t stream) {
+                             void* k, void* v, float* beta, float* g, const float* P_prev,
+                             int Np, const int32_t* parents_prev, const int32_t* last_prev,
+                             float* hist_out, int32_t* dev_status, hipStream_t stream) {
   const long grid = (long)B * N * H;
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)grid), dim3(256), 0, stream, N, H, dk, dv, D, P,
-                     static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W_ab), parents,
-                     conv_w, hist, gate_shift, static_cast<bf16_t*>(q), static_cast<bf16_t*>(k),
-                     static_cast<bf16_t*>(v), beta, g);
+  if (P_prev)
+    hipLaunchKernelGGL(prep_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, N, H, dk,
+                       dv, D, P, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W_ab),
+                       parents, conv_w, hist, gate_shift, static_cast<bf16_t*>(q),
+                       static_cast<bf16_t*>(k), static_cast<bf16_t*>(v), beta, g, P_prev, Np,
+                       parents_prev, last_prev, hist_out, dev_status);
+  else
+    hipLaunchKernelGGL(prep_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, N, H, dk,
+                       dv, D, P, static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(W_ab),
+                       parents, conv_w, hist, gate_shift, static_cast<bf16_t*>(q),
+                       static_cast<bf16_t*>(k), static_cast<bf16_t*>(v), beta, g, nullptr, 1,
+                       nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -84,6 +84,9 @@ def lib() -> ctypes.CDLL:
         L.gdn_layer_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P, F, P, I,
                                        P, P, P, P]
         L.gdn_layer_verify.restype = I
+        L.gdn_layer_prep_delayed.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P,
+                                             P, P, P, P, P, P, P, P]
+        L.gdn_layer_prep_delayed.restype = I
         L.gdn_conv_commit.argtypes = [I, I, I, P, I, P, P, P, P, P]
         L.gdn_conv_commit.restype = I
         L.gdn_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, F, P, P]
@@ -396,6 +399,41 @@ def gdn_layer_prep(P, x, W_ab, parents, conv_w, hist, q, k, v, beta, g,
     _raise_on(lib().gdn_layer_prep(B, N, H, dk, dv, D, _p(P), _p(x), _p(W_ab), _p(parents),
                                    _p(conv_w), _p(hist), float(gate_shift), _p(q), _p(k), _p(v),
                                    _p(beta), _p(g), _stream(stream)))
+
+
+def gdn_layer_prep_delayed(P, x, W_ab, parents, conv_w, hist, q, k, v, beta, g, P_prev,
+                           parents_prev, last_prev, hist_out, gate_shift: float = 2.0,
+                           dev_status=None, stream=None) -> None:
+    """gdn_conv_commit of the previous step's accepted path (into hist_out) and
+    gdn_layer_prep from the result, in one launch; see gdnlayer.h."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B][N][H][dk]")
+    B, N, H, dk = q.shape
+    dv = v.shape[-1]
+    D = x.shape[-1]
+    Cc = H * (2 * dk + dv)
+    Np = parents_prev.shape[-1]
+    _need("P", P, (B, N, 2 * H * (dk + dv)), torch.float32)
+    _need("x", x, (B, N, D), torch.bfloat16)
+    _need("W_ab", W_ab, (2 * H, D), torch.bfloat16)
+    _need("parents", parents, (B, N), torch.int32)
+    _need("conv_w", conv_w, (Cc, 4), torch.float32)
+    _need("hist", hist, (B, 3, Cc), torch.float32)
+    _need("q", q, (B, N, H, dk), torch.bfloat16)
+    _need("k", k, (B, N, H, dk), torch.bfloat16)
+    _need("v", v, (B, N, H, dv), torch.bfloat16)
+    _need("beta", beta, (B, N, H), torch.float32)
+    _need("g", g, (B, N, H), torch.float32)
+    _need("P_prev", P_prev, (B, Np, 2 * H * (dk + dv)), torch.float32)
+    _need("parents_prev", parents_prev, (B, Np), torch.int32)
+    _need("last_prev", last_prev, (B,), torch.int32)
+    _need("hist_out", hist_out, (B, 3, Cc), torch.float32)
+    if dev_status is not None:
+        _need("dev_status", dev_status, (B,), torch.int32)
+    _raise_on(lib().gdn_layer_prep_delayed(
+        B, Np, N, H, dk, dv, D, _p(P), _p(x), _p(W_ab), _p(parents), _p(conv_w), _p(hist),
+        float(gate_shift), _p(q), _p(k), _p(v), _p(beta), _p(g), _p(P_prev), _p(parents_prev),
+        _p(last_prev), _p(hist_out), _p(dev_status), _stream(stream)))
 
 
 def gdn_gate_merge(o, gate, Y, stream=None) -> None:

@@ -16,12 +16,11 @@ of once per node.  Per layer and step:
 and once the accepted node is known, per layer: gdn_commit_path (state) and
 gdn_conv_commit (convolution history).  With the delayed commit (the
 review's Figure 7 caption, right side), a step instead carries the previous
-step's accepted node into every layer: gdn_conv_commit shifts the previous
-path into the history before the layer's prep, and gdn_layer_verify (as
-gdn_tree_verify_delayed) applies it to the layer's state inside the
-verification; records and
-projection outputs alternate between two buffers per layer, and flush()
-applies the last pending commit.  The autoregressive baseline runs one token
+step's accepted node into every layer: gdn_layer_prep_delayed shifts the
+previous path into the convolution history inside the layer's prep, and
+gdn_layer_verify (as gdn_tree_verify_delayed) applies it to the layer's state
+inside the verification; records, projection outputs and histories alternate
+between two buffers per layer, and flush() applies the last pending commit.  The autoregressive baseline runs one token
 per step through the same layers with gdn_decode_step in place of verify +
 commit.
 """
@@ -68,7 +67,9 @@ class GdnStack:
         self.W_o = e(L, D, H * dv, dt=bf)
         self.conv_w = e(L, shape.n_conv, 4)
         self.S = torch.zeros(L, B, H, dv, dk, dtype=f32, device=device)
-        self.hist = torch.zeros(L, B, 3, shape.n_conv, dtype=f32, device=device)
+        # conv histories, two sets: a delayed step reads one and writes the other
+        self.hists = torch.zeros(2, L, B, 3, shape.n_conv, dtype=f32, device=device)
+        self.hc = 0  # the set holding the committed history
         # speculative step buffers (M = B * N rows)
         M = B * N
         self.x = e(M, D)
@@ -114,6 +115,11 @@ class GdnStack:
             self.S[layer].copy_(_f32(S0, self.device))
 
     @property
+    def hist(self) -> torch.Tensor:
+        """The committed convolution histories [L][B][3][n_conv]."""
+        return self.hists[self.hc]
+
+    @property
     def gate_cols(self):
         sh = self.shape
         return sh.n_conv, sh.n_conv + sh.H * sh.dv
@@ -137,14 +143,20 @@ class GdnStack:
         xb3 = self.xb.view(self.B, self.N, sh.D)
         prev, cur = self.cur, 1 - self.cur
         pend = self.pending
+        hc = self.hc
         for l in range(sh.layers):
             P = self.P[cur, l]
-            if pend is not None:  # the previous path enters this layer's history
-                G.gdn_conv_commit(self.P[prev, l], pend[0], pend[1], self.hist[l], stream=stream)
             G.gdn_linear(self.xb, self.W_in[l], C=P.view(M, npj), w_layout=PK, stream=stream)
-            G.gdn_layer_prep(P, xb3, self.W_ab[l], parents, self.conv_w[l], self.hist[l],
-                             self.q, self.k, self.v, self.beta, self.g,
-                             gate_shift=self.gate_shift, stream=stream)
+            if pend is None:
+                G.gdn_layer_prep(P, xb3, self.W_ab[l], parents, self.conv_w[l], self.hists[hc, l],
+                                 self.q, self.k, self.v, self.beta, self.g,
+                                 gate_shift=self.gate_shift, stream=stream)
+            else:  # the previous path enters this layer's history inside the prep
+                G.gdn_layer_prep_delayed(P, xb3, self.W_ab[l], parents, self.conv_w[l],
+                                         self.hists[hc, l], self.q, self.k, self.v, self.beta,
+                                         self.g, self.P[prev, l], pend[0], pend[1],
+                                         self.hists[1 - hc, l], gate_shift=self.gate_shift,
+                                         stream=stream)
             G.gdn_layer_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
                                P.view(M, npj)[:, g0:g1], self.Y, self.rec[cur][l],
                                prev_factors=None if pend is None else self.rec[prev][l],
@@ -153,6 +165,8 @@ class GdnStack:
             G.gdn_linear(self.Y, self.W_o[l], C=self.x, R=self.x, C_bf16=self.xb, w_layout=PK,
                          stream=stream)
         self.cur = cur
+        if pend is not None:
+            self.hc = 1 - hc
         self.pending = None
 
     def commit(self, parents: torch.Tensor, last: torch.Tensor, stream=None):

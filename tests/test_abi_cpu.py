@@ -100,7 +100,8 @@ def test_missing_library_fails_loudly(monkeypatch):
 
 def test_layer_scaffold_exports():
     assert {"gdn_linear", "gdn_pack_weights", "gdn_layer_prep", "gdn_gate_merge",
-            "gdn_conv_commit", "gdn_decode_step", "gdn_layer_verify"} <= set(G.declared_functions())
+            "gdn_conv_commit", "gdn_decode_step", "gdn_layer_verify",
+            "gdn_layer_prep_delayed"} <= set(G.declared_functions())
 
 
 @pytest.mark.parametrize("mnk", [(65, 16, 512), (4, 24, 512), (4, 16, 384), (4, 16, 128),
@@ -176,6 +177,18 @@ def test_layer_scaffold_bad_arguments_rejected():
     assert lv(1, 65, 32, P, P, 2048, P) == G.GDN_ERR_SHAPE
     assert lv(1, 0, 65, None, P, 2048, P) == G.GDN_ERR_SHAPE
     assert lv(0, 0, 32, None, None, 2048, None) == G.GDN_OK
+    # fused history commit + prep: N_prev range, previous-step pointers, distinct histories
+    pd = lambda Np, N, hist, P_prev, hist_out: L.gdn_layer_prep_delayed(
+        1, Np, N, 8, 256, 256, 2048, P, P, P, P, P, hist, 2.0, P, P, P, P, P, P_prev, P, P,
+        hist_out, None, None)
+    H2 = ctypes.c_void_p(4096 + (1 << 20))
+    assert pd(0, 32, P, P, H2) == G.GDN_ERR_SHAPE
+    assert pd(65, 32, P, P, H2) == G.GDN_ERR_SHAPE
+    assert pd(32, 32, P, None, H2) == G.GDN_ERR_ARG
+    assert "P_prev is NULL" in G.gdn_last_error()
+    assert pd(32, 32, P, P, P) == G.GDN_ERR_ARG
+    assert "overlap" in G.gdn_last_error()
+    assert pd(32, 0, P, P, H2) == G.GDN_ERR_SHAPE
 
 
 def test_layer_bindings_refuse_host_tensors():

@@ -221,6 +221,57 @@ def test_conv_commit_is_exact():
                 np.testing.assert_array_equal(got[b], hist0[b])
 
 
+@pytest.mark.parametrize("B,Np,N,H,dk,dv,D,topo", [(1, 32, 32, 8, 256, 256, 2048, "window"),
+                                                   (3, 9, 13, 2, 40, 24, 72, "random"),
+                                                   (2, 64, 5, 1, 16, 8, 8, "branching")])
+def test_layer_prep_delayed_is_conv_commit_then_prep(B, Np, N, H, dk, dv, D, topo):
+    """The fused history commit: gdn_conv_commit of the previous step's path
+    followed by gdn_layer_prep, bitwise (history, q, k, v, beta, g, status),
+    for accepted, empty and out-of-range previous paths."""
+    rng = np.random.default_rng(B * 77 + Np + N)
+    npj = 2 * H * (dk + dv)
+    Cc = H * (2 * dk + dv)
+    P = f32(rng.standard_normal((B, N, npj)).astype(np.float32))
+    P_prev = f32(rng.standard_normal((B, Np, npj)).astype(np.float32))
+    x = bf(W.f32_to_bf16_bits(rng.standard_normal((B, N, D), dtype=np.float32)))
+    W_ab = bf(W.f32_to_bf16_bits(rng.standard_normal((2 * H, D), dtype=np.float32) *
+                                 np.float32(D ** -0.5)))
+    parents = i32(np.stack([_topology(topo, N, rng) for _ in range(B)]))
+    parents_prev = i32(np.stack([_topology(topo, Np, rng) for _ in range(B)]))
+    conv_w = f32((0.5 * rng.standard_normal((Cc, 4))).astype(np.float32))
+    hist0 = f32(rng.standard_normal((B, 3, Cc)).astype(np.float32))
+
+    def outs():
+        return (torch.empty((B, N, H, dk), dtype=torch.bfloat16, device=DEV),
+                torch.empty((B, N, H, dk), dtype=torch.bfloat16, device=DEV),
+                torch.empty((B, N, H, dv), dtype=torch.bfloat16, device=DEV),
+                torch.full((B, N, H), float("nan"), device=DEV),
+                torch.full((B, N, H), float("nan"), device=DEV))
+
+    lasts_cases = [[-1] * B, [Np - 1] * B, [int(rng.integers(0, Np)) for _ in range(B)]]
+    lasts_cases.append([Np] + [0] * (B - 1))  # out of range: that history stays
+    for lasts in lasts_cases:
+        lt = i32(np.array(lasts))
+        # two calls
+        h_a = hist0.clone()
+        st_a = torch.full((B,), 77, dtype=torch.int32, device=DEV)
+        G.gdn_conv_commit(P_prev, parents_prev, lt, h_a, dev_status=st_a)
+        qa, ka, va, ba, ga = outs()
+        G.gdn_layer_prep(P, x, W_ab, parents, conv_w, h_a, qa, ka, va, ba, ga, gate_shift=2.0)
+        # one fused call
+        h_b = torch.full_like(hist0, float("nan"))
+        st_b = torch.full((B,), 77, dtype=torch.int32, device=DEV)
+        qb, kb, vb, bb, gb = outs()
+        G.gdn_layer_prep_delayed(P, x, W_ab, parents, conv_w, hist0, qb, kb, vb, bb, gb, P_prev,
+                                 parents_prev, lt, h_b, gate_shift=2.0, dev_status=st_b)
+        torch.cuda.synchronize()
+        assert torch.equal(h_a, h_b), lasts
+        assert torch.equal(st_a, st_b), lasts
+        for a, b_ in ((qa, qb), (ka, kb), (va, vb)):
+            assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), lasts
+        assert torch.equal(ba, bb) and torch.equal(ga, gb), lasts
+
+
 # ---------------------------------------------------------------------------
 # gdn_decode_step
 # ---------------------------------------------------------------------------
