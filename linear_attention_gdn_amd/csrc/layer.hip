@@ -113,6 +113,14 @@ __global__ __launch_bounds__(512) void linear_w8_kernel(int M, int Nc, int K,
                                                         const float* R, float* C,
                                                         bf16_t* __restrict__ Cb) {
   __shared__ float red[8][MT * 16][NT * 16 + 4];
+  {  // rows of this workgroup: grid.y splits the rows into groups of 16 * MT
+    const size_t m0 = (size_t)blockIdx.y * (16 * MT);
+    A += m0 * K;
+    M -= (int)m0;
+    if (R) R += m0 * Nc;
+    if (C) C += m0 * Nc;
+    if (Cb) Cb += m0 * Nc;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -163,6 +171,14 @@ __global__ __launch_bounds__(256) void linear_kernel(int M, int Nc, int K,
                                                      const bf16_t* __restrict__ W, const float* R,
                                                      float* C, bf16_t* __restrict__ Cb) {
   __shared__ float red[4][MT * 16][NT * 16 + 4];
+  {  // rows of this workgroup: grid.y splits the rows into groups of 16 * MT
+    const size_t m0 = (size_t)blockIdx.y * (16 * MT);
+    A += m0 * K;
+    M -= (int)m0;
+    if (R) R += m0 * Nc;
+    if (C) C += m0 * Nc;
+    if (Cb) Cb += m0 * Nc;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,24 +248,24 @@ __global__ __launch_bounds__(256) void linear_kernel(int M, int Nc, int K,
 template <int MT, int NT, bool PK>
 hipError_t launch_linear_mn(int M, int Nc, int K, const bf16_t* A, const bf16_t* W,
                             const float* R, float* C, bf16_t* Cb, hipStream_t stream) {
-  const int grid = (Nc + 16 * NT - 1) / (16 * NT);
+  const dim3 grid((Nc + 16 * NT - 1) / (16 * NT), (M + 16 * MT - 1) / (16 * MT));
   const int ks = K / 256;
   if (ks * (MT + NT) <= 48 && (ks == 1 || ks == 2 || ks == 4 || ks == 8)) {
     switch (ks) {
-      case 1: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 1, PK>), dim3(grid), dim3(512), 0,
+      case 1: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 1, PK>), grid, dim3(512), 0,
                                  stream, M, Nc, K, A, W, R, C, Cb); break;
-      case 2: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 2, PK>), dim3(grid), dim3(512), 0,
+      case 2: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 2, PK>), grid, dim3(512), 0,
                                  stream, M, Nc, K, A, W, R, C, Cb); break;
-      case 4: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 4, PK>), dim3(grid), dim3(512), 0,
+      case 4: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 4, PK>), grid, dim3(512), 0,
                                  stream, M, Nc, K, A, W, R, C, Cb); break;
-      default: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 8, PK>), dim3(grid), dim3(512), 0,
+      default: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 8, PK>), grid, dim3(512), 0,
                                   stream, M, Nc, K, A, W, R, C, Cb); break;
     }
   } else if ((K / 128) % 4 == 0 && MT + NT <= 4) {
-    hipLaunchKernelGGL((linear_kernel<MT, NT, 4, PK>), dim3(grid), dim3(256), 0, stream, M, Nc,
+    hipLaunchKernelGGL((linear_kernel<MT, NT, 4, PK>), grid, dim3(256), 0, stream, M, Nc,
                        K, A, W, R, C, Cb);
   } else {
-    hipLaunchKernelGGL((linear_kernel<MT, NT, 2, PK>), dim3(grid), dim3(256), 0, stream, M, Nc,
+    hipLaunchKernelGGL((linear_kernel<MT, NT, 2, PK>), grid, dim3(256), 0, stream, M, Nc,
                        K, A, W, R, C, Cb);
   }
   return hipGetLastError();
@@ -266,7 +282,11 @@ hipError_t launch_linear_mt(int M, int Nc, int K, const bf16_t* A, const bf16_t*
 template <bool PK>
 hipError_t launch_linear_pk(int M, int Nc, int K, const bf16_t* a, const bf16_t* w,
                             const float* R, float* C, bf16_t* cb, hipStream_t stream) {
-  switch ((M + 15) / 16) {
+  const int rt = (M + 15) / 16;
+  // Too few column tiles to fill the chip (e.g. the 2048-column output
+  // projection): split the rows across workgroups as well.
+  if (rt > 1 && Nc / 16 < 256) return launch_linear_mn<1, 1, PK>(M, Nc, K, a, w, R, C, cb, stream);
+  switch (rt) {
     case 1: return launch_linear_mt<1, PK>(M, Nc, K, a, w, R, C, cb, stream);
     case 2: return launch_linear_mt<2, PK>(M, Nc, K, a, w, R, C, cb, stream);
     case 3: return launch_linear_mt<3, PK>(M, Nc, K, a, w, R, C, cb, stream);
