@@ -114,9 +114,11 @@ constexpr int kQKStride = kMaxDim + 8;     // bf16 elements per staged row
 constexpr int kQKBytes = kQKRows * kQKStride * 2;
 constexpr int kPathMax = 16;               // register-resident path solve up to this depth
 
-// Optional SiLU output gate fused into the epilogue: Y = bf16(O * SiLU(gate))
-// with gate row t at gate + (b N + t) ldg + h dv (the gate block of the layer's
-// projection output); null `gate` and `Y` leave the epilogue as O only.
+// SiLU output gate fused into the epilogue (the GATE variants, bf16 q/k/v
+// only): Y = bf16(O * SiLU(gate)) with gate row t at gate + (b N + t) ldg + h dv
+// (the gate block of the layer's projection output), written instead of O.
+// A compile-time variant: the gate's loads and registers would otherwise
+// slow every plain verification.
 struct GateArgs {
   const float* gate;
   int ldg;
@@ -229,7 +231,7 @@ struct DelayLds {  // k rows (FP32), u' of the tile's rows, coefficients, node i
   int node[DLY ? kMaxNodes : 1];
 };
 
-template <typename T, int BV, int NQT, bool DLY>
+template <typename T, int BV, int NQT, bool DLY, bool GATE>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
     const int32_t* __restrict__ parents, const T* __restrict__ q, const T* __restrict__ k,
@@ -321,10 +323,10 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   // 16*nb + 4*lg + r, column ccol).
   const int iK0 = NQT > rb ? (NQT - rb + WR - 1) / WR : 0;
   T vreg[MAXNB][4];
-  // Output gate values for the rows this lane stores (node 16 nb + 4 lg + r of
-  // its node blocks nb = rb + WR j, column srow); without a gate the loads
-  // read one valid state element instead, so no load sits under a branch.
-  float gvr[MAXNB][4];
+  // GATE: output gate values for the rows this lane stores (node
+  // 16 nb + 4 lg + r of its node blocks nb = rb + WR j, column srow), requested
+  // with the state tile.
+  float gvr[GATE ? MAXNB : 1][4];
   auto load_state = [&]() {
     const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
 #pragma unroll
@@ -341,13 +343,14 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         const int t = clampi(16 * nb + 4 * lg + r, N - 1);
         vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
       }
-    const float* gp = ga.gate ? ga.gate + (size_t)b * N * ga.ldg + h * dv + clampi(srow, dv - 1)
-                              : S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
-    const size_t gs = ga.gate ? (size_t)ga.ldg : 0;
+    if constexpr (GATE) {
+      const float* gp = ga.gate + (size_t)b * N * ga.ldg + h * dv + clampi(srow, dv - 1);
 #pragma unroll
-    for (int j = 0; j < MAXNB; ++j)
+      for (int j = 0; j < MAXNB; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) gvr[j][r] = gp[clampi(16 * (rb + WR * j) + 4 * lg + r, N - 1) * gs];
+        for (int r = 0; r < 4; ++r)
+          gvr[j][r] = gp[(size_t)clampi(16 * (rb + WR * j) + 4 * lg + r, N - 1) * ga.ldg];
+    }
   };
 
   // delayed commit: the previous draft's last accepted node, and node j's
@@ -918,8 +921,10 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
           const int t = 16 * nb + 4 * lg + r;
           if (t < N) {
             const size_t o = (((size_t)b * N + t) * H + h) * dv + srow;
-            if (out) out[o] = acc[r];
-            if (ga.Y) ga.Y[o] = to_bf16(acc[r] * silu(gvr[j][r]));  // gdn_gate_merge's arithmetic
+            if constexpr (GATE)
+              ga.Y[o] = to_bf16(acc[r] * silu(gvr[j][r]));  // gdn_gate_merge's arithmetic
+            else
+              out[o] = acc[r];
           }
         }
       }
@@ -935,25 +940,41 @@ struct DelayArgs {
   GateArgs gate;
 };
 
-template <typename T, int BV, int NQT>
-hipError_t launch_bvn(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
-                      const T* q, const T* k, const T* v, const float* beta, const float* g,
-                      float scale, float* out, const Record<T>& rec, uint64_t* mask_out,
-                      int32_t* dev_status, const DelayArgs& da, int dtype, hipStream_t stream) {
+template <typename T, int BV, int NQT, bool GATE>
+hipError_t launch_bvng(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
+                       const T* q, const T* k, const T* v, const float* beta, const float* g,
+                       float scale, float* out, const Record<T>& rec, uint64_t* mask_out,
+                       int32_t* dev_status, const DelayArgs& da, int dtype, hipStream_t stream) {
   const int ntiles = (dv + BV - 1) / BV;
   const long grid = (long)B * H * ntiles;
   if (da.prev_factors) {
     const RecordLayout Lp = record_layout(B, da.Np, H, dk, dv, dtype);
     const Record<T> prev = record_views<T>(const_cast<void*>(da.prev_factors), Lp);
-    hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT, true>), dim3((unsigned)grid), dim3(256), 0,
-                       stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out,
-                       rec, mask_out, dev_status, prev, da.Np, da.last, da.commit_status, da.gate);
+    hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT, true, GATE>), dim3((unsigned)grid),
+                       dim3(256), 0, stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g,
+                       scale, out, rec, mask_out, dev_status, prev, da.Np, da.last,
+                       da.commit_status, da.gate);
   } else {
-    hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT, false>), dim3((unsigned)grid), dim3(256),
-                       0, stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale,
-                       out, rec, mask_out, dev_status, Record<T>{}, 1, nullptr, nullptr, da.gate);
+    hipLaunchKernelGGL((tree_verify_kernel<T, BV, NQT, false, GATE>), dim3((unsigned)grid),
+                       dim3(256), 0, stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g,
+                       scale, out, rec, mask_out, dev_status, Record<T>{}, 1, nullptr, nullptr,
+                       da.gate);
   }
   return hipGetLastError();
+}
+
+template <typename T, int BV, int NQT>
+hipError_t launch_bvn(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
+                      const T* q, const T* k, const T* v, const float* beta, const float* g,
+                      float scale, float* out, const Record<T>& rec, uint64_t* mask_out,
+                      int32_t* dev_status, const DelayArgs& da, int dtype, hipStream_t stream) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (da.gate.gate)
+      return launch_bvng<T, BV, NQT, true>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale,
+                                           out, rec, mask_out, dev_status, da, dtype, stream);
+  }
+  return launch_bvng<T, BV, NQT, false>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale,
+                                        out, rec, mask_out, dev_status, da, dtype, stream);
 }
 
 template <typename T, int BV>
