@@ -391,8 +391,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     uint64_t m = t < N ? (1ull << t) : 0ull;
     float G = t < N ? gl : 0.f;
     int a = (t < N && !bad) ? p : -1;
-#pragma unroll
     for (int r = 0; r < 6; ++r) {  // 2^6 = 64 >= path length
+      if (__ballot(a >= 0) == 0ull) break;  // uniform: every path is complete
       const int src = a >= 0 ? a : t;
       const uint64_t ma = __shfl(m, src);
       const float Ga = __shfl(G, src);
@@ -787,30 +787,61 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   f32x4 yacc[MAXRT];
 #pragma unroll
   for (int i = 0; i < MAXRT; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (kStaged && MAXRT >= 4) {
+    // Wide tiles (8 row tiles per wave): the A fragments of the next
+    // 32-column chunk are read while this chunk's MFMAs run (two register
+    // sets).  Row tiles past nrt read staged rows that exist (the staging area
+    // holds 2 * kMaxNodes rows) and are not used.
+    constexpr int KS = kMaxDim / 32;
+    bf16x8 afr[2][MAXRT];
+    auto aload = [&](int ks, bf16x8 (&a)[MAXRT]) {
 #pragma unroll
-  for (int ks = 0; ks < kMaxDim / 32; ++ks) {  // zero-padded past dk: no branch
-    bf16x8 bhi, blo;
-    const bool okk = sok && 32 * ks + koff < dk;
-    split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi, blo);
+      for (int i = 0; i < MAXRT; ++i)
+        a[i] = lds_bf16x8(QKs + (16 * (rb + WR * i) + l16) * kQKStride + 32 * ks + koff);
+    };
+    aload(0, afr[0]);
 #pragma unroll
-    for (int i = 0; i < MAXRT; ++i) {
-      const int rt = rb + WR * i;  // rb < WR, so rt < nrt except on the last i
-      if (WR * i + WR <= nrt || rt < nrt) {
-        if (kStaged) {
-          const bf16x8 a8 = lds_bf16x8(QKs + (16 * rt + l16) * kQKStride + 32 * ks + koff);
-          yacc[i] = mfma16x16x32(a8, bhi, yacc[i]);
-          yacc[i] = mfma16x16x32(a8, blo, yacc[i]);
-        } else {
-          const bool isq = rt < NQT;
-          const int t = 16 * (isq ? rt : rt - NQT) + l16;
-          const float* arow = reinterpret_cast<const float*>(isq ? (const void*)q : (const void*)k) +
-                              (((size_t)b * N + (t < N ? t : 0)) * H + h) * dk;
-          const int kk = 32 * ks + koff;
-          bf16x8 ah, al;
-          frag_global(arow + kk, t < N && kk < dk, ah, al);
-          yacc[i] = mfma16x16x32(ah, bhi, yacc[i]);
-          yacc[i] = mfma16x16x32(ah, blo, yacc[i]);
-          yacc[i] = mfma16x16x32(al, bhi, yacc[i]);
+    for (int ks = 0; ks < KS; ++ks) {  // zero-padded past dk: no branch
+      if (ks + 1 < KS) aload(ks + 1, afr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 bhi, blo;
+      const bool okk = sok && 32 * ks + koff < dk;
+      split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi, blo);
+#pragma unroll
+      for (int i = 0; i < MAXRT; ++i) {
+        const int rt = rb + WR * i;  // rb < WR, so rt < nrt except on the last i
+        if (WR * i + WR <= nrt || rt < nrt) {
+          yacc[i] = mfma16x16x32(afr[ks & 1][i], bhi, yacc[i]);
+          yacc[i] = mfma16x16x32(afr[ks & 1][i], blo, yacc[i]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < kMaxDim / 32; ++ks) {  // zero-padded past dk: no branch
+      bf16x8 bhi, blo;
+      const bool okk = sok && 32 * ks + koff < dk;
+      split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi, blo);
+#pragma unroll
+      for (int i = 0; i < MAXRT; ++i) {
+        const int rt = rb + WR * i;  // rb < WR, so rt < nrt except on the last i
+        if (WR * i + WR <= nrt || rt < nrt) {
+          if (kStaged) {
+            const bf16x8 a8 = lds_bf16x8(QKs + (16 * rt + l16) * kQKStride + 32 * ks + koff);
+            yacc[i] = mfma16x16x32(a8, bhi, yacc[i]);
+            yacc[i] = mfma16x16x32(a8, blo, yacc[i]);
+          } else {
+            const bool isq = rt < NQT;
+            const int t = 16 * (isq ? rt : rt - NQT) + l16;
+            const float* arow = reinterpret_cast<const float*>(isq ? (const void*)q : (const void*)k) +
+                                (((size_t)b * N + (t < N ? t : 0)) * H + h) * dk;
+            const int kk = 32 * ks + koff;
+            bf16x8 ah, al;
+            frag_global(arow + kk, t < N && kk < dk, ah, al);
+            yacc[i] = mfma16x16x32(ah, bhi, yacc[i]);
+            yacc[i] = mfma16x16x32(ah, blo, yacc[i]);
+            yacc[i] = mfma16x16x32(al, bhi, yacc[i]);
+          }
         }
       }
     }
