@@ -19,7 +19,9 @@
 // the storing lane needs, one DPP row broadcast).  A workgroup owns 8 rows,
 // one per SIMD pair of half-waves, so all four SIMDs of a CU run the serial
 // loop.  Everything the loop needs (k, q, v of the 8 rows, alpha, beta) is
-// staged in LDS by one round of loads that overlaps the state-tile load.
+// staged in LDS by one round of loads; the state row is requested last in
+// that round and first read after the k.q products, so the staging runs
+// while it arrives from HBM.
 // The loop is bound by VALU issue (one wave per SIMD), so work that does not
 // depend on the row leaves it: k and q are widened to FP32 once while staging
 // (drafts of up to 32 nodes), k_t . q_t is computed once per step for the

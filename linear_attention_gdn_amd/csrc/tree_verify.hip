@@ -20,16 +20,20 @@
 // One kernel, one workgroup (4 waves) per (sequence, head, tile of BV state
 // rows).  Each workgroup:
 //   0. issues one round of loads: Q and K of its head (staged in LDS as bf16,
-//      rows padded against bank conflicts) and parents / g / beta; its S0 tile
-//      (straight into MFMA B-fragment registers) and V tile are requested
-//      right after step 1, so steps 2-3 overlap the state tile's arrival;
+//      rows padded against bank conflicts), parents / g / beta, and last its
+//      S0 tile (straight into MFMA B-fragment registers) and V tile.  Loads
+//      complete in issue order, so the staging and step 1 wait only for what
+//      precedes them while the state streams in behind steps 1-3;
 //   1. validates the parents and builds ancestor bitmasks and the
-//      path-cumulative G by pointer jumping (one lane per node);
-//   2. forms the Gram blocks Q K^T and K K^T on bf16 MFMA (lower triangle);
+//      path-cumulative G by pointer jumping (one lane per node, stopping when
+//      every path is complete);
+//   2. forms the Gram blocks Q K^T and K K^T on bf16 MFMA (lower triangle,
+//      tiles round-robin over the waves, the next tile's fragments read while
+//      the current tile multiplies);
 //   3. masks and scales them into A and Attn (all threads, only the N x N
-//      block the products read), then solves row t of T on t's root path
-//      (rows of T vanish off the path), one lane per node with the path's
-//      block of A in registers;
+//      block the products read, every operand read before any is used), then
+//      solves row t of T on t's root path (rows of T vanish off the path), one
+//      lane per node with the path's block of A in registers;
 //   4. runs the dense contraction Y = [Q; K] S0_tile^T on bf16 MFMA with the
 //      FP32 state split into bf16 hi + lo (bf16 q, k make every product
 //      exact; only the 2^-16 split residue is lost);
@@ -45,11 +49,16 @@
 // Delayed commit (review: Referee Report summary, mechanism (ii); Figure 7
 // caption, right side): with DLY the kernel also applies the previous draft's
 // accepted path to its register-resident state tile before step 4.  The
-// path (from the previous record's masks) is known after step 0; its k rows,
-// u' of the tile's rows and coefficients e^{G_last - G_i} are loaded during
-// step 1 and staged in LDS (16 path nodes at a time) while steps 2-3 run,
-// then applied in the commit kernel's operation order (so the committed
-// state is bitwise gdn_commit_path's) and the tile is written back once.
+// path (from the previous record's masks) is known after step 1; its k rows,
+// u' of the tile's rows and coefficients e^{G_last - G_i} are loaded then and
+// staged in LDS (16 path nodes at a time) while steps 2-3 run, then applied
+// in the commit kernel's operation order (so the committed state is bitwise
+// gdn_commit_path's) and the tile is written back once.  With tiles of at most
+// 16 rows the four waves split the tile's columns for this and exchange the
+// committed quarters through LDS.
+//
+// GATE variants (gdn_layer_verify) multiply the outputs by SiLU of the
+// layer's gate in the epilogue and store them as bf16.
 #include <type_traits>
 
 #include "gdn_common.h"
