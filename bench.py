@@ -49,7 +49,8 @@ CSRC = os.path.join(ROOT, "linear_attention_gdn_amd", "csrc")
 KERNEL_SOURCES = {"gdn_chain_verify": "chain_verify.hip", "gdn_tree_verify": "tree_verify.hip",
                   "gdn_commit_path": "commit.hip", "gdn_linear": "layer.hip",
                   "gdn_chain_verify_delayed": "chain_verify.hip",
-                  "gdn_tree_verify_delayed": "tree_verify.hip"}
+                  "gdn_tree_verify_delayed": "tree_verify.hip",
+                  "gdn_layer_verify": "tree_verify.hip"}
 
 
 def source_digest(kernel: str) -> str:
