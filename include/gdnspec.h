@@ -196,6 +196,10 @@ int gdn_commit_path(int B, int N, int H, int dk, int dv, int qkv_dtype, float* S
  *                 as it was and the new chain is verified from it
  *   factors       the new record; must not overlap prev_factors
  *   other arguments as for gdn_chain_verify
+ * One workgroup stages the new draft and the previous record's k rows in its
+ * 160 KiB of LDS: with float32 q/k/v and large N + N_prev (e.g. 64 + 64 at
+ * dk = 256) that does not fit, and the call returns GDN_ERR_UNSUPPORTED
+ * before launching anything (bf16 inputs fit at every size).
  */
 int gdn_chain_verify_delayed(int B, int N_prev, int N, int H, int dk, int dv, int qkv_dtype,
                              float* S, const void* prev_factors, const int32_t* last_accepted,

@@ -11,6 +11,7 @@
 #include "../../include/gdnlayer.h"
 
 namespace gdn {
+size_t chain_lds_bytes(int N, int Np, int dk, int dtype);
 hipError_t launch_chain_verify(int B, int N, int H, int dk, int dv, int dtype, float* S0,
                                const void* q, const void* k, const void* v, const float* beta,
                                const float* g, float scale, float* out, void* factors,
@@ -104,6 +105,17 @@ int check_ptr4(const char* fn, const char* name, const void* p, bool required) {
   }
   if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
     return fail(GDN_ERR_ARG, "%s: %s is not 4-byte aligned", fn, name);
+  return GDN_OK;
+}
+
+// One chain workgroup stages the draft (and the previous record) in LDS.
+int check_chain_lds(const char* fn, int N, int N_prev, int dk, int dtype) {
+  const size_t need = gdn::chain_lds_bytes(N, N_prev, dk, dtype);
+  if (need > (size_t)gdn::kMaxLds)
+    return fail(GDN_ERR_UNSUPPORTED,
+                "%s: N=%d, N_prev=%d, dk=%d with %s inputs needs %zu bytes of LDS per workgroup "
+                "(limit %d); use bf16 inputs or smaller drafts",
+                fn, N, N_prev, dk, dtype == GDN_BF16 ? "bf16" : "fp32", need, gdn::kMaxLds);
   return GDN_OK;
 }
 
@@ -234,6 +246,7 @@ int gdn_chain_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const f
   GDN_TRY(check_ptr4(fn, "g", g, true));
   GDN_TRY(check_ptr(fn, "out", out, true));
   GDN_TRY(check_ptr(fn, "factors", factors, true));
+  GDN_TRY(check_chain_lds(fn, N, 0, dk, qkv_dtype));
   return hip_status(fn, gdn::launch_chain_verify(B, N, H, dk, dv, qkv_dtype,
                                                  const_cast<float*>(S0), q, k, v, beta, g,
                                                  scale, out, factors, nullptr, 0, nullptr,
@@ -271,6 +284,7 @@ int gdn_chain_verify_delayed(int B, int N_prev, int N, int H, int dk, int dv, in
   const size_t nb = gdn::record_layout(B, N, H, dk, dv, qkv_dtype).total;
   if (a0 < b0 + nb && b0 < a0 + na)
     return fail(GDN_ERR_ARG, "%s: factors and prev_factors overlap", fn);
+  GDN_TRY(check_chain_lds(fn, N, N_prev, dk, qkv_dtype));
   return hip_status(fn, gdn::launch_chain_verify(B, N, H, dk, dv, qkv_dtype, S, q, k, v, beta, g,
                                                  scale, out, factors, prev_factors, N_prev,
                                                  last_accepted, dev_status,

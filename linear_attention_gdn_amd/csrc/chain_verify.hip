@@ -12,21 +12,24 @@
 //     o_t[r] = scale (alpha_t y_q + (k_t . q_t) u'_t[r])
 //     S_r <- alpha_t S_r + u'_t[r] k_t
 //
-// Mapping: 256 threads = 4 waves; each half-wave (32 lanes) owns one state row
-// and lane s of it holds columns 128*m + 4*s + e (m < dk/128, e < 4), so a row
-// is read as 512-byte coalesced runs and dot products reduce over 32 lanes
-// with DPP row rotations plus one v_permlane16_swap (or, for y_q, which only
-// the storing lane needs, one DPP row broadcast).  A workgroup owns 8 rows,
-// one per SIMD pair of half-waves, so all four SIMDs of a CU run the serial
-// loop.  Everything the loop needs (k, q, v of the 8 rows, alpha, beta) is
-// staged in LDS by one round of loads; the state row is requested last in
-// that round and first read after the k.q products, so the staging runs
-// while it arrives from HBM.
-// The loop is bound by VALU issue (one wave per SIMD), so work that does not
-// depend on the row leaves it: k and q are widened to FP32 once while staging
-// (drafts of up to 32 nodes), k_t . q_t is computed once per step for the
-// whole workgroup before the loop, and column masks exist only for d_k < 256.
-// Each step reads the next step's operands from LDS while it computes.
+// Mapping: 512 threads = 8 waves; each wave owns one state row and lane s
+// holds columns 4s .. 4s + 3, so a row is one 1 KiB coalesced read and the
+// dot products reduce over the wave with DPP row rotations plus
+// v_permlane16_swap and v_permlane32_swap (for y_q, which only the storing
+// lane needs, two DPP row broadcasts instead).  A workgroup owns 8 rows and
+// puts two waves on every SIMD of its CU: the serial loop is a chain of
+// dependent VALU, DPP and LDS operations, and the second wave issues while
+// the first waits on one.  Everything the loop needs is staged in LDS by one
+// round of loads: k and q of every node (interleaved per node, so one address
+// serves both), and per node and row the step scalars {alpha, beta, k.q, v},
+// read as one 16-byte word.  The state row is requested last in that round
+// and first read after the k.q products, so the staging runs while it arrives
+// from HBM.  Work that does not depend on the row leaves the loop: k and q
+// are widened to FP32 once while staging (drafts of up to 32 nodes), k_t . q_t
+// is computed once per node for the whole workgroup before the loop, and
+// column masks exist only for d_k < 256.  Each step reads the next step's
+// operands from LDS while it computes; a padding node after the last one
+// keeps that read-ahead free of clamps.
 //
 // Delayed commit (review: Referee Report summary, mechanism (ii); Figure 7
 // caption, right side): with DLY the same workgroup first applies the
@@ -42,7 +45,8 @@
 
 namespace gdn {
 
-constexpr int kChainRows = 8;  // state rows per workgroup (one per half-wave)
+constexpr int kChainRows = 8;      // state rows per workgroup (one per wave)
+constexpr int kChainThreads = 512;  // 8 waves: two per SIMD
 
 // Stored form of staged k/q rows: FP32 (QF) or as loaded.
 template <typename T, bool QF>
@@ -61,34 +65,32 @@ __device__ inline u32x2 unstage(const f32x4& x, bf16_t*) {
 __device__ inline u32x2 unstage(const u32x2& x, bf16_t*) { return x; }
 
 template <typename T, bool DLY, bool QF, bool FULL>
-__global__ __launch_bounds__(256) void chain_verify_kernel(
+__global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ beta, const float* __restrict__ g, float scale,
     float* __restrict__ out, Record<T> rec, Record<T> prev, int Np,
     const int32_t* __restrict__ last_acc, int32_t* __restrict__ dev_status) {
-  constexpr int MC = kMaxDim / 128;  // float4 chunks per lane
+  static_assert(kMaxDim == 256, "one float4 of each state row per lane");
+  constexpr int NT = kChainThreads;
   using R4 = typename Raw4<T>::type;
   using SK = typename Staged<T, QF>::type;
-  // dynamic LDS: k, q [N][dk] (staged form), v [N][8], alpha, beta, g, k.q [N];
-  // with DLY also the previous record's k [Np][dk] (as loaded), u' of the
-  // tile's rows [Np][8] and the commit coefficients e^{G_last - G_i} [Np]
+  // dynamic LDS: k and q rows interleaved per node [N + 1][2][dk] (staged
+  // form; node N is padding that the loop's read-ahead may touch), the step
+  // scalars {alpha, beta, k.q, v[row]} [N + 1][8], G [N]; with DLY also, in
+  // accepted-path order, the previous record's k rows [Np][dk] (as loaded)
+  // and the commit coefficients e^{G_last - G_p} u'_p[row] [Np][8]
   extern __shared__ f32x4 lds4[];
   const int cpr = dk / 4;
-  SK* sk = reinterpret_cast<SK*>(lds4);
-  SK* sq = sk + N * cpr;
-  R4* skp = reinterpret_cast<R4*>(sq + N * cpr);
-  float* sv = reinterpret_cast<float*>(skp + (DLY ? Np * cpr : 0));
-  float* salpha = sv + N * kChainRows;
-  float* sbeta = salpha + N;
-  float* sG = sbeta + N;
-  float* skq = sG + N;
-  float* sup = skq + N;
-  float* sGp = sup + (DLY ? Np * kChainRows : 0);
+  f32x4* ssc = lds4;                                  // [N + 1][8]
+  SK* skq = reinterpret_cast<SK*>(ssc + (N + 1) * kChainRows);  // [N + 1][2][cpr]
+  R4* skp = reinterpret_cast<R4*>(skq + (N + 1) * 2 * cpr);
+  float* sG = reinterpret_cast<float*>(skp + (DLY ? Np * cpr : 0));
+  float* scp = sG + N;
 
   const int tid = threadIdx.x;
-  const int s = tid & 31;             // lane within the row's half-wave
-  const int rl = tid >> 5;            // row within the tile (0..7)
+  const int s = tid & 63;  // lane: columns 4s .. 4s + 3 of the wave's row
+  const int rl = tid >> 6;  // row within the tile (0..7)
   const int tile = blockIdx.x % ntiles;
   const int bh = blockIdx.x / ntiles;
   const int h = bh % H;
@@ -96,283 +98,262 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
   const int r0 = tile * kChainRows;
   const int row = r0 + rl;
   const bool rok = row < dv;
-  auto colok = [&](int m) { return FULL || 128 * m + 4 * s < dk; };
+  const bool cok = FULL || s < cpr;
+  const int sc = FULL ? s : clampi(s, cpr - 1);
+  auto kidx = [&](int t) { return 2 * t * cpr + sc; };  // k chunk of node t; q is cpr further
+  auto qidx = [&](int t) { return (2 * t + 1) * cpr + sc; };
 
   // ---- every global load first (unconditional, clamped), then the LDS writes
-  const size_t nhl = ((size_t)b * N + clampi(tid, N - 1)) * H + h;
+  const size_t nhl = ((size_t)b * N + clampi(s, N - 1)) * H + h;
   const float gl = g[nhl];
   const float bl = beta[nhl];
-  constexpr int VB = kMaxNodes * kChainRows / 256;  // v values per thread, at most
-  T vb[VB];
-#pragma unroll
-  for (int x = 0; x < VB; ++x) {
-    const int idx = clampi(tid + 256 * x, N * kChainRows - 1);
-    const int r = clampi(r0 + idx % kChainRows, dv - 1);
-    vb[x] = v[(((size_t)b * N + idx / kChainRows) * H + h) * dv + r];
-  }
+  static_assert(kMaxNodes * kChainRows <= NT, "one v value per thread");
+  const int vi = clampi(tid, N * kChainRows - 1);
+  const T vb = v[(((size_t)b * N + vi / kChainRows) * H + h) * dv +
+                 clampi(r0 + vi % kChainRows, dv - 1)];
   // the previous draft's record (delayed commit): masks, G, u' of this tile's
   // rows and the k rows, none of which depends on last_accepted
-  constexpr int BATCH = 4;
-  int last = -1;
+  constexpr int BATCH = 2;
   int last_v = -1;
   uint64_t mlp = 0;
-  float glp = 0.f;
-  float upb[DLY ? VB : 1];
+  float glp = 0.f, gnp = 0.f, upb = 0.f;
   R4 kpb[DLY ? BATCH : 1];
   auto prevk_off = [&](int idx) {
     idx = clampi(idx, Np * cpr - 1);
     return ((size_t)bh * Np + idx / cpr) * dk + 4 * (idx % cpr);
   };
-  uint64_t pm_r = 0;   // accepted path of the previous draft (bit i: node i)
-  float Glast_r = 0.f;
   if (DLY) {
     last_v = last_acc[b];  // a vector load: it joins this round instead of a later scalar one
-    const int tcp = clampi(tid & 63, Np - 1);  // every wave holds node j's mask and G in lane j
+    const int tcp = clampi(s, Np - 1);  // every wave holds node j's mask and G in lane j
     mlp = prev.mask[(size_t)b * Np + tcp];
     glp = prev.G[(size_t)bh * Np + tcp];
+    const int ui = clampi(tid, Np * kChainRows - 1);  // node ui / 8, row ui % 8
+    gnp = prev.G[(size_t)bh * Np + ui / kChainRows];
+    upb = prev.up[((size_t)bh * Np + ui / kChainRows) * dv + clampi(r0 + ui % kChainRows, dv - 1)];
 #pragma unroll
-    for (int x = 0; x < VB; ++x) {
-      const int idx = clampi(tid + 256 * x, Np * kChainRows - 1);
-      const int r = clampi(r0 + idx % kChainRows, dv - 1);
-      upb[x] = prev.up[((size_t)bh * Np + idx / kChainRows) * dv + r];
-    }
-#pragma unroll
-    for (int x = 0; x < BATCH; ++x) kpb[x] = raw4(prev.K + prevk_off(tid + 256 * x));
+    for (int x = 0; x < BATCH; ++x) kpb[x] = raw4(prev.K + prevk_off(tid + NT * x));
   }
   // k and q rows: the first batch is straight-line code (a loop here would
   // drain every outstanding load at its header); larger drafts loop.
   auto stage_load = [&](int base, R4 (&kb)[BATCH], R4 (&qb)[BATCH]) {
 #pragma unroll
     for (int x = 0; x < BATCH; ++x) {
-      const int idx = clampi(base + 256 * x, N * cpr - 1);
+      const int idx = clampi(base + NT * x, N * cpr - 1);
       const size_t off = (((size_t)b * N + idx / cpr) * H + h) * dk + 4 * (idx % cpr);
       kb[x] = raw4(k + off);
       qb[x] = raw4(q + off);
     }
   };
+  // k_t . q_t (the same for every row), stored for all 8 rows by lanes 0..7
+  auto kq_store = [&](int t, const f32x4& kx, const f32x4& qx) {
+    float a = kx.x * qx.x;
+    float a2 = kx.y * qx.y;
+    a = fmaf(kx.z, qx.z, a);
+    a2 = fmaf(kx.w, qx.w, a2);
+    a = wave64_sum(a + a2);
+    if (s < kChainRows) reinterpret_cast<float*>(&ssc[t * kChainRows + s])[2] = a;
+  };
   // No branch around the stores (a load used only under one is sunk into it
   // and waited for together with everything issued before): past the end a
   // thread rewrites the clamped chunk with the bits it loaded for it, which
-  // are the owner's bits.
+  // are the owner's bits.  With d_k = 256 a wave holds whole k and q rows
+  // (chunk c of node t in lane c of wave t % 8), so it forms k_t . q_t here,
+  // from registers.
   auto stage_store = [&](int base, const R4 (&kb)[BATCH], const R4 (&qb)[BATCH]) {
 #pragma unroll
     for (int x = 0; x < BATCH; ++x) {
-      const int idx = clampi(base + 256 * x, N * cpr - 1);
-      sk[idx] = stage_cvt(kb[x], (SK*)nullptr);
-      sq[idx] = stage_cvt(qb[x], (SK*)nullptr);
+      const int idx = clampi(base + NT * x, N * cpr - 1);
+      const int t = idx / cpr, c = idx % cpr;
+      skq[2 * t * cpr + c] = stage_cvt(kb[x], (SK*)nullptr);
+      skq[(2 * t + 1) * cpr + c] = stage_cvt(qb[x], (SK*)nullptr);
+      if (FULL && base - s + NT * x < N * cpr)  // uniform: the wave's node exists
+        kq_store(t, widen4(kb[x]), widen4(qb[x]));
     }
   };
   R4 kb0[BATCH], qb0[BATCH];
   stage_load(tid, kb0, qb0);
   // The state row is requested last: loads complete in issue order, so the
   // staging below waits only for the loads above, and the state (from HBM)
-  // streams in while the staging and the k.q products run.
-  f32x4 Sx[MC];
+  // streams in while the staging runs.
+  f32x4 Sx;
   __builtin_amdgcn_sched_barrier(0);
-  {
-    const float* rp = S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) Sx[m] = load4(rp + clampi(128 * m + 4 * s, dk - 4));
-  }
+  Sx = load4(S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk + 4 * sc);
   __builtin_amdgcn_sched_barrier(0);
-  stage_store(tid, kb0, qb0);
-  for (int base = tid + 256 * BATCH; base < N * cpr; base += 256 * BATCH) {
-    R4 kb[BATCH], qb[BATCH];
-    stage_load(base, kb, qb);
-    stage_store(base, kb, qb);
-  }
+
+  // the previous draft's accepted path (bit i: node i), its length and G_last
+  int last = -1, npath = 0;
+  uint64_t pm = 0;
+  float Glast = 0.f;
   if (DLY) {
-#pragma unroll
-    for (int x = 0; x < BATCH; ++x)
-      if (tid + 256 * x < Np * cpr) skp[tid + 256 * x] = kpb[x];
-    for (int base = tid + 256 * BATCH; base < Np * cpr; base += 256 * BATCH) {
-      R4 kb[BATCH];
-#pragma unroll
-      for (int x = 0; x < BATCH; ++x) kb[x] = raw4(prev.K + prevk_off(base + 256 * x));
-#pragma unroll
-      for (int x = 0; x < BATCH; ++x)
-        if (base + 256 * x < Np * cpr) skp[base + 256 * x] = kb[x];
-    }
-  }
-#pragma unroll
-  for (int x = 0; x < VB; ++x) {
-    const int idx = tid + 256 * x;
-    if (idx < N * kChainRows) sv[idx] = (r0 + idx % kChainRows < dv) ? widen1(vb[x]) : 0.f;
-  }
-  if (tid < N) {
-    salpha[tid] = expf(gl);
-    sbeta[tid] = bl;
-    sG[tid] = gl;
-  }
-  if (DLY) {
-    // the accepted path and each node's coefficient e^{G_last - G_i}, one lane
-    // per node (the same expression the commit kernel evaluates)
     last = __builtin_amdgcn_readfirstlane(last_v);
     const bool in_rng = last >= 0 && last < Np;
     const int lc = in_rng ? last : 0;
     const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)mlp, lc);
     const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(mlp >> 32), lc);
     const uint64_t valid = Np >= 64 ? ~0ull : ((1ull << Np) - 1ull);
-    pm_r = in_rng ? ((((uint64_t)mhi << 32) | mlo) & valid) : 0ull;
-    Glast_r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, glp), lc));
-    if (tid < Np) sGp[tid] = ((pm_r >> tid) & 1ull) ? expf(Glast_r - glp) : 0.f;
+    pm = in_rng ? ((((uint64_t)mhi << 32) | mlo) & valid) : 0ull;
+    npath = __popcll(pm);
+    Glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, glp), lc));
+  }
+  auto rank = [&](int node) { return __popcll(pm & ((1ull << node) - 1ull)); };
+  auto on_path = [&](int node) { return ((pm >> node) & 1ull) != 0ull; };
+
+  stage_store(tid, kb0, qb0);
+  for (int base = tid + NT * BATCH; base < N * cpr; base += NT * BATCH) {
+    R4 kb[BATCH], qb[BATCH];
+    stage_load(base, kb, qb);
+    stage_store(base, kb, qb);
+  }
+  if (DLY) {
+    // path nodes' k rows and coefficients, packed in path order; the
+    // coefficient is the commit kernel's expression, e^{G_last - G_p} * u'_p[row]
 #pragma unroll
-    for (int x = 0; x < VB; ++x) {
-      const int idx = tid + 256 * x;
-      if (idx < Np * kChainRows) sup[idx] = (r0 + idx % kChainRows < dv) ? upb[x] : 0.f;
+    for (int x = 0; x < BATCH; ++x) {
+      const int idx = tid + NT * x;
+      if (idx < Np * cpr && on_path(idx / cpr))
+        skp[rank(idx / cpr) * cpr + idx % cpr] = kpb[x];
     }
+    for (int base = tid + NT * BATCH; base < Np * cpr; base += NT * BATCH) {
+      R4 kb[BATCH];
+#pragma unroll
+      for (int x = 0; x < BATCH; ++x) kb[x] = raw4(prev.K + prevk_off(base + NT * x));
+#pragma unroll
+      for (int x = 0; x < BATCH; ++x) {
+        const int idx = base + NT * x;
+        if (idx < Np * cpr && on_path(idx / cpr))
+          skp[rank(idx / cpr) * cpr + idx % cpr] = kb[x];
+      }
+    }
+    const int node = tid / kChainRows;
+    if (tid < Np * kChainRows && on_path(node))
+      scp[rank(node) * kChainRows + tid % kChainRows] = expf(Glast - gnp) * upb;
+  }
+  // step scalars: alpha and beta from lane t of every wave, v of row r from
+  // thread t * 8 + r; k.q is already there with d_k = 256, else follows
+  if (tid < N * kChainRows)
+    reinterpret_cast<float*>(&ssc[tid])[3] = (r0 + tid % kChainRows < dv) ? widen1(vb) : 0.f;
+  if (tid < N) sG[tid] = gl;
+  if (s < N) {  // wave rl writes alpha, beta of node s for its own row
+    float* e = reinterpret_cast<float*>(&ssc[s * kChainRows + rl]);
+    e[0] = expf(gl);
+    e[1] = bl;
   }
   __syncthreads();
 
-  // ---- k_t . q_t, the same for every row: half-wave rl takes nodes rl, rl + 8, ...
-  auto kchunk = [&](const SK* base, int t, int m) {
-    return mask4(widen4(base[t * cpr + (FULL ? 32 * m + s : clampi(32 * m + s, cpr - 1))]),
-                 colok(m));
-  };
-  for (int t = rl; t < N; t += kChainRows) {
-    float a = 0.f, a2 = 0.f;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      const f32x4 kx = kchunk(sk, t, m);
-      const f32x4 qx = kchunk(sq, t, m);
-      a = fmaf(kx.x, qx.x, a);
-      a2 = fmaf(kx.y, qx.y, a2);
-      a = fmaf(kx.z, qx.z, a);
-      a2 = fmaf(kx.w, qx.w, a2);
-    }
-    a = half32_sum(a + a2);
-    if (s == 0) skq[t] = a;
+  if (!FULL) {
+    // ---- k_t . q_t from LDS: wave rl takes nodes rl, rl + 8, ...
+    for (int t = rl; t < N; t += kChainRows)
+      kq_store(t, mask4(widen4(skq[kidx(t)]), cok), mask4(widen4(skq[qidx(t)]), cok));
   }
 
   // the state row (first needed here)
-  float S[MC][4];
-#pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    const f32x4 x = mask4(Sx[m], rok && colok(m));
-    S[m][0] = x.x;
-    S[m][1] = x.y;
-    S[m][2] = x.z;
-    S[m][3] = x.w;
-  }
+  const f32x4 Sm = mask4(Sx, rok && cok);
+  float S[4] = {Sm.x, Sm.y, Sm.z, Sm.w};
 
   if (DLY) {
-    // ---- the previous draft's accepted path: S <- e^{G_last} S + sum c_i u'_i k_i^T
-    const uint64_t pm = pm_r;
-    const bool okp = last >= 0 && last < Np && ((pm >> last) & 1ull);
+    // ---- the previous draft's accepted path: S <- e^{G_last} S + sum c_p k_p^T,
+    // path nodes in increasing order, four at a time (the LDS reads of a group
+    // are issued before its multiply-adds)
+    const bool okp = last >= 0 && last < Np && on_path(last);
     if (dev_status && tile == 0 && h == 0 && tid == 0)
       dev_status[b] = (last == -1 || okp) ? GDN_OK : GDN_ERR_TOPOLOGY;
     if (okp) {  // uniform
-      const float s0 = expf(Glast_r);
+      const float s0 = expf(Glast);
 #pragma unroll
-      for (int m = 0; m < MC; ++m)
+      for (int e = 0; e < 4; ++e) S[e] = S[e] * s0;
+      auto apply = [&](int i, auto K) {
+        constexpr int KN = decltype(K)::value;
+        float c[KN];
+        f32x4 kc[KN];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[m][e] = S[m][e] * s0;
-      // path nodes in increasing order, four at a time: the LDS reads of a
-      // group are issued before its multiply-adds
-      for (int i0 = 0; i0 <= last; i0 += 4) {
-        float c[4];
-        f32x4 kc[4][MC];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = clampi(i0 + u, Np - 1);
-          c[u] = sGp[i] * sup[i * kChainRows + rl];
-#pragma unroll
-          for (int m = 0; m < MC; ++m) kc[u][m] = widen4(skp[i * cpr + clampi(32 * m + s, cpr - 1)]);
+        for (int u = 0; u < KN; ++u) {
+          c[u] = scp[(i + u) * kChainRows + rl];
+          kc[u] = widen4(skp[(i + u) * cpr + sc]);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          if (i0 + u > last || ((pm >> (i0 + u)) & 1ull) == 0ull) continue;  // uniform
-#pragma unroll
-          for (int m = 0; m < MC; ++m) {
-            S[m][0] = fmaf(c[u], kc[u][m].x, S[m][0]);
-            S[m][1] = fmaf(c[u], kc[u][m].y, S[m][1]);
-            S[m][2] = fmaf(c[u], kc[u][m].z, S[m][2]);
-            S[m][3] = fmaf(c[u], kc[u][m].w, S[m][3]);
-          }
+        for (int u = 0; u < KN; ++u) {
+          S[0] = fmaf(c[u], kc[u].x, S[0]);
+          S[1] = fmaf(c[u], kc[u].y, S[1]);
+          S[2] = fmaf(c[u], kc[u].z, S[2]);
+          S[3] = fmaf(c[u], kc[u].w, S[3]);
         }
+      };
+      int i = 0;
+      for (; i + 4 <= npath; i += 4) apply(i, std::integral_constant<int, 4>());
+      switch (npath - i) {
+        case 3: apply(i, std::integral_constant<int, 3>()); break;
+        case 2: apply(i, std::integral_constant<int, 2>()); break;
+        case 1: apply(i, std::integral_constant<int, 1>()); break;
+        default: break;
       }
-      if (rok) {
-        float* wp = S0 + ((size_t)bh * dv + row) * dk;
-#pragma unroll
-        for (int m = 0; m < MC; ++m)
-          if (colok(m))
-            *reinterpret_cast<f32x4*>(wp + 128 * m + 4 * s) =
-                f32x4{S[m][0], S[m][1], S[m][2], S[m][3]};
-      }
+      if (rok && cok)
+        *reinterpret_cast<f32x4*>(S0 + ((size_t)bh * dv + row) * dk + 4 * s) =
+            f32x4{S[0], S[1], S[2], S[3]};
     }
   }
-  __syncthreads();  // k.q of every node is in LDS
+  if (!FULL) __syncthreads();  // k.q of every node is in LDS
 
-  // ---- the recurrence.  Operands of step t (k_t, q_t chunks; alpha, beta,
-  // v, k.q) are read from LDS during step t - 1; two register sets alternate.
+  // ---- the recurrence.  Operands of step t (k_t, q_t chunks and the step
+  // scalars) are read from LDS during step t - 1; two register sets
+  // alternate.  The read-ahead past the last node lands in the padding node.
   struct Ops {
-    f32x4 kc[MC], qc[MC];
-    float al, be, vt, kq;
+    f32x4 kc, qc, sc;  // sc = {alpha, beta, k.q, v[row]}
   };
+  const SK* kq_lane = skq + sc;
+  const f32x4* sc_row = ssc + rl;
   auto fetch = [&](int t, Ops& o) {
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      o.kc[m] = kchunk(sk, t, m);
-      o.qc[m] = kchunk(sq, t, m);
-    }
-    o.al = salpha[t];
-    o.be = sbeta[t];
-    o.vt = sv[t * kChainRows + rl];
-    o.kq = skq[t];
+    o.kc = mask4(widen4(kq_lane[2 * t * cpr]), cok);
+    o.qc = mask4(widen4(kq_lane[(2 * t + 1) * cpr]), cok);
+    o.sc = sc_row[t * kChainRows];
   };
-  const size_t obase = (size_t)b * N * H * dv + (size_t)h * dv + row;
-  const size_t ubase = (size_t)bh * N * dv + row;
-  auto run = [&](int t, const Ops& o) {
-    float yk = 0.f, yq = 0.f, yk2 = 0.f, yq2 = 0.f;
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      yk = fmaf(S[m][0], o.kc[m].x, yk);
-      yq = fmaf(S[m][0], o.qc[m].x, yq);
-      yk2 = fmaf(S[m][1], o.kc[m].y, yk2);
-      yq2 = fmaf(S[m][1], o.qc[m].y, yq2);
-      yk = fmaf(S[m][2], o.kc[m].z, yk);
-      yq = fmaf(S[m][2], o.qc[m].z, yq);
-      yk2 = fmaf(S[m][3], o.kc[m].w, yk2);
-      yq2 = fmaf(S[m][3], o.qc[m].w, yq2);
+  // lane 63 holds y_q and stores the step's output and u'
+  float* op = out + (size_t)b * N * H * dv + (size_t)h * dv + row;
+  float* up = rec.up + (size_t)bh * N * dv + row;
+  const size_t ostep = (size_t)H * dv;
+  const bool store_lane = s == 63 && rok;
+  auto run = [&](const Ops& o) {
+    const float al = o.sc.x, be = o.sc.y, kq = o.sc.z, vt = o.sc.w;
+    float yk = S[0] * o.kc.x;
+    float yk2 = S[1] * o.kc.y;
+    float yq = S[0] * o.qc.x;
+    float yq2 = S[1] * o.qc.y;
+    yk = fmaf(S[2], o.kc.z, yk);
+    yk2 = fmaf(S[3], o.kc.w, yk2);
+    yq = fmaf(S[2], o.qc.z, yq);
+    yq2 = fmaf(S[3], o.qc.w, yq2);
+    yk = wave64_sum(yk + yk2);
+    yq = wave64_sum_hi(yq + yq2);  // complete in lanes 48..63 only
+    const float u = be * (vt - al * yk);
+    S[0] = fmaf(u, o.kc.x, al * S[0]);
+    S[1] = fmaf(u, o.kc.y, al * S[1]);
+    S[2] = fmaf(u, o.kc.z, al * S[2]);
+    S[3] = fmaf(u, o.kc.w, al * S[3]);
+    if (store_lane) {
+      *op = scale * fmaf(kq, u, al * yq);
+      *up = u;
     }
-    yk = half32_sum(yk + yk2);
-    yq = half32_sum_hi(yq + yq2);  // complete in lanes 16..31 of the half-wave only
-    const float u = o.be * (o.vt - o.al * yk);
-    const float ov = scale * fmaf(o.kq, u, o.al * yq);
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      S[m][0] = fmaf(u, o.kc[m].x, o.al * S[m][0]);
-      S[m][1] = fmaf(u, o.kc[m].y, o.al * S[m][1]);
-      S[m][2] = fmaf(u, o.kc[m].z, o.al * S[m][2]);
-      S[m][3] = fmaf(u, o.kc[m].w, o.al * S[m][3]);
-    }
-    if (s == 16 && rok) {
-      out[obase + (size_t)t * H * dv] = ov;
-      rec.up[ubase + (size_t)t * dv] = u;
-    }
+    op += ostep;
+    up += dv;
   };
   // The prefetched operands pass through an empty asm after the step that
   // overlaps their reads: the values carried around the loop are then not
   // loads, which the optimiser would otherwise re-issue at the top of the
   // next step (folding a phi of loads into a load) and wait for at once.
   auto opaque = [](Ops& o) {
-#pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      asm volatile("" : "+v"(o.kc[m]));
-      asm volatile("" : "+v"(o.qc[m]));
-    }
-    asm volatile("" : "+v"(o.al), "+v"(o.be), "+v"(o.vt), "+v"(o.kq));
+    asm volatile("" : "+v"(o.kc));
+    asm volatile("" : "+v"(o.qc));
+    asm volatile("" : "+v"(o.sc));
   };
   Ops A, Bo;
   fetch(0, A);
   opaque(A);
   for (int t = 0; t < N; t += 2) {
-    fetch(clampi(t + 1, N - 1), Bo);
-    run(t, A);
+    fetch(t + 1, Bo);
+    run(A);
     opaque(Bo);
     if (t + 1 < N) {  // uniform
-      fetch(clampi(t + 2, N - 1), A);
-      run(t + 1, Bo);
+      fetch(t + 2, A);
+      run(Bo);
       opaque(A);
     }
   }
@@ -386,14 +367,26 @@ __global__ __launch_bounds__(256) void chain_verify_kernel(
         rec.G[(size_t)bh * N + t] = G;
       }
     }
-    for (int idx = tid; idx < N * cpr; idx += 256)  // from the staged rows in LDS
+    for (int idx = tid; idx < N * cpr; idx += NT)  // from the staged rows in LDS
       *reinterpret_cast<R4*>(rec.K + ((size_t)bh * N + idx / cpr) * dk + 4 * (idx % cpr)) =
-          unstage(sk[idx], (T*)nullptr);
+          unstage(skq[2 * (idx / cpr) * cpr + idx % cpr], (T*)nullptr);
     if (h == 0 && tid < N) {
       rec.parents[(size_t)b * N + tid] = tid - 1;
       rec.mask[(size_t)b * N + tid] = tid >= 63 ? ~0ull : ((1ull << (tid + 1)) - 1ull);
     }
   }
+}
+
+// k, q staged as FP32 for drafts of up to 32 nodes (bf16 beyond, to bound LDS)
+bool chain_staged_f32(int N, int dtype) { return dtype == GDN_F32 || N <= 32; }
+
+// Dynamic LDS of one workgroup (the layout at the top of the kernel); Np = 0
+// without a previous record.
+size_t chain_lds_bytes(int N, int Np, int dk, int dtype) {
+  const size_t el = dtype == GDN_BF16 ? 2 : 4;
+  const size_t st = chain_staged_f32(N, dtype) ? 4 : el;
+  return (size_t)(N + 1) * kChainRows * 16 + (size_t)(N + 1) * 2 * dk * st +
+         (size_t)Np * dk * el + (size_t)N * 4 + (size_t)Np * kChainRows * 4;
 }
 
 template <typename T, bool DLY, bool QF>
@@ -403,11 +396,13 @@ void launch_chain_qf(bool full, long grid, size_t lds, hipStream_t stream, int N
                      const Record<T>& rec, const Record<T>& prev, int Np, const int32_t* last,
                      int32_t* dev_status) {
   if (full)
-    hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, true>), dim3((unsigned)grid), dim3(256),
+    hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, true>), dim3((unsigned)grid),
+                       dim3(kChainThreads),
                        lds, stream, N, H, dk, dv, ntiles, S0, q, k, v, beta, g, scale, out, rec,
                        prev, Np, last, dev_status);
   else
-    hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, false>), dim3((unsigned)grid), dim3(256),
+    hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, false>), dim3((unsigned)grid),
+                       dim3(kChainThreads),
                        lds, stream, N, H, dk, dv, ntiles, S0, q, k, v, beta, g, scale, out, rec,
                        prev, Np, last, dev_status);
 }
@@ -427,14 +422,12 @@ hipError_t launch_chain_verify_t(int B, int N, int H, int dk, int dv, float* S0,
   } else {
     Np = 0;
   }
-  // k, q staged as FP32 for drafts of up to 32 nodes (bf16 beyond, to bound LDS)
-  const bool qf = sizeof(T) == 4 || N <= 32;
+  const bool qf = chain_staged_f32(N, sizeof(T) == 2 ? GDN_BF16 : GDN_F32);
   const bool full = dk == kMaxDim;
   const int ntiles = (dv + kChainRows - 1) / kChainRows;
   const long grid = (long)B * H * ntiles;
-  const size_t lds = (size_t)N * dk * (qf ? 4 : sizeof(T)) * 2 + (size_t)N * kChainRows * 4 +
-                     (size_t)N * 4 * 4 + (size_t)Np * dk * sizeof(T) +
-                     (size_t)Np * kChainRows * 4 + (size_t)Np * 4;
+  const size_t lds = chain_lds_bytes(N, Np, dk, sizeof(T) == 2 ? GDN_BF16 : GDN_F32);
+  if (lds > (size_t)kMaxLds) return hipErrorInvalidValue;
   const T* qq = static_cast<const T*>(q);
   const T* kk = static_cast<const T*>(k);
   const T* vv = static_cast<const T*>(v);

@@ -14,6 +14,7 @@ namespace gdn {
 
 constexpr int kMaxNodes = 64;  // one wave64 lane / one uint64 mask bit per node
 constexpr int kMaxDim = 256;
+constexpr int kMaxLds = 160 * 1024;  // LDS bytes one workgroup may hold (gfx950)
 constexpr size_t kAlign = 256;
 
 __host__ __device__ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -196,6 +197,34 @@ __device__ inline float half32_sum_hi(float x) {
   const float lo = __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
   return x + lo;
+}
+
+// Sum over the whole wave (64 lanes) into every lane: the 16-lane row sums,
+// then v_permlane16_swap (rows 0<->1, 2<->3) and v_permlane32_swap (the two
+// halves) exchange partial sums on the VALU.
+__device__ inline float wave64_sum(float x) {
+  x = row16_sum(x);
+  unsigned a = __builtin_bit_cast(unsigned, x);
+  unsigned b;
+  asm("" : "=v"(b) : "0"(a));
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  x = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  a = __builtin_bit_cast(unsigned, x);
+  asm("" : "=v"(b) : "0"(a));
+  const auto r2 = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return __builtin_bit_cast(float, (unsigned)r2[0]) + __builtin_bit_cast(float, (unsigned)r2[1]);
+}
+
+// Sum over the whole wave delivered only to its last row (lanes 48..63): the
+// row sums, then DPP row_bcast:15 adds row 0 into row 1 and row 2 into row 3,
+// and row_bcast:31 adds lane 31 (rows 0 + 1) into rows 2 and 3.
+__device__ inline float wave64_sum_hi(float x) {
+  x = row16_sum(x);
+  x += __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
+  x += __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
+  return x;
 }
 
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].

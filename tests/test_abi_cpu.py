@@ -71,6 +71,20 @@ def test_bad_pointers_and_dtype_rejected():
     assert "last_accepted is NULL" in G.gdn_last_error()
 
 
+def test_chain_lds_limit_rejected():
+    """The chain kernel stages the draft (and, delayed, the previous record) in
+    one workgroup's LDS; fp32 inputs at the largest sizes exceed 160 KiB and
+    are refused before any launch, bf16 at the same sizes fits."""
+    L = G.lib()
+    P = ctypes.c_void_p(4096)
+    P2 = ctypes.c_void_p(1 << 30)
+    sz = (1, 64, 64, 8, 256, 256)  # B, N_prev, N, H, dk, dv
+    rc = L.gdn_chain_verify_delayed(*sz, G.GDN_F32, P, P2, P, None, P, P, P, P, P, 1.0, P, P,
+                                    None)
+    assert rc == G.GDN_ERR_UNSUPPORTED
+    assert "LDS" in G.gdn_last_error()
+
+
 def test_empty_problems_are_noops():
     L = G.lib()
     assert L.gdn_tree_verify(0, 8, 8, 256, 256, 0, None, None, None, None, None, None, None,
