@@ -66,11 +66,18 @@ __device__ inline u32x2 unstage(const u32x2& x, bf16_t*) { return x; }
 
 template <typename T, bool DLY, bool QF, bool FULL>
 __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
-    int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ beta, const float* __restrict__ g, float scale,
-    float* __restrict__ out, Record<T> rec, Record<T> prev, int Np,
-    const int32_t* __restrict__ last_acc, int32_t* __restrict__ dev_status) {
+    uint32_t shape, int H, const T* __restrict__ k, const T* __restrict__ q,
+    const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ v,
+    float* __restrict__ S0, float scale, float* __restrict__ out, Record<T> rec,
+    Record<T> prev, int Np, const int32_t* __restrict__ last_acc,
+    int32_t* __restrict__ dev_status) {
+  // The first 14 argument dwords (shape, H and the six input pointers) arrive
+  // preloaded in SGPRs; the rest is fetched from memory, so every load that
+  // needs only those goes out before the first one that needs the rest.
+  const int N = shape & 0xff;
+  const int dk = (shape >> 8) & 0x3ff;
+  const int dv = shape >> 18;
+  const int ntiles = (dv + kChainRows - 1) / kChainRows;
   static_assert(kMaxDim == 256, "one float4 of each state row per lane");
   constexpr int NT = kChainThreads;
   using R4 = typename Raw4<T>::type;
@@ -103,16 +110,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
   auto kidx = [&](int t) { return 2 * t * cpr + sc; };  // k chunk of node t; q is cpr further
   auto qidx = [&](int t) { return (2 * t + 1) * cpr + sc; };
 
-  // ---- every global load first (unconditional, clamped), then the LDS writes
-  const size_t nhl = ((size_t)b * N + clampi(s, N - 1)) * H + h;
-  const float gl = g[nhl];
-  const float bl = beta[nhl];
-  static_assert(kMaxNodes * kChainRows <= NT, "one v value per thread");
-  const int vi = clampi(tid, N * kChainRows - 1);
-  const T vb = v[(((size_t)b * N + vi / kChainRows) * H + h) * dv +
-                 clampi(r0 + vi % kChainRows, dv - 1)];
-  // the previous draft's record (delayed commit): masks, G, u' of this tile's
-  // rows and the k rows, none of which depends on last_accepted
   constexpr int BATCH = 2;
   int last_v = -1;
   uint64_t mlp = 0;
@@ -122,17 +119,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     idx = clampi(idx, Np * cpr - 1);
     return ((size_t)bh * Np + idx / cpr) * dk + 4 * (idx % cpr);
   };
-  if (DLY) {
-    last_v = last_acc[b];  // a vector load: it joins this round instead of a later scalar one
-    const int tcp = clampi(s, Np - 1);  // every wave holds node j's mask and G in lane j
-    mlp = prev.mask[(size_t)b * Np + tcp];
-    glp = prev.G[(size_t)bh * Np + tcp];
-    const int ui = clampi(tid, Np * kChainRows - 1);  // node ui / 8, row ui % 8
-    gnp = prev.G[(size_t)bh * Np + ui / kChainRows];
-    upb = prev.up[((size_t)bh * Np + ui / kChainRows) * dv + clampi(r0 + ui % kChainRows, dv - 1)];
-#pragma unroll
-    for (int x = 0; x < BATCH; ++x) kpb[x] = raw4(prev.K + prevk_off(tid + NT * x));
-  }
   // k and q rows: the first batch is straight-line code (a loop here would
   // drain every outstanding load at its header); larger drafts loop.
   auto stage_load = [&](int base, R4 (&kb)[BATCH], R4 (&qb)[BATCH]) {
@@ -170,14 +156,64 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
         kq_store(t, widen4(kb[x]), widen4(qb[x]));
     }
   };
+  // ---- every global load first (unconditional, clamped), in the order
+  // they are consumed (loads complete in issue order): the first k and q
+  // batch, g, beta and v, then the state row, whose HBM latency the staging
+  // overlaps, and last the previous record, whose pointers come with the
+  // fetched arguments.
   R4 kb0[BATCH], qb0[BATCH];
   stage_load(tid, kb0, qb0);
-  // The state row is requested last: loads complete in issue order, so the
-  // staging below waits only for the loads above, and the state (from HBM)
-  // streams in while the staging runs.
+  const size_t nhl = ((size_t)b * N + clampi(s, N - 1)) * H + h;
+  const float gl = g[nhl];
+  const float bl = beta[nhl];
+  static_assert(kMaxNodes * kChainRows <= NT, "one v value per thread");
+  const int vi = clampi(tid, N * kChainRows - 1);
+  const T vb = v[(((size_t)b * N + vi / kChainRows) * H + h) * dv +
+                 clampi(r0 + vi % kChainRows, dv - 1)];
   f32x4 Sx;
   __builtin_amdgcn_sched_barrier(0);
   Sx = load4(S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk + 4 * sc);
+  __builtin_amdgcn_sched_barrier(0);
+  // the previous draft's record (delayed commit): masks, G, u' of this tile's
+  // rows and the k rows, none of which depends on last_accepted.  Its
+  // pointers pass through an empty asm first: the compiler would otherwise
+  // copy them (and wait for their fetch) before the loads above.
+  if (DLY) {
+    uint32_t z = 0;
+    asm volatile("" : "+s"(z));
+    Np += z;
+    prev.mask += z;
+    prev.G += z;
+    prev.up += z;
+    prev.K += z;
+    last_v = last_acc[b + z];  // uniform: a scalar load, outside the in-order vector queue
+    const int tcp = clampi(s, Np - 1);  // every wave holds node j's mask and G in lane j
+    mlp = prev.mask[(size_t)b * Np + tcp];
+    glp = prev.G[(size_t)bh * Np + tcp];
+    const int ui = clampi(tid, Np * kChainRows - 1);  // node ui / 8, row ui % 8
+    gnp = prev.G[(size_t)bh * Np + ui / kChainRows];
+    upb = prev.up[((size_t)bh * Np + ui / kChainRows) * dv + clampi(r0 + ui % kChainRows, dv - 1)];
+#pragma unroll
+    for (int x = 0; x < BATCH; ++x) kpb[x] = raw4(prev.K + prevk_off(tid + NT * x));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  stage_store(tid, kb0, qb0);
+  for (int base = tid + NT * BATCH; base < N * cpr; base += NT * BATCH) {
+    R4 kb[BATCH], qb[BATCH];
+    stage_load(base, kb, qb);
+    stage_store(base, kb, qb);
+  }
+  // step scalars: alpha and beta from lane t of every wave, v of row r from
+  // thread t * 8 + r; k.q is already there with d_k = 256, else follows
+  if (tid < N * kChainRows)
+    reinterpret_cast<float*>(&ssc[tid])[3] = (r0 + tid % kChainRows < dv) ? widen1(vb) : 0.f;
+  if (tid < N) sG[tid] = gl;
+  if (s < N) {  // wave rl writes alpha, beta of node s for its own row
+    float* e = reinterpret_cast<float*>(&ssc[s * kChainRows + rl]);
+    e[0] = expf(gl);
+    e[1] = bl;
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // the previous draft's accepted path (bit i: node i), its length and G_last
@@ -198,12 +234,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
   auto rank = [&](int node) { return __popcll(pm & ((1ull << node) - 1ull)); };
   auto on_path = [&](int node) { return ((pm >> node) & 1ull) != 0ull; };
 
-  stage_store(tid, kb0, qb0);
-  for (int base = tid + NT * BATCH; base < N * cpr; base += NT * BATCH) {
-    R4 kb[BATCH], qb[BATCH];
-    stage_load(base, kb, qb);
-    stage_store(base, kb, qb);
-  }
   if (DLY) {
     // path nodes' k rows and coefficients, packed in path order; the
     // coefficient is the commit kernel's expression, e^{G_last - G_p} * u'_p[row]
@@ -227,16 +257,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     const int node = tid / kChainRows;
     if (tid < Np * kChainRows && on_path(node))
       scp[rank(node) * kChainRows + tid % kChainRows] = expf(Glast - gnp) * upb;
-  }
-  // step scalars: alpha and beta from lane t of every wave, v of row r from
-  // thread t * 8 + r; k.q is already there with d_k = 256, else follows
-  if (tid < N * kChainRows)
-    reinterpret_cast<float*>(&ssc[tid])[3] = (r0 + tid % kChainRows < dv) ? widen1(vb) : 0.f;
-  if (tid < N) sG[tid] = gl;
-  if (s < N) {  // wave rl writes alpha, beta of node s for its own row
-    float* e = reinterpret_cast<float*>(&ssc[s * kChainRows + rl]);
-    e[0] = expf(gl);
-    e[1] = bl;
   }
   __syncthreads();
 
@@ -391,20 +411,18 @@ size_t chain_lds_bytes(int N, int Np, int dk, int dtype) {
 
 template <typename T, bool DLY, bool QF>
 void launch_chain_qf(bool full, long grid, size_t lds, hipStream_t stream, int N, int H, int dk,
-                     int dv, int ntiles, float* S0, const T* q, const T* k, const T* v,
-                     const float* beta, const float* g, float scale, float* out,
-                     const Record<T>& rec, const Record<T>& prev, int Np, const int32_t* last,
-                     int32_t* dev_status) {
+                     int dv, float* S0, const T* q, const T* k, const T* v, const float* beta,
+                     const float* g, float scale, float* out, const Record<T>& rec,
+                     const Record<T>& prev, int Np, const int32_t* last, int32_t* dev_status) {
+  const uint32_t shape = (uint32_t)N | ((uint32_t)dk << 8) | ((uint32_t)dv << 18);
   if (full)
     hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, true>), dim3((unsigned)grid),
-                       dim3(kChainThreads),
-                       lds, stream, N, H, dk, dv, ntiles, S0, q, k, v, beta, g, scale, out, rec,
-                       prev, Np, last, dev_status);
+                       dim3(kChainThreads), lds, stream, shape, H, k, q, g, beta, v, S0, scale,
+                       out, rec, prev, Np, last, dev_status);
   else
     hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, false>), dim3((unsigned)grid),
-                       dim3(kChainThreads),
-                       lds, stream, N, H, dk, dv, ntiles, S0, q, k, v, beta, g, scale, out, rec,
-                       prev, Np, last, dev_status);
+                       dim3(kChainThreads), lds, stream, shape, H, k, q, g, beta, v, S0, scale,
+                       out, rec, prev, Np, last, dev_status);
 }
 
 template <typename T>
@@ -433,17 +451,17 @@ hipError_t launch_chain_verify_t(int B, int N, int H, int dk, int dv, float* S0,
   const T* vv = static_cast<const T*>(v);
   if (dly) {
     if (qf)
-      launch_chain_qf<T, true, true>(full, grid, lds, stream, N, H, dk, dv, ntiles, S0, qq, kk,
+      launch_chain_qf<T, true, true>(full, grid, lds, stream, N, H, dk, dv, S0, qq, kk,
                                      vv, beta, g, scale, out, rec, prev, Np, last, dev_status);
     else
-      launch_chain_qf<T, true, false>(full, grid, lds, stream, N, H, dk, dv, ntiles, S0, qq, kk,
+      launch_chain_qf<T, true, false>(full, grid, lds, stream, N, H, dk, dv, S0, qq, kk,
                                       vv, beta, g, scale, out, rec, prev, Np, last, dev_status);
   } else {
     if (qf)
-      launch_chain_qf<T, false, true>(full, grid, lds, stream, N, H, dk, dv, ntiles, S0, qq, kk,
+      launch_chain_qf<T, false, true>(full, grid, lds, stream, N, H, dk, dv, S0, qq, kk,
                                       vv, beta, g, scale, out, rec, prev, 0, nullptr, nullptr);
     else
-      launch_chain_qf<T, false, false>(full, grid, lds, stream, N, H, dk, dv, ntiles, S0, qq, kk,
+      launch_chain_qf<T, false, false>(full, grid, lds, stream, N, H, dk, dv, S0, qq, kk,
                                        vv, beta, g, scale, out, rec, prev, 0, nullptr, nullptr);
   }
   return hipGetLastError();
