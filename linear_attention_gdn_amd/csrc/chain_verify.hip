@@ -64,7 +64,7 @@ __device__ inline u32x2 unstage(const f32x4& x, bf16_t*) {
 }
 __device__ inline u32x2 unstage(const u32x2& x, bf16_t*) { return x; }
 
-template <typename T, bool DLY, bool QF, bool FULL>
+template <typename T, bool DLY, bool QF, bool FULL, int KB>
 __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     uint32_t shape, int H, const T* __restrict__ k, const T* __restrict__ q,
     const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ v,
@@ -82,21 +82,28 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
   constexpr int NT = kChainThreads;
   using R4 = typename Raw4<T>::type;
   using SK = typename Staged<T, QF>::type;
+  // 16-byte load units: EPC elements, E4 = EPC / 4 staged chunks of 4 columns
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int E4 = EPC / 4;
+  // k . q from registers: with bf16 rows of 256 a node's k and q rows are 64
+  // units, one wave (k in lanes 0..31, q in lanes 32..63)
+  constexpr bool KQR = FULL && sizeof(T) == 2;
   // dynamic LDS: k and q rows interleaved per node [N + 1][2][dk] (staged
   // form; node N is padding that the loop's read-ahead may touch), the step
   // scalars {alpha, beta, k.q, v[row]} [N + 1][8], G [N]; with DLY also, in
-  // accepted-path order, the previous record's k rows [Np][dk] (as loaded)
-  // and the commit coefficients e^{G_last - G_p} u'_p[row] [Np][8]
+  // accepted-path order, the previous record's k rows widened to FP32
+  // [Np][dk] and the commit coefficients e^{G_last - G_p} u'_p[row] [Np][8]
   extern __shared__ f32x4 lds4[];
   const int cpr = dk / 4;
-  f32x4* ssc = lds4;                                  // [N + 1][8]
+  const int cpu = dk / EPC;  // 16-byte units per row
+  f32x4* ssc = lds4;                                            // [N + 1][8]
   SK* skq = reinterpret_cast<SK*>(ssc + (N + 1) * kChainRows);  // [N + 1][2][cpr]
-  R4* skp = reinterpret_cast<R4*>(skq + (N + 1) * 2 * cpr);
+  f32x4* skp = reinterpret_cast<f32x4*>(skq + (N + 1) * 2 * cpr);
   float* sG = reinterpret_cast<float*>(skp + (DLY ? Np * cpr : 0));
   float* scp = sG + N;
 
   const int tid = threadIdx.x;
-  const int s = tid & 63;  // lane: columns 4s .. 4s + 3 of the wave's row
+  const int s = tid & 63;   // lane: columns 4s .. 4s + 3 of the wave's row
   const int rl = tid >> 6;  // row within the tile (0..7)
   const int tile = blockIdx.x % ntiles;
   const int bh = blockIdx.x / ntiles;
@@ -110,74 +117,99 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
   auto kidx = [&](int t) { return 2 * t * cpr + sc; };  // k chunk of node t; q is cpr further
   auto qidx = [&](int t) { return (2 * t + 1) * cpr + sc; };
 
-  constexpr int BATCH = 2;
-  int last_v = -1;
-  uint64_t mlp = 0;
-  float glp = 0.f, gnp = 0.f, upb = 0.f;
-  R4 kpb[DLY ? BATCH : 1];
-  auto prevk_off = [&](int idx) {
-    idx = clampi(idx, Np * cpr - 1);
-    return ((size_t)bh * Np + idx / cpr) * dk + 4 * (idx % cpr);
-  };
-  // k and q rows: the first batch is straight-line code (a loop here would
-  // drain every outstanding load at its header); larger drafts loop.
-  auto stage_load = [&](int base, R4 (&kb)[BATCH], R4 (&qb)[BATCH]) {
-#pragma unroll
-    for (int x = 0; x < BATCH; ++x) {
-      const int idx = clampi(base + NT * x, N * cpr - 1);
-      const size_t off = (((size_t)b * N + idx / cpr) * H + h) * dk + 4 * (idx % cpr);
-      kb[x] = raw4(k + off);
-      qb[x] = raw4(q + off);
-    }
+  // k and q rows in 16-byte units: unit u = node t's unit c of k (c < cpu) or
+  // of q (c - cpu)
+  const int kq_units = 2 * N * cpu;
+  auto kq_load = [&](int u) {
+    u = clampi(u, kq_units - 1);
+    const int t = u / (2 * cpu), l = u % (2 * cpu);
+    const T* src = l < cpu ? k : q;
+    const int c = l < cpu ? l : l - cpu;
+    return *reinterpret_cast<const u32x4*>(src + (((size_t)b * N + t) * H + h) * dk + c * EPC);
   };
   // k_t . q_t (the same for every row), stored for all 8 rows by lanes 0..7
-  auto kq_store = [&](int t, const f32x4& kx, const f32x4& qx) {
-    float a = kx.x * qx.x;
-    float a2 = kx.y * qx.y;
-    a = fmaf(kx.z, qx.z, a);
-    a2 = fmaf(kx.w, qx.w, a2);
-    a = wave64_sum(a + a2);
+  auto kq_put = [&](int t, float a) {
     if (s < kChainRows) reinterpret_cast<float*>(&ssc[t * kChainRows + s])[2] = a;
   };
   // No branch around the stores (a load used only under one is sunk into it
   // and waited for together with everything issued before): past the end a
-  // thread rewrites the clamped chunk with the bits it loaded for it, which
-  // are the owner's bits.  With d_k = 256 a wave holds whole k and q rows
-  // (chunk c of node t in lane c of wave t % 8), so it forms k_t . q_t here,
-  // from registers.
-  auto stage_store = [&](int base, const R4 (&kb)[BATCH], const R4 (&qb)[BATCH]) {
+  // thread rewrites the clamped unit with the bits it loaded for it, which
+  // are the owner's bits.
+  auto kq_store = [&](int u0, const u32x4& x) {
+    const int u = clampi(u0, kq_units - 1);
+    const int t = u / (2 * cpu), l = u % (2 * cpu);
+    const int slot = 2 * t + (l < cpu ? 0 : 1), c = l < cpu ? l : l - cpu;
+    SK* dst = skq + slot * cpr + c * E4;
+    // q staged as FP32 carries the query scale (applied once here, not per step)
+    const float qs = (QF && slot % 2 == 1) ? scale : 1.f;
+    if constexpr (sizeof(T) == 4) {
+      dst[0] = __builtin_bit_cast(f32x4, x) * qs;
+    } else if constexpr (QF) {
+      dst[0] = widen4(u32x2{x.x, x.y}) * qs;
+      dst[1] = widen4(u32x2{x.z, x.w}) * qs;
+    } else {
+      dst[0] = stage_cvt(u32x2{x.x, x.y}, (SK*)nullptr);
+      dst[1] = stage_cvt(u32x2{x.z, x.w}, (SK*)nullptr);
+    }
+    if constexpr (KQR) {
+      if (u0 - s < kq_units) {  // uniform: the wave holds node t's k (lanes < 32) and q
+        // v_permlane32_swap gives every lane both unit c's k and q (symmetric
+        // in the halves), so each half forms the whole product
+        float a = 0.f, a2 = 0.f;
+        u32x4 kk, qq;
 #pragma unroll
-    for (int x = 0; x < BATCH; ++x) {
-      const int idx = clampi(base + NT * x, N * cpr - 1);
-      const int t = idx / cpr, c = idx % cpr;
-      skq[2 * t * cpr + c] = stage_cvt(kb[x], (SK*)nullptr);
-      skq[(2 * t + 1) * cpr + c] = stage_cvt(qb[x], (SK*)nullptr);
-      if (FULL && base - s + NT * x < N * cpr)  // uniform: the wave's node exists
-        kq_store(t, widen4(kb[x]), widen4(qb[x]));
+        for (int e = 0; e < 4; ++e) {
+          const unsigned own = x[e];
+          unsigned cp;
+          asm("" : "=v"(cp) : "0"(own));
+          const auto r = __builtin_amdgcn_permlane32_swap(own, cp, false, false);
+          kk[e] = r[0];
+          qq[e] = r[1];
+        }
+        const f32x4 k0 = widen4(u32x2{kk.x, kk.y}), k1 = widen4(u32x2{kk.z, kk.w});
+        const f32x4 q0 = widen4(u32x2{qq.x, qq.y}), q1 = widen4(u32x2{qq.z, qq.w});
+        a = k0.x * q0.x;
+        a2 = k0.y * q0.y;
+        a = fmaf(k0.z, q0.z, a);
+        a2 = fmaf(k0.w, q0.w, a2);
+        a = fmaf(k1.x, q1.x, a);
+        a2 = fmaf(k1.y, q1.y, a2);
+        a = fmaf(k1.z, q1.z, a);
+        a2 = fmaf(k1.w, q1.w, a2);
+        kq_put(t, (QF ? scale : 1.f) * half32_sum(a + a2));
+      }
     }
   };
-  // ---- every global load first (unconditional, clamped), in the order
-  // they are consumed (loads complete in issue order): the first k and q
-  // batch, g, beta and v, then the state row, whose HBM latency the staging
-  // overlaps, and last the previous record, whose pointers come with the
-  // fetched arguments.
-  R4 kb0[BATCH], qb0[BATCH];
-  stage_load(tid, kb0, qb0);
-  const size_t nhl = ((size_t)b * N + clampi(s, N - 1)) * H + h;
-  const float gl = g[nhl];
-  const float bl = beta[nhl];
-  static_assert(kMaxNodes * kChainRows <= NT, "one v value per thread");
-  const int vi = clampi(tid, N * kChainRows - 1);
-  const T vb = v[(((size_t)b * N + vi / kChainRows) * H + h) * dv +
-                 clampi(r0 + vi % kChainRows, dv - 1)];
+
+  // ---- every global load first (unconditional, clamped), in the order they
+  // are consumed (loads complete in issue order): the first k and q units,
+  // then the state row, whose HBM latency the staging overlaps, then what
+  // each wave needs for its own row after the barrier (g, beta and v of every
+  // node, lane t holding node t), and last the previous record, whose
+  // pointers come with the fetched arguments.  Every wave-wide load costs the
+  // same issue time whatever its width, and a load under a branch makes the
+  // count of outstanding loads uncertain (the compiler then waits for all),
+  // so there are few loads and none conditional.
+  u32x4 kq0[KB];
+#pragma unroll
+  for (int x = 0; x < KB; ++x) kq0[x] = kq_load(tid + NT * x);
   f32x4 Sx;
   __builtin_amdgcn_sched_barrier(0);
   Sx = load4(S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk + 4 * sc);
   __builtin_amdgcn_sched_barrier(0);
-  // the previous draft's record (delayed commit): masks, G, u' of this tile's
-  // rows and the k rows, none of which depends on last_accepted.  Its
-  // pointers pass through an empty asm first: the compiler would otherwise
-  // copy them (and wait for their fetch) before the loads above.
+  const int cs = clampi(s, N - 1);
+  const size_t nhl = ((size_t)b * N + cs) * H + h;
+  const float gl = g[nhl];
+  const float bl = beta[nhl];
+  const T vb = v[nhl * dv + clampi(row, dv - 1)];
+  // the previous draft's record (delayed commit): k rows, and u' of this row
+  // and G of node s in lane s, none of which depends on last_accepted; its
+  // pointers pass through an empty asm first, since the compiler would
+  // otherwise copy them (and wait for their fetch) before the loads above
+  const int kp_units = Np * cpu;
+  u32x4 kp0 = u32x4{0u, 0u, 0u, 0u};
+  float gnp = 0.f, upb = 0.f;
+  uint64_t mlp = 0;
   if (DLY) {
     uint32_t z = 0;
     asm volatile("" : "+s"(z));
@@ -186,42 +218,30 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     prev.G += z;
     prev.up += z;
     prev.K += z;
-    last_v = last_acc[b + z];  // uniform: a scalar load, outside the in-order vector queue
-    const int tcp = clampi(s, Np - 1);  // every wave holds node j's mask and G in lane j
-    mlp = prev.mask[(size_t)b * Np + tcp];
-    glp = prev.G[(size_t)bh * Np + tcp];
-    const int ui = clampi(tid, Np * kChainRows - 1);  // node ui / 8, row ui % 8
-    gnp = prev.G[(size_t)bh * Np + ui / kChainRows];
-    upb = prev.up[((size_t)bh * Np + ui / kChainRows) * dv + clampi(r0 + ui % kChainRows, dv - 1)];
+    last_acc += z;
+    kp0 = *reinterpret_cast<const u32x4*>(prev.K + ((size_t)bh * Np) * dk +
+                                          (size_t)clampi(tid, kp_units - 1) * EPC);
+    const int ns = clampi(s, Np - 1);
+    mlp = prev.mask[(size_t)b * Np + ns];
+    gnp = prev.G[(size_t)bh * Np + ns];
+    upb = prev.up[((size_t)bh * Np + ns) * dv + clampi(row, dv - 1)];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- LDS writes read by other waves: k and q (and k . q), and the
+  // previous record's path k rows
 #pragma unroll
-    for (int x = 0; x < BATCH; ++x) kpb[x] = raw4(prev.K + prevk_off(tid + NT * x));
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  for (int x = 0; x < KB; ++x) kq_store(tid + NT * x, kq0[x]);
+  for (int base = tid + NT * KB; base < kq_units; base += NT) kq_store(base, kq_load(base));
 
-  stage_store(tid, kb0, qb0);
-  for (int base = tid + NT * BATCH; base < N * cpr; base += NT * BATCH) {
-    R4 kb[BATCH], qb[BATCH];
-    stage_load(base, kb, qb);
-    stage_store(base, kb, qb);
-  }
-  // step scalars: alpha and beta from lane t of every wave, v of row r from
-  // thread t * 8 + r; k.q is already there with d_k = 256, else follows
-  if (tid < N * kChainRows)
-    reinterpret_cast<float*>(&ssc[tid])[3] = (r0 + tid % kChainRows < dv) ? widen1(vb) : 0.f;
-  if (tid < N) sG[tid] = gl;
-  if (s < N) {  // wave rl writes alpha, beta of node s for its own row
-    float* e = reinterpret_cast<float*>(&ssc[s * kChainRows + rl]);
-    e[0] = expf(gl);
-    e[1] = bl;
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // the previous draft's accepted path (bit i: node i), its length and G_last
+  // the previous draft's accepted path (bit i: node i), its length, G_last and
+  // e^{G_last} (wave-uniform: last_accepted by a scalar load, the rest read
+  // from lane `last` of the per-node loads)
   int last = -1, npath = 0;
   uint64_t pm = 0;
-  float Glast = 0.f;
+  float Glast = 0.f, s0 = 1.f;
   if (DLY) {
-    last = __builtin_amdgcn_readfirstlane(last_v);
+    last = last_acc[b];
     const bool in_rng = last >= 0 && last < Np;
     const int lc = in_rng ? last : 0;
     const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)mlp, lc);
@@ -229,41 +249,56 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     const uint64_t valid = Np >= 64 ? ~0ull : ((1ull << Np) - 1ull);
     pm = in_rng ? ((((uint64_t)mhi << 32) | mlo) & valid) : 0ull;
     npath = __popcll(pm);
-    Glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, glp), lc));
+    Glast = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gnp), lc));
+    s0 = expf(Glast);
   }
   auto rank = [&](int node) { return __popcll(pm & ((1ull << node) - 1ull)); };
   auto on_path = [&](int node) { return ((pm >> node) & 1ull) != 0ull; };
 
   if (DLY) {
-    // path nodes' k rows and coefficients, packed in path order; the
-    // coefficient is the commit kernel's expression, e^{G_last - G_p} * u'_p[row]
-#pragma unroll
-    for (int x = 0; x < BATCH; ++x) {
-      const int idx = tid + NT * x;
-      if (idx < Np * cpr && on_path(idx / cpr))
-        skp[rank(idx / cpr) * cpr + idx % cpr] = kpb[x];
-    }
-    for (int base = tid + NT * BATCH; base < Np * cpr; base += NT * BATCH) {
-      R4 kb[BATCH];
-#pragma unroll
-      for (int x = 0; x < BATCH; ++x) kb[x] = raw4(prev.K + prevk_off(base + NT * x));
-#pragma unroll
-      for (int x = 0; x < BATCH; ++x) {
-        const int idx = base + NT * x;
-        if (idx < Np * cpr && on_path(idx / cpr))
-          skp[rank(idx / cpr) * cpr + idx % cpr] = kb[x];
+    // path nodes' k rows, widened, packed in path order
+    auto kp_store = [&](int j, const u32x4& x) {
+      const int node = j / cpu, c = j % cpu;
+      if (j < kp_units && on_path(node)) {
+        f32x4* dst = skp + rank(node) * cpr + c * E4;
+        if constexpr (sizeof(T) == 4) {
+          dst[0] = __builtin_bit_cast(f32x4, x);
+        } else {
+          dst[0] = widen4(u32x2{x.x, x.y});
+          dst[1] = widen4(u32x2{x.z, x.w});
+        }
       }
-    }
-    const int node = tid / kChainRows;
-    if (tid < Np * kChainRows && on_path(node))
-      scp[rank(node) * kChainRows + tid % kChainRows] = expf(Glast - gnp) * upb;
+    };
+    kp_store(tid, kp0);
+    for (int j = tid + NT; j < kp_units; j += NT)
+      kp_store(j, *reinterpret_cast<const u32x4*>(prev.K + ((size_t)bh * Np) * dk + (size_t)j * EPC));
   }
   __syncthreads();
 
-  if (!FULL) {
+  // ---- LDS writes read only by this wave (its row): the step scalars of node
+  // s, and with DLY the commit coefficient of path node s for this row (the
+  // commit kernel's expression, e^{G_last - G_s} u'_s[row]), in path order
+  if (s < N) {
+    float* e = reinterpret_cast<float*>(&ssc[s * kChainRows + rl]);
+    e[0] = expf(gl);
+    e[1] = bl;
+    e[3] = rok ? widen1(vb) : 0.f;
+    if (rl == 0) sG[s] = gl;
+  }
+  if (DLY && s < Np && on_path(s))
+    scp[rank(s) * kChainRows + rl] = expf(Glast - gnp) * upb;
+
+  if (!KQR) {
     // ---- k_t . q_t from LDS: wave rl takes nodes rl, rl + 8, ...
-    for (int t = rl; t < N; t += kChainRows)
-      kq_store(t, mask4(widen4(skq[kidx(t)]), cok), mask4(widen4(skq[qidx(t)]), cok));
+    for (int t = rl; t < N; t += kChainRows) {
+      const f32x4 kx = mask4(widen4(skq[kidx(t)]), cok);
+      const f32x4 qx = mask4(widen4(skq[qidx(t)]), cok);
+      float a = kx.x * qx.x;
+      float a2 = kx.y * qx.y;
+      a = fmaf(kx.z, qx.z, a);
+      a2 = fmaf(kx.w, qx.w, a2);
+      kq_put(t, wave64_sum(a + a2));
+    }
   }
 
   // the state row (first needed here)
@@ -278,7 +313,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     if (dev_status && tile == 0 && h == 0 && tid == 0)
       dev_status[b] = (last == -1 || okp) ? GDN_OK : GDN_ERR_TOPOLOGY;
     if (okp) {  // uniform
-      const float s0 = expf(Glast);
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[e] = S[e] * s0;
       auto apply = [&](int i, auto K) {
@@ -288,7 +322,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
 #pragma unroll
         for (int u = 0; u < KN; ++u) {
           c[u] = scp[(i + u) * kChainRows + rl];
-          kc[u] = widen4(skp[(i + u) * cpr + sc]);
+          kc[u] = skp[(i + u) * cpr + sc];
         }
 #pragma unroll
         for (int u = 0; u < KN; ++u) {
@@ -311,7 +345,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
             f32x4{S[0], S[1], S[2], S[3]};
     }
   }
-  if (!FULL) __syncthreads();  // k.q of every node is in LDS
+  if (!KQR) __syncthreads();  // k.q of every node is in LDS
 
   // ---- the recurrence.  Operands of step t (k_t, q_t chunks and the step
   // scalars) are read from LDS during step t - 1; two register sets
@@ -326,30 +360,36 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     o.qc = mask4(widen4(kq_lane[(2 * t + 1) * cpr]), cok);
     o.sc = sc_row[t * kChainRows];
   };
-  // lane 63 holds y_q and stores the step's output and u'
-  float* op = out + (size_t)b * N * H * dv + (size_t)h * dv + row;
-  float* up = rec.up + (size_t)bh * N * dv + row;
+  // lane 63 holds y_q and stores the step's output and u'; the row is the
+  // wave's, so the pointers are wave-uniform (scalar registers, scalar
+  // increments)
+  const int rlu = __builtin_amdgcn_readfirstlane(rl);
+  float* op = out + (size_t)b * N * H * dv + (size_t)h * dv + r0 + rlu;
+  float* up = rec.up + (size_t)bh * N * dv + r0 + rlu;
   const size_t ostep = (size_t)H * dv;
   const bool store_lane = s == 63 && rok;
   auto run = [&](const Ops& o) {
     const float al = o.sc.x, be = o.sc.y, kq = o.sc.z, vt = o.sc.w;
+    // one multiply-add chain per dot product (the loop is bound by VALU issue,
+    // not by this latency)
     float yk = S[0] * o.kc.x;
-    float yk2 = S[1] * o.kc.y;
     float yq = S[0] * o.qc.x;
-    float yq2 = S[1] * o.qc.y;
+    yk = fmaf(S[1], o.kc.y, yk);
+    yq = fmaf(S[1], o.qc.y, yq);
     yk = fmaf(S[2], o.kc.z, yk);
-    yk2 = fmaf(S[3], o.kc.w, yk2);
     yq = fmaf(S[2], o.qc.z, yq);
-    yq2 = fmaf(S[3], o.qc.w, yq2);
-    yk = wave64_sum(yk + yk2);
-    yq = wave64_sum_hi(yq + yq2);  // complete in lanes 48..63 only
+    yk = fmaf(S[3], o.kc.w, yk);
+    yq = fmaf(S[3], o.qc.w, yq);
+    yk = wave64_sum(yk);
+    yq = wave64_sum_hi(yq);  // complete in lanes 48..63 only
     const float u = be * (vt - al * yk);
     S[0] = fmaf(u, o.kc.x, al * S[0]);
     S[1] = fmaf(u, o.kc.y, al * S[1]);
     S[2] = fmaf(u, o.kc.z, al * S[2]);
     S[3] = fmaf(u, o.kc.w, al * S[3]);
     if (store_lane) {
-      *op = scale * fmaf(kq, u, al * yq);
+      const float ov = fmaf(kq, u, al * yq);  // q (and k.q) carry the scale when staged as FP32
+      *op = QF ? ov : scale * ov;
       *up = u;
     }
     op += ostep;
@@ -406,23 +446,37 @@ size_t chain_lds_bytes(int N, int Np, int dk, int dtype) {
   const size_t el = dtype == GDN_BF16 ? 2 : 4;
   const size_t st = chain_staged_f32(N, dtype) ? 4 : el;
   return (size_t)(N + 1) * kChainRows * 16 + (size_t)(N + 1) * 2 * dk * st +
-         (size_t)Np * dk * el + (size_t)N * 4 + (size_t)Np * kChainRows * 4;
+         (size_t)Np * dk * 4 + (size_t)N * 4 + (size_t)Np * kChainRows * 4;
 }
 
+template <typename T, bool DLY, bool QF, bool FULL, int KB>
+void launch_chain_kb(long grid, size_t lds, hipStream_t stream, uint32_t shape, int H, float* S0,
+                     const T* q, const T* k, const T* v, const float* beta, const float* g,
+                     float scale, float* out, const Record<T>& rec, const Record<T>& prev,
+                     int Np, const int32_t* last, int32_t* dev_status) {
+  hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, FULL, KB>), dim3((unsigned)grid),
+                     dim3(kChainThreads), lds, stream, shape, H, k, q, g, beta, v, S0, scale, out,
+                     rec, prev, Np, last, dev_status);
+}
+
+// KB: 16-byte k/q units per thread in the first round of loads (one when a
+// draft's k and q fit in one unit per thread, else four; more are looped)
 template <typename T, bool DLY, bool QF>
 void launch_chain_qf(bool full, long grid, size_t lds, hipStream_t stream, int N, int H, int dk,
                      int dv, float* S0, const T* q, const T* k, const T* v, const float* beta,
                      const float* g, float scale, float* out, const Record<T>& rec,
                      const Record<T>& prev, int Np, const int32_t* last, int32_t* dev_status) {
   const uint32_t shape = (uint32_t)N | ((uint32_t)dk << 8) | ((uint32_t)dv << 18);
-  if (full)
-    hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, true>), dim3((unsigned)grid),
-                       dim3(kChainThreads), lds, stream, shape, H, k, q, g, beta, v, S0, scale,
-                       out, rec, prev, Np, last, dev_status);
-  else
-    hipLaunchKernelGGL((chain_verify_kernel<T, DLY, QF, false>), dim3((unsigned)grid),
-                       dim3(kChainThreads), lds, stream, shape, H, k, q, g, beta, v, S0, scale,
-                       out, rec, prev, Np, last, dev_status);
+  const bool one = 2L * N * dk * (long)sizeof(T) <= 16L * kChainThreads;
+#define GDN_CHAIN_LAUNCH(FULLV, KBV)                                                           \
+  launch_chain_kb<T, DLY, QF, FULLV, KBV>(grid, lds, stream, shape, H, S0, q, k, v, beta, g,   \
+                                          scale, out, rec, prev, Np, last, dev_status)
+  if (full) {
+    if (one) GDN_CHAIN_LAUNCH(true, 1); else GDN_CHAIN_LAUNCH(true, 4);
+  } else {
+    if (one) GDN_CHAIN_LAUNCH(false, 1); else GDN_CHAIN_LAUNCH(false, 4);
+  }
+#undef GDN_CHAIN_LAUNCH
 }
 
 template <typename T>

@@ -188,17 +188,6 @@ __device__ inline float half32_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Sum over each half-wave delivered only to its upper 16 lanes (rows 1 and 3
-// of the wave): the row sums, then DPP row_bcast:15 adds the lower row's sum
-// into the upper row (GFX9 DPP; rows 0 and 2 keep their own row sum).  One
-// DPP step instead of a row exchange, for values only the upper row consumes.
-__device__ inline float half32_sum_hi(float x) {
-  x = row16_sum(x);
-  const float lo = __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
-  return x + lo;
-}
-
 // Sum over the whole wave (64 lanes) into every lane: the 16-lane row sums,
 // then v_permlane16_swap (rows 0<->1, 2<->3) and v_permlane32_swap (the two
 // halves) exchange partial sums on the VALU.
@@ -216,14 +205,14 @@ __device__ inline float wave64_sum(float x) {
 }
 
 // Sum over the whole wave delivered only to its last row (lanes 48..63): the
-// row sums, then DPP row_bcast:15 adds row 0 into row 1 and row 2 into row 3,
-// and row_bcast:31 adds lane 31 (rows 0 + 1) into rows 2 and 3.
+// row sums, then DPP row_bcast:15 (each row adds the previous row's sum; row 0
+// reads zero) and row_bcast:31 (rows 2 and 3 add lane 31, which then holds
+// rows 0 + 1).  Full row masks with bound_ctrl let each step fuse into one
+// v_add_f32_dpp; rows 0..2 end with partial sums.
 __device__ inline float wave64_sum_hi(float x) {
   x = row16_sum(x);
-  x += __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x142, 0xA, 0xF, false));
-  x += __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x143, 0xC, 0xF, false));
+  x += dpp_f32<0x142>(x);  // row_bcast:15
+  x += dpp_f32<0x143>(x);  // row_bcast:31
   return x;
 }
 
