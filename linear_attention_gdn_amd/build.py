@@ -42,16 +42,23 @@ def sources():
 
 def build(verbose: bool = False) -> str:
     """Compile all HIP sources into the shared library; returns its path."""
-    objs = []
+    from concurrent.futures import ThreadPoolExecutor
+
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
+    cmds = []
     for src in sources():
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmds.append((obj, [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]))
+    for _, cmd in cmds:
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        objs.append(obj)
+    # one hipcc per source, in parallel (each is single-threaded)
+    jobs = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(subprocess.run, cmd, check=True) for _, cmd in cmds]:
+            f.result()
+    objs = [obj for obj, _ in cmds]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -179,12 +179,13 @@ __device__ inline void path_solve_registers(int t, uint64_t m, int d, const floa
   }
 }
 
-// The same for paths of at most 8 nodes with the path's 8 x 8 block of A read
+// The same for paths of at most P nodes with the path's P x P block of A read
 // into registers first (one round of LDS reads), then substituted in
-// registers: each step is a few FMAs instead of a wait on LDS.
-__device__ inline void path_solve_registers8(int t, uint64_t m, int d, const float* A,
-                                             float* Trow) {
-  constexpr int P = 8;
+// registers: each step is a few FMAs instead of a wait on LDS.  The sums run
+// over a = b+1 .. P-1 in the order path_solve_registers uses (its terms with
+// a <= b are exact zeros), so every P gives the same bits.
+template <int P>
+__device__ inline void path_solve_block(int t, uint64_t m, int d, const float* A, float* Trow) {
   int p[P];
   uint64_t mm = m;
 #pragma unroll
@@ -660,53 +661,64 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 
   // ---- 2. Gram blocks C = [Q; K] K^T on MFMA (tiles with j <= t only)
   if constexpr (kStaged) {
-    // The kGT lower-triangle tiles (Q rows, then K rows) go round-robin to
-    // the waves with no branch, so each tile's fragment reads can issue while
-    // the previous tile's MFMAs run.  A wave past the end recomputes the last
-    // tile and stores the same bits again.
-    constexpr int kTri = NQT * (NQT + 1) / 2;
-    constexpr int kGT = 2 * kTri;
-    constexpr int kGPW = (kGT + 3) / 4;
+    // Lower-triangle tiles (t-block >= j-block) of Q K^T and K K^T.  Row
+    // blocks are paired (NQT-1-p, p) so every pair holds NQT+1 tiles, and
+    // wave w takes pair w/2 of Q (w even) or of K (w odd): it reads the A
+    // fragments of its two row blocks once and each K column block once,
+    // shared by both rows (the next column block's fragments are read while
+    // this one multiplies).  The job is a compile-time variant per wave, so
+    // no load or MFMA sits under a runtime branch.  Each tile sums over k in
+    // the same order as any other schedule, so the Gram values do not depend
+    // on it.
     constexpr int KS = kMaxDim / 32;
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    struct GTile {
-      bool isq;
-      int rtl, ct;
-    };
-    auto gtile = [&](int i) {
-      const int tau = wv + 4 * i < kGT ? wv + 4 * i : kGT - 1;
-      GTile g;
-      g.isq = tau < kTri;
-      const int tq = g.isq ? tau : tau - kTri;
-      g.rtl = 0;  // tq = rtl (rtl + 1) / 2 + ct with ct <= rtl
+    auto gram_job = [&](auto wc) {
+      constexpr int Wc = decltype(wc)::value;
+      constexpr int npairs = (NQT + 1) / 2;
+      if constexpr (Wc < 2 * npairs) {
+        constexpr bool isq = Wc % 2 == 0;
+        constexpr int ra = NQT - 1 - Wc / 2;  // the longer row block of the pair
+        constexpr int rs = Wc / 2;            // the shorter one (== ra: a single block)
+        constexpr bool two = rs < ra;
+        const bf16_t* rows = QKs + (isq ? 0 : Np) * kQKStride;
+        float* dst = isq ? QK : KK;
+        bf16x8 fa[KS], fs[two ? KS : 1], kb[2][KS];
 #pragma unroll
-      for (int r = 1; r < NQT; ++r) g.rtl += tq >= r * (r + 1) / 2;
-      g.ct = tq - g.rtl * (g.rtl + 1) / 2;
-      return g;
-    };
-    bf16x8 af[2][KS], bfr[2][KS];  // fragments of tiles i (set i & 1) and i + 1
-    auto gload = [&](int i) {
-      const GTile g = gtile(i);
-      const bf16_t* arow = QKs + (16 * (g.isq ? g.rtl : NQT + g.rtl) + l16) * kQKStride + koff;
-      const bf16_t* brow = QKs + (Np + 16 * g.ct + l16) * kQKStride + koff;
+        for (int ks = 0; ks < KS; ++ks) {  // columns past dk are zero
+          fa[ks] = lds_bf16x8(rows + (16 * ra + l16) * kQKStride + 32 * ks + koff);
+          if constexpr (two) fs[ks] = lds_bf16x8(rows + (16 * rs + l16) * kQKStride + 32 * ks + koff);
+        }
+        auto kload = [&](int ct, bf16x8 (&dstf)[KS]) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {  // columns past dk are zero
-        af[i & 1][ks] = lds_bf16x8(arow + 32 * ks);
-        bfr[i & 1][ks] = lds_bf16x8(brow + 32 * ks);
+          for (int ks = 0; ks < KS; ++ks)
+            dstf[ks] = lds_bf16x8(QKs + (Np + 16 * ct + l16) * kQKStride + 32 * ks + koff);
+        };
+        kload(0, kb[0]);
+#pragma unroll
+        for (int ct = 0; ct <= ra; ++ct) {
+          if (ct + 1 <= ra) kload(ct + 1, kb[(ct + 1) & 1]);  // in flight while ct multiplies
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(fa[ks], kb[ct & 1][ks], acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(16 * ra + 4 * lg + r) * kLd + 16 * ct + l16] = acc[r];
+          if (two && ct <= rs) {  // compile-time after unrolling
+            f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              acc2 = mfma16x16x32(fs[two ? ks : 0], kb[ct & 1][ks], acc2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              dst[(16 * rs + 4 * lg + r) * kLd + 16 * ct + l16] = acc2[r];
+          }
+        }
       }
     };
-    gload(0);
-#pragma unroll
-    for (int i = 0; i < kGPW; ++i) {
-      if (i + 1 < kGPW) gload(i + 1);  // in flight while tile i multiplies
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(af[i & 1][ks], bfr[i & 1][ks], acc);
-      const GTile g = gtile(i);
-      float* dst = g.isq ? QK : KK;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * g.rtl + 4 * lg + r) * kLd + 16 * g.ct + l16] = acc[r];
+    switch (__builtin_amdgcn_readfirstlane(wave)) {
+      case 0: gram_job(std::integral_constant<int, 0>{}); break;
+      case 1: gram_job(std::integral_constant<int, 1>{}); break;
+      case 2: gram_job(std::integral_constant<int, 2>{}); break;
+      default: gram_job(std::integral_constant<int, 3>{}); break;
     }
   } else {
   for (int tileid = wave; tileid < nrt * NQT; tileid += 4) {
@@ -782,8 +794,12 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int t = tid;
     const uint64_t m = smask[t];
     const int d = __popcll(m);
-    if (d <= 8)
-      path_solve_registers8(t, m, d, KK, Tl + t * kLd);
+    // one variant per wave, chosen by its deepest path, so the lanes of a
+    // wave never run two solves one after the other
+    if (__ballot(d > 8) == 0ull)
+      path_solve_block<8>(t, m, d, KK, Tl + t * kLd);
+    else if (__ballot(d > 12) == 0ull)
+      path_solve_block<12>(t, m, d, KK, Tl + t * kLd);
     else if (d <= kPathMax)
       path_solve_registers(t, m, d, KK, Tl + t * kLd);
     else
