@@ -151,8 +151,8 @@ struct TreeLds {
 // solves x^T (I + A)|_path = e_t^T and T[t][p_b] = x_b.  Terms with a <= b or
 // a >= d vanish on their own (x_a not yet set, or the padding), so the sum is
 // unconditional and its LDS reads issue together.
-__device__ inline void path_solve_registers(int t, uint64_t m, int d, const float* A,
-                                            float* Trow) {
+template <typename Put>
+__device__ inline void path_solve_registers(int t, uint64_t m, int d, const float* A, Put put) {
   int p[kPathMax];
   float x[kPathMax];
   uint64_t mm = m;
@@ -162,7 +162,7 @@ __device__ inline void path_solve_registers(int t, uint64_t m, int d, const floa
     mm &= mm - 1ull;
     x[a] = (a == d - 1) ? 1.f : 0.f;
   }
-  Trow[t] = 1.f;
+  put(t, 1.f);
   for (int b = d - 2; b >= 0; --b) {
     int pb = t;
 #pragma unroll
@@ -172,7 +172,7 @@ __device__ inline void path_solve_registers(int t, uint64_t m, int d, const floa
 #pragma unroll
     for (int a = 0; a < kPathMax; ++a) acc = fmaf(x[a], A[p[a] * kLd + pb], acc);
     const float xb = -acc;
-    Trow[pb] = xb;
+    put(pb, xb);
 #pragma unroll
     for (int a = 0; a < kPathMax; ++a)
       if (a == b) x[a] = xb;
@@ -184,8 +184,8 @@ __device__ inline void path_solve_registers(int t, uint64_t m, int d, const floa
 // registers: each step is a few FMAs instead of a wait on LDS.  The sums run
 // over a = b+1 .. P-1 in the order path_solve_registers uses (its terms with
 // a <= b are exact zeros), so every P gives the same bits.
-template <int P>
-__device__ inline void path_solve_block(int t, uint64_t m, int d, const float* A, float* Trow) {
+template <int P, typename Put>
+__device__ inline void path_solve_block(int t, uint64_t m, int d, const float* A, Put put) {
   int p[P];
   uint64_t mm = m;
 #pragma unroll
@@ -209,10 +209,10 @@ __device__ inline void path_solve_block(int t, uint64_t m, int d, const float* A
     for (int a = b + 1; a < P; ++a) acc = fmaf(x[a], Ab[a][b], acc);
     if (b < d - 1) x[b] = -acc;
   }
-  Trow[t] = 1.f;
+  put(t, 1.f);
 #pragma unroll
   for (int b = 0; b < P; ++b)
-    if (b < d - 1) Trow[p[b]] = x[b];
+    if (b < d - 1) put(p[b], x[b]);
 }
 
 // The same for any depth, with the row in LDS (slower).
@@ -267,6 +267,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   __shared__ uint64_t smask[kMaxNodes];
   __shared__ float sG[kMaxNodes], seG[kMaxNodes], sbeta[kMaxNodes];
   __shared__ int sbad;
+  __shared__ int sdeep;  // some root path is deeper than kPathMax: T is solved in FP32
   __shared__ __attribute__((aligned(16))) DelayLds<DLY, BV> dly;
   __shared__ int sdly_n;
   __shared__ float sdly_s0;
@@ -390,7 +391,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
       *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
     }
   }
-  for (int idx = tid; idx < Np * kLd; idx += 256) Tl[idx] = 0.f;
+  // T starts as zeros in both of its layouts (FP32 rows, or bf16 hi + lo rows)
+  for (int idx = tid; idx < L::kMat / 16; idx += 256)
+    reinterpret_cast<f32x4*>(Tl)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- 1. parents -> validation, ancestor-or-self masks and G (pointer jumping)
   if (wave == 0) {
@@ -794,16 +797,28 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int t = tid;
     const uint64_t m = smask[t];
     const int d = __popcll(m);
-    // one variant per wave, chosen by its deepest path, so the lanes of a
-    // wave never run two solves one after the other
-    if (__ballot(d > 8) == 0ull)
-      path_solve_block<8>(t, m, d, KK, Tl + t * kLd);
-    else if (__ballot(d > 12) == 0ull)
-      path_solve_block<12>(t, m, d, KK, Tl + t * kLd);
-    else if (d <= kPathMax)
-      path_solve_registers(t, m, d, KK, Tl + t * kLd);
-    else
-      path_solve_lds(t, m, KK, Tl + t * kLd);
+    // Rows of T go straight into the split bf16 layout the epilogue's
+    // products read (T[t][j] = hi + lo); only drafts with a path deeper than
+    // kPathMax solve in FP32 rows (the LDS solve reads its row back) and are
+    // split in the epilogue.  One variant per wave (all nodes are in wave
+    // 0), chosen by its deepest path, so the lanes never run two solves one
+    // after the other.
+    const bool deep = __ballot(d > kPathMax) != 0ull;
+    if (t == 0) sdeep = deep;
+    auto put_split = [&](int j, float x) { store_split1(Ts + t * kLdH + j, kSplitLo, x); };
+    auto put_f32 = [&](int j, float x) { Tl[t * kLd + j] = x; };
+    if (deep) {
+      if (d <= kPathMax)
+        path_solve_registers(t, m, d, KK, put_f32);
+      else
+        path_solve_lds(t, m, KK, Tl + t * kLd);
+    } else if (__ballot(d > 8) == 0ull) {
+      path_solve_block<8>(t, m, d, KK, put_split);
+    } else if (__ballot(d > 12) == 0ull) {
+      path_solve_block<12>(t, m, d, KK, put_split);
+    } else {
+      path_solve_registers(t, m, d, KK, put_split);
+    }
   }
 
   if (DLY) dly_commit(true, true);
@@ -874,12 +889,16 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   __syncthreads();  // Q/K reads and the solves are done: region A becomes R^T, U'^T
 
   // ---- 5. epilogue
-  // T rows (FP32) -> registers, split in place after the barrier
+  // T is already split, except after an FP32 solve (deep paths): then its
+  // rows go to registers and are split in place after a barrier
+  const bool deep = sdeep != 0;  // uniform
   float trow[EPT];
+  if (deep) {
 #pragma unroll
-  for (int x = 0; x < EPT; ++x) {
-    const int idx = tid + 256 * x;
-    trow[x] = Tl[(idx / NK) * kLd + idx % NK];
+    for (int x = 0; x < EPT; ++x) {
+      const int idx = tid + 256 * x;
+      trow[x] = Tl[(idx / NK) * kLd + idx % NK];
+    }
   }
   // R = diag(beta) (V - diag(e^G) K S0^T) from the K-row accumulators
   f32x4 rv[MAXNB];
@@ -903,11 +922,13 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         }
     }
   }
-  __syncthreads();
+  if (deep) {
+    __syncthreads();  // every FP32 row is read before the split rows overwrite it
 #pragma unroll
-  for (int x = 0; x < EPT; ++x) {
-    const int idx = tid + 256 * x;
-    store_split1(Ts + (idx / NK) * kLdH + idx % NK, kSplitLo, trow[x]);
+    for (int x = 0; x < EPT; ++x) {
+      const int idx = tid + 256 * x;
+      store_split1(Ts + (idx / NK) * kLdH + idx % NK, kSplitLo, trow[x]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < MAXNB; ++j) {

@@ -124,6 +124,9 @@ SHAPES = [
     (2, 1, 2, 8, 4, "bf16", "chain"),
     (1, 33, 1, 128, 100, "bf16", "window"),
     (4, 64, 1, 256, 256, "bf16", "branching"),
+    # root paths of 9-12 and 13-16 nodes: the two register-block solves
+    (2, 11, 2, 32, 48, "f32", "chain"),
+    (1, 14, 2, 64, 64, "bf16", "chain"),
 ]
 
 
