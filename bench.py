@@ -21,7 +21,9 @@ Prints one JSON line:
                   algorithmic bytes per launch / duration against 8 TB/s; for
                   the tree kernel its FP32-equivalent contraction flops per
                   launch / duration against the 157.3 TFLOP/s FP32 peak (with
-                  the bf16 rate it issues and its HBM rate alongside);
+                  the bf16 rate of its two-pass S0 contraction, its HBM rate,
+                  and all bf16 MFMA work it issues as counted by rocprofv3,
+                  alongside);
                   `traffic` from the rocprofv3 counter summaries in profiles/
   cpu_baseline    the CPU oracle (per-path fp64 replay + commit replay) on a
                   bounded number of steps of the same workload
@@ -45,6 +47,7 @@ from linear_attention_gdn_amd import workloads as W  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+CLOCK_HZ = 2.4e9  # peak engine clock, for MFMA-busy fractions
 CSRC = os.path.join(ROOT, "linear_attention_gdn_amd", "csrc")
 KERNEL_SOURCES = {"gdn_chain_verify": "chain_verify.hip", "gdn_tree_verify": "tree_verify.hip",
                   "gdn_commit_path": "commit.hip", "gdn_linear": "layer.hip",
@@ -63,10 +66,10 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:12]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current source of that kernel (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+def _counter_summary(kind: str, kernel: str, workload: str):
+    """Fields of a committed rocprofv3 counter summary (profiles/<kind>_<kernel>_<workload>.txt)
+    if it was taken on the current source of that kernel, else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -77,10 +80,36 @@ def measured_traffic(kernel: str, workload: str):
                 fields[key.strip()] = val.strip()
     if fields.get("source_digest") != source_digest(kernel):
         return None
+    return fields
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current source of that kernel (else None)."""
+    fields = _counter_summary("traffic", kernel, workload)
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields["hbm_bytes_per_launch"]) if fields else None
     except (KeyError, ValueError):
         return None
+
+
+def measured_mfma(kernel: str, workload: str, avg_us: float):
+    """Issued bf16 MFMA work per launch from the committed counter summary
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP; MFMA-busy cycles per SIMD), as
+    rates over this run's measured launch time; None if absent or stale."""
+    fields = _counter_summary("mfma", kernel, workload)
+    if not fields:
+        return None
+    try:
+        f = float(fields["bf16_mfma_flop_per_launch"])
+        busy = float(fields["mfma_busy_cycles_per_simd"])
+    except (KeyError, ValueError):
+        return None
+    t_s = avg_us * 1e-6
+    return {"bf16_flop_per_launch": f, "issued_tflops": round(f / t_s / 1e12, 2),
+            "issued_frac": round(f / t_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "busy_cycles_per_simd": busy,
+            "busy_frac_at_2p4ghz": round(busy / (t_s * CLOCK_HZ), 4)}
 
 
 def calibrate_copy(mib: int, iters: int) -> None:
@@ -389,16 +418,17 @@ def main():
         flops = 4.0 * B * H * N * dk * dv          # algorithmic (FP32-equivalent) per launch
         t_s = kd["avg_us"] * 1e-6
         tflops = flops / t_s / 1e12
-        issued = 2.0 * flops                        # hi + lo passes of the dominant product
+        issued = 2.0 * flops                        # hi + lo passes of the S0 contraction
         roofline = {"bound": "mfma", "achieved": round(tflops, 2),
                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4),
                     "traffic": measured_traffic(kd["name"], d.name), "kernel": kd["name"],
                     "algorithmic_flops": flops,
-                    "issued_bf16_tflops": round(issued / t_s / 1e12, 2),
-                    "issued_bf16_frac": round(issued / t_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "contraction_bf16_tflops": round(issued / t_s / 1e12, 2),
+                    "contraction_bf16_frac": round(issued / t_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                     "hbm_gbs": round(kd["gbs"], 2), "hbm_frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
-                    "algorithmic_bytes": kd["bytes"]}
+                    "algorithmic_bytes": kd["bytes"],
+                    "mfma_counters": measured_mfma(kd["name"], d.name, kd["avg_us"])}
 
     cpu = None
     if not args.no_cpu_baseline:
