@@ -336,8 +336,20 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   T vreg[MAXNB][4];
   // GATE: output gate values for the rows this lane stores (node
   // 16 nb + 4 lg + r of its node blocks nb = rb + WR j, column srow), requested
-  // with the state tile.
+  // once the contraction has consumed the state registers (load_gate below):
+  // in the first round of loads they would exceed the register budget and
+  // make the compiler wait for the whole state tile before issuing them.
   float gvr[GATE ? MAXNB : 1][4];
+  auto load_gate = [&]() {
+    if constexpr (GATE) {
+      const float* gp = ga.gate + (size_t)b * N * ga.ldg + h * dv + clampi(srow, dv - 1);
+#pragma unroll
+      for (int j = 0; j < MAXNB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          gvr[j][r] = gp[(size_t)clampi(16 * (rb + WR * j) + 4 * lg + r, N - 1) * ga.ldg];
+    }
+  };
   auto load_state = [&]() {
     const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
 #pragma unroll
@@ -354,14 +366,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         const int t = clampi(16 * nb + 4 * lg + r, N - 1);
         vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
       }
-    if constexpr (GATE) {
-      const float* gp = ga.gate + (size_t)b * N * ga.ldg + h * dv + clampi(srow, dv - 1);
-#pragma unroll
-      for (int j = 0; j < MAXNB; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          gvr[j][r] = gp[(size_t)clampi(16 * (rb + WR * j) + 4 * lg + r, N - 1) * ga.ldg];
-    }
   };
 
   // delayed commit: the previous draft's last accepted node, and node j's
@@ -656,7 +660,11 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int c = tid % BV;
     for (int t = tid / BV; t < N; t += 256 / BV)
       if (r0 + c < dv) {
-        out[(((size_t)b * N + t) * H + h) * dv + r0 + c] = 0.f;
+        const size_t o = (((size_t)b * N + t) * H + h) * dv + r0 + c;
+        if constexpr (GATE)  // the gated form has no O: Y = bf16(0 * SiLU(gate)), as gated zeros
+          ga.Y[o] = to_bf16(0.f * silu(ga.gate[((size_t)b * N + t) * ga.ldg + h * dv + r0 + c]));
+        else
+          out[o] = 0.f;
         rec.up[((size_t)bh * N + t) * dv + r0 + c] = 0.f;
       }
     return;
@@ -886,6 +894,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
       }
     }
   }
+  load_gate();      // consumed by the output step, after R and U'
   __syncthreads();  // Q/K reads and the solves are done: region A becomes R^T, U'^T
 
   // ---- 5. epilogue

@@ -172,20 +172,27 @@ def test_delayed_tree_commit_lands_when_new_topology_is_rejected():
     assert (out[1] == 0).all() and torch.isfinite(out[0]).all()
 
 
-@pytest.mark.parametrize("B,Np,N,H,dk,dv,topo,delayed", [
-    (1, 32, 32, 8, 256, 256, "window", True),     # the 24-layer step's shape
-    (1, 32, 32, 8, 256, 256, "window", False),
-    (2, 9, 17, 3, 64, 40, "random", True),        # ragged: N and dv not multiples of 16
-    (8, 64, 64, 8, 256, 256, "branching", True),  # wide tiles
+@pytest.mark.parametrize("B,Np,N,H,dk,dv,topo,delayed,reject", [
+    (1, 32, 32, 8, 256, 256, "window", True, False),     # the 24-layer step's shape
+    (1, 32, 32, 8, 256, 256, "window", False, False),
+    (2, 9, 17, 3, 64, 40, "random", True, False),        # ragged: N and dv not multiples of 16
+    (8, 64, 64, 8, 256, 256, "branching", True, False),  # wide tiles
+    (2, 9, 17, 3, 64, 40, "random", True, True),         # sequence 1's new parents rejected
+    (2, 12, 12, 2, 32, 16, "random", False, True),
 ])
-def test_layer_verify_is_verify_then_gate(B, Np, N, H, dk, dv, topo, delayed):
+def test_layer_verify_is_verify_then_gate(B, Np, N, H, dk, dv, topo, delayed, reject):
     """gdn_layer_verify == the verify call followed by gdn_gate_merge, bitwise
-    (outputs through the gate, state, record, status words)."""
+    (outputs through the gate, state, record, status words), also when a
+    sequence's topology is rejected (its outputs are gated zeros)."""
     seed = 7000 + B * 100 + N
     prev = W.make_draft(B, Np, H, dk, dv, topology=topo, accept="leaf_geometric",
                         dtype="bf16", seed=seed)
     new = W.make_draft(B, N, H, dk, dv, topology=topo, accept="none", dtype="bf16",
                        seed=seed + 1)
+    if reject:
+        bad = new.parents.copy()
+        bad[B - 1, N - 2] = N - 1  # a parent after its child
+        new = new.replace(parents=bad)
     _, rec_prev, _, st, tp = run_tree(prev)
     assert (st.cpu().numpy() == G.GDN_OK).all()
     tn = dev_tensors(new)
@@ -227,5 +234,8 @@ def test_layer_verify_is_verify_then_gate(B, Np, N, H, dk, dv, topo, delayed):
     assert torch.equal(S_a, S_b)
     assert torch.equal(rec_a.buf, rec_b.buf)
     assert torch.equal(st_a, st_b)
+    if reject:
+        assert int(st_b[B - 1]) == G.GDN_ERR_TOPOLOGY
+        assert torch.all(Y_b.view(B, N, H * dv)[B - 1].float() == 0)
     if delayed:
         assert torch.equal(cs_a, cs_b)
