@@ -386,6 +386,36 @@ def main():
                  "state_copy_us": round(t_copy * 1e3, 3),
                  "state_copy_bytes": 2 * state_bytes,
                  "state_copy_gbs": round(2 * state_bytes / (t_copy * 1e-3) / 1e9, 1)}
+    # The same step on one resident state (hot: back-to-back in a graph, the
+    # state served from the caches), and single steps called eagerly from
+    # Python and waited for (host call to completion, rotating states), median.
+    variants = None
+    if not args.no_graph:
+        def step_on(j, i):
+            if delayed:
+                if chain:
+                    G.gdn_chain_verify_delayed(states[j], recs[j][(i + 1) % 2], lasts[i], q, k,
+                                               v, beta, g, out, recs[j][i % 2])
+                else:
+                    G.gdn_tree_verify_delayed(states[j], recs[j][(i + 1) % 2], lasts[i], parents,
+                                              q, k, v, beta, g, out, recs[j][i % 2])
+            else:
+                if chain:
+                    G.gdn_chain_verify(states[j], q, k, v, beta, g, out, rec)
+                else:
+                    G.gdn_tree_verify(states[j], parents, q, k, v, beta, g, out, rec)
+                G.gdn_commit_path(states[j], rec, lasts[i])
+
+        t_hot = graph_time(lambda i: step_on(0, i))
+        ts = []
+        for j in range(60):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step_on(j % R, args.warmup + j)
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        variants = {"hot_state_graph_us_per_step": round(t_hot * 1e3, 3),
+                    "eager_single_step_us_median": round(float(np.median(ts[10:])) * 1e6, 2)}
     plens = path_lengths(d, lasts_np[args.warmup:args.warmup + nper])
     b_ver = bytes_verify(d, not chain)
     b_com = np.mean([bytes_commit(d, p) for p in plens])
@@ -455,6 +485,7 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roofline,
         "latency_floor": floor,
+        "timing_variants": variants,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
