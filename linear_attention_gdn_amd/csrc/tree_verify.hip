@@ -27,13 +27,15 @@
 //   1. validates the parents and builds ancestor bitmasks and the
 //      path-cumulative G by pointer jumping (one lane per node, stopping when
 //      every path is complete);
-//   2. forms the Gram blocks Q K^T and K K^T on bf16 MFMA (lower triangle,
-//      tiles round-robin over the waves, the next tile's fragments read while
-//      the current tile multiplies);
+//   2. forms the Gram blocks Q K^T and K K^T on bf16 MFMA (lower triangle;
+//      each wave owns a pair of row blocks of Q or of K, reads their
+//      fragments once and each K column block once for both rows, the next
+//      column block's fragments read while the current one multiplies);
 //   3. masks and scales them into A and Attn (all threads, only the N x N
 //      block the products read, every operand read before any is used), then
 //      solves row t of T on t's root path (rows of T vanish off the path), one
-//      lane per node with the path's block of A in registers;
+//      lane per node with the path's block of A in registers, writing T
+//      already split into bf16 hi + lo for step 5;
 //   4. runs the dense contraction Y = [Q; K] S0_tile^T on bf16 MFMA with the
 //      FP32 state split into bf16 hi + lo (bf16 q, k make every product
 //      exact; only the 2^-16 split residue is lost);
@@ -767,7 +769,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 
   // ---- 3. A (FP32, in place of K K^T) and Attn (split bf16, in place of
   // Q K^T) over all N x N entries, exact zeros off the masks; then the rows
-  // of T on root paths (one lane per node).
+  // of T on root paths (one lane per node, written split into bf16 hi + lo).
   // Every operand is read unconditionally first (all in bounds: t < Np,
   // j < NK), so the reads issue together instead of one masked round trip
   // per entry.
