@@ -55,3 +55,21 @@ def test_counter_traffic_needs_the_current_source(tmp_path, monkeypatch):
     assert bench.measured_traffic(kern, wl) is None  # taken on other code
     f.write_text(f"hbm_bytes_per_launch: 12345\nsource_digest: {bench.source_digest(kern)}\n")
     assert bench.measured_traffic(kern, wl) == 12345.0
+
+
+def test_mfma_counters_need_the_current_source(tmp_path, monkeypatch):
+    kern, wl = "gdn_tree_verify", "tree64-b8-h8-d256"
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    f = prof / f"mfma_{kern}_{wl}.txt"
+    assert bench.measured_mfma(kern, wl, 10.0) is None  # no summary
+    body = "bf16_mfma_flop_per_launch: 1000000000\nmfma_busy_cycles_per_simd: 1200\n"
+    f.write_text(body + "source_digest: 000000000000\n")
+    assert bench.measured_mfma(kern, wl, 10.0) is None  # taken on other code
+    f.write_text(body + f"source_digest: {bench.source_digest(kern)}\n")
+    m = bench.measured_mfma(kern, wl, 10.0)
+    # 1 GFLOP in 10 us = 100 TFLOP/s = 4% of 2.5 PFLOP/s; 1200 of the
+    # 24000 cycles of 10 us at 2.4 GHz = 5% busy
+    assert m["issued_tflops"] == 100.0 and m["issued_frac"] == 0.04
+    assert m["busy_cycles_per_simd"] == 1200.0 and m["busy_frac_at_2p4ghz"] == 0.05
