@@ -239,3 +239,31 @@ def test_layer_verify_is_verify_then_gate(B, Np, N, H, dk, dv, topo, delayed, re
         assert torch.all(Y_b.view(B, N, H * dv)[B - 1].float() == 0)
     if delayed:
         assert torch.equal(cs_a, cs_b)
+
+
+@pytest.mark.parametrize("B,N,H,topo", [(1, 32, 8, "window"), (8, 64, 8, "branching")])
+def test_delayed_tree_verify_repeats_bitwise(B, N, H, topo):
+    """The delayed tree verify gives the same bits on every run (state, outputs,
+    record), with nothing to commit and with a path: each workgroup's result
+    depends only on its inputs, never on the timing of other waves."""
+    dk = dv = 256
+    prev = W.make_draft(B, N, H, dk, dv, topology=topo, accept="leaf_geometric", dtype="bf16",
+                        seed=31)
+    new = W.make_draft(B, N, H, dk, dv, topology=topo, accept="none", dtype="bf16", seed=32)
+    _, rec_prev, _, _, tp = run_tree(prev)
+    tn = dev_tensors(new)
+    for last_np in (np.full(B, -1, np.int32), prev.last_accepted.astype(np.int32)):
+        last = torch.from_numpy(last_np).cuda()
+        runs = []
+        for _ in range(5):
+            S = tp["S0"].clone()
+            out = torch.empty((B, N, H, dv), device="cuda")
+            rec = G.FactorRecord.empty(B, N, H, dk, dv, code_of(new))
+            rec.buf.zero_()
+            G.gdn_tree_verify_delayed(S, rec_prev, last, tn["parents"], tn["q"], tn["k"], tn["v"],
+                                      tn["beta"], tn["g"], out, rec)
+            runs.append((S, out, rec.buf))
+        torch.cuda.synchronize()
+        for r in runs[1:]:
+            for a, b_ in zip(runs[0], r):
+                assert torch.equal(a, b_), last_np
