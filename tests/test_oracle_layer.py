@@ -135,3 +135,67 @@ def test_round_bf16_matches_float32_bit_rounding():
     x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
     ref = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x)).astype(np.float64)
     np.testing.assert_array_equal(LY.round_bf16(x.astype(np.float64)), ref)
+
+
+# ---------------------------------------------------------------------------
+# the activation: SiLU(x) = x sigmoid(x), pinned by closed forms
+# ---------------------------------------------------------------------------
+
+LN3 = np.log(3.0)  # sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 exactly
+
+
+def test_silu_closed_forms():
+    """SiLU is odd up to the identity (silu(x) - silu(-x) = x), vanishes at 0,
+    tends to x for large x and to 0 for very negative x, and is known in
+    closed form at +-ln 3.  A logistic sigmoid in its place fails every line."""
+    s = LY.silu
+    assert s(0.0) == 0.0
+    x = np.linspace(-6.0, 6.0, 49)
+    np.testing.assert_allclose(s(x) - s(-x), x, rtol=0, atol=1e-14)
+    assert abs(s(30.0) - 30.0) < 1e-10 and abs(s(40.0) - 40.0) < 1e-14
+    assert abs(s(-40.0)) < 1e-15
+    np.testing.assert_allclose(s(np.array([LN3, -LN3])), [0.75 * LN3, -0.25 * LN3],
+                               rtol=1e-15)
+    # minimum of x sigmoid(x): at x* with 1 + x*(1 - sigmoid(x*)) = 0, x* = -1.27846...
+    xs = np.linspace(-1.4, -1.15, 25001)
+    assert abs(xs[np.argmin(s(xs))] + 1.2784645) < 2e-5
+
+
+def test_gate_merge_closed_forms():
+    """o * SiLU(gate): zero gate closes the output, a large gate passes it,
+    and gate = +-ln 3 scales it by 3/4 ln 3 and -1/4 ln 3."""
+    rng = np.random.default_rng(11)
+    o = rng.standard_normal((3, 2, 4))
+    flat = o.reshape(3, 8)
+    np.testing.assert_array_equal(LY.gate_merge(o, np.zeros((3, 8))), np.zeros((3, 8)))
+    np.testing.assert_allclose(LY.gate_merge(o, np.full((3, 8), 40.0)), 40.0 * flat, rtol=1e-15)
+    gate = np.where(np.arange(8) % 2 == 0, LN3, -LN3)[None, :].repeat(3, 0)
+    want = flat * np.where(np.arange(8) % 2 == 0, 0.75 * LN3, -0.25 * LN3)
+    np.testing.assert_allclose(LY.gate_merge(o, gate), want, rtol=1e-14)
+
+
+def test_prep_applies_silu_after_the_path_convolution():
+    """A 2-node chain with all-ones taps: node 1's convolution input is
+    node 1, node 0, then the two most recent history rows.  The channel sums
+    are chosen to be +-ln 3 (and 0), so the activation's output is known in
+    closed form: v = SiLU(c) and q, k are SiLU(c) normalised per head."""
+    H, d = 1, 2
+    Cc = 3 * H * d
+    w = np.ones((Cc, LY.CONV_TAPS))
+    # per channel: (node 0, node 1, hist row 0, hist row 1); node 1's sum =
+    # x1 + x0 + h0 + h1, node 0's sum = x0 + h0 + h1 + h2
+    P = np.zeros((2, 4 * H * d + 2 * H))
+    hist = np.zeros((3, Cc))
+    sums = np.array([LN3, -LN3, -LN3, LN3, LN3, 0.0])  # q^ (2), k^ (2), v^ (2) at node 1
+    P[1, :Cc] = sums / 2
+    P[0, :Cc] = sums / 4
+    hist[0] = sums / 8
+    hist[1] = sums / 8
+    q, k, v, beta, g, _ = LY.layer_prep(P, W.chain_parents(2), w, hist, H, d, d)
+    np.testing.assert_allclose(v[1, 0], [0.75 * LN3, 0.0], rtol=1e-15, atol=1e-16)
+    # SiLU(+-ln 3) = (3/4, -1/4) ln 3, so the normalised rows are (3, -1)/sqrt(10)
+    np.testing.assert_allclose(q[1, 0], np.array([3.0, -1.0]) / np.sqrt(10.0), rtol=1e-14)
+    np.testing.assert_allclose(k[1, 0], np.array([-1.0, 3.0]) / np.sqrt(10.0), rtol=1e-14)
+    # node 0: history rows 0..2 and node 0 itself: sums/4 + sums/8 + sums/8 + 0
+    np.testing.assert_allclose(v[0, 0], [0.5 * LN3 / (1 + 3.0 ** -0.5), 0.0], rtol=1e-14,
+                               atol=1e-16)
