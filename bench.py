@@ -13,20 +13,29 @@ over enough distinct layer states (default 1 GiB in total, several times the
 256 MB Infinity Cache) that every state read comes from HBM.  The
 decode24-b1-h8-d256 workload runs the 24-layer decode loop instead.
 
+The default workload is tree64-b8-h8-d256 (batch 8, 64-node trees: the
+largest single-GPU per-layer configuration); the 8-node chain
+(chain8-b1-h8-d256) is measured in the same run for the HBM half of the
+metric.
+
 Prints one JSON line:
-  value           verified draft nodes per second (B * N per step), measured on
-                  a HIP-graph replay of K steps (no host launch overhead)
-  roofline        dominant kernel, timed alone (events around a HIP-graph
-                  replay of back-to-back launches): for the chain kernel its
-                  algorithmic bytes per launch / duration against 8 TB/s; for
+  value           verified draft nodes per second (B * N per step); K steps
+                  replayed as one HIP graph, timed with HIP events on the
+                  stream the kernels run on (no host launch overhead)
+  ms_per_step     that time per step; with the delayed commit a step is one
+                  launch, so it is also the kernel's average launch duration
+  roofline        of the step's kernel, every fraction from ms_per_step: for
                   the tree kernel its FP32-equivalent contraction flops per
-                  launch / duration against the 157.3 TFLOP/s FP32 peak (with
-                  the bf16 rate of its two-pass S0 contraction, its HBM rate,
-                  and all bf16 MFMA work it issues as counted by rocprofv3,
-                  alongside);
-                  `traffic` from the rocprofv3 counter summaries in profiles/
-  cpu_baseline    the CPU oracle (per-path fp64 replay + commit replay) on a
-                  bounded number of steps of the same workload
+                  launch against the 157.3 TFLOP/s FP32 peak (frac), the bf16
+                  MFMA work it actually issues and the matrix units' busy
+                  fraction from the committed rocprofv3 counters
+                  (issued_mfma), and its algorithmic HBM bytes against 8 TB/s
+                  (hbm); for the chain kernel its algorithmic bytes against
+                  8 TB/s; `traffic` = HBM bytes per launch from the
+                  rocprofv3 counter summaries in profiles/
+  chain8          the 8-node chain's step with its HBM roofline
+  cpu_baseline    the CPU oracle (per-path fp64 replay + commit replay):
+                  median of 5 trials on all threads and on one thread
 """
 
 from __future__ import annotations
@@ -48,6 +57,11 @@ HBM_PEAK_GBS = 8000.0
 FP32_MFMA_PEAK_TFLOPS = 157.3
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 CLOCK_HZ = 2.4e9  # peak engine clock, for MFMA-busy fractions
+# the configuration the bench line is quoted on: the largest single-GPU
+# per-layer workload (batch-8 64-node trees), with the 8-node chain's HBM
+# figures alongside
+DEFAULT_WORKLOAD = "tree64-b8-h8-d256"
+CHAIN_WORKLOAD = "chain8-b1-h8-d256"
 CSRC = os.path.join(ROOT, "linear_attention_gdn_amd", "csrc")
 KERNEL_SOURCES = {"gdn_chain_verify": "chain_verify.hip", "gdn_tree_verify": "tree_verify.hip",
                   "gdn_commit_path": "commit.hip", "gdn_linear": "layer.hip",
@@ -182,67 +196,63 @@ def path_lengths(d: W.Draft, lasts: np.ndarray) -> np.ndarray:
     return np.array([[0 if l < 0 else depth[b, l] for b, l in enumerate(row)] for row in lasts])
 
 
+def _median_rate(run_once, units_per_call, trials: int, min_s: float):
+    """Median over `trials` of (units done / seconds) where each trial repeats
+    run_once() for at least min_s seconds (and at least once)."""
+    rates, calls = [], 0
+    for _ in range(trials):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            run_once(calls)
+            n += 1
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                break
+        rates.append(n * units_per_call / el)
+    return float(np.median(rates)), calls
+
+
 def cpu_baseline(d: W.Draft, lasts: np.ndarray, budget_s: float):
+    """The oracle (per-path fp64 replay + commit replay) on the host: median of
+    5 timed trials on all OpenMP threads and median of 5 on one thread, each
+    trial at least budget_s / 10 seconds."""
     from oracle import oracle as O
 
-    threads = O.set_threads(0)
     q, k, v = d.q64(), d.k64(), d.v64()
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def step(i):
         O.tree_verify(d.S0, d.parents, q, k, v, d.beta, d.g, d.scale)
-        O.commit(d.S0, d.parents, k, v, d.beta, d.g, lasts[steps % len(lasts)])
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": steps * d.B * d.N / el, "unit": "nodes/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{steps} steps of {d.name} (verify by per-path fp64 replay + commit "
-                      f"replay) in {el:.1f} s"}
+        O.commit(d.S0, d.parents, k, v, d.beta, d.g, lasts[i % len(lasts)])
+
+    threads = O.set_threads(0)
+    t0 = time.perf_counter()
+    step(0)  # warm-up (library load, page-in)
+    many, n_many = _median_rate(step, d.B * d.N, 5, budget_s / 10)
+    O.set_threads(1)
+    one, n_one = _median_rate(step, d.B * d.N, 5, budget_s / 10)
+    O.set_threads(threads)
+    el = time.perf_counter() - t0
+    return {"value": round(many, 1), "unit": "nodes/s", "cores": threads, "kind": "oracle",
+            "value_1_thread": round(one, 1), "trials": 5, "statistic": "median",
+            "sample": f"{d.name}: one step = verify by per-path fp64 replay + commit replay of "
+                      f"a drawn accepted path; median of 5 trials on {threads} threads "
+                      f"({n_many} steps) and of 5 on 1 thread ({n_one} steps); {el:.1f} s "
+                      f"of CPU work in total"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="chain8-b1-h8-d256",
-                    choices=sorted(W.WORKLOADS) + sorted(W.STACK_WORKLOADS))
-    ap.add_argument("--rotate-mib", type=int, default=1024,
-                    help="total size of the rotating layer states")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
-    ap.add_argument("--separate-commit", action="store_true",
-                    help="verify and commit as two launches per step instead of the delayed "
-                         "commit fused into the next verification")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
-    args = ap.parse_args()
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy, 20)
-        return
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the verify/commit path shards over "
-              "(sequence, head, state-row tile) units with no exchange, so there is no "
-              "multi-GPU step to time; run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
-    if args.workload in W.STACK_WORKLOADS:
-        bench_decode_loop(args)
-        return
-
+def layer_run(args, workload: str, extras: bool) -> dict:
+    """One GDN layer's verify + commit steps on `workload`: the timed graph of
+    K steps (HIP events on the launching stream), the roofline of the step's
+    kernel, and with `extras` the separate kernels, the latency floor and the
+    timing variants as context."""
     import torch
 
     from linear_attention_gdn_amd import gdnspec as G
 
-    torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    d = W.WORKLOADS[args.workload](0)
-    chain = args.workload.startswith("chain")
+    d = W.WORKLOADS[workload](0)
+    chain = workload.startswith("chain")
     B, N, H, dk, dv = d.B, d.N, d.H, d.dk, d.dv
     code = G.GDN_BF16 if d.dtype == "bf16" else G.GDN_F32
 
@@ -310,13 +320,17 @@ def main():
 
     stream = torch.cuda.current_stream()
     timed = range(args.warmup, total)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     if args.no_graph:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        e0.record(stream)
         for i in timed:
             step(i)
+        e1.record(stream)
         torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+        wall = time.perf_counter() - t0
     else:
         graph = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -329,11 +343,27 @@ def main():
         graph.replay()  # first replay uploads the graph; not timed
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        graph.replay()
+        e0.record(stream)
+        graph.replay()  # on the current stream: the stream every kernel of the step runs on
+        e1.record(stream)
         torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+        wall = time.perf_counter() - t0
+    elapsed = e0.elapsed_time(e1) * 1e-3  # seconds, HIP events
     ms_per_step = elapsed * 1e3 / args.steps
     value = B * N / (elapsed / args.steps)
+    res = {"d": d, "chain": chain, "delayed": delayed, "R": R, "ms_per_step": ms_per_step,
+           "wall_ms_per_step": wall * 1e3 / args.steps, "value": value}
+
+    # algorithmic bytes of the step's kernel(s), over the accepted paths drawn
+    # for the timed steps
+    plens = path_lengths(d, lasts_np[args.warmup:total])
+    b_step = (np.mean([bytes_delayed(d, p, not chain) for p in plens]) if delayed else
+              bytes_verify(d, not chain) + np.mean([bytes_commit(d, p) for p in plens]))
+    res["step_bytes"] = float(b_step)
+    res["step_kernel"] = (("gdn_chain_verify_delayed" if chain else "gdn_tree_verify_delayed")
+                          if delayed else None)
+    if not extras:
+        return res
 
     # Per-kernel durations: each kernel alone, `nper` back-to-back launches
     # captured in a HIP graph, timed with events on the stream it runs on.
@@ -350,13 +380,13 @@ def main():
         stream.wait_stream(gs)
         gph.replay()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        a0 = torch.cuda.Event(enable_timing=True)
+        a1 = torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
         gph.replay()
-        e1.record(stream)
+        a1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / nper
+        return a0.elapsed_time(a1) / nper
 
     if args.no_graph:  # eager: event pairs around single launches
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(4 * nper)]
@@ -417,77 +447,148 @@ def main():
         variants = {"hot_state_graph_us_per_step": round(t_hot * 1e3, 3),
                     "eager_single_step_us_median":
                         round(float(np.median(ts[len(ts) // 6:])) * 1e6, 2)}
-    plens = path_lengths(d, lasts_np[args.warmup:args.warmup + nper])
+    plens_k = path_lengths(d, lasts_np[args.warmup:args.warmup + nper])
     b_ver = bytes_verify(d, not chain)
-    b_com = np.mean([bytes_commit(d, p) for p in plens])
+    b_com = np.mean([bytes_commit(d, p) for p in plens_k])
     kernels = {
         "verify": {"name": "gdn_chain_verify" if chain else "gdn_tree_verify",
-                   "avg_us": float(t_ver.mean() * 1e3), "bytes": int(b_ver),
-                   "gbs": float(b_ver / (t_ver.mean() * 1e-3) / 1e9)},
-        "commit": {"name": "gdn_commit_path", "avg_us": float(t_com.mean() * 1e3),
-                   "bytes": float(b_com), "gbs": float(b_com / (t_com.mean() * 1e-3) / 1e9)},
+                   "avg_us": round(float(t_ver.mean() * 1e3), 3), "bytes": int(b_ver),
+                   "gbs": round(float(b_ver / (t_ver.mean() * 1e-3) / 1e9), 1)},
+        "commit": {"name": "gdn_commit_path", "avg_us": round(float(t_com.mean() * 1e3), 3),
+                   "bytes": float(b_com),
+                   "gbs": round(float(b_com / (t_com.mean() * 1e-3) / 1e9), 1)},
     }
     if not chain:
         flops = 4.0 * B * H * N * dk * dv
-        kernels["verify"]["fp32_equiv_tflops"] = float(flops / (t_ver.mean() * 1e-3) / 1e12)
-    dom = "verify" if t_ver.mean() >= t_com.mean() else "commit"
-    if delayed:
-        t_fus = graph_time(fused)
-        b_fus = np.mean([bytes_delayed(d, p, not chain) for p in plens])
-        kernels["verify_delayed"] = {"name": "gdn_chain_verify_delayed" if chain
-                                     else "gdn_tree_verify_delayed",
-                                     "avg_us": float(t_fus * 1e3), "bytes": float(b_fus),
-                                     "gbs": float(b_fus / (t_fus * 1e-3) / 1e9)}
-        dom = "verify_delayed"  # the only kernel of the timed step
-    kd = kernels[dom]
+        kernels["verify"]["fp32_equiv_tflops"] = round(float(flops / (t_ver.mean() * 1e-3) / 1e12), 2)
+    res.update(kernels=kernels, floor=floor, variants=variants)
+    return res
+
+
+def roofline_of(res: dict) -> dict:
+    """Roofline of the step's kernel.  The step is one launch (the delayed
+    commit fused into the verification), so the kernel's average launch
+    duration is the event-timed step itself (ms_per_step), and every fraction
+    below is computed from it."""
+    d, chain = res["d"], res["chain"]
+    t_s = res["ms_per_step"] * 1e-3
+    kern = res["step_kernel"] or ("gdn_chain_verify + gdn_commit_path" if chain
+                                  else "gdn_tree_verify + gdn_commit_path")
+    gbs = res["step_bytes"] / t_s / 1e9
+    traffic = measured_traffic(res["step_kernel"], d.name) if res["step_kernel"] else None
+    hbm = {"achieved_gbs": round(gbs, 2), "peak_gbs": HBM_PEAK_GBS,
+           "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": round(res["step_bytes"])}
     if chain:  # the serial chain kernel streams the state: HBM roofline
-        roofline = {"bound": "hbm", "achieved": round(kd["gbs"], 2), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(kd["name"], d.name), "kernel": kd["name"],
-                    "algorithmic_bytes": kd["bytes"]}
-    else:  # the tree kernel's S0 contraction, FP32-accurate on bf16 matrix cores
-        flops = 4.0 * B * H * N * dk * dv          # algorithmic (FP32-equivalent) per launch
-        t_s = kd["avg_us"] * 1e-6
-        tflops = flops / t_s / 1e12
-        issued = 2.0 * flops                        # hi + lo passes of the S0 contraction
-        roofline = {"bound": "mfma", "achieved": round(tflops, 2),
-                    "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic(kd["name"], d.name), "kernel": kd["name"],
-                    "algorithmic_flops": flops,
-                    "contraction_bf16_tflops": round(issued / t_s / 1e12, 2),
-                    "contraction_bf16_frac": round(issued / t_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                    "hbm_gbs": round(kd["gbs"], 2), "hbm_frac": round(kd["gbs"] / HBM_PEAK_GBS, 4),
-                    "algorithmic_bytes": kd["bytes"],
-                    "mfma_counters": measured_mfma(kd["name"], d.name, kd["avg_us"])}
+        return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kern,
+                "duration_us": round(t_s * 1e6, 3), "algorithmic_bytes": round(res["step_bytes"])}
+    # the tree kernel's S0 contraction, FP32-accurate on bf16 matrix cores
+    B, N, H, dk, dv = d.B, d.N, d.H, d.dk, d.dv
+    flops = 4.0 * B * H * N * dk * dv  # algorithmic (FP32-equivalent) per launch
+    tflops = flops / t_s / 1e12
+    mf = measured_mfma(res["step_kernel"], d.name, t_s * 1e6) if res["step_kernel"] else None
+    issued = None
+    if mf:
+        issued = {"type": "bf16 (v_mfma_f32_16x16x32_bf16)",
+                  "flop_per_launch": mf["bf16_flop_per_launch"],
+                  "achieved_tflops": mf["issued_tflops"], "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                  "frac": mf["issued_frac"],
+                  "busy_cycles_per_simd": mf["busy_cycles_per_simd"],
+                  "busy_frac": mf["busy_frac_at_2p4ghz"]}
+    return {"bound": "mfma", "achieved": round(tflops, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4),
+            "traffic": traffic, "kernel": kern, "duration_us": round(t_s * 1e6, 3),
+            "algorithmic_flops": flops,
+            "fp32_equiv": {"achieved_tflops": round(tflops, 2),
+                           "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
+                           "frac": round(tflops / FP32_MFMA_PEAK_TFLOPS, 4)},
+            "issued_mfma": issued, "hbm": hbm}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(W.WORKLOADS) + sorted(W.STACK_WORKLOADS))
+    ap.add_argument("--rotate-mib", type=int, default=1024,
+                    help="total size of the rotating layer states")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the 8-node chain's HBM figures that accompany a tree workload")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--separate-commit", action="store_true",
+                    help="verify and commit as two launches per step instead of the delayed "
+                         "commit fused into the next verification")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, 20)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the verify/commit path shards over "
+              "(sequence, head, state-row tile) units with no exchange, so there is no "
+              "multi-GPU step to time; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.workload in W.STACK_WORKLOADS:
+        bench_decode_loop(args)
+        return
+
+    import torch
+
+    torch.cuda.set_device(0)
+    res = layer_run(args, args.workload, extras=True)
+    d = res["d"]
+    roofline = roofline_of(res)
+    # The 8-node chain (the HBM half of the metric), measured in the same run
+    # with the same step count and timing.
+    chain8 = None
+    if not res["chain"] and not args.no_chain:
+        rc = layer_run(args, CHAIN_WORKLOAD, extras=False)
+        rr = roofline_of(rc)
+        chain8 = {"workload": CHAIN_WORKLOAD, "ms_per_step": round(rc["ms_per_step"], 6),
+                  "value": round(rc["value"], 1), "unit": "nodes/s", "kernel": rr["kernel"],
+                  "bound": "hbm", "achieved": rr["achieved"], "peak": HBM_PEAK_GBS,
+                  "unit_roofline": "GB/s", "frac": rr["frac"], "traffic": rr["traffic"],
+                  "algorithmic_bytes": rr["algorithmic_bytes"]}
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(d, lasts_np, args.cpu_seconds)
+        rng = np.random.default_rng(99)
+        cpu = cpu_baseline(d, draw_lasts(d, rng, 64, res["chain"]), args.cpu_seconds)
 
+    B, N, H, dk, dv = d.B, d.N, d.H, d.dk, d.dv
     line = {
         "metric": "verified draft nodes/sec per GDN layer (h=8,d=256)",
-        "value": round(value, 1),
+        "value": round(res["value"], 1),
         "unit": "nodes/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(res["ms_per_step"], 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": d.name, "B": B, "N": N, "H": H, "dk": dk, "dv": dv,
-                   "qkv_dtype": d.dtype, "state_dtype": "f32", "rotating_states": R,
+                   "qkv_dtype": d.dtype, "state_dtype": "f32", "rotating_states": res["R"],
                    "timing": "eager" if args.no_graph else "hip_graph",
-                   "commit": "delayed, fused into the next verification" if delayed
+                   "commit": "delayed, fused into the next verification" if res["delayed"]
                              else "separate launch after each verification",
                    "parallelism": "single-gpu"},
         "roofline": roofline,
-        "latency_floor": floor,
-        "timing_variants": variants,
-        "kernels": kernels,
+        "chain8": chain8,
+        "wall_ms_per_step": round(res["wall_ms_per_step"], 6),
+        "latency_floor": res["floor"],
+        "timing_variants": res["variants"],
+        "kernels": res["kernels"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -619,7 +720,7 @@ def bench_decode_loop(args):
         spec_step(i % slots)
         ar_step(i % slots)
     torch.cuda.synchronize()
-    assert int(st.status[0]) == G.GDN_OK
+    st.check_status()
 
     def timed(step_fn):
         reps, rem = divmod(args.steps, chunk)

@@ -121,9 +121,11 @@ int gdn_layer_prep(int B, int N, int H, int dk, int dv, int D, const float* P, c
  *              the previous draft and its deepest accepted node
  *   hist_out   FP32 [B][3][Cc], written: the history after that commit,
  *              bitwise gdn_conv_commit's result (hist itself when last_prev is
- *              -1 or out of range); must not overlap hist
+ *              -1, out of range or on a rejected topology); must not overlap hist
  *   dev_status optional int32 [B]: GDN_OK, or GDN_ERR_TOPOLOGY when last_prev
- *              is out of range
+ *              is out of range or parents_prev fails the verifier's topology
+ *              check (some p[j] < -1 or p[j] >= j); the history then does not
+ *              advance, as the state commit of that draft does not apply
  * The other arguments and all outputs are gdn_layer_prep's, computed from
  * hist_out, bitwise equal to gdn_conv_commit(P_prev, ...) followed by
  * gdn_layer_prep.  It is the history half of the delayed commit (SpecLA
@@ -188,7 +190,10 @@ int gdn_layer_verify(int B, int N_prev, int N, int H, int dk, int dv, float* S,
  *   last_accepted int32 [B], -1 <= last < N
  *   hist     FP32 [B][3][Cc], updated in place
  *   dev_status optional int32 [B]: GDN_OK, or GDN_ERR_TOPOLOGY when last is
- *            out of range (hist[b] then stays unchanged)
+ *            out of range, or last >= 0 and parents fails the verifier's
+ *            topology check (some p[j] < -1 or p[j] >= j): the rule under which
+ *            gdn_commit_path rejects the same path.  hist[b] then stays
+ *            unchanged
  * Cc % 4 == 0 and ldP % 4 == 0 are required.
  */
 int gdn_conv_commit(int B, int N, int Cc, const float* P, int ldP, const int32_t* parents,

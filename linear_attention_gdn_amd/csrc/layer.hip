@@ -340,6 +340,13 @@ hipError_t launch_pack_weights(int Nc, int K, const void* W, void* Wp, hipStream
 
 __device__ inline int checked_parent(int p, int cur) { return (p >= -1 && p < cur) ? p : -1; }
 
+// The verifier's topology check of a draft of n <= 64 nodes, from the parent
+// array held one entry per lane (lane j: parents[j], clamped past n): true,
+// in every lane, when some node j < n has p < -1 or p >= j.
+__device__ inline bool prev_topology_bad(int p, int lane, int n) {
+  return __ballot(lane < n && (p < -1 || p >= lane)) != 0ull;
+}
+
 __device__ inline float dot8_bf16(const u32x4& x, const u32x4& w, float acc) {
   const bf16x8 xv = __builtin_bit_cast(bf16x8, x);
   const bf16x8 wv = __builtin_bit_cast(bf16x8, w);
@@ -411,10 +418,15 @@ __global__ __launch_bounds__(256) void prep_kernel(int N, int H, int dk, int dv,
     hk[j] = hb[(size_t)j * Cc + ck];
     hv[j] = hb[(size_t)j * Cc + cv];
   }
-  // previous accepted path (uniform): node L and its nearest two ancestors
+  // previous accepted path (uniform): node L and its nearest two ancestors.
+  // It is accepted under the state commit's rule: L in range and a previous
+  // parent array that passed the verifier's topology check (a rejected draft
+  // has empty masks, so its state is not committed and its history must not
+  // advance either).
   const int L = DLY ? __builtin_amdgcn_readfirstlane(lastv) : -1;
-  const bool pbad = DLY && (L < -1 || L >= Np);
-  const bool padv = DLY && L >= 0 && L < Np;
+  const bool ptopo_bad = DLY && prev_topology_bad(myppar, lane, Np);
+  const bool pbad = DLY && (L < -1 || L >= Np || (L >= 0 && ptopo_bad));
+  const bool padv = DLY && L >= 0 && L < Np && !ptopo_bad;
   const int Lc = padv ? L : 0;
   const int p1 = padv ? checked_parent(__builtin_amdgcn_readlane(myppar, Lc), Lc) : -1;
   const int p2 = p1 >= 0 ? checked_parent(__builtin_amdgcn_readlane(myppar, p1), p1) : -1;
@@ -568,7 +580,9 @@ __global__ __launch_bounds__(256) void conv_commit_kernel(int N, int Cc,
   const int lane = tid & 63;
   const int L = __builtin_amdgcn_readfirstlane(last_acc[b]);
   const int mypar = parents[(size_t)b * N + clampi(lane, N - 1)];
-  const bool bad = L < -1 || L >= N;
+  // the state commit's rule: L in range and a parent array that passed the
+  // verifier's topology check
+  const bool bad = L < -1 || L >= N || (L >= 0 && prev_topology_bad(mypar, lane, N));
   if (dev_status && blockIdx.x == 0 && tid == 0) dev_status[b] = bad ? GDN_ERR_TOPOLOGY : GDN_OK;
   if (bad || L == -1) return;
   const int c = 4 * (blockIdx.x * 256 + tid);

@@ -87,7 +87,11 @@ class GdnStack:
             for _ in range(2)]
         self.cur = 0  # buffer set of the latest verification
         self.pending = None  # (parents, last) of a verified step not yet committed
+        # per-sequence status words: the draft's topology check (verify), the
+        # previous path's state commit and its history commit (delayed or not)
         self.status = torch.zeros(B, dtype=torch.int32, device=device)
+        self.commit_status = torch.zeros(B, dtype=torch.int32, device=device)
+        self.hist_status = torch.zeros(B, dtype=torch.int32, device=device)
         # autoregressive step buffers (one token per sequence)
         self.x1 = e(B, D)
         self.x1b = e(B, D, dt=bf)
@@ -131,11 +135,16 @@ class GdnStack:
         self.x.copy_(x)
         self.xb.copy_(x_bf16)
 
-    def verify(self, parents: torch.Tensor, stream=None):
+    def verify(self, parents: torch.Tensor, stream=None, layer_inputs=None, layer_outputs=None):
         """All layers, layer-major, for the draft tree `parents` [B][N]; the final
         hidden rows are left in self.x (FP32) and self.xb (bf16).  A step
         verified earlier and not yet committed (see step()) is committed first,
-        fused into each layer's verification."""
+        fused into each layer's verification.
+
+        layer_inputs: optional per-layer pairs (FP32 [B*N][D], bf16 [B*N][D])
+        copied into the hidden rows before each layer (each layer then runs on
+        given inputs instead of the previous layer's output); layer_outputs:
+        optional list that receives a copy of each layer's FP32 output rows."""
         sh = self.shape
         g0, g1 = self.gate_cols
         M = self.B * self.N
@@ -145,6 +154,9 @@ class GdnStack:
         pend = self.pending
         hc = self.hc
         for l in range(sh.layers):
+            if layer_inputs is not None:
+                self.x.copy_(layer_inputs[l][0])
+                self.xb.copy_(layer_inputs[l][1])
             P = self.P[cur, l]
             G.gdn_linear(self.xb, self.W_in[l], C=P.view(M, npj), w_layout=PK, stream=stream)
             if pend is None:
@@ -156,14 +168,17 @@ class GdnStack:
                                          self.hists[hc, l], self.q, self.k, self.v, self.beta,
                                          self.g, self.P[prev, l], pend[0], pend[1],
                                          self.hists[1 - hc, l], gate_shift=self.gate_shift,
-                                         stream=stream)
+                                         dev_status=self.hist_status, stream=stream)
             G.gdn_layer_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
                                P.view(M, npj)[:, g0:g1], self.Y, self.rec[cur][l],
                                prev_factors=None if pend is None else self.rec[prev][l],
                                last_accepted=None if pend is None else pend[1],
+                               commit_status=None if pend is None else self.commit_status,
                                dev_status=self.status, stream=stream)
             G.gdn_linear(self.Y, self.W_o[l], C=self.x, R=self.x, C_bf16=self.xb, w_layout=PK,
                          stream=stream)
+            if layer_outputs is not None:
+                layer_outputs.append(self.x.clone())
         self.cur = cur
         if pend is not None:
             self.hc = 1 - hc
@@ -174,20 +189,34 @@ class GdnStack:
         [B], -1 = none) in every layer now."""
         cur = self.cur
         for l in range(self.shape.layers):
-            G.gdn_commit_path(self.S[l], self.rec[cur][l], last, stream=stream)
-            G.gdn_conv_commit(self.P[cur, l], parents, last, self.hist[l], stream=stream)
+            G.gdn_commit_path(self.S[l], self.rec[cur][l], last, dev_status=self.commit_status,
+                              stream=stream)
+            G.gdn_conv_commit(self.P[cur, l], parents, last, self.hist[l],
+                              dev_status=self.hist_status, stream=stream)
+
+    def check_status(self):
+        """Raise if the latest verification rejected a draft's topology or a
+        commit (state or history) rejected its accepted node (waits for the
+        stream)."""
+        for name, st in (("draft topology", self.status), ("state commit", self.commit_status),
+                         ("history commit", self.hist_status)):
+            bad = [int(x) for x in st.cpu()]
+            if any(x != G.GDN_OK for x in bad):
+                raise G.GdnError(G.GDN_ERR_TOPOLOGY, f"{name} status per sequence: {bad}")
 
     def defer_commit(self, parents: torch.Tensor, last: torch.Tensor):
         """Leave the latest verification's accepted path to the next verify()."""
         self.pending = (parents, last)
 
-    def step(self, parents: torch.Tensor, last_prev=None, parents_prev=None, stream=None):
+    def step(self, parents: torch.Tensor, last_prev=None, parents_prev=None, stream=None,
+             layer_inputs=None, layer_outputs=None):
         """One speculative step with the delayed commit: the previous step's
         accepted node (last_prev, on its tree parents_prev) is committed inside
         this step's verification."""
         if last_prev is not None:
             self.defer_commit(parents_prev, last_prev)
-        self.verify(parents, stream=stream)
+        self.verify(parents, stream=stream, layer_inputs=layer_inputs,
+                    layer_outputs=layer_outputs)
 
     def flush(self, parents: torch.Tensor, last: torch.Tensor, stream=None):
         """Commit the latest verification's accepted path (end of a run)."""

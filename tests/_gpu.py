@@ -84,6 +84,22 @@ def slice_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     return worst
 
 
+def elem_rel_err(gpu: np.ndarray, ref: np.ndarray, floor: float = 1e-6) -> float:
+    """Largest elementwise |gpu - ref| / max(|ref|, floor * max|ref| of the slice)
+    per (b, h) slice; inputs shaped [B][H][...].  Reported beside
+    slice_rel_err (the gated metric): it shows how small elements fare."""
+    B, H = ref.shape[:2]
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            r = np.asarray(ref[b, h], np.float64)
+            den = np.maximum(np.abs(r), floor * np.abs(r).max())
+            if not den.any():
+                continue
+            worst = max(worst, float((np.abs(gpu[b, h].astype(np.float64) - r) / den).max()))
+    return worst
+
+
 def out_err(out_gpu: torch.Tensor, out_ref: np.ndarray) -> float:
     """Outputs are [B][N][H][dv]; compare per (b, h)."""
     g = out_gpu.cpu().numpy().transpose(0, 2, 1, 3)

@@ -13,8 +13,8 @@ import numpy as np
 import pytest
 import torch
 
-from _gpu import (TOL_OUT, TOL_STATE, TOL_UP, dev_tensors, out_err, run_chain, run_commit,
-                  run_tree, slice_rel_err, to_np)
+from _gpu import (TOL_OUT, TOL_STATE, TOL_UP, dev_tensors, elem_rel_err, out_err, run_chain,
+                  run_commit, run_tree, slice_rel_err, to_np)
 from linear_attention_gdn_amd import workloads as W
 from oracle import oracle as O
 
@@ -30,6 +30,10 @@ def _check_verify(d, out, rec, mask=None, st=None):
     ref_out, ref_up, ref_G = O.draft_verify(d)
     e_out = out_err(out, ref_out)
     e_up = slice_rel_err(to_np(rec.uprime), ref_up)
+    el_out = elem_rel_err(to_np(out).transpose(0, 2, 1, 3), ref_out.transpose(0, 2, 1, 3))
+    el_up = elem_rel_err(to_np(rec.uprime), ref_up)
+    _say(f"  slice max rel err: out {e_out:.2e}, u' {e_up:.2e}; elementwise (floor 1e-6 of "
+         f"the slice max): out {el_out:.2e}, u' {el_up:.2e}")
     assert e_out <= TOL_OUT, f"outputs: {e_out:.3e}"
     assert e_up <= TOL_UP, f"u': {e_up:.3e}"
     np.testing.assert_allclose(to_np(rec.G), ref_G, rtol=1e-5, atol=1e-5)
@@ -55,6 +59,8 @@ def _check_commits(d, rec, t, lasts):
         assert np.array_equal(to_np(path), ref_path)
         assert np.all(to_np(st) == 0)
         e = slice_rel_err(to_np(S), ref_S)
+        _say(f"  commit {last.tolist()}: slice max rel err {e:.2e}, elementwise "
+             f"{elem_rel_err(to_np(S), ref_S):.2e}")
         assert e <= TOL_STATE, f"state after commit to {last}: {e:.3e}"
         for b in range(d.B):
             if last[b] < 0:
