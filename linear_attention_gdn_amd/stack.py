@@ -135,16 +135,22 @@ class GdnStack:
         self.x.copy_(x)
         self.xb.copy_(x_bf16)
 
-    def verify(self, parents: torch.Tensor, stream=None, layer_inputs=None, layer_outputs=None):
+    def verify(self, parents: torch.Tensor, stream=None, layer_inputs=None, layer_outputs=None,
+               prep_outputs=None, verify_inputs=None):
         """All layers, layer-major, for the draft tree `parents` [B][N]; the final
         hidden rows are left in self.x (FP32) and self.xb (bf16).  A step
         verified earlier and not yet committed (see step()) is committed first,
         fused into each layer's verification.
 
+        Taps for checking the stack layer by layer (sequencing only):
         layer_inputs: optional per-layer pairs (FP32 [B*N][D], bf16 [B*N][D])
         copied into the hidden rows before each layer (each layer then runs on
         given inputs instead of the previous layer's output); layer_outputs:
-        optional list that receives a copy of each layer's FP32 output rows."""
+        optional list that receives a copy of each layer's FP32 output rows;
+        prep_outputs: optional list that receives copies of each layer's
+        (q, k, v, beta, g) as the prep wrote them; verify_inputs: optional
+        per-layer (q, k, v, beta, g) copied over the prep's before the layer's
+        verification."""
         sh = self.shape
         g0, g1 = self.gate_cols
         M = self.B * self.N
@@ -169,6 +175,12 @@ class GdnStack:
                                          self.g, self.P[prev, l], pend[0], pend[1],
                                          self.hists[1 - hc, l], gate_shift=self.gate_shift,
                                          dev_status=self.hist_status, stream=stream)
+            vin = (self.q, self.k, self.v, self.beta, self.g)
+            if prep_outputs is not None:
+                prep_outputs.append(tuple(t.clone() for t in vin))
+            if verify_inputs is not None:
+                for dst, src in zip(vin, verify_inputs[l]):
+                    dst.copy_(src)
             G.gdn_layer_verify(self.S[l], parents, self.q, self.k, self.v, self.beta, self.g,
                                P.view(M, npj)[:, g0:g1], self.Y, self.rec[cur][l],
                                prev_factors=None if pend is None else self.rec[prev][l],
@@ -209,14 +221,13 @@ class GdnStack:
         self.pending = (parents, last)
 
     def step(self, parents: torch.Tensor, last_prev=None, parents_prev=None, stream=None,
-             layer_inputs=None, layer_outputs=None):
+             **taps):
         """One speculative step with the delayed commit: the previous step's
         accepted node (last_prev, on its tree parents_prev) is committed inside
         this step's verification."""
         if last_prev is not None:
             self.defer_commit(parents_prev, last_prev)
-        self.verify(parents, stream=stream, layer_inputs=layer_inputs,
-                    layer_outputs=layer_outputs)
+        self.verify(parents, stream=stream, **taps)
 
     def flush(self, parents: torch.Tensor, last: torch.Tensor, stream=None):
         """Commit the latest verification's accepted path (end of a run)."""

@@ -393,30 +393,61 @@ def _elem_rel_err(gpu, ref, floor=1e-6):
     return float((np.abs(np.asarray(gpu, np.float64) - ref) / den).max())
 
 
+def _bf16_decisions(gpu_bits, exact, window=2.0 ** -14, window_row=2.0 ** -18):
+    """Check the GPU's bf16 rounding decisions against the exact values
+    ([..][d] rows).  Both sides round independently: the oracle its exact
+    value, the GPU an FP32 value within tol = window * |x| + window_row *
+    max|row| of it (a few units in the last place of the row's projections).
+    So each GPU value must be the bf16 rounding of some value within tol of
+    the exact one: |g - x| <= half a bf16 unit of g (<= 2^-8 |g|) + tol.
+    Returns how many GPU values differ from the oracle's own rounding."""
+    x = np.asarray(exact, np.float64)
+    r = LY.round_bf16(x)
+    g = wide(gpu_bits)
+    tol = window * np.abs(x) + window_row * np.abs(x).max(axis=-1, keepdims=True)
+    other = g != r
+    if other.any():
+        xo, go = x[other], g[other]
+        bad = np.abs(go - xo) > 2.0 ** -8 * np.abs(go) + tol[other]
+        assert not bad.any(), (f"{bad.sum()} bf16 values are not a rounding of a value within "
+                               f"the FP32 error of the exact one; worst |gpu - exact| = "
+                               f"{np.abs(go - xo)[bad].max():.3e}")
+    return int(other.sum())
+
+
 @pytest.mark.timeout(300)  # 24 layers of weights drawn on the host, three oracle steps
 def test_stack_layerwise_matches_oracle_24_layers_three_delayed_steps():
-    """Config-5 parity layer by layer and over consecutive steps: the 24-layer
+    """Config-5 parity layer by layer and over consecutive steps.  The 24-layer
     stack (hidden 2048, h=8, d=256) runs three speculative steps on 32-node
     window trees with the delayed commit (each step commits the previous
-    step's accepted path inside its verification; a flush commits the last),
-    and every GPU layer is fed the oracle's input rows of that layer and step.
-    Each layer's output is held to 2e-3 and, after every commit, each layer's
-    committed state to 1e-3 (max |err| / max |ref| per head) against the
-    oracle's step-by-step replay; the convolution histories to 1e-4."""
+    step's accepted path inside its verification; a flush commits the last).
+    Data flows from the oracle to the GPU only:
+    - every GPU layer gets the oracle's input rows of that layer and step;
+    - its prep (projection, path convolution, SiLU, norms, gates) is checked
+      against the oracle's exact values: beta and g to 2e-5, and every bf16
+      q, k, v value is the oracle's rounding or, within 2^-14 of a rounding
+      midpoint, the other valid rounding (both sides decide independently);
+    - its verification and commit then run on the oracle's rounded q, k, v,
+      beta, g, so one such decision cannot move a state by a bf16 unit of a
+      key: each layer's output is held to 2e-3 and, after every commit, each
+      layer's committed state to 1e-3 (max |err| / max |ref| per head), the
+      convolution histories (from the GPU's own projections) to 1e-4."""
     shape = W.StackShape(layers=24)
     N, steps = 32, 3
+    H, dk, dv = shape.H, shape.dk, shape.dv
     rng, layers, S0 = _stack_case(shape, 1, N, seed=31)
     parents, last = W.stack_drafts(rng, steps, N=N)
     x0 = [W.stack_inputs(rng, N, shape.D) for _ in range(steps)]
     st = _load(shape, layers, S0, 1, N)
 
     wt = LY.StackWeights([wide(w) for w, _, _ in layers], [c for _, c, _ in layers],
-                         [wide(w) for _, _, w in layers], shape.H, shape.dk, shape.dv, bf16=True)
+                         [wide(w) for _, _, w in layers], H, dk, dv, bf16=True)
     states = [S0[l][0].astype(np.float64) for l in range(shape.layers)]
     hists = [np.zeros((3, shape.n_conv)) for _ in range(shape.layers)]
     par_t = [i32(parents[s][None]) for s in range(steps)]
     last_t = [i32(last[s:s + 1]) for s in range(steps)]
-    worst = dict(out=0.0, state=0.0, hist=0.0, out_elem=0.0)
+    worst = dict(out=0.0, state=0.0, hist=0.0, out_elem=0.0, gates=0.0)
+    flips = 0
 
     def check_committed(tag):
         S_gpu = st.S.cpu().numpy()
@@ -432,17 +463,34 @@ def test_stack_layerwise_matches_oracle_24_layers_three_delayed_steps():
     for s_ in range(steps):
         x_ref, per_layer = LY.stack_spec_step(wt, wide(x0[s_]), parents[s_], states, hists)
         inputs = [_oracle_inputs(per_layer[l]["x_in"]) for l in range(shape.layers)]
-        outs = []
+        exact, vin = [], []
+        for l in range(shape.layers):
+            qx, kx, vx, bx, gx, _ = LY.layer_prep(per_layer[l]["P"], parents[s_], wt.conv_w[l],
+                                                  hists[l], H, dk, dv, wt.gate_shift)
+            exact.append((qx, kx, vx, bx, gx))
+            rb = [W.f32_to_bf16_bits(LY.round_bf16(a).astype(np.float32)[None])
+                  for a in (qx, kx, vx)]
+            vin.append((bf(rb[0]), bf(rb[1]), bf(rb[2]), f32(bx[None]), f32(gx[None])))
+        outs, preps = [], []
+        taps = dict(layer_inputs=inputs, layer_outputs=outs, prep_outputs=preps,
+                    verify_inputs=vin)
         if s_ == 0:
-            st.verify(par_t[0], layer_inputs=inputs, layer_outputs=outs)
+            st.verify(par_t[0], **taps)
         else:
-            st.step(par_t[s_], last_prev=last_t[s_ - 1], parents_prev=par_t[s_ - 1],
-                    layer_inputs=inputs, layer_outputs=outs)
+            st.step(par_t[s_], last_prev=last_t[s_ - 1], parents_prev=par_t[s_ - 1], **taps)
         torch.cuda.synchronize()
         st.check_status()
         if s_ > 0:  # the previous step's path is now committed on the GPU
             check_committed(f"after step {s_ - 1}")
         for l in range(shape.layers):
+            qx, kx, vx, bx, gx = exact[l]
+            gq, gk, gv, gb, gg = preps[l]
+            for got, ex in ((gq, qx), (gk, kx), (gv, vx)):
+                flips += _bf16_decisions(bits_of(got)[0], ex)
+            for got, ex in ((gb, bx), (gg, gx)):
+                e = np.abs(got.cpu().numpy()[0] - ex) / np.maximum(np.abs(ex), 1e-6)
+                worst["gates"] = max(worst["gates"], float(e.max()))
+            assert worst["gates"] <= 2e-5, (s_, l, worst["gates"])
             ref = per_layer[l + 1]["x_in"] if l + 1 < shape.layers else x_ref
             got = outs[l].cpu().numpy()
             e = rel(got, ref)
@@ -454,9 +502,11 @@ def test_stack_layerwise_matches_oracle_24_layers_three_delayed_steps():
     torch.cuda.synchronize()
     st.check_status()
     check_committed(f"after step {steps - 1}")
+    total = steps * shape.layers * N * H * (2 * dk + dv)
     print(f"\n24 layers x {steps} delayed steps, oracle-fed: outputs {worst['out']:.2e} "
           f"(elementwise, floor 1e-6: {worst['out_elem']:.2e}); committed states "
-          f"{worst['state']:.2e}; histories {worst['hist']:.2e}")
+          f"{worst['state']:.2e}; histories {worst['hist']:.2e}; beta, g {worst['gates']:.2e}; "
+          f"bf16 q/k/v decisions at a midpoint taken the other way: {flips} of {total}")
 
 
 def test_stack_chain_verify_equals_token_by_token_decode():
