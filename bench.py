@@ -461,7 +461,28 @@ def layer_run(args, workload: str, extras: bool) -> dict:
     if not chain:
         flops = 4.0 * B * H * N * dk * dv
         kernels["verify"]["fp32_equiv_tflops"] = round(float(flops / (t_ver.mean() * 1e-3) / 1e12), 2)
-    res.update(kernels=kernels, floor=floor, variants=variants)
+    # The pages' baselines on this GPU (root-to-leaf replay against tree
+    # verification, token replay against the factor-buffer commit), timed the
+    # same way as the kernels above.
+    replay = None
+    if not args.no_graph:
+        leaves = [W.leaves_of(p) for p in d.parents]
+        P = max(len(l) for l in leaves)
+        ends_np = np.full((B, P), -1, np.int32)
+        for b, l in enumerate(leaves):
+            ends_np[b, :len(l)] = l
+        ends = torch.from_numpy(ends_np).to(dev)
+        t_rv = graph_time(lambda i: G.gdn_replay_verify(states[i % R], parents, q, k, v, beta, g,
+                                                        ends, out))
+        t_rc = graph_time(lambda i: G.gdn_replay_commit(states[i % R], parents, k, v, beta, g,
+                                                        lasts[i]))
+        replay = {"root_to_leaf_replay_us": round(t_rv * 1e3, 3), "paths_per_sequence": P,
+                  "verify_us": round(float(t_ver.mean() * 1e3), 3),
+                  "verify_speedup_over_replay": round(t_rv / float(t_ver.mean()), 2),
+                  "token_replay_commit_us": round(t_rc * 1e3, 3),
+                  "commit_us": round(float(t_com.mean() * 1e3), 3),
+                  "commit_speedup_over_replay": round(t_rc / float(t_com.mean()), 2)}
+    res.update(kernels=kernels, floor=floor, variants=variants, replay=replay)
     return res
 
 
@@ -589,6 +610,7 @@ def main():
         "latency_floor": res["floor"],
         "timing_variants": res["variants"],
         "kernels": res["kernels"],
+        "replay_baselines": res["replay"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

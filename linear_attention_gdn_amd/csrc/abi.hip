@@ -9,6 +9,7 @@
 
 #include "gdn_common.h"
 #include "../../include/gdnlayer.h"
+#include "../../include/gdnnext.h"
 
 namespace gdn {
 size_t chain_lds_bytes(int N, int Np, int dk, int dtype);
@@ -44,6 +45,10 @@ hipError_t launch_conv_commit(int B, int N, int Cc, const float* P, int ldP,
 hipError_t launch_decode_step(int B, int H, int dk, int dv, int dtype, float* S, const void* q,
                               const void* k, const void* v, const float* beta, const float* g,
                               float scale, float* out, hipStream_t stream);
+hipError_t launch_replay(bool verify, int B, int N, int H, int dk, int dv, int dtype, float* S,
+                         const int32_t* parents, const void* q, const void* k, const void* v,
+                         const float* beta, const float* g, float scale, const int32_t* ends,
+                         int P, float* out, int32_t* dev_status, hipStream_t stream);
 }  // namespace gdn
 
 namespace {
@@ -520,6 +525,59 @@ int gdn_decode_step(int B, int H, int dk, int dv, int qkv_dtype, float* S, const
   GDN_TRY(check_ptr4(fn, "out", out, true));
   return hip_status(fn, gdn::launch_decode_step(B, H, dk, dv, qkv_dtype, S, q, k, v, beta, g,
                                                 scale, out, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// replay baselines (gdnnext.h)
+// ---------------------------------------------------------------------------
+
+int gdn_replay_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const float* S0,
+                      const int32_t* parents, const void* q, const void* k, const void* v,
+                      const float* beta, const float* g, float scale, const int32_t* ends,
+                      int P, float* out, int32_t* dev_status, void* stream) {
+  const char* fn = "gdn_replay_verify";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (P < 1 || P > gdn::kMaxNodes)
+    return fail(GDN_ERR_SHAPE, "%s: P=%d path slots outside 1..64", fn, P);
+  if (!std::isfinite(scale)) return fail(GDN_ERR_ARG, "%s: scale is not finite", fn);
+  if (B == 0 || N == 0) return ok();
+  GDN_TRY(check_ptr(fn, "S0", S0, true));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr4(fn, "ends", ends, true));
+  GDN_TRY(check_ptr4(fn, "out", out, true));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  return hip_status(fn, gdn::launch_replay(true, B, N, H, dk, dv, qkv_dtype,
+                                           const_cast<float*>(S0), parents, q, k, v, beta, g,
+                                           scale, ends, P, out, dev_status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int gdn_replay_commit(int B, int N, int H, int dk, int dv, int qkv_dtype, float* S,
+                      const int32_t* parents, const void* k, const void* v, const float* beta,
+                      const float* g, const int32_t* last_accepted, int32_t* dev_status,
+                      void* stream) {
+  const char* fn = "gdn_replay_commit";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (B == 0) return ok();
+  GDN_TRY(check_ptr4(fn, "last_accepted", last_accepted, true));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  if (N == 0) return ok();  // only last_accepted = -1 is possible: nothing to apply
+  GDN_TRY(check_ptr(fn, "S", S, true));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  return hip_status(fn, gdn::launch_replay(false, B, N, H, dk, dv, qkv_dtype, S, parents, nullptr,
+                                           k, v, beta, g, 1.0f, last_accepted, 1, nullptr,
+                                           dev_status, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,4 +1,5 @@
-"""ctypes binding of libgdnspec (``include/gdnspec.h``, ``include/gdnlayer.h``),
+"""ctypes binding of libgdnspec (``include/gdnspec.h``, ``include/gdnlayer.h``,
+``include/gdnnext.h``),
 with the same names.
 
 Argument marshalling only: every step of verification, commit and the layer
@@ -20,7 +21,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdnspec.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-HEADERS = [os.path.join(INCLUDE, "gdnspec.h"), os.path.join(INCLUDE, "gdnlayer.h")]
+HEADERS = [os.path.join(INCLUDE, "gdnspec.h"), os.path.join(INCLUDE, "gdnlayer.h"),
+           os.path.join(INCLUDE, "gdnnext.h")]
 
 GDN_OK = 0
 GDN_ERR_ARG = -1
@@ -91,6 +93,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_conv_commit.restype = I
         L.gdn_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, F, P, P]
         L.gdn_decode_step.restype = I
+        L.gdn_replay_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, I, P, P, P]
+        L.gdn_replay_verify.restype = I
+        L.gdn_replay_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        L.gdn_replay_commit.restype = I
         _lib = L
     return _lib
 
@@ -510,3 +516,48 @@ def gdn_decode_step(S, q, k, v, beta, g, out, scale: float = 1.0, stream=None) -
     _need("out", out, (B, H, dv), torch.float32)
     _raise_on(lib().gdn_decode_step(B, H, dk, dv, dtype_code(dt), _p(S), _p(q), _p(k), _p(v),
                                     _p(beta), _p(g), float(scale), _p(out), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# gdnnext.h
+# ---------------------------------------------------------------------------
+
+def gdn_replay_verify(S0, parents, q, k, v, beta, g, ends, out, scale: float = 1.0,
+                      dev_status=None, stream=None) -> None:
+    """Root-to-leaf replay of the paths ending at ``ends`` [B][P]; see
+    ``gdn_replay_verify`` in gdnnext.h."""
+    B, N, H, dk, dv, code = _check_draft(S0, q, k, v, beta, g)
+    _need("parents", parents, (B, N), torch.int32)
+    if ends.dim() != 2:
+        raise ValueError("ends must be [B][P]")
+    _need("ends", ends, (B, ends.shape[1]), torch.int32)
+    _need("out", out, (B, N, H, dv), torch.float32)
+    if dev_status is not None:
+        _need("dev_status", dev_status, (B,), torch.int32)
+    _raise_on(lib().gdn_replay_verify(B, N, H, dk, dv, code, _p(S0), _p(parents), _p(q), _p(k),
+                                      _p(v), _p(beta), _p(g), float(scale), _p(ends),
+                                      int(ends.shape[1]), _p(out), _p(dev_status),
+                                      _stream(stream)))
+
+
+def gdn_replay_commit(S, parents, k, v, beta, g, last_accepted, dev_status=None,
+                      stream=None) -> None:
+    """Token replay of the accepted path into S (in place); see
+    ``gdn_replay_commit`` in gdnnext.h."""
+    if S.dim() != 4 or k.dim() != 4:
+        raise ValueError("S must be [B][H][dv][dk] and k [B][N][H][dk]")
+    B, H, dv, dk = S.shape
+    N = k.shape[1]
+    dt = k.dtype
+    _need("S", S, (B, H, dv, dk), torch.float32)
+    _need("parents", parents, (B, N), torch.int32)
+    _need("k", k, (B, N, H, dk), dt)
+    _need("v", v, (B, N, H, dv), dt)
+    _need("beta", beta, (B, N, H), torch.float32)
+    _need("g", g, (B, N, H), torch.float32)
+    _need("last_accepted", last_accepted, (B,), torch.int32)
+    if dev_status is not None:
+        _need("dev_status", dev_status, (B,), torch.int32)
+    _raise_on(lib().gdn_replay_commit(B, N, H, dk, dv, dtype_code(dt), _p(S), _p(parents),
+                                      _p(k), _p(v), _p(beta), _p(g), _p(last_accepted),
+                                      _p(dev_status), _stream(stream)))

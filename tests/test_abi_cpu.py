@@ -211,3 +211,21 @@ def test_layer_bindings_refuse_host_tensors():
     W = torch.zeros(16, 512, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         G.gdn_linear(A, W, C=torch.zeros(4, 16))
+
+
+def test_replay_entry_points_validate_arguments():
+    L = G.lib()
+    P = ctypes.c_void_p(4096)
+    sz = (1, 8, 8, 256, 256)
+    for bad_p in (0, 65):
+        assert L.gdn_replay_verify(*sz, 0, P, P, P, P, P, P, P, 1.0, P, bad_p, P, None,
+                                   None) == G.GDN_ERR_SHAPE
+        assert "path slots" in G.gdn_last_error()
+    assert L.gdn_replay_verify(*sz, 0, P, P, P, P, P, P, P, 1.0, None, 4, P, None,
+                               None) == G.GDN_ERR_ARG
+    assert "ends is NULL" in G.gdn_last_error()
+    assert L.gdn_replay_verify(1, 65, 8, 256, 256, 0, P, P, P, P, P, P, P, 1.0, P, 4, P, None,
+                               None) == G.GDN_ERR_SHAPE
+    assert L.gdn_replay_commit(*sz, 0, P, P, P, P, P, P, None, None, None) == G.GDN_ERR_ARG
+    assert "last_accepted is NULL" in G.gdn_last_error()
+    assert L.gdn_replay_commit(*sz, 5, P, P, P, P, P, P, P, None, None) == G.GDN_ERR_ARG
