@@ -27,6 +27,10 @@ HIPCC_FLAGS = [
     # the first 16 dwords of kernel arguments arrive in SGPRs at wave launch
     # instead of through a scalar load the first global loads would wait for
     "-mllvm", "-amdgpu-kernarg-preload-count=16",
+    # keep the intermediate files (among them the gfx950 assembly,
+    # _build/<source>-hip-amdgcn-amd-amdhsa-gfx950.s) beside the objects, for
+    # the static checks of the generated code
+    "-save-temps=obj",
 ]
 
 
@@ -38,6 +42,12 @@ def hipcc() -> str:
 
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def device_asm_path(src: str) -> str:
+    """Where the build leaves the gfx950 assembly of one source."""
+    stem = os.path.splitext(os.path.basename(src))[0]
+    return os.path.join(HERE, "_build", f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
 
 
 def build(verbose: bool = False) -> str:

@@ -35,7 +35,10 @@
 //      block the products read, every operand read before any is used), then
 //      solves row t of T on t's root path (rows of T vanish off the path), one
 //      lane per node with the path's block of A in registers, writing T
-//      already split into bf16 hi + lo for step 5;
+//      already split into bf16 hi + lo for step 5.  A draft with a root path
+//      deeper than 16 is solved by blocks instead: each lane solves its row
+//      of its 16-node diagonal block, then block rows of T follow by blocked
+//      forward substitution on FP32 MFMA (T in FP32, split in step 5);
 //   4. runs the dense contraction Y = [Q; K] S0_tile^T on bf16 MFMA with the
 //      FP32 state split into bf16 hi + lo (bf16 q, k make every product
 //      exact; only the 2^-16 split residue is lost);
@@ -217,19 +220,25 @@ __device__ inline void path_solve_block(int t, uint64_t m, int d, const float* A
     if (b < d - 1) put(p[b], x[b]);
 }
 
-// The same for any depth, with the row in LDS (slower).
-__device__ inline void path_solve_lds(int t, uint64_t m, const float* A, float* Trow) {
-  Trow[t] = 1.f;
-  for (uint64_t rest = m & ~(1ull << t); rest;) {
-    const int j = 63 - __builtin_clzll(rest);
-    rest &= ~(1ull << j);
-    float acc = 0.f;
-    for (uint64_t above = m & ~((2ull << j) - 1ull); above; above &= above - 1ull) {
-      const int i = __builtin_ctzll(above);
-      acc = fmaf(Trow[i], A[i * kLd + j], acc);
-    }
-    Trow[j] = -acc;
-  }
+// v_mfma_f32_16x16x4f32: D[16x16] += A[16x4] * B[4x16] in FP32.  Lane l holds
+// A[l % 16][l / 16] and B[l / 16][l % 16]; D as for the bf16 form (row
+// 4 * (l / 16) + r, column l % 16).
+__device__ inline f32x4 mfma16x16x4f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Wait states after the last MFMA of a chain whose accumulators are read on
+// the far side of a branch.  The compiler pads a read of an MFMA result in
+// the same basic block, but not on a path that leaves the block right after
+// the MFMA: after the Y contraction, a wave that is last at the following
+// barrier passes it at once and, through the uniform branch behind it, read
+// the last accumulator register before the MFMA had written it (a few
+// outputs then varied from run to run in the last bits).  Two s_nop 7 give
+// 16 wait states on every path, more than any MFMA here needs.
+__device__ inline void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 constexpr int kDlyChunk = 16;  // path nodes staged per round for the delayed commit
@@ -269,7 +278,6 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
   __shared__ uint64_t smask[kMaxNodes];
   __shared__ float sG[kMaxNodes], seG[kMaxNodes], sbeta[kMaxNodes];
   __shared__ int sbad;
-  __shared__ int sdeep;  // some root path is deeper than kPathMax: T is solved in FP32
   __shared__ __attribute__((aligned(16))) DelayLds<DLY, BV> dly;
   __shared__ int sdly_n;
   __shared__ float sdly_s0;
@@ -713,6 +721,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(fa[ks], kb[ct & 1][ks], acc);
+          mfma_drain();  // the stores below may sit behind a branch
 #pragma unroll
           for (int r = 0; r < 4; ++r) dst[(16 * ra + 4 * lg + r) * kLd + 16 * ct + l16] = acc[r];
           if (two && ct <= rs) {  // compile-time after unrolling
@@ -720,6 +729,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
               acc2 = mfma16x16x32(fs[two ? ks : 0], kb[ct & 1][ks], acc2);
+            mfma_drain();
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               dst[(16 * rs + 4 * lg + r) * kLd + 16 * ct + l16] = acc2[r];
@@ -803,31 +813,70 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int idx = tid + 256 * x;
     store_split1(Attn + (idx / NK) * kLdH + idx % NK, kSplitLo, attn[x]);
   }
+  // A draft with a root path deeper than kPathMax is "deep": its T is solved
+  // in FP32 by blocks (below) and split in the epilogue.  Every wave reads
+  // the depths (smask is complete since step 1), so the decision is uniform
+  // without a barrier.
+  const bool deep = __ballot(lane < N && __popcll(smask[lane < N ? lane : 0]) > kPathMax) != 0ull;
   if (tid < N) {
     const int t = tid;
     const uint64_t m = smask[t];
     const int d = __popcll(m);
     // Rows of T go straight into the split bf16 layout the epilogue's
-    // products read (T[t][j] = hi + lo); only drafts with a path deeper than
-    // kPathMax solve in FP32 rows (the LDS solve reads its row back) and are
-    // split in the epilogue.  One variant per wave (all nodes are in wave
-    // 0), chosen by its deepest path, so the lanes never run two solves one
-    // after the other.
-    const bool deep = __ballot(d > kPathMax) != 0ull;
-    if (t == 0) sdeep = deep;
+    // products read (T[t][j] = hi + lo).  One variant per wave (all nodes are
+    // in wave 0), chosen by its deepest path, so the lanes never run two
+    // solves one after the other.
     auto put_split = [&](int j, float x) { store_split1(Ts + t * kLdH + j, kSplitLo, x); };
     auto put_f32 = [&](int j, float x) { Tl[t * kLd + j] = x; };
     if (deep) {
-      if (d <= kPathMax)
-        path_solve_registers(t, m, d, KK, put_f32);
-      else
-        path_solve_lds(t, m, KK, Tl + t * kLd);
+      // diagonal block of t's 16-node block: t's root path restricted to the
+      // block is a suffix of it (parents precede children), at most 16 nodes
+      const uint64_t mb = m & (0xFFFFull << (16 * (t / 16)));
+      path_solve_registers(t, mb, __popcll(mb), KK, put_f32);
     } else if (__ballot(d > 8) == 0ull) {
       path_solve_block<8>(t, m, d, KK, put_split);
     } else if (__ballot(d > 12) == 0ull) {
       path_solve_block<12>(t, m, d, KK, put_split);
     } else {
       path_solve_registers(t, m, d, KK, put_split);
+    }
+  }
+  if (deep) {  // uniform
+    // Blocked forward substitution for T = (I + A)^{-1} over 16-node blocks:
+    // with the diagonal blocks D_ii = (I + A_ii)^{-1} in place, block row i
+    // (i = 1 .. NQT-1, in order) is T_ij = -D_ii sum_{k=j}^{i-1} A_ik T_kj for
+    // j < i, wave j taking column block j, on FP32 MFMA.  Entries off the
+    // ancestor relation stay exact zeros (each term holds a masked factor).
+    __syncthreads();  // the diagonal blocks are in Tl
+#pragma unroll
+    for (int i = 1; i < NQT; ++i) {
+      const int j = wave;
+      // X = sum_k A_ik T_kj goes to T's (i, j) block, where D_ii X reads it
+      // back as its B operand after a barrier (other lanes wrote it)
+      float* blk = Tl + (16 * i) * kLd + 16 * j;
+      if (j < i) {  // uniform per wave
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = j; kb < i; ++kb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            x = mfma16x16x4f32(KK[(16 * i + l16) * kLd + 16 * kb + 4 * c + lg],
+                               Tl[(16 * kb + 4 * c + lg) * kLd + 16 * j + l16], x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) blk[(4 * lg + r) * kLd + l16] = x[r];
+      }
+      __syncthreads();
+      if (j < i) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          y = mfma16x16x4f32(Tl[(16 * i + l16) * kLd + 16 * i + 4 * c + lg],
+                             blk[(4 * c + lg) * kLd + l16], y);
+        // every lane's reads of X were issued before these writes, which
+        // depend on their results
+#pragma unroll
+        for (int r = 0; r < 4; ++r) blk[(4 * lg + r) * kLd + l16] = -y[r];
+      }
+      __syncthreads();  // block row i is complete before row i + 1 reads it
     }
   }
 
@@ -896,13 +945,13 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
       }
     }
   }
+  mfma_drain();     // the Y accumulators are read after the barrier's branch
   load_gate();      // consumed by the output step, after R and U'
   __syncthreads();  // Q/K reads and the solves are done: region A becomes R^T, U'^T
 
   // ---- 5. epilogue
   // T is already split, except after an FP32 solve (deep paths): then its
   // rows go to registers and are split in place after a barrier
-  const bool deep = sdeep != 0;  // uniform
   float trow[EPT];
   if (deep) {
 #pragma unroll

@@ -126,6 +126,20 @@ def branching_tree_parents(n: int, rng: np.random.Generator, branches=(1, 2, 3),
             return np.asarray(p, dtype=np.int32)
 
 
+def spine_tree_parents(n: int, rng: np.random.Generator, p_chain: float = 0.75,
+                       window: int = 6) -> np.ndarray:
+    """Deep, narrow tree: node t continues the chain (parent t - 1) with
+    probability p_chain, else branches off one of the `window` nodes before
+    t - 1; root paths run to about p_chain * n nodes."""
+    p = np.full(n, -1, dtype=np.int32)
+    for t in range(1, n):
+        if t == 1 or rng.random() < p_chain:
+            p[t] = t - 1
+        else:
+            p[t] = int(rng.integers(max(0, t - 1 - window), t - 1))
+    return p
+
+
 def random_parents(n: int, rng: np.random.Generator) -> np.ndarray:
     """Uniform random recursive tree: parent of node t uniform over 0..t-1."""
     p = np.full(n, -1, dtype=np.int32)
@@ -249,7 +263,8 @@ def make_draft(B: int, N: int, H: int, dk: int, dv: int, *, topology: str = "cha
     """Draw a draft in the fixed order S0, q, k, v, beta, g, topology, acceptance.
 
     topology: "chain" | "window" (parent in the previous 4 nodes, depth <= 8) |
-              "branching" (branching factor in {1,2,3}, depth <= 10) | "random"
+              "branching" (branching factor in {1,2,3}, depth <= 10) | "random" |
+              "spine" (long main chain with short side branches: deep drafts)
     accept:   "uniform" (length uniform in 0..N on a chain) |
               "leaf_geometric" (uniform leaf, path cut to geometric(accept_mean)) |
               "full" (deepest node N-1) | "none" (-1)
@@ -269,6 +284,8 @@ def make_draft(B: int, N: int, H: int, dk: int, dv: int, *, topology: str = "cha
             parents[b] = random_parents(N, rng)
         elif topology == "binary":
             parents[b] = binary_tree_parents(N)
+        elif topology == "spine":
+            parents[b] = spine_tree_parents(N, rng)
         else:
             raise ValueError(topology)
     last = np.empty(B, dtype=np.int32)

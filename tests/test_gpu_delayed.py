@@ -114,6 +114,9 @@ def _prev_record(prev: W.Draft):
     ("bf16", 2, 40, 12, 3, 64, 40, "chain", "random"),         # 40-node path: 3 chunks
     ("f32", 2, 9, 17, 2, 40, 24, "random", "window"),
     ("bf16", 1, 5, 1, 1, 16, 8, "binary", "chain"),
+    # deep drafts (blocked solve) with long previous paths, wide and narrow tiles
+    ("bf16", 8, 64, 64, 8, 256, 256, "spine", "spine"),
+    ("bf16", 1, 48, 48, 8, 256, 256, "spine", "spine"),
 ])
 def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo,
                                                    new_topo):

@@ -133,6 +133,13 @@ SHAPES = [
     # root paths of 9-12 and 13-16 nodes: the two register-block solves
     (2, 11, 2, 32, 48, "f32", "chain"),
     (1, 14, 2, 64, 64, "bf16", "chain"),
+    # deep drafts (root paths of 17 to 64 nodes): the blocked solve
+    (2, 17, 2, 64, 32, "bf16", "chain"),
+    (2, 20, 2, 64, 64, "f32", "spine"),
+    (3, 33, 2, 128, 96, "bf16", "spine"),
+    (2, 48, 8, 256, 256, "bf16", "spine"),
+    (8, 64, 8, 256, 256, "bf16", "spine"),
+    (1, 40, 3, 72, 52, "f32", "chain"),
 ]
 
 
@@ -169,11 +176,19 @@ def test_runs_are_bitwise_deterministic():
     assert torch.equal(o1, o2) and torch.equal(r1.buf, r2.buf)
 
 
-def test_non_descendants_bitwise_unchanged():
-    d = W.tree32_layer(3)
+@pytest.mark.parametrize("kind", ["window", "spine"])
+def test_non_descendants_bitwise_unchanged(kind):
+    """Masked terms are exact zeros, in the per-path solve (window trees) and
+    in the blocked solve of deep drafts (spine trees, paths past 16 nodes)."""
+    if kind == "window":
+        d = W.tree32_layer(3)
+        x = 5
+    else:
+        d = W.make_draft(1, 64, 8, 256, 256, topology="spine", accept="full", seed=12)
+        assert W.depths_of(d.parents[0]).max() > 16
+        x = 20
     out, _, mask, _, t = run_tree(d)
     m = to_np(mask).view(np.uint64)[0]
-    x = 5
     desc = np.array([(int(m[i]) >> x) & 1 for i in range(d.N)], dtype=bool)
     t2 = dict(t)
     for key in ("q", "k", "v"):
