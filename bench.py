@@ -462,8 +462,8 @@ def layer_run(args, workload: str, extras: bool) -> dict:
         flops = 4.0 * B * H * N * dk * dv
         kernels["verify"]["fp32_equiv_tflops"] = round(float(flops / (t_ver.mean() * 1e-3) / 1e12), 2)
     # The pages' baselines on this GPU (root-to-leaf replay against tree
-    # verification, token replay against the factor-buffer commit), timed the
-    # same way as the kernels above.
+    # verification, token replay against the factor-buffer commit) and the
+    # chain-decomposed hybrid verifier, timed the same way as the kernels above.
     replay = None
     if not args.no_graph:
         leaves = [W.leaves_of(p) for p in d.parents]
@@ -476,7 +476,14 @@ def layer_run(args, workload: str, extras: bool) -> dict:
                                                         ends, out))
         t_rc = graph_time(lambda i: G.gdn_replay_commit(states[i % R], parents, k, v, beta, g,
                                                         lasts[i]))
+        hplan = G.HybridPlan(d.parents, device=dev)
+        t_hy = graph_time(lambda i: G.gdn_hybrid_verify(states[i % R], parents, q, k, v, beta, g,
+                                                        out, rec, hplan))
         replay = {"root_to_leaf_replay_us": round(t_rv * 1e3, 3), "paths_per_sequence": P,
+                  "hybrid_chain_verify_us": round(t_hy * 1e3, 3),
+                  "hybrid_levels": hplan.levels,
+                  "hybrid_chains_per_level": [int(c) for c in
+                                              hplan.chains_per_level[:hplan.levels]],
                   "verify_us": round(float(t_ver.mean() * 1e3), 3),
                   "verify_speedup_over_replay": round(t_rv / float(t_ver.mean()), 2),
                   "token_replay_commit_us": round(t_rc * 1e3, 3),

@@ -45,6 +45,13 @@ hipError_t launch_conv_commit(int B, int N, int Cc, const float* P, int ldP,
 hipError_t launch_decode_step(int B, int H, int dk, int dv, int dtype, float* S, const void* q,
                               const void* k, const void* v, const float* beta, const float* g,
                               float scale, float* out, hipStream_t stream);
+hipError_t launch_hybrid(int B, int N, int H, int dk, int dv, int dtype, const float* S0,
+                         const int32_t* parents, const void* q, const void* k, const void* v,
+                         const float* beta, const float* g, float scale, float* out,
+                         void* factors, const int32_t* plan, int levels,
+                         const int32_t* chains_per_level, int32_t* dev_status,
+                         hipStream_t stream);
+int hybrid_plan(int B, int N, const int32_t* parents, int32_t* plan, int32_t* chains_per_level);
 hipError_t launch_replay(bool verify, int B, int N, int H, int dk, int dv, int dtype, float* S,
                          const int32_t* parents, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, float scale, const int32_t* ends,
@@ -578,6 +585,64 @@ int gdn_replay_commit(int B, int N, int H, int dk, int dv, int qkv_dtype, float*
   return hip_status(fn, gdn::launch_replay(false, B, N, H, dk, dv, qkv_dtype, S, parents, nullptr,
                                            k, v, beta, g, 1.0f, last_accepted, 1, nullptr,
                                            dev_status, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// chain-decomposed hybrid verifier (gdnnext.h)
+// ---------------------------------------------------------------------------
+
+size_t gdn_hybrid_plan_entries(int B, int N) {
+  if (B < 1 || N < 1 || N > gdn::kMaxNodes) return 0;
+  return 2 * (size_t)N * B * N;
+}
+
+int gdn_hybrid_plan(int B, int N, const int32_t* parents, int32_t* plan,
+                    int32_t* chains_per_level, int32_t* levels) {
+  const char* fn = "gdn_hybrid_plan";
+  if (B < 1 || N < 1 || N > gdn::kMaxNodes || (long long)B * N * N >= (1ll << 31))
+    return fail(GDN_ERR_SHAPE, "%s: unsupported sizes B=%d N=%d (need B>=1, 1<=N<=64)", fn, B,
+                N);
+  if (!parents || !plan || !chains_per_level || !levels)
+    return fail(GDN_ERR_ARG, "%s: NULL argument", fn);
+  const int L = gdn::hybrid_plan(B, N, parents, plan, chains_per_level);
+  if (L < 0)
+    return fail(GDN_ERR_TOPOLOGY, "%s: parents fail the topology check (-1 <= p[t] < t)", fn);
+  *levels = L;
+  return ok();
+}
+
+int gdn_hybrid_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const float* S0,
+                      const int32_t* parents, const void* q, const void* k, const void* v,
+                      const float* beta, const float* g, float scale, float* out,
+                      void* factors, const int32_t* plan, int levels,
+                      const int32_t* chains_per_level, int32_t* dev_status, void* stream) {
+  const char* fn = "gdn_hybrid_verify";
+  GDN_TRY(check_sizes(fn, B, N, H, dk, dv));
+  GDN_TRY(check_dtype(fn, qkv_dtype));
+  if (!std::isfinite(scale)) return fail(GDN_ERR_ARG, "%s: scale is not finite", fn);
+  if (B == 0 || N == 0) return ok();
+  if (levels < 1 || levels > N)
+    return fail(GDN_ERR_SHAPE, "%s: levels=%d outside 1..N=%d", fn, levels, N);
+  if (!chains_per_level) return fail(GDN_ERR_ARG, "%s: chains_per_level is NULL", fn);
+  for (int l = 0; l < levels; ++l)
+    if (chains_per_level[l] < 1 || chains_per_level[l] > N)
+      return fail(GDN_ERR_SHAPE, "%s: level %d has %d chains (need 1..N)", fn, l,
+                  chains_per_level[l]);
+  GDN_TRY(check_ptr(fn, "S0", S0, true));
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr(fn, "q", q, true));
+  GDN_TRY(check_ptr(fn, "k", k, true));
+  GDN_TRY(check_ptr(fn, "v", v, true));
+  GDN_TRY(check_ptr4(fn, "beta", beta, true));
+  GDN_TRY(check_ptr4(fn, "g", g, true));
+  GDN_TRY(check_ptr4(fn, "out", out, true));
+  GDN_TRY(check_ptr(fn, "factors", factors, true));
+  GDN_TRY(check_ptr4(fn, "plan", plan, true));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  return hip_status(fn, gdn::launch_hybrid(B, N, H, dk, dv, qkv_dtype, S0, parents, q, k, v, beta,
+                                           g, scale, out, factors, plan, levels,
+                                           chains_per_level, dev_status,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -97,6 +97,13 @@ def lib() -> ctypes.CDLL:
         L.gdn_replay_verify.restype = I
         L.gdn_replay_commit.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
         L.gdn_replay_commit.restype = I
+        L.gdn_hybrid_plan_entries.argtypes = [I, I]
+        L.gdn_hybrid_plan_entries.restype = S
+        L.gdn_hybrid_plan.argtypes = [I, I, P, P, P, P]
+        L.gdn_hybrid_plan.restype = I
+        L.gdn_hybrid_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, P, I, P,
+                                        P, P]
+        L.gdn_hybrid_verify.restype = I
         _lib = L
     return _lib
 
@@ -561,3 +568,49 @@ def gdn_replay_commit(S, parents, k, v, beta, g, last_accepted, dev_status=None,
     _raise_on(lib().gdn_replay_commit(B, N, H, dk, dv, dtype_code(dt), _p(S), _p(parents),
                                       _p(k), _p(v), _p(beta), _p(g), _p(last_accepted),
                                       _p(dev_status), _stream(stream)))
+
+
+class HybridPlan:
+    """gdn_hybrid_plan's result: the plan on the device and its level sizes on
+    the host."""
+
+    def __init__(self, parents_host, device="cuda"):
+        import numpy as np
+        par = np.ascontiguousarray(parents_host, dtype=np.int32)
+        if par.ndim != 2:
+            raise ValueError("parents must be [B][N]")
+        B, N = par.shape
+        n = int(lib().gdn_hybrid_plan_entries(B, N))
+        if n == 0:
+            raise GdnError(GDN_ERR_SHAPE, f"unsupported plan sizes B={B} N={N}")
+        plan = np.empty(n, dtype=np.int32)
+        cpl = np.zeros(N, dtype=np.int32)
+        lev = np.zeros(1, dtype=np.int32)
+        _raise_on(lib().gdn_hybrid_plan(B, N, par.ctypes.data_as(ctypes.c_void_p),
+                                        plan.ctypes.data_as(ctypes.c_void_p),
+                                        cpl.ctypes.data_as(ctypes.c_void_p),
+                                        lev.ctypes.data_as(ctypes.c_void_p)))
+        self.B, self.N = B, N
+        self.levels = int(lev[0])
+        self.chains_per_level = cpl  # host, kept alive for the launches
+        self.plan_host = plan
+        self.plan = torch.from_numpy(plan).to(device)
+
+
+def gdn_hybrid_verify(S0, parents, q, k, v, beta, g, out, factors: FactorRecord,
+                      plan: HybridPlan, scale: float = 1.0, dev_status=None,
+                      stream=None) -> None:
+    """Chain-decomposed hybrid verification; see ``gdn_hybrid_verify`` in gdnnext.h."""
+    B, N, H, dk, dv, code = _check_draft(S0, q, k, v, beta, g)
+    _need("parents", parents, (B, N), torch.int32)
+    _need("out", out, (B, N, H, dv), torch.float32)
+    _check_record(factors, B, N, H, dk, dv, code)
+    if (plan.B, plan.N) != (B, N):
+        raise ValueError("the plan was made for other sizes")
+    if dev_status is not None:
+        _need("dev_status", dev_status, (B,), torch.int32)
+    _raise_on(lib().gdn_hybrid_verify(
+        B, N, H, dk, dv, code, _p(S0), _p(parents), _p(q), _p(k), _p(v), _p(beta), _p(g),
+        float(scale), _p(out), _p(factors.buf), _p(plan.plan), plan.levels,
+        plan.chains_per_level.ctypes.data_as(ctypes.c_void_p), _p(dev_status),
+        _stream(stream)))

@@ -347,10 +347,28 @@ def tree64_batch8(seed: int = 0) -> Draft:
                       accept_mean=4.0, seed=seed, name="tree64-b8-h8-d256")
 
 
+def chain64_layer(seed: int = 0) -> Draft:
+    """Deep-draft case: the same layer, B=1, a 64-node chain (root paths up to
+    64 nodes), geometric(4) acceptance along it."""
+    return make_draft(1, 64, 8, 256, 256, topology="chain", accept="leaf_geometric",
+                      accept_mean=4.0, seed=seed, name="chain64-b1-h8-d256")
+
+
+def spine64_batch8(seed: int = 0) -> Draft:
+    """Deep-draft case: B=8 sequences, each a 64-node spine tree (a long main
+    chain with short side branches, root paths of 25-35 nodes)."""
+    return make_draft(8, 64, 8, 256, 256, topology="spine", accept="leaf_geometric",
+                      accept_mean=4.0, seed=seed, name="spine64-b8-h8-d256")
+
+
 WORKLOADS = {
     "chain8-b1-h8-d256": chain8_layer,
     "tree32-b1-h8-d256": tree32_layer,
     "tree64-b8-h8-d256": tree64_batch8,
+    # deep drafts (paths past 16 nodes): timing cases for the blocked solve
+    # and the chain-decomposed verifier, not configurations of the metric
+    "chain64-b1-h8-d256": chain64_layer,
+    "spine64-b8-h8-d256": spine64_batch8,
 }
 
 

@@ -61,10 +61,10 @@ def test_replay_verify_matches_oracle(name, make):
     assert e <= TOL_OUT
 
 
-def test_replay_verify_every_node_as_an_end_writes_each_node_once():
-    """Ends = all nodes (many paths share prefixes): the result is the same,
-    and slots past the first that hold a node do not rewrite it (the outputs
-    equal those of the leaf ends bitwise)."""
+def test_replay_verify_every_node_as_an_end_agrees_bitwise():
+    """Ends = all nodes (many paths share prefixes, so every node is written
+    by several slots): the outputs equal those of the leaf ends bitwise, since
+    each slot replays a node's root path in the same order."""
     d = W.tree32_layer(2)
     t = dev_tensors(d)
     outs = []
