@@ -493,6 +493,44 @@ def layer_run(args, workload: str, extras: bool) -> dict:
     return res
 
 
+def prune_timing(args) -> dict:
+    """Confidence-guided pruning of batch-8 candidate trees shaped like the
+    pages' drafter (top-4 continuations to depth 4: 341 candidates, budget 16
+    nodes, margin 3 nats), HIP-graph timing of back-to-back launches."""
+    import torch
+
+    from linear_attention_gdn_amd import gdnspec as G
+    B, T, tau = 8, 16, 3.0
+    par, conf = W.candidate_batch(B, seed=5, top_k=4, depth=4)
+    dev = torch.device("cuda:0")
+    pt = torch.from_numpy(par).to(dev)
+    ct = torch.from_numpy(conf).to(dev)
+    kept = torch.empty(B, T, dtype=torch.int32, device=dev)
+    newp = torch.empty(B, T, dtype=torch.int32, device=dev)
+    cnt = torch.empty(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    n = 200
+    gph = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(gph, stream=gs):
+            for _ in range(n):
+                G.gdn_prune_draft(pt, ct, tau, kept, newp, cnt)
+    stream.wait_stream(gs)
+    gph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    gph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    return {"B": B, "candidates": int(par.shape[1]), "budget": T, "tau": tau, "avg_us": round(us, 3),
+            "mean_kept": round(float(cnt.float().mean()), 2)}
+
+
 def roofline_of(res: dict) -> dict:
     """Roofline of the step's kernel.  The step is one launch (the delayed
     commit fused into the verification), so the kernel's average launch
@@ -586,6 +624,8 @@ def main():
                   "unit_roofline": "GB/s", "frac": rr["frac"], "traffic": rr["traffic"],
                   "algorithmic_bytes": rr["algorithmic_bytes"]}
 
+    pruning = None if args.no_graph else prune_timing(args)
+
     cpu = None
     if not args.no_cpu_baseline:
         rng = np.random.default_rng(99)
@@ -618,6 +658,7 @@ def main():
         "timing_variants": res["variants"],
         "kernels": res["kernels"],
         "replay_baselines": res["replay"],
+        "pruning": pruning,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

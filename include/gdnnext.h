@@ -14,6 +14,9 @@
  *   gdn_hybrid_plan, gdn_hybrid_verify     the chain-decomposed hybrid
  *       verifier (review, "What carries the argument"; Figures, Figure 6
  *       caption).
+ *   gdn_prune_draft                        confidence-guided pruning of a
+ *       candidate tree before verification (review, Figures, Figure 8
+ *       caption).
  */
 #ifndef GDNNEXT_H
 #define GDNNEXT_H
@@ -129,6 +132,39 @@ int gdn_hybrid_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const 
                       const float* beta, const float* g, float scale, float* out,
                       void* factors, const int32_t* plan, int levels,
                       const int32_t* chains_per_level, int32_t* dev_status, void* stream);
+
+/*
+ * gdn_prune_draft: confidence-guided pruning of a candidate draft tree
+ * (review, Figures, Figure 8 caption; Axiom & Free-Parameter Ledger: tree
+ * margin tau_tree, draft budget).  Per sequence b, with q[t] the confidence of
+ * candidate t (a path score that never increases from a node to its
+ * children, such as the cumulative log-probability) and q* = max_t q[t]:
+ *   window  = {t : q[t] >= q* - tau}, the threshold formed in FP32, which is
+ *             ancestor-closed because q never increases along a path;
+ *   kept    = the first T window nodes in the order (q descending, index
+ *             ascending): every parent precedes its children, so the kept set
+ *             is ancestor-closed too;
+ *   outputs = the kept nodes in their original order, renumbered 0..n-1.
+ *   B        sequences; M candidates per sequence, 1 <= M <= 1024
+ *   T        budget, 1 <= T <= 64 (a draft the verifiers take)
+ *   tau      tree margin, finite, >= 0
+ *   parents  int32 [B][M] device, topological: -1 <= parents[t] < t
+ *   conf     FP32 [B][M] device: q, no NaN, q[t] <= q[parents[t]]
+ *   kept     int32 [B][T] device, written: kept[b][i] = the original index of
+ *            new node i, -1 past the count
+ *   new_parents int32 [B][T] device, written: the parent of new node i in the
+ *            new numbering (-1 for a root), -1 past the count
+ *   count    int32 [B] device, written: the number of kept nodes, or -1 when
+ *            the candidates break a precondition (kept, new_parents all -1)
+ *   dev_status optional int32 [B]: GDN_OK, or GDN_ERR_TOPOLOGY for broken
+ *            preconditions
+ * Integer outputs: they depend on q only through FP32 comparisons.
+ * Errors: GDN_ERR_SHAPE (B < 0, M, T), GDN_ERR_ARG (NULL or misaligned
+ * pointers, tau not finite or negative).
+ */
+int gdn_prune_draft(int B, int M, int T, float tau, const int32_t* parents, const float* conf,
+                    int32_t* kept, int32_t* new_parents, int32_t* count, int32_t* dev_status,
+                    void* stream);
 
 #ifdef __cplusplus
 }

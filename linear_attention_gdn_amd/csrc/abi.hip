@@ -52,6 +52,9 @@ hipError_t launch_hybrid(int B, int N, int H, int dk, int dv, int dtype, const f
                          const int32_t* chains_per_level, int32_t* dev_status,
                          hipStream_t stream);
 int hybrid_plan(int B, int N, const int32_t* parents, int32_t* plan, int32_t* chains_per_level);
+hipError_t launch_prune(int B, int M, int T, float tau, const int32_t* parents, const float* conf,
+                        int32_t* kept, int32_t* new_parents, int32_t* count, int32_t* dev_status,
+                        hipStream_t stream);
 hipError_t launch_replay(bool verify, int B, int N, int H, int dk, int dv, int dtype, float* S,
                          const int32_t* parents, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, float scale, const int32_t* ends,
@@ -643,6 +646,30 @@ int gdn_hybrid_verify(int B, int N, int H, int dk, int dv, int qkv_dtype, const 
                                            g, scale, out, factors, plan, levels,
                                            chains_per_level, dev_status,
                                            static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// confidence-guided pruning (gdnnext.h)
+// ---------------------------------------------------------------------------
+
+int gdn_prune_draft(int B, int M, int T, float tau, const int32_t* parents, const float* conf,
+                    int32_t* kept, int32_t* new_parents, int32_t* count, int32_t* dev_status,
+                    void* stream) {
+  const char* fn = "gdn_prune_draft";
+  if (B < 0 || B > 65535 || M < 1 || M > 1024 || T < 1 || T > gdn::kMaxNodes)
+    return fail(GDN_ERR_SHAPE, "%s: unsupported sizes B=%d M=%d T=%d (need 0<=B<=65535, "
+                "1<=M<=1024, 1<=T<=64)", fn, B, M, T);
+  if (!std::isfinite(tau) || tau < 0.f)
+    return fail(GDN_ERR_ARG, "%s: tau must be finite and >= 0", fn);
+  if (B == 0) return ok();
+  GDN_TRY(check_ptr4(fn, "parents", parents, true));
+  GDN_TRY(check_ptr4(fn, "conf", conf, true));
+  GDN_TRY(check_ptr4(fn, "kept", kept, true));
+  GDN_TRY(check_ptr4(fn, "new_parents", new_parents, true));
+  GDN_TRY(check_ptr4(fn, "count", count, true));
+  GDN_TRY(check_ptr4(fn, "dev_status", dev_status, false));
+  return hip_status(fn, gdn::launch_prune(B, M, T, tau, parents, conf, kept, new_parents, count,
+                                          dev_status, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_hybrid_verify.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, P, P, P, I, P,
                                         P, P]
         L.gdn_hybrid_verify.restype = I
+        L.gdn_prune_draft.argtypes = [I, I, I, F, P, P, P, P, P, P, P]
+        L.gdn_prune_draft.restype = I
         _lib = L
     return _lib
 
@@ -614,3 +616,22 @@ def gdn_hybrid_verify(S0, parents, q, k, v, beta, g, out, factors: FactorRecord,
         float(scale), _p(out), _p(factors.buf), _p(plan.plan), plan.levels,
         plan.chains_per_level.ctypes.data_as(ctypes.c_void_p), _p(dev_status),
         _stream(stream)))
+
+
+def gdn_prune_draft(parents, conf, tau: float, kept, new_parents, count, dev_status=None,
+                    stream=None) -> None:
+    """Confidence-guided pruning of candidate trees [B][M] to at most T = kept.shape[1]
+    nodes; see ``gdn_prune_draft`` in gdnnext.h."""
+    if parents.dim() != 2 or kept.dim() != 2:
+        raise ValueError("parents must be [B][M] and kept [B][T]")
+    B, M = parents.shape
+    T = kept.shape[1]
+    _need("parents", parents, (B, M), torch.int32)
+    _need("conf", conf, (B, M), torch.float32)
+    _need("kept", kept, (B, T), torch.int32)
+    _need("new_parents", new_parents, (B, T), torch.int32)
+    _need("count", count, (B,), torch.int32)
+    if dev_status is not None:
+        _need("dev_status", dev_status, (B,), torch.int32)
+    _raise_on(lib().gdn_prune_draft(B, M, T, float(tau), _p(parents), _p(conf), _p(kept),
+                                    _p(new_parents), _p(count), _p(dev_status), _stream(stream)))

@@ -373,6 +373,42 @@ WORKLOADS = {
 
 
 # --------------------------------------------------------------------------
+# candidate trees with confidences, for draft pruning
+# --------------------------------------------------------------------------
+
+
+def candidate_tree(rng: np.random.Generator, top_k: int = 4, depth: int = 4,
+                   logit_std: float = 2.0):
+    """A synthetic drafter's candidate tree: every node above `depth` expands
+    its top_k continuations (BFS numbering, so parents precede children).  The
+    edge probabilities of one node's children are a softmax of N(0,
+    logit_std^2) logits over top_k draws (the top_k of a longer vocabulary are
+    stood in for by the draws themselves); a node's confidence is the
+    cumulative log-probability of its root path (root 0), so it never
+    increases from a node to its children.  Returns parents int32 [M] and
+    confidences float32 [M]."""
+    parents, conf, level = [-1], [0.0], [0]
+    i = 0
+    while i < len(parents):
+        if level[i] < depth:
+            z = rng.standard_normal(top_k) * logit_std
+            logp = z - np.logaddexp.reduce(z)
+            for j in np.argsort(-logp):  # most likely continuation first
+                parents.append(i)
+                conf.append(conf[i] + float(logp[j]))
+                level.append(level[i] + 1)
+        i += 1
+    return np.asarray(parents, np.int32), np.asarray(conf, np.float32)
+
+
+def candidate_batch(B: int, seed: int = 0, **kw):
+    """B candidate trees of the same shape: parents [B][M], conf [B][M]."""
+    rng = np.random.default_rng(seed)
+    trees = [candidate_tree(rng, **kw) for _ in range(B)]
+    return np.stack([t[0] for t in trees]), np.stack([t[1] for t in trees])
+
+
+# --------------------------------------------------------------------------
 # the decode loop over a stack of GDN layers
 # --------------------------------------------------------------------------
 

@@ -229,3 +229,14 @@ def test_replay_entry_points_validate_arguments():
     assert L.gdn_replay_commit(*sz, 0, P, P, P, P, P, P, None, None, None) == G.GDN_ERR_ARG
     assert "last_accepted is NULL" in G.gdn_last_error()
     assert L.gdn_replay_commit(*sz, 5, P, P, P, P, P, P, P, None, None) == G.GDN_ERR_ARG
+
+
+def test_prune_entry_point_validates_arguments():
+    L = G.lib()
+    P = ctypes.c_void_p(4096)
+    for B, M, T in ((1, 0, 4), (1, 1025, 4), (1, 10, 0), (1, 10, 65), (-1, 10, 4)):
+        assert L.gdn_prune_draft(B, M, T, 1.0, P, P, P, P, P, None, None) == G.GDN_ERR_SHAPE
+    for tau in (float("nan"), float("inf"), -0.5):
+        assert L.gdn_prune_draft(1, 10, 4, tau, P, P, P, P, P, None, None) == G.GDN_ERR_ARG
+    assert L.gdn_prune_draft(1, 10, 4, 1.0, P, None, P, P, P, None, None) == G.GDN_ERR_ARG
+    assert "conf is NULL" in G.gdn_last_error()
