@@ -225,4 +225,27 @@ __device__ inline f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_bf16: D[16x16] += A[16x16] * B[16x16], operands as the
+// bit patterns of 4 bf16 values:
+//   A: row i = l % 16, k = 4 * (l / 16) + e, e = 0..3
+//   B: col j = l % 16, k = 4 * (l / 16) + e
+//   D: row i = 4 * (l / 16) + r, col j = l % 16, r = 0..3
+// A lane's four D rows of one product are exactly its B operand for the same
+// 16-wide block of k in the next product, so a chain of products over a
+// 16-row blocking passes its intermediate from registers to registers.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+__device__ inline f32x4 mfma16x16x16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Split 4 floats into bf16 hi + lo operand bits (as split8).
+__device__ inline void split4(const f32x4& x, s16x4& hi, s16x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    hi[e] = __builtin_bit_cast(short, h);
+    lo[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)h));
+  }
+}
+
 }  // namespace gdn

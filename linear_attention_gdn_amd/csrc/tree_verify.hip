@@ -66,67 +66,9 @@
 // layer's gate in the epilogue and store them as bf16.
 #include <type_traits>
 
-#include "gdn_common.h"
+#include "tree_common.h"
 
 namespace gdn {
-
-__device__ inline void copy4e(float* d, const float* s) {
-  *reinterpret_cast<f32x4*>(d) = *reinterpret_cast<const f32x4*>(s);
-}
-
-// 8-element k-slice of a global row as MFMA operand(s): FP32 input is split
-// into bf16 hi + lo (used only on the FP32-input path).
-__device__ inline void frag_global(const float* p, bool ok, bf16x8& hi, bf16x8& lo) {
-  f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
-  if (ok) {
-    a = load4(p);
-    b = load4(p + 4);
-  }
-  split8(a, b, hi, lo);
-}
-
-__device__ inline bf16x8 lds_bf16x8(const bf16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
-}
-
-// Store 4 floats as bf16 hi (at p) and lo (at p + lo_off), 8 bytes each.
-__device__ inline void store_split4(bf16_t* p, int lo_off, const f32x4& x) {
-  u32x2 hi, lo;
-  float r[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const __bf16 hb = (__bf16)x[e];
-    r[e] = x[e] - (float)hb;
-    reinterpret_cast<__bf16*>(&hi)[e] = hb;
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) reinterpret_cast<__bf16*>(&lo)[e] = (__bf16)r[e];
-  *reinterpret_cast<u32x2*>(p) = hi;
-  *reinterpret_cast<u32x2*>(p + lo_off) = lo;
-}
-
-// Store one float as bf16 hi (at p) and lo (at p + lo_off).
-__device__ inline void store_split1(bf16_t* p, int lo_off, float x) {
-  const __bf16 hb = (__bf16)x;
-  reinterpret_cast<__bf16*>(p)[0] = hb;
-  reinterpret_cast<__bf16*>(p)[lo_off] = (__bf16)(x - (float)hb);
-}
-
-// Hardware dispatches workgroup ids round-robin over the 8 XCDs; renumber so
-// that consecutive logical ids (the tiles of one head) share an XCD.
-__device__ inline int xcd_logical_id(int bid, int nblocks) {
-  constexpr int kXcds = 8;
-  if (nblocks % kXcds) return bid;
-  return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
-}
-
-constexpr int kLd = kMaxNodes + 8;         // row stride (floats) of N x N matrices: 288 B
-constexpr int kLdH = kLd;                  // row stride (bf16) of split matrices: 144 B
-constexpr int kSplitLo = kMaxNodes * kLdH; // bf16 offset of the lo half of a split matrix
-constexpr int kQKRows = 2 * kMaxNodes;     // Q rows then K rows
-constexpr int kQKStride = kMaxDim + 8;     // bf16 elements per staged row
-constexpr int kQKBytes = kQKRows * kQKStride * 2;
-constexpr int kPathMax = 16;               // register-resident path solve up to this depth
 
 // SiLU output gate fused into the epilogue (the GATE variants, bf16 q/k/v
 // only): Y = bf16(O * SiLU(gate)) with gate row t at gate + (b N + t) ldg + h dv
@@ -150,96 +92,6 @@ struct TreeLds {
   static constexpr int kOffT = kOffQK + kMat;    // T (FP32) -> T (bf16 hi + lo)
   static constexpr int kBytes = kOffT + kMat;
 };
-
-// Row t of T on t's root path p_0..p_{d-1} = t, for d <= kPathMax:
-//   x_{d-1} = 1,  x_b = -sum_{a > b} x_a A[p_a][p_b]
-// solves x^T (I + A)|_path = e_t^T and T[t][p_b] = x_b.  Terms with a <= b or
-// a >= d vanish on their own (x_a not yet set, or the padding), so the sum is
-// unconditional and its LDS reads issue together.
-template <typename Put>
-__device__ inline void path_solve_registers(int t, uint64_t m, int d, const float* A, Put put) {
-  int p[kPathMax];
-  float x[kPathMax];
-  uint64_t mm = m;
-#pragma unroll
-  for (int a = 0; a < kPathMax; ++a) {
-    p[a] = mm ? __builtin_ctzll(mm) : t;
-    mm &= mm - 1ull;
-    x[a] = (a == d - 1) ? 1.f : 0.f;
-  }
-  put(t, 1.f);
-  for (int b = d - 2; b >= 0; --b) {
-    int pb = t;
-#pragma unroll
-    for (int a = 0; a < kPathMax; ++a)
-      if (a == b) pb = p[a];
-    float acc = 0.f;
-#pragma unroll
-    for (int a = 0; a < kPathMax; ++a) acc = fmaf(x[a], A[p[a] * kLd + pb], acc);
-    const float xb = -acc;
-    put(pb, xb);
-#pragma unroll
-    for (int a = 0; a < kPathMax; ++a)
-      if (a == b) x[a] = xb;
-  }
-}
-
-// The same for paths of at most P nodes with the path's P x P block of A read
-// into registers first (one round of LDS reads), then substituted in
-// registers: each step is a few FMAs instead of a wait on LDS.  The sums run
-// over a = b+1 .. P-1 in the order path_solve_registers uses (its terms with
-// a <= b are exact zeros), so every P gives the same bits.
-template <int P, typename Put>
-__device__ inline void path_solve_block(int t, uint64_t m, int d, const float* A, Put put) {
-  int p[P];
-  uint64_t mm = m;
-#pragma unroll
-  for (int a = 0; a < P; ++a) {
-    p[a] = mm ? __builtin_ctzll(mm) : t;
-    mm &= mm - 1ull;
-  }
-  float Ab[P][P];  // Ab[a][b] = A[p_a][p_b] for a > b (zero above the path)
-#pragma unroll
-  for (int a = 0; a < P; ++a)
-#pragma unroll
-    for (int b = 0; b < a; ++b) Ab[a][b] = A[p[a] * kLd + p[b]];
-  float x[P];
-#pragma unroll
-  for (int a = 0; a < P; ++a) x[a] = (a == d - 1) ? 1.f : 0.f;
-  // x_b = -sum_{a > b} x_a A[p_a][p_b], b = d-2 .. 0; entries a >= d have x_a = 0
-#pragma unroll
-  for (int b = P - 2; b >= 0; --b) {
-    float acc = 0.f;
-#pragma unroll
-    for (int a = b + 1; a < P; ++a) acc = fmaf(x[a], Ab[a][b], acc);
-    if (b < d - 1) x[b] = -acc;
-  }
-  put(t, 1.f);
-#pragma unroll
-  for (int b = 0; b < P; ++b)
-    if (b < d - 1) put(p[b], x[b]);
-}
-
-// v_mfma_f32_16x16x4f32: D[16x16] += A[16x4] * B[4x16] in FP32.  Lane l holds
-// A[l % 16][l / 16] and B[l / 16][l % 16]; D as for the bf16 form (row
-// 4 * (l / 16) + r, column l % 16).
-__device__ inline f32x4 mfma16x16x4f32(float a, float b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// Wait states after the last MFMA of a chain whose accumulators are read on
-// the far side of a branch.  The compiler pads a read of an MFMA result in
-// the same basic block, but not on a path that leaves the block right after
-// the MFMA: after the Y contraction, a wave that is last at the following
-// barrier passes it at once and, through the uniform branch behind it, read
-// the last accumulator register before the MFMA had written it (a few
-// outputs then varied from run to run in the last bits).  Two s_nop 7 give
-// 16 wait states on every path, more than any MFMA here needs.
-__device__ inline void mfma_drain() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 constexpr int kDlyChunk = 16;  // path nodes staged per round for the delayed commit
 
@@ -721,7 +573,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(fa[ks], kb[ct & 1][ks], acc);
-          mfma_drain();  // the stores below may sit behind a branch
+          mfma_drain(acc);  // the stores below may sit behind a branch
 #pragma unroll
           for (int r = 0; r < 4; ++r) dst[(16 * ra + 4 * lg + r) * kLd + 16 * ct + l16] = acc[r];
           if (two && ct <= rs) {  // compile-time after unrolling
@@ -729,7 +581,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
               acc2 = mfma16x16x32(fs[two ? ks : 0], kb[ct & 1][ks], acc2);
-            mfma_drain();
+            mfma_drain(acc2);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               dst[(16 * rs + 4 * lg + r) * kLd + 16 * ct + l16] = acc2[r];
@@ -945,125 +797,220 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
       }
     }
   }
-  mfma_drain();     // the Y accumulators are read after the barrier's branch
+  mfma_drain_all(yacc);  // the Y accumulators are read after the barrier's branch
   load_gate();      // consumed by the output step, after R and U'
   __syncthreads();  // Q/K reads and the solves are done: region A becomes R^T, U'^T
 
   // ---- 5. epilogue
-  // T is already split, except after an FP32 solve (deep paths): then its
-  // rows go to registers and are split in place after a barrier
-  float trow[EPT];
-  if (deep) {
-#pragma unroll
-    for (int x = 0; x < EPT; ++x) {
-      const int idx = tid + 256 * x;
-      trow[x] = Tl[(idx / NK) * kLd + idx % NK];
-    }
-  }
   // R = diag(beta) (V - diag(e^G) K S0^T) from the K-row accumulators
   f32x4 rv[MAXNB];
 #pragma unroll
   for (int j = 0; j < MAXNB; ++j) rv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto form_r = [&]() {
 #pragma unroll
-  for (int i = 0; i < MAXRT; ++i) {
-    const int rt = rb + WR * i;
-    if (rt >= NQT && rt < nrt) {
-      const int nb = rt - NQT;
-      const int j = i - iK0;  // this wave's j-th K tile: see the vreg loads
+    for (int i = 0; i < MAXRT; ++i) {
+      const int rt = rb + WR * i;
+      if (rt >= NQT && rt < nrt) {
+        const int nb = rt - NQT;
+        const int j = i - iK0;  // this wave's j-th K tile: see the vreg loads
 #pragma unroll
-      for (int jj = 0; jj < MAXNB; ++jj)
-        if (jj == j) {
+        for (int jj = 0; jj < MAXNB; ++jj)
+          if (jj == j) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * nb + 4 * lg + r;
-            const float vv = sok ? widen1(vreg[jj][r]) : 0.f;
-            rv[jj][r] = sbeta[t] * (vv - seG[t] * yacc[i][r]);
+            for (int r = 0; r < 4; ++r) {
+              const int t = 16 * nb + 4 * lg + r;
+              const float vv = sok ? widen1(vreg[jj][r]) : 0.f;
+              rv[jj][r] = sbeta[t] * (vv - seG[t] * yacc[i][r]);
+            }
           }
-        }
-    }
-  }
-  if (deep) {
-    __syncthreads();  // every FP32 row is read before the split rows overwrite it
-#pragma unroll
-    for (int x = 0; x < EPT; ++x) {
-      const int idx = tid + 256 * x;
-      store_split1(Ts + (idx / NK) * kLdH + idx % NK, kSplitLo, trow[x]);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < MAXNB; ++j) {
-    const int nb = rb + WR * (iK0 + j) - NQT;
-    if (nb >= 0 && nb < NQT) store_split4(RTs + ccol * kLdH + 16 * nb + 4 * lg, kRTLo, rv[j]);
-  }
-  if (NK > Np) {  // zero the k padding [Np, NK) of R^T and U'^T
-    constexpr int PAD = NK > Np ? NK - Np : 1;
-    for (int idx = tid; idx < L::kBVT * PAD; idx += 256) {
-      const int o = (idx / PAD) * kLdH + Np + idx % PAD;
-      RTs[o] = 0;
-      RTs[kRTLo + o] = 0;
-      UTs[o] = 0;
-      UTs[kRTLo + o] = 0;
-    }
-  }
-  __syncthreads();
-  // U' = T R  (A = T rows, B = R^T rows; three passes)
-#pragma unroll
-  for (int j = 0; j < MAXNB; ++j) {
-    const int nb = rb + WR * j;
-    if (nb < NQT) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NK / 32; ++ks) {
-        const int ao = (16 * nb + l16) * kLdH + 32 * ks + koff;
-        const int bo = ccol * kLdH + 32 * ks + koff;
-        const bf16x8 ah = lds_bf16x8(Ts + ao), al = lds_bf16x8(Ts + kSplitLo + ao);
-        const bf16x8 bh8 = lds_bf16x8(RTs + bo), bl8 = lds_bf16x8(RTs + kRTLo + bo);
-        acc = mfma16x16x32(ah, bh8, acc);
-        acc = mfma16x16x32(ah, bl8, acc);
-        acc = mfma16x16x32(al, bh8, acc);
       }
-      store_split4(UTs + ccol * kLdH + 16 * nb + 4 * lg, kRTLo, acc);
-      if (sok) {
+    }
+  };
+  // the node outputs of block nb (rows 16 nb + 4 lg + r, column srow), from
+  // the accumulator of O's block
+  auto store_out = [&](int nb, int j, const f32x4& acc) {
+    if (sok) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * nb + 4 * lg + r;
-          if (t < N) rec.up[((size_t)bh * N + t) * dv + srow] = acc[r];
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * nb + 4 * lg + r;
+        if (t < N) {
+          const size_t o = (((size_t)b * N + t) * H + h) * dv + srow;
+          if constexpr (GATE)
+            ga.Y[o] = to_bf16(acc[r] * silu(gvr[j][r]));  // gdn_gate_merge's arithmetic
+          else
+            out[o] = acc[r];
         }
       }
     }
-  }
-  __syncthreads();
-  // O = scale e^G Y_q + Attn U'   (Attn carries the scale).  Node block nb of
-  // this wave is Q row tile rt = nb = rb + WR*j, whose Y accumulator is yacc[j].
+  };
+  auto store_up = [&](int nb, const f32x4& acc) {
+    if (sok) {
 #pragma unroll
-  for (int j = 0; j < MAXNB; ++j) {
-    const int nb = rb + WR * j;
-    if (nb < NQT) {
-      f32x4 acc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = scale * seG[16 * nb + 4 * lg + r] * yacc[j][r];
-#pragma unroll
-      for (int ks = 0; ks < NK / 32; ++ks) {
-        const int ao = (16 * nb + l16) * kLdH + 32 * ks + koff;
-        const int bo = ccol * kLdH + 32 * ks + koff;
-        const bf16x8 ah = lds_bf16x8(Attn + ao), al = lds_bf16x8(Attn + kSplitLo + ao);
-        const bf16x8 bh8 = lds_bf16x8(UTs + bo), bl8 = lds_bf16x8(UTs + kRTLo + bo);
-        acc = mfma16x16x32(ah, bh8, acc);
-        acc = mfma16x16x32(ah, bl8, acc);
-        acc = mfma16x16x32(al, bh8, acc);
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * nb + 4 * lg + r;
+        if (t < N) rec.up[((size_t)bh * N + t) * dv + srow] = acc[r];
       }
-      if (sok) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * nb + 4 * lg + r;
-          if (t < N) {
-            const size_t o = (((size_t)b * N + t) * H + h) * dv + srow;
-            if constexpr (GATE)
-              ga.Y[o] = to_bf16(acc[r] * silu(gvr[j][r]));  // gdn_gate_merge's arithmetic
-            else
-              out[o] = acc[r];
-          }
+    }
+  };
+
+  if constexpr (WR == 1) {
+    // Every node block of this wave's 16 state rows is in its registers (the
+    // Q and K row tiles of all NQT blocks), so U' = T R and O = Attn U' run
+    // as chains of 16x16x16 products whose B operands are the previous
+    // result's accumulators, split into bf16 hi + lo: R and U' never leave
+    // the registers and no barrier separates the steps.  T and Attn are lower
+    // triangular (parents precede children), so block row i sums over the
+    // k blocks 0..i only.  A operands come from LDS: T split into bf16, or in
+    // FP32 after the blocked solve of a deep draft (split here).
+    form_r();
+    auto run = [&](auto deep_c) {
+      constexpr bool kDeep = decltype(deep_c)::value;
+      auto tfrag = [&](int i, int kb, s16x4& ah, s16x4& al) {
+        const int row = 16 * i + l16, col = 16 * kb + 4 * lg;
+        if constexpr (kDeep) {
+          split4(*reinterpret_cast<const f32x4*>(Tl + row * kLd + col), ah, al);
+        } else {
+          ah = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Ts + row * kLdH + col));
+          al = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Ts + kSplitLo + row * kLdH + col));
         }
+      };
+      auto afrag = [&](int i, int kb, s16x4& ah, s16x4& al) {
+        const int o = (16 * i + l16) * kLdH + 16 * kb + 4 * lg;
+        ah = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Attn + o));
+        al = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Attn + kSplitLo + o));
+      };
+      constexpr int NPAIR = NQT * (NQT + 1) / 2;  // lower-triangular blocks (i, kb <= i)
+      s16x4 th[NPAIR], tl[NPAIR];
+#pragma unroll
+      for (int i = 0, x = 0; i < NQT; ++i)
+#pragma unroll
+        for (int kb = 0; kb <= i; ++kb, ++x) tfrag(i, kb, th[x], tl[x]);
+      s16x4 rh[NQT], rl[NQT];
+#pragma unroll
+      for (int kb = 0; kb < NQT; ++kb) split4(rv[kb], rh[kb], rl[kb]);
+      f32x4 ua[NQT];
+#pragma unroll
+      for (int i = 0, x = 0; i < NQT; ++i) {
+        ua[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb <= i; ++kb, ++x) {
+          ua[i] = mfma16x16x16(th[x], rh[kb], ua[i]);
+          ua[i] = mfma16x16x16(th[x], rl[kb], ua[i]);
+          ua[i] = mfma16x16x16(tl[x], rh[kb], ua[i]);
+        }
+      }
+      s16x4 ah[NPAIR], al[NPAIR];  // Attn fragments, read while U' multiplies
+#pragma unroll
+      for (int i = 0, x = 0; i < NQT; ++i)
+#pragma unroll
+        for (int kb = 0; kb <= i; ++kb, ++x) afrag(i, kb, ah[x], al[x]);
+      mfma_drain_all(ua);  // U' is read below, partly under branches
+      s16x4 uh[NQT], ul[NQT];
+#pragma unroll
+      for (int kb = 0; kb < NQT; ++kb) split4(ua[kb], uh[kb], ul[kb]);
+      f32x4 oa[NQT];
+#pragma unroll
+      for (int i = 0, x = 0; i < NQT; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oa[i][r] = scale * seG[16 * i + 4 * lg + r] * yacc[i][r];
+#pragma unroll
+        for (int kb = 0; kb <= i; ++kb, ++x) {
+          oa[i] = mfma16x16x16(ah[x], uh[kb], oa[i]);
+          oa[i] = mfma16x16x16(ah[x], ul[kb], oa[i]);
+          oa[i] = mfma16x16x16(al[x], uh[kb], oa[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NQT; ++i) store_up(i, ua[i]);
+      mfma_drain_all(oa);
+#pragma unroll
+      for (int i = 0; i < NQT; ++i) store_out(i, i, oa[i]);
+    };
+    if (deep)
+      run(std::integral_constant<bool, true>{});
+    else
+      run(std::integral_constant<bool, false>{});
+  } else {
+    // Narrow tiles: the waves hold different node blocks of the same state
+    // rows, so R and U' pass through LDS (R^T, U'^T split into bf16 hi + lo).
+    // T is already split, except after an FP32 solve (deep paths): then its
+    // rows go to registers and are split in place after a barrier.
+    float trow[EPT];
+    if (deep) {
+#pragma unroll
+      for (int x = 0; x < EPT; ++x) {
+        const int idx = tid + 256 * x;
+        trow[x] = Tl[(idx / NK) * kLd + idx % NK];
+      }
+    }
+    form_r();
+    if (deep) {
+      __syncthreads();  // every FP32 row is read before the split rows overwrite it
+#pragma unroll
+      for (int x = 0; x < EPT; ++x) {
+        const int idx = tid + 256 * x;
+        store_split1(Ts + (idx / NK) * kLdH + idx % NK, kSplitLo, trow[x]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < MAXNB; ++j) {
+      const int nb = rb + WR * (iK0 + j) - NQT;
+      if (nb >= 0 && nb < NQT) store_split4(RTs + ccol * kLdH + 16 * nb + 4 * lg, kRTLo, rv[j]);
+    }
+    if (NK > Np) {  // zero the k padding [Np, NK) of R^T and U'^T
+      constexpr int PAD = NK > Np ? NK - Np : 1;
+      for (int idx = tid; idx < L::kBVT * PAD; idx += 256) {
+        const int o = (idx / PAD) * kLdH + Np + idx % PAD;
+        RTs[o] = 0;
+        RTs[kRTLo + o] = 0;
+        UTs[o] = 0;
+        UTs[kRTLo + o] = 0;
+      }
+    }
+    __syncthreads();
+    // U' = T R  (A = T rows, B = R^T rows; three passes)
+#pragma unroll
+    for (int j = 0; j < MAXNB; ++j) {
+      const int nb = rb + WR * j;
+      if (nb < NQT) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NK / 32; ++ks) {
+          const int ao = (16 * nb + l16) * kLdH + 32 * ks + koff;
+          const int bo = ccol * kLdH + 32 * ks + koff;
+          const bf16x8 ah = lds_bf16x8(Ts + ao), al = lds_bf16x8(Ts + kSplitLo + ao);
+          const bf16x8 bh8 = lds_bf16x8(RTs + bo), bl8 = lds_bf16x8(RTs + kRTLo + bo);
+          acc = mfma16x16x32(ah, bh8, acc);
+          acc = mfma16x16x32(ah, bl8, acc);
+          acc = mfma16x16x32(al, bh8, acc);
+        }
+        mfma_drain(acc);
+        store_split4(UTs + ccol * kLdH + 16 * nb + 4 * lg, kRTLo, acc);
+        store_up(nb, acc);
+      }
+    }
+    __syncthreads();
+    // O = scale e^G Y_q + Attn U'   (Attn carries the scale).  Node block nb of
+    // this wave is Q row tile rt = nb = rb + WR*j, whose Y accumulator is yacc[j].
+#pragma unroll
+    for (int j = 0; j < MAXNB; ++j) {
+      const int nb = rb + WR * j;
+      if (nb < NQT) {
+        f32x4 acc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = scale * seG[16 * nb + 4 * lg + r] * yacc[j][r];
+#pragma unroll
+        for (int ks = 0; ks < NK / 32; ++ks) {
+          const int ao = (16 * nb + l16) * kLdH + 32 * ks + koff;
+          const int bo = ccol * kLdH + 32 * ks + koff;
+          const bf16x8 ah = lds_bf16x8(Attn + ao), al = lds_bf16x8(Attn + kSplitLo + ao);
+          const bf16x8 bh8 = lds_bf16x8(UTs + bo), bl8 = lds_bf16x8(UTs + kRTLo + bo);
+          acc = mfma16x16x32(ah, bh8, acc);
+          acc = mfma16x16x32(ah, bl8, acc);
+          acc = mfma16x16x32(al, bh8, acc);
+        }
+        mfma_drain(acc);
+        store_out(nb, j, acc);
       }
     }
   }
@@ -1135,6 +1082,13 @@ hipError_t launch_bv(int B, int N, int H, int dk, int dv, float* S0, const int32
   }
 }
 
+hipError_t launch_tree_ws(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
+                          const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* beta,
+                          const float* g, float scale, float* out, const Record<bf16_t>& rec,
+                          uint64_t* mask_out, int32_t* dev_status, const void* prev_factors,
+                          int Npv, const int32_t* last, int32_t* commit_status,
+                          hipStream_t stream);
+
 template <typename T>
 hipError_t launch_tree_verify_t(int B, int N, int H, int dk, int dv, float* S0,
                                 const int32_t* parents, const T* q, const T* k, const T* v,
@@ -1150,9 +1104,17 @@ hipError_t launch_tree_verify_t(int B, int N, int H, int dk, int dv, float* S0,
   // 128 tiles of 16 rows finish as soon as 256 tiles of 8 and read Q and K
   // half as often (measured: 1-3% faster).
   const long heads = (long)B * H;
-  if (heads * ((dv + 63) / 64) >= 256)
+  if (heads * ((dv + 63) / 64) >= 256) {
+    // 64-row tiles with bf16 inputs: the split-role kernel (tree_verify_ws.hip)
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      if (!da.gate.gate)
+        return launch_tree_ws(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                              mask_out, dev_status, da.prev_factors, da.Np, da.last,
+                              da.commit_status, stream);
+    }
     return launch_bv<T, 64>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
                             mask_out, dev_status, da, dtype, stream);
+  }
   if (heads * ((dv + 31) / 32) >= 256)
     return launch_bv<T, 32>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
                             mask_out, dev_status, da, dtype, stream);

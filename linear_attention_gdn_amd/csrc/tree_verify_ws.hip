@@ -1,0 +1,709 @@
+// Tree verification with split wave roles (gfx950), for 64-row state tiles
+// and bf16 q/k/v: the form gdn_tree_verify and gdn_tree_verify_delayed take
+// when batch x heads fill the GPU with 64-row tiles (B H ceil(dv/64) >= 256).
+//
+// SpecLA review, "What carries the argument" and Figures, Figure 4 caption:
+// the same factorized verification as tree_verify.hip (one workgroup per
+// (sequence, head, 64 state rows); outputs, factor record and the delayed
+// commit identical in definition), organised for this GPU so that the long
+// read of the state tile overlaps the chain of small per-head steps instead
+// of preceding it.  512 threads, two roles of four waves each:
+//
+//   head waves (0-3): load and stage Q and K in LDS, build the topology
+//     (wave 0, pointer jumping), the Gram blocks Q K^T and K K^T (bf16 MFMA),
+//     the masked and scaled A and Attn, and T = (I + A)^{-1} (per-node path
+//     solves; blocked forward substitution for paths deeper than 16);
+//   state waves (4-7): wave 4 + c owns state rows 16 c .. 16 c + 15 of the
+//     tile.  They request their state rows and V at once (straight into MFMA
+//     operand registers), apply the previous draft's accepted path for the
+//     delayed form (each wave stages the path's k rows in its own LDS area,
+//     so no workgroup barrier is needed), run the contraction [Q; K] S0^T on
+//     bf16 MFMA (FP32 state split into bf16 hi + lo) while writing the
+//     committed rows back, form R = beta (V - e^G K S0^T), and after T is ready chain
+//     U' = T R and O = scale e^G Q S0^T + Attn U' through registers as
+//     16x16x16 products, the transposed products giving each lane four
+//     consecutive state rows of one node, stored as 16-byte vectors.
+//
+// The head waves synchronise among themselves through an LDS counter (the
+// state waves only wait for the staging and topology), and the two roles
+// meet at one workgroup barrier where T is complete.  Two waves share each
+// SIMD, so a head wave's scalar-heavy steps and a state wave's matrix
+// products issue side by side.
+#include <type_traits>
+
+#include "tree_common.h"
+
+namespace gdn {
+
+constexpr int kWsChunk = 16;  // accepted-path nodes staged per round by each state wave
+
+template <bool DLY>
+struct WsLds {
+  alignas(16) bf16_t qk[kQKRows * kQKStride];  // Q rows, then K rows (bf16, zero-padded)
+  alignas(16) float A[kMaxNodes * kLd];        // K K^T, then A (FP32)
+  alignas(16) float QK[kMaxNodes * kLd];       // Q K^T (FP32), then Attn (split bf16)
+  alignas(16) float T[kMaxNodes * kLd];        // T: zeros, then FP32 rows or split bf16
+  uint64_t mask[kMaxNodes];
+  float G[kMaxNodes], eG[kMaxNodes], beta[kMaxNodes];
+  int bad;
+  // delayed commit: the accepted path (root first) and its coefficients, and
+  // each state wave's staged k rows
+  int dnode[kMaxNodes];
+  float dc[kMaxNodes];
+  int dn;
+  float ds0;
+  int sync;  // arrivals at the head waves' own barriers
+  alignas(16) bf16_t dk[DLY ? 4 * kWsChunk * kMaxDim : 8];
+};
+
+// The head waves synchronise among themselves through an LDS counter, so the
+// state waves, busy issuing the loads of their state rows (which the memory
+// system accepts only as fast as it drains them), never hold them up: each
+// head wave completes its LDS operations, adds one, and waits until the
+// counter reaches `target` (four arrivals per round).  A state wave waits
+// without arriving.  One wave's LDS operations complete in order, and LDS is
+// one memory, so the data written before an arrival is visible to every wave
+// that has seen the count.  The wait is bounded (far beyond any real wait),
+// so a wave can never spin forever.
+__device__ inline void ws_arrive(int* ctr) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ inline void ws_wait(int* ctr, int target) {
+  for (int i = 0; i < (1 << 22); ++i) {
+    const int c = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(c) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+__device__ inline void ws_sync(int* ctr, int target) {
+  ws_arrive(ctr);
+  ws_wait(ctr, target);
+}
+
+template <int NQT, bool DLY>
+__global__ __launch_bounds__(512) void tree_ws_kernel(
+    int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
+    const int32_t* __restrict__ parents, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ beta,
+    const float* __restrict__ g, float scale, float* __restrict__ out, Record<bf16_t> rec,
+    uint64_t* __restrict__ mask_out, int32_t* __restrict__ dev_status, Record<bf16_t> prev,
+    int Npv, const int32_t* __restrict__ last_acc, int32_t* __restrict__ commit_status) {
+  constexpr int BV = 64;
+  constexpr int Np = 16 * NQT;
+  constexpr int NK = 32 * ((NQT + 1) / 2);  // k extent of the Gram tiles' mask pass
+  constexpr int EPT = Np * NK / 256;        // mask-pass entries per head thread
+  constexpr int KS = kMaxDim / 32;          // 32-wide k steps of the contraction
+
+  __shared__ WsLds<DLY> sm;
+  bf16_t* const QKs = sm.qk;
+  float* const KK = sm.A;
+  float* const QK = sm.QK;
+  bf16_t* const Attn = reinterpret_cast<bf16_t*>(sm.QK);
+  float* const Tl = sm.T;
+  bf16_t* const Ts = reinterpret_cast<bf16_t*>(sm.T);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool head = wave < 4;  // uniform per wave
+  const int l16 = lane & 15;
+  const int lg = lane >> 4;
+  const int koff = 8 * lg;
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int tile = lid % ntiles;
+  const int bh = lid / ntiles;
+  const int b = bh / H;
+  const int h = bh % H;
+  const int r0 = tile * BV;
+  // state waves: rows 16 cj .. 16 cj + 15 of the tile; lane l16's row (as an
+  // MFMA operand) and the four rows 16 cj + 4 lg .. + 3 (as a transposed result)
+  const int cj = wave & 3;
+  const int srow = r0 + 16 * cj + l16;
+  const bool sok = srow < dv;
+  const int srow4 = r0 + 16 * cj + 4 * lg;
+  const bool sok4 = srow4 < dv;  // dv % 4 == 0: all four rows or none
+
+  if (tid == 0) sm.sync = 0;
+  __syncthreads();  // the counter is zero before any wave arrives
+  // the head waves carry the chain of dependent per-head steps: their
+  // instructions go first when both roles compete for a SIMD or the memory
+  // pipeline
+  if (head) __builtin_amdgcn_s_setprio(3);
+
+  // ---- 0. loads.  Head waves: Q/K (staged in LDS), parents, g, beta (and the
+  // previous record's masks and G).  State waves: the state rows and V.
+  constexpr int qk_cpr = kMaxDim / 8;  // 16-byte chunks per staged row
+  constexpr int qk_total = 2 * Np * qk_cpr;
+  constexpr int QKB = qk_total / 256;  // chunks per head thread
+  static_assert(qk_total % 256 == 0, "every head thread stages QKB chunks");
+  f32x4 Sraw[KS][2];
+  bf16_t vreg[NQT][4];
+  if (head) {
+    u32x4 qkw[QKB];
+#pragma unroll
+    for (int x = 0; x < QKB; ++x) {
+      const int idx = tid + 256 * x;
+      const int r = idx / qk_cpr;
+      const bool isq = r < Np;
+      const int t = clampi(isq ? r : r - Np, N - 1);
+      const int c8 = clampi(8 * (idx % qk_cpr), dk - 8);
+      qkw[x] = *reinterpret_cast<const u32x4*>((isq ? q : k) + (((size_t)b * N + t) * H + h) * dk + c8);
+    }
+    const int tn = clampi(lane, N - 1);
+    const int pl = parents[(size_t)b * N + tn];
+    const float gl = g[((size_t)b * N + tn) * H + h];
+    const float bl = beta[((size_t)b * N + tn) * H + h];
+    int last_v = -1;
+    uint64_t pmask_l = 0;
+    float pG_l = 0.f;
+    if (DLY) {
+      last_v = last_acc[b];
+      const int tj = clampi(lane, Npv - 1);
+      pmask_l = prev.mask[(size_t)b * Npv + tj];
+      pG_l = prev.G[(size_t)bh * Npv + tj];
+    }
+#pragma unroll
+    for (int x = 0; x < QKB; ++x) {  // no branch: a load under one is waited for at once
+      const int idx = tid + 256 * x;
+      const int r = idx / qk_cpr;
+      const int t = r < Np ? r : r - Np;
+      const int c8 = 8 * (idx % qk_cpr);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
+    }
+    for (int idx = tid; idx < kMaxNodes * kLd / 4; idx += 256)  // T starts as zeros
+      reinterpret_cast<f32x4*>(Tl)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // 1. wave 0: parents -> validation, ancestor-or-self masks and G
+    if (wave == 0) {
+      const int t = lane;
+      const int p = t < N ? pl : -1;
+      const bool bad = t < N && (p < -1 || p >= t);
+      const uint64_t anybad = __ballot(bad);
+      uint64_t m = t < N ? (1ull << t) : 0ull;
+      float G = t < N ? gl : 0.f;
+      int a = (t < N && !bad) ? p : -1;
+      for (int r = 0; r < 6; ++r) {  // 2^6 = 64 >= path length
+        if (__ballot(a >= 0) == 0ull) break;  // uniform: every path is complete
+        const int src = a >= 0 ? a : t;
+        const uint64_t ma = __shfl(m, src);
+        const float Ga = __shfl(G, src);
+        const int aa = __shfl(a, src);
+        if (a >= 0) {
+          m |= ma;
+          G += Ga;
+          a = aa;
+        }
+      }
+      if (anybad) m = 0ull;
+      sm.mask[t] = m;
+      sm.G[t] = G;
+      sm.eG[t] = expf(G);
+      sm.beta[t] = t < N ? bl : 0.f;
+      if (t == 0) sm.bad = anybad != 0ull;
+      if (tile == 0 && t < N) {
+        rec.G[(size_t)bh * N + t] = anybad ? 0.f : G;
+        if (h == 0) {
+          rec.parents[(size_t)b * N + t] = pl;
+          rec.mask[(size_t)b * N + t] = m;
+          if (mask_out) mask_out[(size_t)b * N + t] = m;
+        }
+      }
+      if (tile == 0 && t == 0 && h == 0 && dev_status)
+        dev_status[b] = anybad ? GDN_ERR_TOPOLOGY : GDN_OK;
+      if (DLY) {  // the previous draft's accepted path, root first, and its coefficients
+        const int lst = __builtin_amdgcn_readfirstlane(last_v);
+        const bool in_rng = lst >= 0 && lst < Npv;
+        const int lc = in_rng ? lst : 0;
+        const uint64_t valid = Npv >= 64 ? ~0ull : ((1ull << Npv) - 1ull);
+        const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)pmask_l, lc);
+        const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(pmask_l >> 32), lc);
+        const uint64_t pm = in_rng ? ((((uint64_t)mhi << 32) | mlo) & valid) : 0ull;
+        const bool okp = in_rng && ((pm >> lst) & 1ull);
+        const float Glast =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pG_l), lc));
+        if (okp && ((pm >> t) & 1ull)) {
+          const int pos = __popcll(pm & ((1ull << t) - 1ull));
+          sm.dnode[pos] = t;
+          sm.dc[pos] = expf(Glast - pG_l);  // the commit kernel's coefficient
+        }
+        if (t == 0) {
+          sm.dn = okp ? __popcll(pm) : 0;
+          sm.ds0 = expf(Glast);
+          if (tile == 0 && h == 0 && commit_status)
+            commit_status[b] = (lst == -1 || okp) ? GDN_OK : GDN_ERR_TOPOLOGY;
+        }
+      }
+    }
+  } else {
+    const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kk = clampi(32 * ks + koff, dk - 8);
+      Sraw[ks][0] = load4(sptr + kk);
+      Sraw[ks][1] = load4(sptr + kk + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NQT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = clampi(16 * j + 4 * lg + r, N - 1);
+        vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
+      }
+  }
+  if (head)
+    ws_sync(&sm.sync, 4);  // staged Q/K, T zeroed, topology, path
+  else
+    ws_wait(&sm.sync, 4);
+
+  // the previous draft's accepted path applied to this state wave's rows in
+  // the commit kernel's operation order (scale by e^{G_last}, then one fmaf
+  // per path node in path order), then the committed rows written back
+  auto dly_commit = [&]() {
+    const int dn = sm.dn;
+    if (dn == 0) return;  // uniform
+    // every state register is consumed here, before the first write-back
+    // store, so no later wait on a load also waits for the stores
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) pin_vgpr(Sraw[ks][0]), pin_vgpr(Sraw[ks][1]);
+    const float s0 = sm.ds0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Sraw[ks][0][e] = Sraw[ks][0][e] * s0;
+        Sraw[ks][1][e] = Sraw[ks][1][e] * s0;
+      }
+    bf16_t* kst = sm.dk + (wave - 4) * (kWsChunk * kMaxDim);
+    constexpr int KR = kWsChunk * kMaxDim / 8 / 64;  // 16-byte chunks per lane and round
+    for (int c0 = 0; c0 < dn; c0 += kWsChunk) {  // uniform
+      u32x4 kr[KR];
+#pragma unroll
+      for (int x = 0; x < KR; ++x) {
+        const int idx = lane + 64 * x;
+        const int j = idx / (kMaxDim / 8);
+        const int col = clampi(8 * (idx % (kMaxDim / 8)), dk - 8);
+        const int nd = sm.dnode[clampi(c0 + j, dn - 1)];
+        kr[x] = *reinterpret_cast<const u32x4*>(prev.K + ((size_t)bh * Npv + nd) * dk + col);
+      }
+      float cu[kWsChunk];
+#pragma unroll
+      for (int j = 0; j < kWsChunk; ++j) {
+        const int jc = clampi(c0 + j, dn - 1);
+        cu[j] = sm.dc[jc] * prev.up[((size_t)bh * Npv + sm.dnode[jc]) * dv + clampi(srow, dv - 1)];
+      }
+      // this wave's reads of the previous round precede these writes (one
+      // wave's LDS operations complete in order)
+#pragma unroll
+      for (int x = 0; x < KR; ++x) {
+        const int idx = lane + 64 * x;
+        const int c8 = 8 * (idx % (kMaxDim / 8));
+        *reinterpret_cast<u32x4*>(kst + (idx / (kMaxDim / 8)) * kMaxDim + c8) = kr[x];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
+      const int nc = __builtin_amdgcn_readfirstlane(dn - c0 < kWsChunk ? dn - c0 : kWsChunk);
+#pragma unroll
+      for (int jj = 0; jj < kWsChunk; ++jj) {
+        if (jj < nc) {  // uniform
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(kst + jj * kMaxDim + 32 * ks + koff);
+            const f32x4 k0 = widen4(u32x2{w.x, w.y});
+            const f32x4 k1 = widen4(u32x2{w.z, w.w});
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              Sraw[ks][0][e] = fmaf(cu[jj], k0[e], Sraw[ks][0][e]);
+              Sraw[ks][1][e] = fmaf(cu[jj], k1[e], Sraw[ks][1][e]);
+            }
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next round's writes
+    }
+  };
+  // write-back of the committed columns 32 ks + 8 lg .. + 7 of this lane's row
+  auto dly_store = [&](int ks) {
+    const int col = 32 * ks + koff;
+    if (sok && col < dk) {
+      float* wp = S0 + ((size_t)bh * dv + srow) * dk + col;
+      *reinterpret_cast<f32x4*>(wp) = Sraw[ks][0];
+      *reinterpret_cast<f32x4*>(wp + 4) = Sraw[ks][1];
+    }
+  };
+
+  if (sm.bad) {  // uniform: zero this tile's outputs (a delayed commit still applies)
+    if (!head) {
+      if (DLY && sm.dn > 0) {
+        dly_commit();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dly_store(ks);
+      }
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int t0 = 0; t0 < N; t0 += 16) {
+        const int t = t0 + l16;
+        if (t < N && sok4) {
+          *reinterpret_cast<f32x4*>(out + (((size_t)b * N + t) * H + h) * dv + srow4) = z;
+          *reinterpret_cast<f32x4*>(rec.up + ((size_t)bh * N + t) * dv + srow4) = z;
+        }
+      }
+    }
+    return;
+  }
+  // every wave reads the depths, so the choice of solve is uniform
+  const bool deep =
+      __ballot(lane < N && __popcll(sm.mask[lane < N ? lane : 0]) > kPathMax) != 0ull;
+
+  if (head) {
+    if (tile == 0) {  // factor record: this head's k rows (the staged bits)
+      constexpr int kC8 = kMaxDim / 8;
+      constexpr int RKC = Np * kC8 / 256;
+      u32x4 kc[RKC];
+#pragma unroll
+      for (int x = 0; x < RKC; ++x) {
+        const int idx = tid + 256 * x;
+        kc[x] = *reinterpret_cast<const u32x4*>(QKs + (Np + idx / kC8) * kQKStride + 8 * (idx % kC8));
+      }
+#pragma unroll
+      for (int x = 0; x < RKC; ++x) {
+        const int idx = tid + 256 * x;
+        const int t = idx / kC8;
+        const int c8 = 8 * (idx % kC8);
+        if (t < N && c8 < dk)
+          *reinterpret_cast<u32x4*>(rec.K + ((size_t)bh * N + t) * dk + c8) = kc[x];
+      }
+    }
+    // 2. Gram blocks Q K^T and K K^T, lower-triangle tiles: wave w takes row
+    // block pair w / 2 of Q (w even) or of K (w odd), as in tree_verify.hip
+    auto gram_job = [&](auto wc) {
+      constexpr int Wc = decltype(wc)::value;
+      constexpr int npairs = (NQT + 1) / 2;
+      if constexpr (Wc < 2 * npairs) {
+        constexpr bool isq = Wc % 2 == 0;
+        constexpr int ra = NQT - 1 - Wc / 2;
+        constexpr int rs = Wc / 2;
+        constexpr bool two = rs < ra;
+        const bf16_t* rows = QKs + (isq ? 0 : Np) * kQKStride;
+        float* dst = isq ? QK : KK;
+        bf16x8 fa[KS], fs[two ? KS : 1], kb[2][KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          fa[ks] = lds_bf16x8(rows + (16 * ra + l16) * kQKStride + 32 * ks + koff);
+          if constexpr (two) fs[ks] = lds_bf16x8(rows + (16 * rs + l16) * kQKStride + 32 * ks + koff);
+        }
+        auto kload = [&](int ct, bf16x8 (&dstf)[KS]) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            dstf[ks] = lds_bf16x8(QKs + (Np + 16 * ct + l16) * kQKStride + 32 * ks + koff);
+        };
+        kload(0, kb[0]);
+#pragma unroll
+        for (int ct = 0; ct <= ra; ++ct) {
+          if (ct + 1 <= ra) kload(ct + 1, kb[(ct + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(fa[ks], kb[ct & 1][ks], acc);
+          mfma_drain(acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[(16 * ra + 4 * lg + r) * kLd + 16 * ct + l16] = acc[r];
+          if (two && ct <= rs) {
+            f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              acc2 = mfma16x16x32(fs[two ? ks : 0], kb[ct & 1][ks], acc2);
+            mfma_drain(acc2);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(16 * rs + 4 * lg + r) * kLd + 16 * ct + l16] = acc2[r];
+          }
+        }
+      }
+    };
+    switch (__builtin_amdgcn_readfirstlane(wave)) {
+      case 0: gram_job(std::integral_constant<int, 0>{}); break;
+      case 1: gram_job(std::integral_constant<int, 1>{}); break;
+      case 2: gram_job(std::integral_constant<int, 2>{}); break;
+      default: gram_job(std::integral_constant<int, 3>{}); break;
+    }
+  }
+  if (head) ws_sync(&sm.sync, 8);  // Gram blocks
+
+  // 3. A (FP32, in place of K K^T) and Attn (split bf16, in place of Q K^T),
+  // exact zeros off the masks (head threads; every operand read first)
+  float attn[EPT];
+  if (head) {
+    float kkv[EPT], qkv[EPT], gt[EPT], gj[EPT], bt[EPT];
+    uint64_t mt[EPT];
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int idx = tid + 256 * x;
+      const int t = idx / NK;
+      const int j = idx % NK;
+      mt[x] = sm.mask[t];
+      gt[x] = sm.G[t];
+      gj[x] = sm.G[j];
+      bt[x] = sm.beta[t];
+      kkv[x] = KK[t * kLd + j];
+      qkv[x] = QK[t * kLd + j];
+    }
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int idx = tid + 256 * x;
+      const int t = idx / NK;
+      const int j = idx % NK;
+      const bool on = (mt[x] >> j) & 1ull;
+      const float dec = __expf(gt[x] - gj[x]);
+      KK[t * kLd + j] = (on && j != t) ? bt[x] * dec * kkv[x] : 0.f;
+      attn[x] = on ? scale * dec * qkv[x] : 0.f;
+    }
+  }
+  if (head) ws_sync(&sm.sync, 12);  // every Q K^T entry is read before Attn overwrites it
+  if (head) {
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int idx = tid + 256 * x;
+      store_split1(Attn + (idx / NK) * kLdH + idx % NK, kSplitLo, attn[x]);
+    }
+    // rows of T on root paths, one lane per node (wave 0): split bf16, or FP32
+    // diagonal blocks for a deep draft
+    if (tid < N) {
+      const int t = tid;
+      const uint64_t m = sm.mask[t];
+      const int d = __popcll(m);
+      auto put_split = [&](int j, float x) { store_split1(Ts + t * kLdH + j, kSplitLo, x); };
+      auto put_f32 = [&](int j, float x) { Tl[t * kLd + j] = x; };
+      if (deep) {
+        const uint64_t mb = m & (0xFFFFull << (16 * (t / 16)));
+        path_solve_registers(t, mb, __popcll(mb), KK, put_f32);
+      } else if (__ballot(d > 8) == 0ull) {
+        path_solve_block<8>(t, m, d, KK, put_split);
+      } else if (__ballot(d > 12) == 0ull) {
+        path_solve_block<12>(t, m, d, KK, put_split);
+      } else {
+        path_solve_registers(t, m, d, KK, put_split);
+      }
+    }
+  }
+
+  // state waves: delayed commit, contraction, R
+  f32x4 yacc[2 * NQT];
+  f32x4 rv[NQT];
+  if (!head) {
+    if (DLY) dly_commit();
+#pragma unroll
+    for (int i = 0; i < 2 * NQT; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // 4. Y: the K row tiles as K S0^T (rows = nodes, as the B operand of
+    // T R), the Q row tiles transposed as S0 Q^T (each lane then holds four
+    // consecutive state rows of one node, as O^T needs).  The next k step's
+    // A fragments are read while this one multiplies.
+    bf16x8 afr[2][2 * NQT];
+    auto aload = [&](int ks, bf16x8 (&a)[2 * NQT]) {
+#pragma unroll
+      for (int i = 0; i < 2 * NQT; ++i)
+        a[i] = lds_bf16x8(QKs + (16 * i + l16) * kQKStride + 32 * ks + koff);
+    };
+    // With a delayed commit, the committed columns of each k step are written
+    // back as the step is contracted: the memory system accepts the stores
+    // only as fast as it drains them, and the matrix products of the previous
+    // steps keep running meanwhile.
+    const bool wb = DLY && sm.dn > 0;  // uniform
+    aload(0, afr[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {  // zero-padded past dk: no branch
+      if (wb) dly_store(ks);
+      if (ks + 1 < KS) aload(ks + 1, afr[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 bhi, blo;
+      const bool okk = sok && 32 * ks + koff < dk;
+      split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi, blo);
+#pragma unroll
+      for (int i = 0; i < 2 * NQT; ++i) {
+        if (i < NQT) {
+          yacc[i] = mfma16x16x32(bhi, afr[ks & 1][i], yacc[i]);
+          yacc[i] = mfma16x16x32(blo, afr[ks & 1][i], yacc[i]);
+        } else {
+          yacc[i] = mfma16x16x32(afr[ks & 1][i], bhi, yacc[i]);
+          yacc[i] = mfma16x16x32(afr[ks & 1][i], blo, yacc[i]);
+        }
+      }
+    }
+    mfma_drain_all(yacc);
+    // R = diag(beta) (V - diag(e^G) K S0^T): lane (row srow, lg) holds nodes
+    // 16 nb + 4 lg + r
+#pragma unroll
+    for (int nb = 0; nb < NQT; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * nb + 4 * lg + r;
+        const float vv = sok ? widen1(vreg[nb][r]) : 0.f;
+        rv[nb][r] = sm.beta[t] * (vv - sm.eG[t] * yacc[NQT + nb][r]);
+      }
+  }
+
+  if (head && deep) {  // uniform: blocked forward substitution, as in tree_verify.hip
+    int tgt = 12;
+    ws_sync(&sm.sync, tgt += 4);  // the diagonal blocks are in T
+#pragma unroll
+    for (int i = 1; i < NQT; ++i) {
+      const int j = wave;
+      float* blk = Tl + (16 * i) * kLd + 16 * j;
+      if (j < i) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = j; kb < i; ++kb)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            x = mfma16x16x4f32(KK[(16 * i + l16) * kLd + 16 * kb + 4 * c + lg],
+                               Tl[(16 * kb + 4 * c + lg) * kLd + 16 * j + l16], x);
+        mfma_drain(x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) blk[(4 * lg + r) * kLd + l16] = x[r];
+      }
+      ws_sync(&sm.sync, tgt += 4);
+      if (j < i) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          y = mfma16x16x4f32(Tl[(16 * i + l16) * kLd + 16 * i + 4 * c + lg],
+                             blk[(4 * c + lg) * kLd + l16], y);
+        mfma_drain(y);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) blk[(4 * lg + r) * kLd + l16] = -y[r];
+      }
+      ws_sync(&sm.sync, tgt += 4);  // block row i is complete before row i + 1 reads it
+    }
+  }
+  __syncthreads();  // T and Attn are complete; the only barrier of both roles after the start
+  if (head) return;
+
+  // ---- 5. epilogue (state waves): U' = T R, its transpose for the record,
+  // O^T = (Attn U')^T + scale e^G (S0 Q^T); T and Attn are lower triangular,
+  // so block row i sums over k blocks 0..i
+  auto run = [&](auto deep_c) {
+    constexpr bool kDeep = decltype(deep_c)::value;
+    constexpr int NPAIR = NQT * (NQT + 1) / 2;
+    s16x4 th[NPAIR], tl[NPAIR];
+#pragma unroll
+    for (int i = 0, x = 0; i < NQT; ++i)
+#pragma unroll
+      for (int kb = 0; kb <= i; ++kb, ++x) {
+        const int row = 16 * i + l16, col = 16 * kb + 4 * lg;
+        if constexpr (kDeep) {
+          split4(*reinterpret_cast<const f32x4*>(Tl + row * kLd + col), th[x], tl[x]);
+        } else {
+          th[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Ts + row * kLdH + col));
+          tl[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Ts + kSplitLo + row * kLdH + col));
+        }
+      }
+    s16x4 rh[NQT], rl[NQT];
+#pragma unroll
+    for (int kb = 0; kb < NQT; ++kb) split4(rv[kb], rh[kb], rl[kb]);
+    f32x4 ua[NQT], ut[NQT];
+#pragma unroll
+    for (int i = 0, x = 0; i < NQT; ++i) {
+      ua[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ut[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb <= i; ++kb, ++x) {
+        ua[i] = mfma16x16x16(th[x], rh[kb], ua[i]);
+        ua[i] = mfma16x16x16(th[x], rl[kb], ua[i]);
+        ua[i] = mfma16x16x16(tl[x], rh[kb], ua[i]);
+        ut[i] = mfma16x16x16(rh[kb], th[x], ut[i]);
+        ut[i] = mfma16x16x16(rl[kb], th[x], ut[i]);
+        ut[i] = mfma16x16x16(rh[kb], tl[x], ut[i]);
+      }
+    }
+    s16x4 ah[NPAIR], al[NPAIR];  // Attn fragments, read while U' multiplies
+#pragma unroll
+    for (int i = 0, x = 0; i < NQT; ++i)
+#pragma unroll
+      for (int kb = 0; kb <= i; ++kb, ++x) {
+        const int o = (16 * i + l16) * kLdH + 16 * kb + 4 * lg;
+        ah[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Attn + o));
+        al[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Attn + kSplitLo + o));
+      }
+    mfma_drain_all(ua);
+    s16x4 uh[NQT], ul[NQT];
+#pragma unroll
+    for (int kb = 0; kb < NQT; ++kb) split4(ua[kb], uh[kb], ul[kb]);
+    f32x4 ot[NQT];
+#pragma unroll
+    for (int i = 0, x = 0; i < NQT; ++i) {
+      const float se = scale * sm.eG[16 * i + l16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ot[i][r] = se * yacc[i][r];
+#pragma unroll
+      for (int kb = 0; kb <= i; ++kb, ++x) {
+        ot[i] = mfma16x16x16(uh[kb], ah[x], ot[i]);
+        ot[i] = mfma16x16x16(ul[kb], ah[x], ot[i]);
+        ot[i] = mfma16x16x16(uh[kb], al[x], ot[i]);
+      }
+    }
+    mfma_drain_all(ut);
+#pragma unroll
+    for (int i = 0; i < NQT; ++i) {
+      const int t = 16 * i + l16;
+      if (t < N && sok4)
+        *reinterpret_cast<f32x4*>(rec.up + ((size_t)bh * N + t) * dv + srow4) = ut[i];
+    }
+    mfma_drain_all(ot);
+#pragma unroll
+    for (int i = 0; i < NQT; ++i) {
+      const int t = 16 * i + l16;
+      if (t < N && sok4)
+        *reinterpret_cast<f32x4*>(out + (((size_t)b * N + t) * H + h) * dv + srow4) = ot[i];
+    }
+  };
+  if (deep)
+    run(std::integral_constant<bool, true>{});
+  else
+    run(std::integral_constant<bool, false>{});
+}
+
+template <int NQT>
+hipError_t launch_ws_n(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
+                       const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* beta,
+                       const float* g, float scale, float* out, const Record<bf16_t>& rec,
+                       uint64_t* mask_out, int32_t* dev_status, const void* prev_factors,
+                       int Npv, const int32_t* last, int32_t* commit_status, hipStream_t stream) {
+  const int ntiles = (dv + 63) / 64;
+  const long grid = (long)B * H * ntiles;
+  if (prev_factors) {
+    const RecordLayout Lp = record_layout(B, Npv, H, dk, dv, GDN_BF16);
+    const Record<bf16_t> prev = record_views<bf16_t>(const_cast<void*>(prev_factors), Lp);
+    hipLaunchKernelGGL((tree_ws_kernel<NQT, true>), dim3((unsigned)grid), dim3(512), 0, stream, N,
+                       H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out, rec, mask_out,
+                       dev_status, prev, Npv, last, commit_status);
+  } else {
+    hipLaunchKernelGGL((tree_ws_kernel<NQT, false>), dim3((unsigned)grid), dim3(512), 0, stream,
+                       N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out, rec,
+                       mask_out, dev_status, Record<bf16_t>{}, 1, nullptr, nullptr);
+  }
+  return hipGetLastError();
+}
+
+// The split-role form for 64-row tiles with bf16 inputs (the caller has
+// chosen 64-row tiles and checked every size).
+hipError_t launch_tree_ws(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
+                          const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* beta,
+                          const float* g, float scale, float* out, const Record<bf16_t>& rec,
+                          uint64_t* mask_out, int32_t* dev_status, const void* prev_factors,
+                          int Npv, const int32_t* last, int32_t* commit_status,
+                          hipStream_t stream) {
+  switch ((N + 15) / 16) {
+    case 1:
+      return launch_ws_n<1>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, prev_factors, Npv, last, commit_status, stream);
+    case 2:
+      return launch_ws_n<2>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, prev_factors, Npv, last, commit_status, stream);
+    case 3:
+      return launch_ws_n<3>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, prev_factors, Npv, last, commit_status, stream);
+    default:
+      return launch_ws_n<4>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, prev_factors, Npv, last, commit_status, stream);
+  }
+}
+
+}  // namespace gdn

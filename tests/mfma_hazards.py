@@ -12,10 +12,13 @@ wait states have passed.  An MFMA that takes the destination as its
 accumulator input is not counted as a reader (the hardware forwards an
 accumulator from one MFMA to the next); its A and B operands are.
 
-The required count is taken from the compiler itself: the smallest number of
-wait states it leaves between an MFMA and a read of its result inside one
-basic block (where its own hazard rule applies).  Every path must leave at
-least that many.
+The required count is taken from the compiler itself.  A probe kernel per
+MFMA opcode (``probe_source``) reads the result right after the instruction,
+so the compiler pads that read with exactly the wait states its hazard rule
+asks for (``probed_requirements``).  Without a probe, the fallback is the
+smallest number of wait states the compiler leaves between an MFMA and a read
+of its result inside one basic block of the checked code, which can only
+overstate the rule.  Every path must leave at least the required count.
 """
 
 from __future__ import annotations
@@ -223,3 +226,45 @@ def device_asm(src: str, flags: List[str], hipcc: str) -> str:
     """gfx950 assembly of one HIP source, built with the library's flags."""
     cmd = [hipcc, *[f for f in flags if f != "-fPIC"], "--cuda-device-only", "-S", src, "-o", "-"]
     return subprocess.run(cmd, check=True, capture_output=True, text=True).stdout
+
+
+# One probe kernel per MFMA opcode the library uses: operand type and builtin.
+PROBES = {
+    "v_mfma_f32_16x16x32_bf16": ("bf16x8", "__builtin_amdgcn_mfma_f32_16x16x32_bf16"),
+    "v_mfma_f32_16x16x16_bf16": ("s16x4", "__builtin_amdgcn_mfma_f32_16x16x16bf16_1k"),
+    "v_mfma_f32_16x16x4_f32": ("float", "__builtin_amdgcn_mfma_f32_16x16x4f32"),
+}
+
+
+def probe_source() -> str:
+    """A HIP source with one kernel per probed opcode whose result is read by
+    the next instruction."""
+    lines = [
+        "#include <hip/hip_runtime.h>",
+        "typedef __attribute__((ext_vector_type(4))) float f32x4;",
+        "typedef __attribute__((ext_vector_type(4))) short s16x4;",
+        "typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;",
+    ]
+    for n, (ty, builtin) in enumerate(PROBES.values()):
+        lines += [
+            f"__global__ void probe{n}(const {ty}* a, const {ty}* b, float* o) {{",
+            "  f32x4 c = {0.f, 0.f, 0.f, 0.f};",
+            f"  c = {builtin}(a[threadIdx.x], b[threadIdx.x], c, 0, 0, 0);",
+            "  o[threadIdx.x] = c[0] + 1.0f;",
+            "}",
+        ]
+    return "\n".join(lines) + "\n"
+
+
+def probed_requirements(flags: List[str], hipcc: str, workdir: str) -> Dict[str, int]:
+    """Wait states the compiler leaves before reading each probed MFMA's
+    result in straight-line code."""
+    src = os.path.join(workdir, "mfma_probe.hip")
+    with open(src, "w") as f:
+        f.write(probe_source())
+    req: Dict[str, int] = {}
+    for k in parse_kernels(device_asm(src, flags, hipcc)):
+        for op, w in same_block_distances(k):
+            req[op] = min(req.get(op, w), w)
+    return req
+

@@ -140,6 +140,10 @@ SHAPES = [
     (2, 48, 8, 256, 256, "bf16", "spine"),
     (8, 64, 8, 256, 256, "bf16", "spine"),
     (1, 40, 3, 72, 52, "f32", "chain"),
+    # 64-row state tiles (batch x heads >= 256 tiles): products chained in
+    # registers, ragged dv (a partial last tile) and N
+    (32, 37, 8, 72, 100, "bf16", "random"),
+    (16, 24, 16, 40, 68, "f32", "spine"),
 ]
 
 
@@ -176,15 +180,21 @@ def test_runs_are_bitwise_deterministic():
     assert torch.equal(o1, o2) and torch.equal(r1.buf, r2.buf)
 
 
-@pytest.mark.parametrize("kind", ["window", "spine"])
+@pytest.mark.parametrize("kind", ["window", "spine", "window_b8", "spine_b8"])
 def test_non_descendants_bitwise_unchanged(kind):
     """Masked terms are exact zeros, in the per-path solve (window trees) and
-    in the blocked solve of deep drafts (spine trees, paths past 16 nodes)."""
+    in the blocked solve of deep drafts (spine trees, paths past 16 nodes),
+    with narrow state-row tiles (batch 1: products through LDS) and wide ones
+    (batch 8: products chained in registers)."""
     if kind == "window":
         d = W.tree32_layer(3)
         x = 5
+    elif kind == "window_b8":
+        d = W.make_draft(8, 64, 8, 256, 256, topology="window", accept="full", seed=13)
+        x = 7
     else:
-        d = W.make_draft(1, 64, 8, 256, 256, topology="spine", accept="full", seed=12)
+        B = 8 if kind == "spine_b8" else 1
+        d = W.make_draft(B, 64, 8, 256, 256, topology="spine", accept="full", seed=12)
         assert W.depths_of(d.parents[0]).max() > 16
         x = 20
     out, _, mask, _, t = run_tree(d)

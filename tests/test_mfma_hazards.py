@@ -11,12 +11,12 @@ import pytest
 import mfma_hazards as M
 from linear_attention_gdn_amd import build as B
 
-HEADER = os.path.join(B.CSRC, "gdn_common.h")
+HEADERS = [os.path.join(B.CSRC, n) for n in ("gdn_common.h", "tree_common.h")]
 
 
 def _asm(src):
     path = B.device_asm_path(src)
-    newest = max(os.path.getmtime(src), os.path.getmtime(HEADER))
+    newest = max([os.path.getmtime(src)] + [os.path.getmtime(p) for p in HEADERS])
     if os.path.exists(path) and os.path.getmtime(path) >= newest:
         with open(path) as f:
             return f.read()
@@ -24,9 +24,24 @@ def _asm(src):
     return M.device_asm(src, flags, B.hipcc())
 
 
+@pytest.fixture(scope="module")
+def probed(tmp_path_factory):
+    flags = [f for f in B.HIPCC_FLAGS if f not in ("-save-temps=obj", "-fPIC")]
+    req = M.probed_requirements(flags, B.hipcc(), str(tmp_path_factory.mktemp("probe")))
+    assert set(req) == set(M.PROBES), req  # every probe read its result in straight line
+    return req
+
+
+def test_probed_requirements_are_positive(probed):
+    assert all(w >= 1 for w in probed.values()), probed
+
+
 @pytest.mark.parametrize("src", B.sources(), ids=lambda p: os.path.basename(p))
-def test_no_mfma_result_read_too_early(src):
-    bad, req = M.check(_asm(src))
+def test_no_mfma_result_read_too_early(src, probed):
+    asm = _asm(src)
+    used = {ins.op for k in M.parse_kernels(asm) for ins in k.instrs if ins.op.startswith("v_mfma")}
+    assert used <= set(probed), f"no probe for {sorted(used - set(probed))}"
+    bad, req = M.check(asm, probed)
     detail = "\n".join(f"{k[:70]}: {mf} -> {rd} after {w} < {need} wait states"
                        for k, mf, w, rd, need in bad[:10])
     assert not bad, f"{len(bad)} early reads of MFMA results:\n{detail}"
