@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
   for (int x = 0; x < KB; ++x) kq0[x] = kq_load(tid + NT * x);
   f32x4 Sx;
   __builtin_amdgcn_sched_barrier(0);
-  Sx = load4(S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk + 4 * sc);
+  Sx = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S0 + ((size_t)bh * dv + clampi(row, dv - 1)) * dk + 4 * sc));
   __builtin_amdgcn_sched_barrier(0);
   const int cs = clampi(s, N - 1);
   const size_t nhl = ((size_t)b * N + cs) * H + h;
@@ -341,8 +341,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
         default: break;
       }
       if (rok && cok)
-        *reinterpret_cast<f32x4*>(S0 + ((size_t)bh * dv + row) * dk + 4 * s) =
-            f32x4{S[0], S[1], S[2], S[3]};
+        __builtin_nontemporal_store(f32x4{S[0], S[1], S[2], S[3]}, reinterpret_cast<f32x4*>(S0 + ((size_t)bh * dv + row) * dk + 4 * s));
     }
   }
   if (!KQR) __syncthreads();  // k.q of every node is in LDS

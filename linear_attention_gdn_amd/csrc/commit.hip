@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void commit_kernel(
   for (int j = 0; j < J; ++j) {
     const int row = r0 + rg + RG * j;
     ok[j] = active && row < dv;
-    acc[j] = load4(Sb + (size_t)clampi(row, dv - 1) * dk + 4 * ccl);
+    acc[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sb + (size_t)clampi(row, dv - 1) * dk + 4 * ccl));
   }
   const T* Kb = rec.K + (size_t)bh * N * dk + 4 * ccl;
   typename Raw4<T>::type kpre[PRE ? kPreloadNodes : 1];
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void commit_kernel(
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int row = r0 + rg + RG * j;
-    if (ok[j]) *reinterpret_cast<f32x4*>(Sb + (size_t)row * dk + 4 * cc) = acc[j];
+    if (ok[j]) __builtin_nontemporal_store(acc[j], reinterpret_cast<f32x4*>(Sb + (size_t)row * dk + 4 * cc));
   }
 }
 

@@ -238,12 +238,15 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       }
     }
   } else {
+    // The state is read and written once per step: non-temporal accesses
+    // stream it past the caches, which keep Q, K (read by the head's four
+    // tiles) and leave less to write back when the kernel ends.
     const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int kk = clampi(32 * ks + koff, dk - 8);
-      Sraw[ks][0] = load4(sptr + kk);
-      Sraw[ks][1] = load4(sptr + kk + 4);
+      Sraw[ks][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sptr + kk));
+      Sraw[ks][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sptr + kk + 4));
     }
 #pragma unroll
     for (int j = 0; j < NQT; ++j)
@@ -288,11 +291,16 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
         const int nd = sm.dnode[clampi(c0 + j, dn - 1)];
         kr[x] = *reinterpret_cast<const u32x4*>(prev.K + ((size_t)bh * Npv + nd) * dk + col);
       }
-      float cu[kWsChunk];
+      // B operand of group m: lane (row l16, k = lg) holds c u' of path node
+      // c0 + 4 m + lg for this lane's state row; past the path -0, whose
+      // product leaves every accumulator bit unchanged (x + -0 = x)
+      float cu[kWsChunk / 4];
 #pragma unroll
-      for (int j = 0; j < kWsChunk; ++j) {
-        const int jc = clampi(c0 + j, dn - 1);
-        cu[j] = sm.dc[jc] * prev.up[((size_t)bh * Npv + sm.dnode[jc]) * dv + clampi(srow, dv - 1)];
+      for (int m = 0; m < kWsChunk / 4; ++m) {
+        const int jn = c0 + 4 * m + lg;
+        const int jc = clampi(jn, dn - 1);
+        const float c = sm.dc[jc] * prev.up[((size_t)bh * Npv + sm.dnode[jc]) * dv + clampi(srow, dv - 1)];
+        cu[m] = jn < dn ? c : -0.0f;
       }
       // this wave's reads of the previous round precede these writes (one
       // wave's LDS operations complete in order)
@@ -304,32 +312,44 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
       const int nc = __builtin_amdgcn_readfirstlane(dn - c0 < kWsChunk ? dn - c0 : kWsChunk);
+      // The rank-n update on FP32 MFMA, four path nodes per product: for the
+      // tile (ks, half), D row 4 g + r is state column 32 ks + 8 g + 4 half + r
+      // and D column j is state row 16 cj + j, so a lane's accumulator is its
+      // own Sraw[ks][half].  v_mfma_f32_16x16x4_f32 adds its four products
+      // one after another, each as a fused multiply-add in k order, so node
+      // by node in path order this is bitwise the commit kernel's fmaf
+      // sequence.  A operand: lane (row l16, k = lg) holds k of node
+      // c0 + 4 m + lg at that row's column.
+      const int kcol = 8 * (l16 >> 2) + (l16 & 3);
 #pragma unroll
-      for (int jj = 0; jj < kWsChunk; ++jj) {
-        if (jj < nc) {  // uniform
+      for (int m = 0; m < kWsChunk / 4; ++m) {
+        if (4 * m < nc) {  // uniform
+          const int jn = 4 * m + lg;
+          const bool on = c0 + jn < dn;
+          const bf16_t* kr0 = kst + jn * kMaxDim + kcol;
+          float av[KS][2];
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(kst + jj * kMaxDim + 32 * ks + koff);
-            const f32x4 k0 = widen4(u32x2{w.x, w.y});
-            const f32x4 k1 = widen4(u32x2{w.z, w.w});
+          for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              Sraw[ks][0][e] = fmaf(cu[jj], k0[e], Sraw[ks][0][e]);
-              Sraw[ks][1][e] = fmaf(cu[jj], k1[e], Sraw[ks][1][e]);
-            }
-          }
+            for (int hf = 0; hf < 2; ++hf) av[ks][hf] = on ? widen1(kr0[32 * ks + 4 * hf]) : 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) Sraw[ks][hf] = mfma16x16x4f32(av[ks][hf], cu[m], Sraw[ks][hf]);
         }
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next round's writes
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
   };
   // write-back of the committed columns 32 ks + 8 lg .. + 7 of this lane's row
   auto dly_store = [&](int ks) {
     const int col = 32 * ks + koff;
     if (sok && col < dk) {
       float* wp = S0 + ((size_t)bh * dv + srow) * dk + col;
-      *reinterpret_cast<f32x4*>(wp) = Sraw[ks][0];
-      *reinterpret_cast<f32x4*>(wp + 4) = Sraw[ks][1];
+      __builtin_nontemporal_store(Sraw[ks][0], reinterpret_cast<f32x4*>(wp));
+      __builtin_nontemporal_store(Sraw[ks][1], reinterpret_cast<f32x4*>(wp + 4));
     }
   };
 
@@ -371,7 +391,7 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
         const int t = idx / kC8;
         const int c8 = 8 * (idx % kC8);
         if (t < N && c8 < dk)
-          *reinterpret_cast<u32x4*>(rec.K + ((size_t)bh * N + t) * dk + c8) = kc[x];
+          __builtin_nontemporal_store(kc[x], reinterpret_cast<u32x4*>(rec.K + ((size_t)bh * N + t) * dk + c8));
       }
     }
     // 2. Gram blocks Q K^T and K K^T, lower-triangle tiles: wave w takes row
@@ -644,14 +664,14 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
     for (int i = 0; i < NQT; ++i) {
       const int t = 16 * i + l16;
       if (t < N && sok4)
-        *reinterpret_cast<f32x4*>(rec.up + ((size_t)bh * N + t) * dv + srow4) = ut[i];
+        __builtin_nontemporal_store(ut[i], reinterpret_cast<f32x4*>(rec.up + ((size_t)bh * N + t) * dv + srow4));
     }
     mfma_drain_all(ot);
 #pragma unroll
     for (int i = 0; i < NQT; ++i) {
       const int t = 16 * i + l16;
       if (t < N && sok4)
-        *reinterpret_cast<f32x4*>(out + (((size_t)b * N + t) * H + h) * dv + srow4) = ot[i];
+        __builtin_nontemporal_store(ot[i], reinterpret_cast<f32x4*>(out + (((size_t)b * N + t) * H + h) * dv + srow4));
     }
   };
   if (deep)

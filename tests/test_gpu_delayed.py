@@ -117,6 +117,10 @@ def _prev_record(prev: W.Draft):
     # deep drafts (blocked solve) with long previous paths, wide and narrow tiles
     ("bf16", 8, 64, 64, 8, 256, 256, "spine", "spine"),
     ("bf16", 1, 48, 48, 8, 256, 256, "spine", "spine"),
+    # 64-row tiles: a 64-node accepted path (four staging rounds, a full last
+    # group of four) and ragged dk, dv and N with short paths
+    ("bf16", 8, 64, 16, 8, 256, 256, "chain", "window"),
+    ("bf16", 32, 23, 17, 8, 72, 100, "random", "random"),
 ])
 def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo,
                                                    new_topo):
