@@ -40,8 +40,8 @@ constexpr int kWsChunk = 16;  // accepted-path nodes staged per round by each st
 template <bool DLY>
 struct WsLds {
   alignas(16) bf16_t qk[kQKRows * kQKStride];  // Q rows, then K rows (bf16, zero-padded)
-  alignas(16) float A[kMaxNodes * kLd];        // K K^T, then A (FP32)
-  alignas(16) float QK[kMaxNodes * kLd];       // Q K^T (FP32), then Attn (split bf16)
+  alignas(16) float A[kMaxNodes * kLd];        // A (FP32)
+  alignas(16) float QK[kMaxNodes * kLd];       // Attn (split bf16)
   alignas(16) float T[kMaxNodes * kLd];        // T: zeros, then FP32 rows or split bf16
   uint64_t mask[kMaxNodes];
   float G[kMaxNodes], eG[kMaxNodes], beta[kMaxNodes];
@@ -92,14 +92,11 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
     int Npv, const int32_t* __restrict__ last_acc, int32_t* __restrict__ commit_status) {
   constexpr int BV = 64;
   constexpr int Np = 16 * NQT;
-  constexpr int NK = 32 * ((NQT + 1) / 2);  // k extent of the Gram tiles' mask pass
-  constexpr int EPT = Np * NK / 256;        // mask-pass entries per head thread
   constexpr int KS = kMaxDim / 32;          // 32-wide k steps of the contraction
 
   __shared__ WsLds<DLY> sm;
   bf16_t* const QKs = sm.qk;
   float* const KK = sm.A;
-  float* const QK = sm.QK;
   bf16_t* const Attn = reinterpret_cast<bf16_t*>(sm.QK);
   float* const Tl = sm.T;
   bf16_t* const Ts = reinterpret_cast<bf16_t*>(sm.T);
@@ -173,8 +170,13 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       const u32x4 z = {0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
     }
-    for (int idx = tid; idx < kMaxNodes * kLd / 4; idx += 256)  // T starts as zeros
+    // T and A start as zeros: the Gram tiles write only A's lower-triangle
+    // blocks, and the path solves multiply the entries above the diagonal by
+    // exact zeros, which needs them finite
+    for (int idx = tid; idx < kMaxNodes * kLd / 4; idx += 256) {
       reinterpret_cast<f32x4*>(Tl)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
+      reinterpret_cast<f32x4*>(KK)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // 1. wave 0: parents -> validation, ancestor-or-self masks and G
     if (wave == 0) {
@@ -394,8 +396,11 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
           __builtin_nontemporal_store(kc[x], reinterpret_cast<u32x4*>(rec.K + ((size_t)bh * N + t) * dk + c8));
       }
     }
-    // 2. Gram blocks Q K^T and K K^T, lower-triangle tiles: wave w takes row
-    // block pair w / 2 of Q (w even) or of K (w odd), as in tree_verify.hip
+    // 2-3. Gram blocks Q K^T and K K^T, lower-triangle tiles: wave w takes
+    // row block pair w / 2 of Q (w even) or of K (w odd), as in
+    // tree_verify.hip; each tile is masked, decayed and scaled in registers
+    // into A (FP32) or Attn (split bf16), so no N x N pass follows.  Only the
+    // lower-triangle blocks are ever read.
     auto gram_job = [&](auto wc) {
       constexpr int Wc = decltype(wc)::value;
       constexpr int npairs = (NQT + 1) / 2;
@@ -405,8 +410,38 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
         constexpr int rs = Wc / 2;
         constexpr bool two = rs < ra;
         const bf16_t* rows = QKs + (isq ? 0 : Np) * kQKStride;
-        float* dst = isq ? QK : KK;
         bf16x8 fa[KS], fs[two ? KS : 1], kb[2][KS];
+        // per-row values of this lane's four rows 4 lg + r of each row block
+        uint64_t mra[4], mrs[4];
+        float gra[4], grs[4], bra[4], brs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ta = 16 * ra + 4 * lg + r, ts = 16 * rs + 4 * lg + r;
+          mra[r] = sm.mask[ta];
+          gra[r] = sm.G[ta];
+          bra[r] = sm.beta[ta];
+          mrs[r] = sm.mask[ts];
+          grs[r] = sm.G[ts];
+          brs[r] = sm.beta[ts];
+        }
+        // the tile's entries of A (K K^T: beta_t e^{G_t - G_j} (k_t . k_j) for
+        // j a proper ancestor of t) or of Attn (Q K^T: scale e^{G_t - G_j}
+        // (q_t . k_j) for j on t's root path), exact zeros elsewhere
+        auto put = [&](int rblk, int ct, const f32x4& acc, const uint64_t (&m)[4],
+                       const float (&gr)[4], const float (&br)[4]) {
+          const int j = 16 * ct + l16;
+          const float gj = sm.G[j];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * rblk + 4 * lg + r;
+            const bool on = (m[r] >> j) & 1ull;
+            const float dec = __expf(gr[r] - gj);
+            if constexpr (isq)
+              store_split1(Attn + t * kLdH + j, kSplitLo, on ? scale * dec * acc[r] : 0.f);
+            else
+              KK[t * kLd + j] = (on && j != t) ? br[r] * dec * acc[r] : 0.f;
+          }
+        };
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           fa[ks] = lds_bf16x8(rows + (16 * ra + l16) * kQKStride + 32 * ks + koff);
@@ -426,16 +461,14 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(fa[ks], kb[ct & 1][ks], acc);
           mfma_drain(acc);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dst[(16 * ra + 4 * lg + r) * kLd + 16 * ct + l16] = acc[r];
+          put(ra, ct, acc, mra, gra, bra);
           if (two && ct <= rs) {
             f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
               acc2 = mfma16x16x32(fs[two ? ks : 0], kb[ct & 1][ks], acc2);
             mfma_drain(acc2);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(16 * rs + 4 * lg + r) * kLd + 16 * ct + l16] = acc2[r];
+            put(rs, ct, acc2, mrs, grs, brs);
           }
         }
       }
@@ -447,44 +480,9 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       default: gram_job(std::integral_constant<int, 3>{}); break;
     }
   }
-  if (head) ws_sync(&sm.sync, 8);  // Gram blocks
+  if (head) ws_sync(&sm.sync, 8);  // A and Attn
 
-  // 3. A (FP32, in place of K K^T) and Attn (split bf16, in place of Q K^T),
-  // exact zeros off the masks (head threads; every operand read first)
-  float attn[EPT];
   if (head) {
-    float kkv[EPT], qkv[EPT], gt[EPT], gj[EPT], bt[EPT];
-    uint64_t mt[EPT];
-#pragma unroll
-    for (int x = 0; x < EPT; ++x) {
-      const int idx = tid + 256 * x;
-      const int t = idx / NK;
-      const int j = idx % NK;
-      mt[x] = sm.mask[t];
-      gt[x] = sm.G[t];
-      gj[x] = sm.G[j];
-      bt[x] = sm.beta[t];
-      kkv[x] = KK[t * kLd + j];
-      qkv[x] = QK[t * kLd + j];
-    }
-#pragma unroll
-    for (int x = 0; x < EPT; ++x) {
-      const int idx = tid + 256 * x;
-      const int t = idx / NK;
-      const int j = idx % NK;
-      const bool on = (mt[x] >> j) & 1ull;
-      const float dec = __expf(gt[x] - gj[x]);
-      KK[t * kLd + j] = (on && j != t) ? bt[x] * dec * kkv[x] : 0.f;
-      attn[x] = on ? scale * dec * qkv[x] : 0.f;
-    }
-  }
-  if (head) ws_sync(&sm.sync, 12);  // every Q K^T entry is read before Attn overwrites it
-  if (head) {
-#pragma unroll
-    for (int x = 0; x < EPT; ++x) {
-      const int idx = tid + 256 * x;
-      store_split1(Attn + (idx / NK) * kLdH + idx % NK, kSplitLo, attn[x]);
-    }
     // rows of T on root paths, one lane per node (wave 0): split bf16, or FP32
     // diagonal blocks for a deep draft
     if (tid < N) {
@@ -562,7 +560,7 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
   }
 
   if (head && deep) {  // uniform: blocked forward substitution, as in tree_verify.hip
-    int tgt = 12;
+    int tgt = 8;
     ws_sync(&sm.sync, tgt += 4);  // the diagonal blocks are in T
 #pragma unroll
     for (int i = 1; i < NQT; ++i) {
