@@ -161,6 +161,15 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       pmask_l = prev.mask[(size_t)b * Npv + tj];
       pG_l = prev.G[(size_t)bh * Npv + tj];
     }
+    // the head's loads are queued: the state waves may now request theirs
+    ws_arrive(&sm.sync);
+    // (while the loads are in flight) T and A start as zeros: the Gram tiles write only A's lower-triangle
+    // blocks, and the path solves multiply the entries above the diagonal by
+    // exact zeros, which needs them finite
+    for (int idx = tid; idx < kMaxNodes * kLd / 4; idx += 256) {
+      reinterpret_cast<f32x4*>(Tl)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
+      reinterpret_cast<f32x4*>(KK)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int x = 0; x < QKB; ++x) {  // no branch: a load under one is waited for at once
       const int idx = tid + 256 * x;
@@ -169,13 +178,6 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       const int c8 = 8 * (idx % qk_cpr);
       const u32x4 z = {0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
-    }
-    // T and A start as zeros: the Gram tiles write only A's lower-triangle
-    // blocks, and the path solves multiply the entries above the diagonal by
-    // exact zeros, which needs them finite
-    for (int idx = tid; idx < kMaxNodes * kLd / 4; idx += 256) {
-      reinterpret_cast<f32x4*>(Tl)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
-      reinterpret_cast<f32x4*>(KK)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     // 1. wave 0: parents -> validation, ancestor-or-self masks and G
@@ -240,6 +242,9 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       }
     }
   } else {
+    // The head waves' Q and K requests go first (the state's would otherwise
+    // fill the memory queues ahead of them and delay every per-head step).
+    ws_wait(&sm.sync, 4);
     // The state is read and written once per step: non-temporal accesses
     // stream it past the caches, which keep Q, K (read by the head's four
     // tiles) and leave less to write back when the kernel ends.
@@ -259,9 +264,9 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       }
   }
   if (head)
-    ws_sync(&sm.sync, 4);  // staged Q/K, T zeroed, topology, path
+    ws_sync(&sm.sync, 8);  // staged Q/K, T zeroed, topology, path
   else
-    ws_wait(&sm.sync, 4);
+    ws_wait(&sm.sync, 8);
 
   // the previous draft's accepted path applied to this state wave's rows in
   // the commit kernel's operation order (scale by e^{G_last}, then one fmaf
@@ -480,7 +485,7 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       default: gram_job(std::integral_constant<int, 3>{}); break;
     }
   }
-  if (head) ws_sync(&sm.sync, 8);  // A and Attn
+  if (head) ws_sync(&sm.sync, 12);  // A and Attn
 
   if (head) {
     // rows of T on root paths, one lane per node (wave 0): split bf16, or FP32
@@ -560,7 +565,7 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
   }
 
   if (head && deep) {  // uniform: blocked forward substitution, as in tree_verify.hip
-    int tgt = 8;
+    int tgt = 12;
     ws_sync(&sm.sync, tgt += 4);  // the diagonal blocks are in T
 #pragma unroll
     for (int i = 1; i < NQT; ++i) {
