@@ -63,18 +63,24 @@ CLOCK_HZ = 2.4e9  # peak engine clock, for MFMA-busy fractions
 DEFAULT_WORKLOAD = "tree64-b8-h8-d256"
 CHAIN_WORKLOAD = "chain8-b1-h8-d256"
 CSRC = os.path.join(ROOT, "linear_attention_gdn_amd", "csrc")
-KERNEL_SOURCES = {"gdn_chain_verify": "chain_verify.hip", "gdn_tree_verify": "tree_verify.hip",
-                  "gdn_commit_path": "commit.hip", "gdn_linear": "layer.hip",
-                  "gdn_chain_verify_delayed": "chain_verify.hip",
-                  "gdn_tree_verify_delayed": "tree_verify.hip",
-                  "gdn_layer_verify": "tree_verify.hip"}
+# the sources each entry point's kernels are built from (tree verification at
+# batch x heads >= 256 runs the split-role kernel of tree_verify_ws.hip)
+KERNEL_SOURCES = {
+    "gdn_chain_verify": ["chain_verify.hip"],
+    "gdn_chain_verify_delayed": ["chain_verify.hip"],
+    "gdn_tree_verify": ["tree_verify.hip", "tree_verify_ws.hip", "tree_common.h"],
+    "gdn_tree_verify_delayed": ["tree_verify.hip", "tree_verify_ws.hip", "tree_common.h"],
+    "gdn_layer_verify": ["tree_verify.hip", "tree_common.h"],
+    "gdn_commit_path": ["commit.hip"],
+    "gdn_linear": ["layer.hip"],
+}
 
 
 def source_digest(kernel: str) -> str:
-    """Short hash of a kernel's source (and the shared header) to tie counters to code."""
+    """Short hash of a kernel's sources (and the shared header) to tie counters to code."""
     import hashlib
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "gdn_common.h"):
+    for f in KERNEL_SOURCES[kernel] + ["gdn_common.h"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:12]
@@ -555,7 +561,7 @@ def roofline_of(res: dict) -> dict:
     mf = measured_mfma(res["step_kernel"], d.name, t_s * 1e6) if res["step_kernel"] else None
     issued = None
     if mf:
-        issued = {"type": "bf16 (v_mfma_f32_16x16x32_bf16)",
+        issued = {"type": "bf16 (v_mfma_f32_16x16x32_bf16, v_mfma_f32_16x16x16_bf16)",
                   "flop_per_launch": mf["bf16_flop_per_launch"],
                   "achieved_tflops": mf["issued_tflops"], "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
                   "frac": mf["issued_frac"],
