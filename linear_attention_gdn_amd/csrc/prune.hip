@@ -14,10 +14,11 @@
 // thread, all in LDS:
 //   1. checks: -1 <= p[t] < t, q[t] not NaN, q[t] <= q[p[t]];
 //   2. q* by a block reduction; the threshold q* - tau in FP32;
-//   3. the window nodes compacted into a list (a block prefix sum), then each
-//      window node's rank = the number of window nodes before it in
-//      (q descending, index ascending), read from LDS;
-//   4. kept = window and rank < T; new numbers by a second prefix sum.
+//   3. the window nodes compacted into a list (a prefix count by ballots),
+//      then each window node's rank = the number of window nodes before it
+//      in (q descending, index ascending), one list entry per thread, from
+//      one pass over the list in LDS (four entries per read);
+//   4. kept = window and rank < T; new numbers by a second prefix count.
 #include "gdn_common.h"
 
 namespace gdn {
@@ -25,29 +26,51 @@ namespace gdn {
 constexpr int kPruneThreads = 256;
 constexpr int kPruneMax = 1024;
 constexpr int kPrunePer = kPruneMax / kPruneThreads;
+static_assert(kPrunePer == 4, "four candidates per thread");
 
-// Exclusive prefix sum of one count per thread over the workgroup; returns
-// this thread's offset and leaves the total in *total (both in every thread).
-__device__ inline int block_exclusive_scan(int x, int* swave, int* total) {
+// Exclusive prefix count of per-thread flags over the workgroup in node
+// order (thread tid holds nodes 4 tid .. 4 tid + 3): within a wave one ballot
+// per flag slot and a popcount of the lanes below, across the four waves one
+// LDS round (swave: this scan's own four entries).  Returns the number of set
+// flags before this thread's nodes and leaves the total in *total.
+__device__ inline int block_flag_scan(const int (&f)[kPrunePer], int* swave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = x;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int before = 0, cnt = 0;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
+  for (int i = 0; i < kPrunePer; ++i) {
+    const uint64_t m = __ballot(f[i] != 0);
+    before += __popcll(m & below);
+    cnt += __popcll(m);
   }
-  if (lane == 63) swave[wave] = incl;
+  if (lane == 0) swave[wave] = cnt;
   __syncthreads();
-  int before = 0, all = 0;
+  int all = 0;
 #pragma unroll
   for (int w = 0; w < kPruneThreads / 64; ++w) {
     const int c = swave[w];
     if (w < wave) before += c;
     all += c;
   }
-  __syncthreads();  // swave may be reused
   *total = all;
-  return before + incl - x;
+  return before;
+}
+
+// Maximum over the wave into every lane: DPP within rows of 16, then the
+// row and half exchanges on the VALU.
+__device__ inline float wave64_max(float x) {
+  x = fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8
+  x = fmaxf(x, dpp_f32<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
+  unsigned a = __builtin_bit_cast(unsigned, x), c;
+  asm("" : "=v"(c) : "0"(a));
+  const auto r = __builtin_amdgcn_permlane16_swap(a, c, false, false);
+  x = fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  a = __builtin_bit_cast(unsigned, x);
+  asm("" : "=v"(c) : "0"(a));
+  const auto r2 = __builtin_amdgcn_permlane32_swap(a, c, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r2[0]), __builtin_bit_cast(float, (unsigned)r2[1]));
 }
 
 __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
@@ -57,9 +80,10 @@ __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
   __shared__ float sq[kPruneMax];
   __shared__ int sp[kPruneMax];
   __shared__ int snew[kPruneMax];    // new number of a kept node, -1 otherwise
-  __shared__ int swin[kPruneMax];    // window nodes, ascending
-  __shared__ float swq[kPruneMax];   // their confidences
-  __shared__ int swave[kPruneThreads / 64];
+  __shared__ __attribute__((aligned(16))) int swin[kPruneMax];   // window nodes, ascending
+  __shared__ __attribute__((aligned(16))) float swq[kPruneMax];  // their confidences
+  __shared__ int swave[kPruneThreads / 64], swave2[kPruneThreads / 64];
+  __shared__ int skeep[kPruneMax];   // window nodes: 1 if within the budget
   __shared__ float sred[kPruneThreads / 64];
   __shared__ int sbad;
   const int b = blockIdx.x;
@@ -95,8 +119,7 @@ __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
   }
   if (bad) sbad = 1;
   // 2. q* and the FP32 threshold
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, d));
+  qmax = wave64_max(qmax);
   if (lane == 0) sred[wave] = qmax;
   __syncthreads();
   float qs = sred[0];
@@ -123,7 +146,7 @@ __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
     nloc += inw[i];
   }
   int W;
-  int off = block_exclusive_scan(nloc, swave, &W);
+  int off = block_flag_scan(inw, swave, &W);
 #pragma unroll
   for (int i = 0; i < kPrunePer; ++i) {
     if (inw[i]) {
@@ -132,26 +155,41 @@ __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
       ++off;
     }
   }
+  // pad the list to a multiple of four with entries that rank before no
+  // node: confidence -inf, index past every node
+  const int W4 = (W + 3) & ~3;
+  if (tid < W4 - W) {
+    swq[W + tid] = -INFINITY;
+    swin[W + tid] = kPruneMax;
+  }
+  __syncthreads();
+  // rank of each window node among the window in (q descending, index
+  // ascending), one list entry per thread: one pass over the list, four
+  // entries per 16-byte read
+  for (int x = tid; x < W; x += kPruneThreads) {
+    const float qx = swq[x];
+    const int tx = swin[x];
+    int rank = 0;
+    for (int j = 0; j < W4; j += 4) {
+      const f32x4 qv = *reinterpret_cast<const f32x4*>(&swq[j]);
+      const int4 tv = *reinterpret_cast<const int4*>(&swin[j]);
+      rank += (qv.x > qx || (qv.x == qx && tv.x < tx)) ? 1 : 0;
+      rank += (qv.y > qx || (qv.y == qx && tv.y < tx)) ? 1 : 0;
+      rank += (qv.z > qx || (qv.z == qx && tv.z < tx)) ? 1 : 0;
+      rank += (qv.w > qx || (qv.w == qx && tv.w < tx)) ? 1 : 0;
+    }
+    skeep[tx] = rank < T ? 1 : 0;
+  }
   __syncthreads();
   int keep[kPrunePer], nk = 0;
 #pragma unroll
   for (int i = 0; i < kPrunePer; ++i) {
-    const int t = kPrunePer * tid + i;
-    keep[i] = 0;
-    if (inw[i]) {
-      int rank = 0;
-      for (int j = 0; j < W; ++j) {  // uniform bound
-        const float qj = swq[j];
-        const int tj = swin[j];
-        rank += (qj > q[i] || (qj == q[i] && tj < t)) ? 1 : 0;
-      }
-      keep[i] = rank < T ? 1 : 0;
-    }
+    keep[i] = inw[i] ? skeep[kPrunePer * tid + i] : 0;
     nk += keep[i];
   }
   // 4. renumbering
   int K;
-  int nn = block_exclusive_scan(nk, swave, &K);
+  int nn = block_flag_scan(keep, swave2, &K);
 #pragma unroll
   for (int i = 0; i < kPrunePer; ++i) {
     const int t = kPrunePer * tid + i;
