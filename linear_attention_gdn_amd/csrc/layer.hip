@@ -55,6 +55,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes
 __device__ inline u32x4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// The weights are streamed once per step (0.96 GiB over the 24 layers, far
+// beyond the caches): non-temporal loads leave the caches to the activations
+// read by every workgroup (24-layer step 0.742 -> 0.717 ms).
+__device__ inline u32x4 bload16nt(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 
 // Sum of the per-wave partial tiles in LDS (fixed wave order) plus residual,
 // written as FP32 and/or bf16.
@@ -137,7 +143,7 @@ __global__ __launch_bounds__(512) void linear_w8_kernel(int M, int Nc, int K,
   for (int s = 0; s < KS; ++s) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      b[s][nt] = bload16(rW, wfrag_off<PK>(nt, w * KS + s, li, lg, K));
+      b[s][nt] = bload16nt(rW, wfrag_off<PK>(nt, w * KS + s, li, lg, K));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       a[s][mt] = bload16(rA, ((16 * mt + li) * K + w * kw + 8 * lg) * 2 + 64 * s);
@@ -205,7 +211,7 @@ __global__ __launch_bounds__(256) void linear_kernel(int M, int Nc, int K,
     for (int s = 0; s < KB; ++s) {
       const int ks = bi * KB + s;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) b[s][nt] = bload16(rW, offW[nt] + kWStep * ks);
+      for (int nt = 0; nt < NT; ++nt) b[s][nt] = bload16nt(rW, offW[nt] + kWStep * ks);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) a[s][mt] = bload16(rA, offA[mt] + 64 * ks);
     }

@@ -176,4 +176,15 @@ __device__ inline void mfma_drain_all(f32x4 (&acc)[NA]) {
   mfma_drain();
 }
 
+// SiLU output gate fused into the epilogue (the GATE variants, bf16 q/k/v
+// only): Y = bf16(O * SiLU(gate)) with gate row t at gate + (b N + t) ldg + h dv
+// (the gate block of the layer's projection output), written instead of O.
+// A compile-time variant: the gate's loads and registers would otherwise
+// slow every plain verification.
+struct GateArgs {
+  const float* gate;
+  int ldg;
+  bf16_t* Y;
+};
+
 }  // namespace gdn

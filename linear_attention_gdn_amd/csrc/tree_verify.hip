@@ -70,17 +70,6 @@
 
 namespace gdn {
 
-// SiLU output gate fused into the epilogue (the GATE variants, bf16 q/k/v
-// only): Y = bf16(O * SiLU(gate)) with gate row t at gate + (b N + t) ldg + h dv
-// (the gate block of the layer's projection output), written instead of O.
-// A compile-time variant: the gate's loads and registers would otherwise
-// slow every plain verification.
-struct GateArgs {
-  const float* gate;
-  int ldg;
-  bf16_t* Y;
-};
-
 template <int BV>
 struct TreeLds {
   static constexpr int kBVT = ((BV + 15) / 16) * 16;            // padded tile width
@@ -1082,11 +1071,12 @@ hipError_t launch_bv(int B, int N, int H, int dk, int dv, float* S0, const int32
   }
 }
 
-hipError_t launch_tree_ws(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
-                          const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* beta,
-                          const float* g, float scale, float* out, const Record<bf16_t>& rec,
-                          uint64_t* mask_out, int32_t* dev_status, const void* prev_factors,
-                          int Npv, const int32_t* last, int32_t* commit_status,
+hipError_t launch_tree_ws(int SW, int B, int N, int H, int dk, int dv, float* S0,
+                          const int32_t* parents, const bf16_t* q, const bf16_t* k,
+                          const bf16_t* v, const float* beta, const float* g, float scale,
+                          float* out, const Record<bf16_t>& rec, uint64_t* mask_out,
+                          int32_t* dev_status, const void* prev_factors, int Npv,
+                          const int32_t* last, int32_t* commit_status, GateArgs ga,
                           hipStream_t stream);
 
 template <typename T>
@@ -1104,17 +1094,21 @@ hipError_t launch_tree_verify_t(int B, int N, int H, int dk, int dv, float* S0,
   // 128 tiles of 16 rows finish as soon as 256 tiles of 8 and read Q and K
   // half as often (measured: 1-3% faster).
   const long heads = (long)B * H;
-  if (heads * ((dv + 63) / 64) >= 256) {
-    // 64-row tiles with bf16 inputs: the split-role kernel (tree_verify_ws.hip)
-    if constexpr (std::is_same<T, bf16_t>::value) {
-      if (!da.gate.gate)
-        return launch_tree_ws(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                              mask_out, dev_status, da.prev_factors, da.Np, da.last,
-                              da.commit_status, stream);
-    }
+  // bf16 inputs with tiles of 16, 32 or 64 rows: the split-role kernel
+  // (tree_verify_ws.hip) with one state wave per 16 rows
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    int sw = 0;
+    if (heads * ((dv + 63) / 64) >= 256) sw = 4;
+    else if (heads * ((dv + 31) / 32) >= 256) sw = 2;
+    else if (heads * ((dv + 15) / 16) >= 128) sw = 1;
+    if (sw)
+      return launch_tree_ws(sw, B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, da.prev_factors, da.Np, da.last,
+                            da.commit_status, da.gate, stream);
+  }
+  if (heads * ((dv + 63) / 64) >= 256)
     return launch_bv<T, 64>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
                             mask_out, dev_status, da, dtype, stream);
-  }
   if (heads * ((dv + 31) / 32) >= 256)
     return launch_bv<T, 32>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
                             mask_out, dev_status, da, dtype, stream);

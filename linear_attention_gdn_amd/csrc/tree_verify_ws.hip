@@ -37,7 +37,7 @@ namespace gdn {
 
 constexpr int kWsChunk = 16;  // accepted-path nodes staged per round by each state wave
 
-template <bool DLY>
+template <bool DLY, int SW>
 struct WsLds {
   alignas(16) bf16_t qk[kQKRows * kQKStride];  // Q rows, then K rows (bf16, zero-padded)
   alignas(16) float A[kMaxNodes * kLd];        // A (FP32)
@@ -53,7 +53,7 @@ struct WsLds {
   int dn;
   float ds0;
   int sync;  // arrivals at the head waves' own barriers
-  alignas(16) bf16_t dk[DLY ? 4 * kWsChunk * kMaxDim : 8];
+  alignas(16) bf16_t dk[DLY ? SW * kWsChunk * kMaxDim : 8];
 };
 
 // The head waves synchronise among themselves through an LDS counter, so the
@@ -82,19 +82,20 @@ __device__ inline void ws_sync(int* ctr, int target) {
   ws_wait(ctr, target);
 }
 
-template <int NQT, bool DLY>
-__global__ __launch_bounds__(512) void tree_ws_kernel(
+template <int NQT, bool DLY, int SW, bool GATE>
+__global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
     const int32_t* __restrict__ parents, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ beta,
     const float* __restrict__ g, float scale, float* __restrict__ out, Record<bf16_t> rec,
     uint64_t* __restrict__ mask_out, int32_t* __restrict__ dev_status, Record<bf16_t> prev,
-    int Npv, const int32_t* __restrict__ last_acc, int32_t* __restrict__ commit_status) {
-  constexpr int BV = 64;
+    int Npv, const int32_t* __restrict__ last_acc, int32_t* __restrict__ commit_status,
+    GateArgs ga) {
+  constexpr int BV = 16 * SW;  // state rows per tile: 16 per state wave
   constexpr int Np = 16 * NQT;
   constexpr int KS = kMaxDim / 32;          // 32-wide k steps of the contraction
 
-  __shared__ WsLds<DLY> sm;
+  __shared__ WsLds<DLY, SW> sm;
   bf16_t* const QKs = sm.qk;
   float* const KK = sm.A;
   bf16_t* const Attn = reinterpret_cast<bf16_t*>(sm.QK);
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
   const int r0 = tile * BV;
   // state waves: rows 16 cj .. 16 cj + 15 of the tile; lane l16's row (as an
   // MFMA operand) and the four rows 16 cj + 4 lg .. + 3 (as a transposed result)
-  const int cj = wave & 3;
+  const int cj = wave >= 4 ? wave - 4 : 0;
   const int srow = r0 + 16 * cj + l16;
   const bool sok = srow < dv;
   const int srow4 = r0 + 16 * cj + 4 * lg;
@@ -360,6 +361,16 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
     }
   };
 
+  // gated form (gdn_layer_verify): Y = bf16(O * SiLU(gate)) for node t and the
+  // four state rows srow4 .. srow4 + 3, with gdn_gate_merge's arithmetic
+  auto store_gated = [&](int t, size_t o, const f32x4& x) {
+    const float* gp = ga.gate + ((size_t)b * N + t) * ga.ldg + h * dv + srow4;
+    u32x2 w;
+    w.x = (uint32_t)to_bf16(x.x * silu(gp[0])) | ((uint32_t)to_bf16(x.y * silu(gp[1])) << 16);
+    w.y = (uint32_t)to_bf16(x.z * silu(gp[2])) | ((uint32_t)to_bf16(x.w * silu(gp[3])) << 16);
+    *reinterpret_cast<u32x2*>(ga.Y + o) = w;
+  };
+
   if (sm.bad) {  // uniform: zero this tile's outputs (a delayed commit still applies)
     if (!head) {
       if (DLY && sm.dn > 0) {
@@ -371,7 +382,11 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
       for (int t0 = 0; t0 < N; t0 += 16) {
         const int t = t0 + l16;
         if (t < N && sok4) {
-          *reinterpret_cast<f32x4*>(out + (((size_t)b * N + t) * H + h) * dv + srow4) = z;
+          const size_t o = (((size_t)b * N + t) * H + h) * dv + srow4;
+          if constexpr (GATE)  // the gated form writes the gated zeros bf16(0 * SiLU(gate))
+            store_gated(t, o, z);
+          else
+            *reinterpret_cast<f32x4*>(out + o) = z;
           *reinterpret_cast<f32x4*>(rec.up + ((size_t)bh * N + t) * dv + srow4) = z;
         }
       }
@@ -673,8 +688,13 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
 #pragma unroll
     for (int i = 0; i < NQT; ++i) {
       const int t = 16 * i + l16;
-      if (t < N && sok4)
-        __builtin_nontemporal_store(ot[i], reinterpret_cast<f32x4*>(out + (((size_t)b * N + t) * H + h) * dv + srow4));
+      if (t < N && sok4) {
+        const size_t o = (((size_t)b * N + t) * H + h) * dv + srow4;
+        if constexpr (GATE)
+          store_gated(t, o, ot[i]);
+        else
+          __builtin_nontemporal_store(ot[i], reinterpret_cast<f32x4*>(out + o));
+      }
     }
   };
   if (deep)
@@ -683,49 +703,78 @@ __global__ __launch_bounds__(512) void tree_ws_kernel(
     run(std::integral_constant<bool, false>{});
 }
 
-template <int NQT>
-hipError_t launch_ws_n(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
+template <int NQT, int SW, bool GATE>
+hipError_t launch_ws_g(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
                        const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* beta,
                        const float* g, float scale, float* out, const Record<bf16_t>& rec,
                        uint64_t* mask_out, int32_t* dev_status, const void* prev_factors,
-                       int Npv, const int32_t* last, int32_t* commit_status, hipStream_t stream) {
-  const int ntiles = (dv + 63) / 64;
+                       int Npv, const int32_t* last, int32_t* commit_status, GateArgs ga,
+                       hipStream_t stream) {
+  const int ntiles = (dv + 16 * SW - 1) / (16 * SW);
   const long grid = (long)B * H * ntiles;
+  const dim3 block(256 + 64 * SW);
   if (prev_factors) {
     const RecordLayout Lp = record_layout(B, Npv, H, dk, dv, GDN_BF16);
     const Record<bf16_t> prev = record_views<bf16_t>(const_cast<void*>(prev_factors), Lp);
-    hipLaunchKernelGGL((tree_ws_kernel<NQT, true>), dim3((unsigned)grid), dim3(512), 0, stream, N,
-                       H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out, rec, mask_out,
-                       dev_status, prev, Npv, last, commit_status);
+    hipLaunchKernelGGL((tree_ws_kernel<NQT, true, SW, GATE>), dim3((unsigned)grid), block, 0,
+                       stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out,
+                       rec, mask_out, dev_status, prev, Npv, last, commit_status, ga);
   } else {
-    hipLaunchKernelGGL((tree_ws_kernel<NQT, false>), dim3((unsigned)grid), dim3(512), 0, stream,
-                       N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out, rec,
-                       mask_out, dev_status, Record<bf16_t>{}, 1, nullptr, nullptr);
+    hipLaunchKernelGGL((tree_ws_kernel<NQT, false, SW, GATE>), dim3((unsigned)grid), block, 0,
+                       stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out,
+                       rec, mask_out, dev_status, Record<bf16_t>{}, 1, nullptr, nullptr, ga);
   }
   return hipGetLastError();
 }
 
-// The split-role form for 64-row tiles with bf16 inputs (the caller has
-// chosen 64-row tiles and checked every size).
-hipError_t launch_tree_ws(int B, int N, int H, int dk, int dv, float* S0, const int32_t* parents,
-                          const bf16_t* q, const bf16_t* k, const bf16_t* v, const float* beta,
-                          const float* g, float scale, float* out, const Record<bf16_t>& rec,
-                          uint64_t* mask_out, int32_t* dev_status, const void* prev_factors,
-                          int Npv, const int32_t* last, int32_t* commit_status,
+template <int NQT>
+hipError_t launch_ws_n(int SW, int B, int N, int H, int dk, int dv, float* S0,
+                       const int32_t* parents, const bf16_t* q, const bf16_t* k, const bf16_t* v,
+                       const float* beta, const float* g, float scale, float* out,
+                       const Record<bf16_t>& rec, uint64_t* mask_out, int32_t* dev_status,
+                       const void* prev_factors, int Npv, const int32_t* last,
+                       int32_t* commit_status, GateArgs ga, hipStream_t stream) {
+#define GDN_WS(SWV, G)                                                                        \
+  return launch_ws_g<NQT, SWV, G>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out,  \
+                                  rec, mask_out, dev_status, prev_factors, Npv, last,          \
+                                  commit_status, ga, stream)
+  if (ga.gate) {
+    if (SW == 1) GDN_WS(1, true);
+    if (SW == 2) GDN_WS(2, true);
+    GDN_WS(4, true);
+  }
+  if (SW == 1) GDN_WS(1, false);
+  if (SW == 2) GDN_WS(2, false);
+  GDN_WS(4, false);
+#undef GDN_WS
+}
+
+// The split-role form with bf16 inputs, SW state waves of 16 rows each (the
+// caller has chosen the tile width 16 SW and checked every size).
+hipError_t launch_tree_ws(int SW, int B, int N, int H, int dk, int dv, float* S0,
+                          const int32_t* parents, const bf16_t* q, const bf16_t* k,
+                          const bf16_t* v, const float* beta, const float* g, float scale,
+                          float* out, const Record<bf16_t>& rec, uint64_t* mask_out,
+                          int32_t* dev_status, const void* prev_factors, int Npv,
+                          const int32_t* last, int32_t* commit_status, GateArgs ga,
                           hipStream_t stream) {
   switch ((N + 15) / 16) {
     case 1:
-      return launch_ws_n<1>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                            mask_out, dev_status, prev_factors, Npv, last, commit_status, stream);
+      return launch_ws_n<1>(SW, B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, prev_factors, Npv, last, commit_status, ga,
+                            stream);
     case 2:
-      return launch_ws_n<2>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                            mask_out, dev_status, prev_factors, Npv, last, commit_status, stream);
+      return launch_ws_n<2>(SW, B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, prev_factors, Npv, last, commit_status, ga,
+                            stream);
     case 3:
-      return launch_ws_n<3>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                            mask_out, dev_status, prev_factors, Npv, last, commit_status, stream);
+      return launch_ws_n<3>(SW, B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, prev_factors, Npv, last, commit_status, ga,
+                            stream);
     default:
-      return launch_ws_n<4>(B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
-                            mask_out, dev_status, prev_factors, Npv, last, commit_status, stream);
+      return launch_ws_n<4>(SW, B, N, H, dk, dv, S0, parents, q, k, v, beta, g, scale, out, rec,
+                            mask_out, dev_status, prev_factors, Npv, last, commit_status, ga,
+                            stream);
   }
 }
 
