@@ -138,12 +138,11 @@ __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
     return;
   }
   // 3. the window, compacted in ascending order, then ranks within it
-  int inw[kPrunePer], nloc = 0;
+  int inw[kPrunePer];
 #pragma unroll
   for (int i = 0; i < kPrunePer; ++i) {
     const int t = kPrunePer * tid + i;
     inw[i] = (t < M && q[i] >= thr) ? 1 : 0;
-    nloc += inw[i];
   }
   int W;
   int off = block_flag_scan(inw, swave, &W);
@@ -181,12 +180,9 @@ __global__ __launch_bounds__(kPruneThreads) void prune_kernel(
     skeep[tx] = rank < T ? 1 : 0;
   }
   __syncthreads();
-  int keep[kPrunePer], nk = 0;
+  int keep[kPrunePer];
 #pragma unroll
-  for (int i = 0; i < kPrunePer; ++i) {
-    keep[i] = inw[i] ? skeep[kPrunePer * tid + i] : 0;
-    nk += keep[i];
-  }
+  for (int i = 0; i < kPrunePer; ++i) keep[i] = inw[i] ? skeep[kPrunePer * tid + i] : 0;
   // 4. renumbering
   int K;
   int nn = block_flag_scan(keep, swave2, &K);

@@ -1,33 +1,36 @@
-// Tree verification with split wave roles (gfx950), for 64-row state tiles
-// and bf16 q/k/v: the form gdn_tree_verify and gdn_tree_verify_delayed take
-// when batch x heads fill the GPU with 64-row tiles (B H ceil(dv/64) >= 256).
+// Tree verification with split wave roles (gfx950), bf16 q/k/v: the form
+// gdn_tree_verify, gdn_tree_verify_delayed and the gated layer verify take
+// for bf16 inputs, with 16, 32 or 64 state rows per tile (one state wave per
+// 16 rows), the tile width chosen by the caller from the number of heads so
+// that the grid covers the GPU.
 //
 // SpecLA review, "What carries the argument" and Figures, Figure 4 caption:
 // the same factorized verification as tree_verify.hip (one workgroup per
-// (sequence, head, 64 state rows); outputs, factor record and the delayed
-// commit identical in definition), organised for this GPU so that the long
-// read of the state tile overlaps the chain of small per-head steps instead
-// of preceding it.  512 threads, two roles of four waves each:
+// (sequence, head, tile of state rows); outputs, factor record and the
+// delayed commit identical in definition), organised for this GPU so that the
+// long read of the state tile overlaps the chain of small per-head steps
+// instead of preceding it.  Two roles:
 //
 //   head waves (0-3): load and stage Q and K in LDS, build the topology
 //     (wave 0, pointer jumping), the Gram blocks Q K^T and K K^T (bf16 MFMA),
 //     the masked and scaled A and Attn, and T = (I + A)^{-1} (per-node path
 //     solves; blocked forward substitution for paths deeper than 16);
-//   state waves (4-7): wave 4 + c owns state rows 16 c .. 16 c + 15 of the
-//     tile.  They request their state rows and V at once (straight into MFMA
-//     operand registers), apply the previous draft's accepted path for the
-//     delayed form (each wave stages the path's k rows in its own LDS area,
-//     so no workgroup barrier is needed), run the contraction [Q; K] S0^T on
-//     bf16 MFMA (FP32 state split into bf16 hi + lo) while writing the
-//     committed rows back, form R = beta (V - e^G K S0^T), and after T is ready chain
+//   state waves (4 .. 3 + SW): wave 4 + c owns state rows 16 c .. 16 c + 15
+//     of the tile.  They request their state rows and V at once (straight
+//     into MFMA operand registers); for the delayed form each finds the
+//     previous draft's accepted path itself, stages the path's k rows in its
+//     own LDS area and applies the path to its rows before it first waits for
+//     the head waves.  They then run the contraction [Q; K] S0^T on bf16 MFMA
+//     (FP32 state split into bf16 hi + lo) while writing the committed rows
+//     back, form R = beta (V - e^G K S0^T), and after T is ready chain
 //     U' = T R and O = scale e^G Q S0^T + Attn U' through registers as
 //     16x16x16 products, the transposed products giving each lane four
 //     consecutive state rows of one node, stored as 16-byte vectors.
 //
 // The head waves synchronise among themselves through an LDS counter (the
 // state waves only wait for the staging and topology), and the two roles
-// meet at one workgroup barrier where T is complete.  Two waves share each
-// SIMD, so a head wave's scalar-heavy steps and a state wave's matrix
+// meet at one workgroup barrier where T is complete.  A head wave and a state
+// wave share a SIMD, so the head's scalar-heavy steps and the state's matrix
 // products issue side by side.
 #include <type_traits>
 
@@ -46,13 +49,11 @@ struct WsLds {
   uint64_t mask[kMaxNodes];
   float G[kMaxNodes], eG[kMaxNodes], beta[kMaxNodes];
   int bad;
-  // delayed commit: the accepted path (root first) and its coefficients, and
-  // each state wave's staged k rows
-  int dnode[kMaxNodes];
-  float dc[kMaxNodes];
-  int dn;
-  float ds0;
   int sync;  // arrivals at the head waves' own barriers
+  // delayed commit, per state wave: the accepted path (root first), its
+  // coefficients and the staged k rows
+  int dnode[DLY ? SW : 1][kMaxNodes];
+  float dc[DLY ? SW : 1][kMaxNodes];
   alignas(16) bf16_t dk[DLY ? SW * kWsChunk * kMaxDim : 8];
 };
 
@@ -138,6 +139,120 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   static_assert(qk_total % 256 == 0, "every head thread stages QKB chunks");
   f32x4 Sraw[KS][2];
   bf16_t vreg[NQT][4];
+  int dn_s = 0;  // state waves: length of the previous draft's accepted path
+  // Delayed commit (state waves): the previous draft's accepted path applied
+  // to this wave's rows in the commit kernel's operation order (scale by
+  // e^{G_last}, then one fmaf per path node in path order).  Each state wave
+  // finds the path itself from the last accepted node's ancestor mask and the
+  // path's G, so the k rows and u' of the path are requested while the head
+  // waves still stage Q and K, and the commit is done before the state waves
+  // first wait for the head.  Returns the path length (uniform).
+  auto dly_commit = [&](int last_v, uint64_t pmask_l, float pG_l) -> int {
+    const int sw = wave - 4;
+    int* const dnode = sm.dnode[DLY ? sw : 0];
+    float* const dc = sm.dc[DLY ? sw : 0];
+    const int lst = __builtin_amdgcn_readfirstlane(last_v);
+    const bool in_rng = lst >= 0 && lst < Npv;
+    const int lc = in_rng ? lst : 0;
+    const uint64_t valid = Npv >= 64 ? ~0ull : ((1ull << Npv) - 1ull);
+    const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)pmask_l, lc);
+    const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(pmask_l >> 32), lc);
+    const uint64_t pm = in_rng ? ((((uint64_t)mhi << 32) | mlo) & valid) : 0ull;
+    const bool okp = in_rng && ((pm >> lst) & 1ull);
+    const float Glast =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pG_l), lc));
+    if (okp && ((pm >> lane) & 1ull)) {  // lane = node of the previous draft
+      const int pos = __popcll(pm & ((1ull << lane) - 1ull));
+      dnode[pos] = lane;
+      dc[pos] = expf(Glast - pG_l);  // the commit kernel's coefficient
+    }
+    const int dn = okp ? __popcll(pm) : 0;
+    if (dn == 0) return 0;  // uniform
+    // (one wave's LDS operations complete in order: the reads below see the
+    // path just written)
+    bf16_t* kst = sm.dk + (DLY ? sw : 0) * (kWsChunk * kMaxDim);
+    constexpr int KR = kWsChunk * kMaxDim / 8 / 64;  // 16-byte chunks per lane and round
+    u32x4 kr[KR];
+    float cu[kWsChunk / 4];
+    // the k rows of path nodes c0 .. c0 + 15 and the B operand of group m: lane
+    // (row l16, k = lg) holds c u' of path node c0 + 4 m + lg for this lane's
+    // state row; past the path -0, whose product leaves every accumulator bit
+    // unchanged (x + -0 = x)
+    auto fetch = [&](int c0) {
+#pragma unroll
+      for (int x = 0; x < KR; ++x) {
+        const int idx = lane + 64 * x;
+        const int j = idx / (kMaxDim / 8);
+        const int col = clampi(8 * (idx % (kMaxDim / 8)), dk - 8);
+        const int nd = dnode[clampi(c0 + j, dn - 1)];
+        kr[x] = *reinterpret_cast<const u32x4*>(prev.K + ((size_t)bh * Npv + nd) * dk + col);
+      }
+#pragma unroll
+      for (int m = 0; m < kWsChunk / 4; ++m) {
+        const int jn = c0 + 4 * m + lg;
+        const int jc = clampi(jn, dn - 1);
+        const float c = dc[jc] * prev.up[((size_t)bh * Npv + dnode[jc]) * dv + clampi(srow, dv - 1)];
+        cu[m] = jn < dn ? c : -0.0f;
+      }
+    };
+    fetch(0);
+    // every state register is consumed here, before the first write-back
+    // store, so no later wait on a load also waits for the stores
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) pin_vgpr(Sraw[ks][0]), pin_vgpr(Sraw[ks][1]);
+    const float s0 = expf(Glast);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Sraw[ks][0][e] = Sraw[ks][0][e] * s0;
+        Sraw[ks][1][e] = Sraw[ks][1][e] * s0;
+      }
+    for (int c0 = 0; c0 < dn; c0 += kWsChunk) {  // uniform
+      if (c0 > 0) fetch(c0);
+      // this wave's reads of the previous round precede these writes (one
+      // wave's LDS operations complete in order)
+#pragma unroll
+      for (int x = 0; x < KR; ++x) {
+        const int idx = lane + 64 * x;
+        const int c8 = 8 * (idx % (kMaxDim / 8));
+        *reinterpret_cast<u32x4*>(kst + (idx / (kMaxDim / 8)) * kMaxDim + c8) = kr[x];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
+      const int nc = __builtin_amdgcn_readfirstlane(dn - c0 < kWsChunk ? dn - c0 : kWsChunk);
+      // The rank-n update on FP32 MFMA, four path nodes per product: for the
+      // tile (ks, half), D row 4 g + r is state column 32 ks + 8 g + 4 half + r
+      // and D column j is state row 16 cj + j, so a lane's accumulator is its
+      // own Sraw[ks][half].  v_mfma_f32_16x16x4_f32 adds its four products
+      // one after another, each as a fused multiply-add in k order, so node
+      // by node in path order this is bitwise the commit kernel's fmaf
+      // sequence.  A operand: lane (row l16, k = lg) holds k of node
+      // c0 + 4 m + lg at that row's column.
+      const int kcol = 8 * (l16 >> 2) + (l16 & 3);
+#pragma unroll
+      for (int m = 0; m < kWsChunk / 4; ++m) {
+        if (4 * m < nc) {  // uniform
+          const int jn = 4 * m + lg;
+          const bool on = c0 + jn < dn;
+          const bf16_t* kr0 = kst + jn * kMaxDim + kcol;
+          float av[KS][2];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) av[ks][hf] = on ? widen1(kr0[32 * ks + 4 * hf]) : 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) Sraw[ks][hf] = mfma16x16x4f32(av[ks][hf], cu[m], Sraw[ks][hf]);
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next round's writes
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
+    return dn;
+  };
+
   if (head) {
     u32x4 qkw[QKB];
 #pragma unroll
@@ -155,12 +270,9 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     const float bl = beta[((size_t)b * N + tn) * H + h];
     int last_v = -1;
     uint64_t pmask_l = 0;
-    float pG_l = 0.f;
-    if (DLY) {
+    if (DLY && tile == 0 && h == 0 && commit_status) {
       last_v = last_acc[b];
-      const int tj = clampi(lane, Npv - 1);
-      pmask_l = prev.mask[(size_t)b * Npv + tj];
-      pG_l = prev.G[(size_t)bh * Npv + tj];
+      pmask_l = prev.mask[(size_t)b * Npv + clampi(lane, Npv - 1)];
     }
     // the head's loads are queued: the state waves may now request theirs
     ws_arrive(&sm.sync);
@@ -218,34 +330,29 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
       }
       if (tile == 0 && t == 0 && h == 0 && dev_status)
         dev_status[b] = anybad ? GDN_ERR_TOPOLOGY : GDN_OK;
-      if (DLY) {  // the previous draft's accepted path, root first, and its coefficients
+      if (DLY && tile == 0 && h == 0 && commit_status) {  // the previous draft's last accepted node
         const int lst = __builtin_amdgcn_readfirstlane(last_v);
         const bool in_rng = lst >= 0 && lst < Npv;
-        const int lc = in_rng ? lst : 0;
-        const uint64_t valid = Npv >= 64 ? ~0ull : ((1ull << Npv) - 1ull);
-        const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)pmask_l, lc);
-        const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(pmask_l >> 32), lc);
-        const uint64_t pm = in_rng ? ((((uint64_t)mhi << 32) | mlo) & valid) : 0ull;
-        const bool okp = in_rng && ((pm >> lst) & 1ull);
-        const float Glast =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pG_l), lc));
-        if (okp && ((pm >> t) & 1ull)) {
-          const int pos = __popcll(pm & ((1ull << t) - 1ull));
-          sm.dnode[pos] = t;
-          sm.dc[pos] = expf(Glast - pG_l);  // the commit kernel's coefficient
-        }
-        if (t == 0) {
-          sm.dn = okp ? __popcll(pm) : 0;
-          sm.ds0 = expf(Glast);
-          if (tile == 0 && h == 0 && commit_status)
-            commit_status[b] = (lst == -1 || okp) ? GDN_OK : GDN_ERR_TOPOLOGY;
-        }
+        const uint32_t mlo = __builtin_amdgcn_readlane((uint32_t)pmask_l, in_rng ? lst : 0);
+        const uint32_t mhi = __builtin_amdgcn_readlane((uint32_t)(pmask_l >> 32), in_rng ? lst : 0);
+        const bool okp = in_rng && ((((((uint64_t)mhi << 32) | mlo)) >> lst) & 1ull);
+        if (t == 0) commit_status[b] = (lst == -1 || okp) ? GDN_OK : GDN_ERR_TOPOLOGY;
       }
     }
   } else {
     // The head waves' Q and K requests go first (the state's would otherwise
     // fill the memory queues ahead of them and delay every per-head step).
     ws_wait(&sm.sync, 4);
+    // the previous draft's last accepted node, the masks and G (the path)
+    int last_v = -1;
+    uint64_t pmask_l = 0;
+    float pG_l = 0.f;
+    if (DLY) {
+      last_v = last_acc[b];
+      const int tj = clampi(lane, Npv - 1);
+      pmask_l = prev.mask[(size_t)b * Npv + tj];
+      pG_l = prev.G[(size_t)bh * Npv + tj];
+    }
     // The state is read and written once per step: non-temporal accesses
     // stream it past the caches, which keep Q, K (read by the head's four
     // tiles) and leave less to write back when the kernel ends.
@@ -263,94 +370,13 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
         const int t = clampi(16 * j + 4 * lg + r, N - 1);
         vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
       }
+    if (DLY) dn_s = dly_commit(last_v, pmask_l, pG_l);
   }
   if (head)
     ws_sync(&sm.sync, 8);  // staged Q/K, T zeroed, topology, path
   else
     ws_wait(&sm.sync, 8);
 
-  // the previous draft's accepted path applied to this state wave's rows in
-  // the commit kernel's operation order (scale by e^{G_last}, then one fmaf
-  // per path node in path order), then the committed rows written back
-  auto dly_commit = [&]() {
-    const int dn = sm.dn;
-    if (dn == 0) return;  // uniform
-    // every state register is consumed here, before the first write-back
-    // store, so no later wait on a load also waits for the stores
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) pin_vgpr(Sraw[ks][0]), pin_vgpr(Sraw[ks][1]);
-    const float s0 = sm.ds0;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Sraw[ks][0][e] = Sraw[ks][0][e] * s0;
-        Sraw[ks][1][e] = Sraw[ks][1][e] * s0;
-      }
-    bf16_t* kst = sm.dk + (wave - 4) * (kWsChunk * kMaxDim);
-    constexpr int KR = kWsChunk * kMaxDim / 8 / 64;  // 16-byte chunks per lane and round
-    for (int c0 = 0; c0 < dn; c0 += kWsChunk) {  // uniform
-      u32x4 kr[KR];
-#pragma unroll
-      for (int x = 0; x < KR; ++x) {
-        const int idx = lane + 64 * x;
-        const int j = idx / (kMaxDim / 8);
-        const int col = clampi(8 * (idx % (kMaxDim / 8)), dk - 8);
-        const int nd = sm.dnode[clampi(c0 + j, dn - 1)];
-        kr[x] = *reinterpret_cast<const u32x4*>(prev.K + ((size_t)bh * Npv + nd) * dk + col);
-      }
-      // B operand of group m: lane (row l16, k = lg) holds c u' of path node
-      // c0 + 4 m + lg for this lane's state row; past the path -0, whose
-      // product leaves every accumulator bit unchanged (x + -0 = x)
-      float cu[kWsChunk / 4];
-#pragma unroll
-      for (int m = 0; m < kWsChunk / 4; ++m) {
-        const int jn = c0 + 4 * m + lg;
-        const int jc = clampi(jn, dn - 1);
-        const float c = sm.dc[jc] * prev.up[((size_t)bh * Npv + sm.dnode[jc]) * dv + clampi(srow, dv - 1)];
-        cu[m] = jn < dn ? c : -0.0f;
-      }
-      // this wave's reads of the previous round precede these writes (one
-      // wave's LDS operations complete in order)
-#pragma unroll
-      for (int x = 0; x < KR; ++x) {
-        const int idx = lane + 64 * x;
-        const int c8 = 8 * (idx % (kMaxDim / 8));
-        *reinterpret_cast<u32x4*>(kst + (idx / (kMaxDim / 8)) * kMaxDim + c8) = kr[x];
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
-      const int nc = __builtin_amdgcn_readfirstlane(dn - c0 < kWsChunk ? dn - c0 : kWsChunk);
-      // The rank-n update on FP32 MFMA, four path nodes per product: for the
-      // tile (ks, half), D row 4 g + r is state column 32 ks + 8 g + 4 half + r
-      // and D column j is state row 16 cj + j, so a lane's accumulator is its
-      // own Sraw[ks][half].  v_mfma_f32_16x16x4_f32 adds its four products
-      // one after another, each as a fused multiply-add in k order, so node
-      // by node in path order this is bitwise the commit kernel's fmaf
-      // sequence.  A operand: lane (row l16, k = lg) holds k of node
-      // c0 + 4 m + lg at that row's column.
-      const int kcol = 8 * (l16 >> 2) + (l16 & 3);
-#pragma unroll
-      for (int m = 0; m < kWsChunk / 4; ++m) {
-        if (4 * m < nc) {  // uniform
-          const int jn = 4 * m + lg;
-          const bool on = c0 + jn < dn;
-          const bf16_t* kr0 = kst + jn * kMaxDim + kcol;
-          float av[KS][2];
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) av[ks][hf] = on ? widen1(kr0[32 * ks + 4 * hf]) : 0.f;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) Sraw[ks][hf] = mfma16x16x4f32(av[ks][hf], cu[m], Sraw[ks][hf]);
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next round's writes
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
-  };
   // write-back of the committed columns 32 ks + 8 lg .. + 7 of this lane's row
   auto dly_store = [&](int ks) {
     const int col = 32 * ks + koff;
@@ -373,8 +399,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
 
   if (sm.bad) {  // uniform: zero this tile's outputs (a delayed commit still applies)
     if (!head) {
-      if (DLY && sm.dn > 0) {
-        dly_commit();
+      if (DLY && dn_s > 0) {  // uniform
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) dly_store(ks);
       }
@@ -524,11 +549,10 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     }
   }
 
-  // state waves: delayed commit, contraction, R
+  // state waves: contraction (with the committed rows written back), R
   f32x4 yacc[2 * NQT];
   f32x4 rv[NQT];
   if (!head) {
-    if (DLY) dly_commit();
 #pragma unroll
     for (int i = 0; i < 2 * NQT; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     // 4. Y: the K row tiles as K S0^T (rows = nodes, as the B operand of
@@ -545,7 +569,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     // back as the step is contracted: the memory system accepts the stores
     // only as fast as it drains them, and the matrix products of the previous
     // steps keep running meanwhile.
-    const bool wb = DLY && sm.dn > 0;  // uniform
+    const bool wb = DLY && dn_s > 0;  // uniform
     aload(0, afr[0]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {  // zero-padded past dk: no branch
