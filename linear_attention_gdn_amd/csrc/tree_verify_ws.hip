@@ -18,11 +18,14 @@
 //   state waves (4 .. 3 + SW): wave 4 + c owns state rows 16 c .. 16 c + 15
 //     of the tile.  They request their state rows and V at once (straight
 //     into MFMA operand registers); for the delayed form each finds the
-//     previous draft's accepted path itself, stages the path's k rows in its
-//     own LDS area and applies the path to its rows before it first waits for
-//     the head waves.  They then run the contraction [Q; K] S0^T on bf16 MFMA
-//     (FP32 state split into bf16 hi + lo) while writing the committed rows
-//     back, form R = beta (V - e^G K S0^T), and after T is ready chain
+//     previous draft's accepted path itself and requests the path's k rows
+//     (staged in LDS together) and u' of its rows, and the path is applied to
+//     its rows either block by block inside the contraction (64-row tiles,
+//     where the state rows arrive only as fast as the memory system drains
+//     them) or at once while the head waves still wait for Q and K (narrower
+//     tiles).  They run the contraction [Q; K] S0^T on bf16 MFMA (FP32 state
+//     split into bf16 hi + lo) while writing the committed rows back, form
+//     R = beta (V - e^G K S0^T), and after T is ready chain
 //     U' = T R and O = scale e^G Q S0^T + Attn U' through registers as
 //     16x16x16 products, the transposed products giving each lane four
 //     consecutive state rows of one node, stored as 16-byte vectors.
@@ -49,12 +52,14 @@ struct WsLds {
   uint64_t mask[kMaxNodes];
   float G[kMaxNodes], eG[kMaxNodes], beta[kMaxNodes];
   int bad;
-  int sync;  // arrivals at the head waves' own barriers
-  // delayed commit, per state wave: the accepted path (root first), its
-  // coefficients and the staged k rows
+  int sync;   // arrivals at the head waves' own barriers
+  int csync;  // arrivals of the state waves at the staged k rows
+  // delayed commit: per state wave the accepted path (root first) and its
+  // coefficients; the k rows of the path's first kWsChunk nodes (zero rows
+  // past the path), staged by the state waves together
   int dnode[DLY ? SW : 1][kMaxNodes];
   float dc[DLY ? SW : 1][kMaxNodes];
-  alignas(16) bf16_t dk[DLY ? SW * kWsChunk * kMaxDim : 8];
+  alignas(16) bf16_t ck[DLY ? kWsChunk * kMaxDim : 8];
 };
 
 // The head waves synchronise among themselves through an LDS counter, so the
@@ -62,7 +67,8 @@ struct WsLds {
 // system accepts only as fast as it drains them), never hold them up: each
 // head wave completes its LDS operations, adds one, and waits until the
 // counter reaches `target` (four arrivals per round).  A state wave waits
-// without arriving.  One wave's LDS operations complete in order, and LDS is
+// without arriving (the state waves arrive only at a second counter of the
+// same kind, for the delayed commit's staged k rows).  One wave's LDS operations complete in order, and LDS is
 // one memory, so the data written before an arrival is visible to every wave
 // that has seen the count.  The wait is bounded (far beyond any real wait),
 // so a wave can never spin forever.
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   const int srow4 = r0 + 16 * cj + 4 * lg;
   const bool sok4 = srow4 < dv;  // dv % 4 == 0: all four rows or none
 
-  if (tid == 0) sm.sync = 0;
+  if (tid == 0) sm.sync = 0, sm.csync = 0;
   __syncthreads();  // the counter is zero before any wave arrives
   // the head waves carry the chain of dependent per-head steps: their
   // instructions go first when both roles compete for a SIMD or the memory
@@ -144,11 +150,23 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   // to this wave's rows in the commit kernel's operation order (scale by
   // e^{G_last}, then one fmaf per path node in path order).  Each state wave
   // finds the path itself from the last accepted node's ancestor mask and the
-  // path's G, so the k rows and u' of the path are requested while the head
-  // waves still stage Q and K, and the commit is done before the state waves
-  // first wait for the head.  Returns the path length (uniform).
-  auto dly_commit = [&](int last_v, uint64_t pmask_l, float pG_l) -> int {
-    const int sw = wave - 4;
+  // path's G, and requests the path's k rows (its share of them, staged in
+  // LDS for all state waves) and u' of its own rows before its state rows,
+  // so that they arrive first.
+  const int sw = wave >= 4 ? wave - 4 : 0;
+  // Two schedules.  With four state waves (a grid that fills the GPU, whose
+  // memory system accepts the state rows only as fast as it drains them) the
+  // path's operands are requested ahead of the state rows and the commit is
+  // applied block by block inside the contraction, as the rows arrive.  With
+  // fewer (an idle memory system, the state rows arriving at once) they are
+  // requested after the state rows and the whole commit is applied while the
+  // head waves still wait for Q and K.
+  constexpr bool kBlockCommit = SW == 4;
+  constexpr int KQ = kWsChunk * (kMaxDim / 8) / (64 * SW);  // 16-byte k chunks per lane
+  u32x4 kq[DLY ? KQ : 1];
+  float upr[kWsChunk / 4];  // u' of path node 4 m + lg for this lane's state row
+  float s0c = 1.f;          // e^{G_last}
+  auto path_fetch = [&](int last_v, uint64_t pmask_l, float pG_l) -> int {
     int* const dnode = sm.dnode[DLY ? sw : 0];
     float* const dc = sm.dc[DLY ? sw : 0];
     const int lst = __builtin_amdgcn_readfirstlane(last_v);
@@ -166,91 +184,149 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
       dnode[pos] = lane;
       dc[pos] = expf(Glast - pG_l);  // the commit kernel's coefficient
     }
+    s0c = expf(Glast);
     const int dn = okp ? __popcll(pm) : 0;
-    if (dn == 0) return 0;  // uniform
     // (one wave's LDS operations complete in order: the reads below see the
-    // path just written)
-    bf16_t* kst = sm.dk + (DLY ? sw : 0) * (kWsChunk * kMaxDim);
-    constexpr int KR = kWsChunk * kMaxDim / 8 / 64;  // 16-byte chunks per lane and round
-    u32x4 kr[KR];
-    float cu[kWsChunk / 4];
-    // the k rows of path nodes c0 .. c0 + 15 and the B operand of group m: lane
-    // (row l16, k = lg) holds c u' of path node c0 + 4 m + lg for this lane's
-    // state row; past the path -0, whose product leaves every accumulator bit
-    // unchanged (x + -0 = x)
-    auto fetch = [&](int c0) {
+    // path just written).  No branch around the loads: clamped addresses.
+    const int lastp = dn > 0 ? dn - 1 : 0;
 #pragma unroll
-      for (int x = 0; x < KR; ++x) {
-        const int idx = lane + 64 * x;
-        const int j = idx / (kMaxDim / 8);
-        const int col = clampi(8 * (idx % (kMaxDim / 8)), dk - 8);
-        const int nd = dnode[clampi(c0 + j, dn - 1)];
-        kr[x] = *reinterpret_cast<const u32x4*>(prev.K + ((size_t)bh * Npv + nd) * dk + col);
+    for (int x = 0; x < KQ; ++x) {
+      const int idx = 64 * KQ * sw + lane + 64 * x;
+      const int c8 = clampi(8 * (idx % (kMaxDim / 8)), dk - 8);
+      const int nd = dn > 0 ? dnode[clampi(idx / (kMaxDim / 8), lastp)] : 0;
+      kq[x] = *reinterpret_cast<const u32x4*>(prev.K + ((size_t)bh * Npv + nd) * dk + c8);
+    }
+#pragma unroll
+    for (int m = 0; m < kWsChunk / 4; ++m) {
+      const int nd = dn > 0 ? dnode[clampi(4 * m + lg, lastp)] : 0;
+      upr[m] = prev.up[((size_t)bh * Npv + nd) * dv + clampi(srow, dv - 1)];
+    }
+    return dn;
+  };
+  // this wave's share of the k rows into LDS (after the state rows were
+  // requested), announced to the other state waves
+  auto stage_k = [&](int dn) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int x = 0; x < KQ; ++x) {
+      const int idx = 64 * KQ * sw + lane + 64 * x;
+      const int j = idx / (kMaxDim / 8), c8 = 8 * (idx % (kMaxDim / 8));
+      *reinterpret_cast<u32x4*>(sm.ck + j * kMaxDim + c8) = (j < dn && c8 < dk) ? kq[x] : z;
+    }
+    ws_arrive(&sm.csync);
+  };
+  // The update on FP32 MFMA, four path nodes per product.  For the tile
+  // (ks, half), D row 4 g + r is state column 32 ks + 8 g + 4 half + r and D
+  // column j is state row 16 cj + j, so a lane's accumulator is its own
+  // Sraw[ks][half]; the A operand, lane (row l16, k = lg), holds k of path
+  // node 4 m + lg at that row's column, the B operand c u' of that node for
+  // the lane's state row.  v_mfma_f32_16x16x4_f32 adds its four products one
+  // after another, each as a fused multiply-add in k order, so node by node
+  // in path order this is bitwise the commit kernel's fmaf sequence.  Past
+  // the path the operands are 0 and -0, whose product leaves every
+  // accumulator bit unchanged (x + -0 = x).
+  const int kcol = 8 * (l16 >> 2) + (l16 & 3);
+  // Paths of at most kWsChunk nodes (the usual case): the 32-column blocks
+  // ks are committed one by one inside the contraction, each issued one
+  // block ahead of the contraction products that take it, so the commit
+  // overlaps the arrival of the state rows as the contraction does and its
+  // products are complete when the block is written back and split.
+  auto commit_ks = [&](int ks, int ng, const float (&cuv)[kWsChunk / 4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Sraw[ks][0][e] = Sraw[ks][0][e] * s0c;
+      Sraw[ks][1][e] = Sraw[ks][1][e] * s0c;
+    }
+#pragma unroll
+    for (int m = 0; m < kWsChunk / 4; ++m) {
+      if (m < ng) {  // uniform
+        const bf16_t* kr0 = sm.ck + (4 * m + lg) * kMaxDim + 32 * ks + kcol;
+        Sraw[ks][0] = mfma16x16x4f32(widen1(kr0[0]), cuv[m], Sraw[ks][0]);
+        Sraw[ks][1] = mfma16x16x4f32(widen1(kr0[4]), cuv[m], Sraw[ks][1]);
       }
-#pragma unroll
-      for (int m = 0; m < kWsChunk / 4; ++m) {
-        const int jn = c0 + 4 * m + lg;
-        const int jc = clampi(jn, dn - 1);
-        const float c = dc[jc] * prev.up[((size_t)bh * Npv + dnode[jc]) * dv + clampi(srow, dv - 1)];
-        cu[m] = jn < dn ? c : -0.0f;
-      }
-    };
-    fetch(0);
-    // every state register is consumed here, before the first write-back
-    // store, so no later wait on a load also waits for the stores
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) pin_vgpr(Sraw[ks][0]), pin_vgpr(Sraw[ks][1]);
-    const float s0 = expf(Glast);
+    }
+  };
+  // Longer paths, and drafts that failed validation: every operand read from
+  // global memory, four path nodes at a time, the whole commit done before
+  // the contraction (it consumes every state register before the first
+  // write-back store, so no later wait on a load also waits for the stores).
+  auto commit_global = [&](int dn) {
+    const int* const dnode = sm.dnode[DLY ? sw : 0];
+    const float* const dc = sm.dc[DLY ? sw : 0];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        Sraw[ks][0][e] = Sraw[ks][0][e] * s0;
-        Sraw[ks][1][e] = Sraw[ks][1][e] * s0;
+        Sraw[ks][0][e] = Sraw[ks][0][e] * s0c;
+        Sraw[ks][1][e] = Sraw[ks][1][e] * s0c;
       }
-    for (int c0 = 0; c0 < dn; c0 += kWsChunk) {  // uniform
-      if (c0 > 0) fetch(c0);
-      // this wave's reads of the previous round precede these writes (one
-      // wave's LDS operations complete in order)
+    for (int g0 = 0; g0 < dn; g0 += 4) {  // uniform
+      const int jn = g0 + lg;
+      const bool on = jn < dn;
+      const int jc = clampi(jn, dn - 1);
+      const int nd = dnode[jc];
+      const float c = dc[jc] * prev.up[((size_t)bh * Npv + nd) * dv + clampi(srow, dv - 1)];
+      const float cuv = on ? c : -0.0f;
+      const bf16_t* kr0 = prev.K + ((size_t)bh * Npv + nd) * dk;
+      float av[KS][2];
 #pragma unroll
-      for (int x = 0; x < KR; ++x) {
-        const int idx = lane + 64 * x;
-        const int c8 = 8 * (idx % (kMaxDim / 8));
-        *reinterpret_cast<u32x4*>(kst + (idx / (kMaxDim / 8)) * kMaxDim + c8) = kr[x];
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's rows are in LDS
-      const int nc = __builtin_amdgcn_readfirstlane(dn - c0 < kWsChunk ? dn - c0 : kWsChunk);
-      // The rank-n update on FP32 MFMA, four path nodes per product: for the
-      // tile (ks, half), D row 4 g + r is state column 32 ks + 8 g + 4 half + r
-      // and D column j is state row 16 cj + j, so a lane's accumulator is its
-      // own Sraw[ks][half].  v_mfma_f32_16x16x4_f32 adds its four products
-      // one after another, each as a fused multiply-add in k order, so node
-      // by node in path order this is bitwise the commit kernel's fmaf
-      // sequence.  A operand: lane (row l16, k = lg) holds k of node
-      // c0 + 4 m + lg at that row's column.
-      const int kcol = 8 * (l16 >> 2) + (l16 & 3);
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          av[ks][hf] = on ? widen1(kr0[clampi(32 * ks + 4 * hf + kcol, dk - 1)]) : 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) Sraw[ks][hf] = mfma16x16x4f32(av[ks][hf], cuv, Sraw[ks][hf]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
+  };
+  // c u' of path node 4 m + lg for this lane's state row (the commit kernel's
+  // product), -0 past the path
+  auto make_cuv = [&](int dn, float (&cuv)[kWsChunk / 4]) {
+    const float* const dc = sm.dc[DLY ? sw : 0];
+#pragma unroll
+    for (int m = 0; m < kWsChunk / 4; ++m) {
+      const int j = 4 * m + lg;
+      cuv[m] = j < dn ? dc[clampi(j, dn - 1)] * upr[m] : -0.0f;
+    }
+  };
+  // the whole commit at once
+  auto commit_all = [&](int dn) {
+    if (dn > kWsChunk) {  // uniform
+      commit_global(dn);
+    } else {
+      float cuv[kWsChunk / 4];
+      make_cuv(dn, cuv);
+      ws_wait(&sm.csync, SW);  // every state wave's share of the k rows is in LDS
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Sraw[ks][0][e] = Sraw[ks][0][e] * s0c;
+          Sraw[ks][1][e] = Sraw[ks][1][e] * s0c;
+        }
+      // node group by node group: the group's operands read at once, then
+      // 2 KS independent products
 #pragma unroll
       for (int m = 0; m < kWsChunk / 4; ++m) {
-        if (4 * m < nc) {  // uniform
-          const int jn = 4 * m + lg;
-          const bool on = c0 + jn < dn;
-          const bf16_t* kr0 = kst + jn * kMaxDim + kcol;
+        if (4 * m < dn) {  // uniform
+          const bf16_t* kr0 = sm.ck + (4 * m + lg) * kMaxDim + kcol;
           float av[KS][2];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) av[ks][hf] = on ? widen1(kr0[32 * ks + 4 * hf]) : 0.f;
+            for (int hf = 0; hf < 2; ++hf) av[ks][hf] = widen1(kr0[32 * ks + 4 * hf]);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) Sraw[ks][hf] = mfma16x16x4f32(av[ks][hf], cu[m], Sraw[ks][hf]);
+            for (int hf = 0; hf < 2; ++hf) Sraw[ks][hf] = mfma16x16x4f32(av[ks][hf], cuv[m], Sraw[ks][hf]);
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next round's writes
-    }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
-    return dn;
+      for (int ks = 0; ks < KS; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
+    }
   };
 
   if (head) {
@@ -342,17 +418,20 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   } else {
     // The head waves' Q and K requests go first (the state's would otherwise
     // fill the memory queues ahead of them and delay every per-head step).
-    ws_wait(&sm.sync, 4);
-    // the previous draft's last accepted node, the masks and G (the path)
+    // the previous draft's last accepted node, the masks and G (the path),
+    // then the path's operands (ahead of the state rows for the block-wise
+    // commit, after them otherwise)
     int last_v = -1;
     uint64_t pmask_l = 0;
     float pG_l = 0.f;
     if (DLY) {
-      last_v = last_acc[b];
       const int tj = clampi(lane, Npv - 1);
+      last_v = last_acc[b];
       pmask_l = prev.mask[(size_t)b * Npv + tj];
       pG_l = prev.G[(size_t)bh * Npv + tj];
     }
+    if (DLY && kBlockCommit) dn_s = path_fetch(last_v, pmask_l, pG_l);
+    ws_wait(&sm.sync, 4);
     // The state is read and written once per step: non-temporal accesses
     // stream it past the caches, which keep Q, K (read by the head's four
     // tiles) and leave less to write back when the kernel ends.
@@ -370,7 +449,9 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
         const int t = clampi(16 * j + 4 * lg + r, N - 1);
         vreg[j][r] = v[(((size_t)b * N + t) * H + h) * dv + clampi(srow, dv - 1)];
       }
-    if (DLY) dn_s = dly_commit(last_v, pmask_l, pG_l);
+    if (DLY && !kBlockCommit) dn_s = path_fetch(last_v, pmask_l, pG_l);
+    if (DLY && dn_s > 0 && dn_s <= kWsChunk) stage_k(dn_s);  // uniform
+    if (DLY && !kBlockCommit && dn_s > 0) commit_all(dn_s);  // uniform
   }
   if (head)
     ws_sync(&sm.sync, 8);  // staged Q/K, T zeroed, topology, path
@@ -400,6 +481,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   if (sm.bad) {  // uniform: zero this tile's outputs (a delayed commit still applies)
     if (!head) {
       if (DLY && dn_s > 0) {  // uniform
+        if (kBlockCommit) commit_global(dn_s);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) dly_store(ks);
       }
@@ -569,25 +651,47 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     // back as the step is contracted: the memory system accepts the stores
     // only as fast as it drains them, and the matrix products of the previous
     // steps keep running meanwhile.
-    const bool wb = DLY && dn_s > 0;  // uniform
+    const bool wb = DLY && dn_s > 0;                       // uniform
+    const bool lcm = DLY && kBlockCommit && dn_s > 0 && dn_s <= kWsChunk;  // uniform: block by block
+    float cuv[kWsChunk / 4] = {};
+    const int ngc = (dn_s + 3) >> 2;
+    if (DLY && kBlockCommit && dn_s > kWsChunk) commit_global(dn_s);
+    if (lcm) {
+      make_cuv(dn_s, cuv);
+      ws_wait(&sm.csync, SW);  // every state wave's share of the k rows is in LDS
+    }
+    // block ks of the (committed) rows: written back, then split into the
+    // bf16 hi + lo operands of the contraction
+    bf16x8 bhi[2], blo[2];
+    auto prep = [&](int ks) {
+      if (wb) dly_store(ks);
+      const bool okk = sok && 32 * ks + koff < dk;
+      split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi[ks & 1], blo[ks & 1]);
+    };
+    if (lcm) {
+      commit_ks(0, ngc, cuv);
+      mfma_drain(Sraw[0][0], Sraw[0][1]);
+    }
+    prep(0);
     aload(0, afr[0]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {  // zero-padded past dk: no branch
-      if (wb) dly_store(ks);
       if (ks + 1 < KS) aload(ks + 1, afr[(ks + 1) & 1]);
+      if (lcm && ks + 1 < KS) commit_ks(ks + 1, ngc, cuv);
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 bhi, blo;
-      const bool okk = sok && 32 * ks + koff < dk;
-      split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi, blo);
 #pragma unroll
       for (int i = 0; i < 2 * NQT; ++i) {
         if (i < NQT) {
-          yacc[i] = mfma16x16x32(bhi, afr[ks & 1][i], yacc[i]);
-          yacc[i] = mfma16x16x32(blo, afr[ks & 1][i], yacc[i]);
+          yacc[i] = mfma16x16x32(bhi[ks & 1], afr[ks & 1][i], yacc[i]);
+          yacc[i] = mfma16x16x32(blo[ks & 1], afr[ks & 1][i], yacc[i]);
         } else {
-          yacc[i] = mfma16x16x32(afr[ks & 1][i], bhi, yacc[i]);
-          yacc[i] = mfma16x16x32(afr[ks & 1][i], blo, yacc[i]);
+          yacc[i] = mfma16x16x32(afr[ks & 1][i], bhi[ks & 1], yacc[i]);
+          yacc[i] = mfma16x16x32(afr[ks & 1][i], blo[ks & 1], yacc[i]);
         }
+      }
+      if (ks + 1 < KS) {
+        if (lcm) mfma_drain(Sraw[ks + 1][0], Sraw[ks + 1][1]);
+        prep(ks + 1);
       }
     }
     mfma_drain_all(yacc);
