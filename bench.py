@@ -70,7 +70,7 @@ KERNEL_SOURCES = {
     "gdn_chain_verify_delayed": ["chain_verify.hip"],
     "gdn_tree_verify": ["tree_verify.hip", "tree_verify_ws.hip", "tree_common.h"],
     "gdn_tree_verify_delayed": ["tree_verify.hip", "tree_verify_ws.hip", "tree_common.h"],
-    "gdn_layer_verify": ["tree_verify.hip", "tree_common.h"],
+    "gdn_layer_verify": ["tree_verify.hip", "tree_verify_ws.hip", "tree_common.h"],
     "gdn_commit_path": ["commit.hip"],
     "gdn_linear": ["layer.hip"],
 }
