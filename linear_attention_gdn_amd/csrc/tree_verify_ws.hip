@@ -457,6 +457,15 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     ws_sync(&sm.sync, 8);  // staged Q/K, T zeroed, topology, path
   else
     ws_wait(&sm.sync, 8);
+  // With a delayed commit the state waves carry the longer chain from here
+  // (commit, write-back and contraction against the head's Gram and solve):
+  // their instructions now go first.
+  if (DLY) {
+    if (head)
+      __builtin_amdgcn_s_setprio(1);
+    else
+      __builtin_amdgcn_s_setprio(2);
+  }
 
   // write-back of the committed columns 32 ks + 8 lg .. + 7 of this lane's row
   auto dly_store = [&](int ks) {
