@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     yq = fmaf(S[2], o.qc.z, yq);
     yk = fmaf(S[3], o.kc.w, yk);
     yq = fmaf(S[3], o.qc.w, yq);
-    yk = wave64_sum(yk);
+    yk = wave64_sum_uniform(yk);
     yq = wave64_sum_hi(yq);  // complete in lanes 48..63 only
     const float u = be * (vt - al * yk);
     S[0] = fmaf(u, o.kc.x, al * S[0]);

@@ -216,6 +216,15 @@ __device__ inline float wave64_sum_hi(float x) {
   return x;
 }
 
+// Sum over the whole wave as a wave-uniform value: the last row's complete
+// sum (wave64_sum_hi) read from lane 63 into a scalar register.  The row
+// sums are added in the same pairs as in wave64_sum, (r3 + r2) + (r1 + r0)
+// against (r0 + r1) + (r2 + r3), so the result is bitwise the same.
+__device__ inline float wave64_sum_uniform(float x) {
+  x = wave64_sum_hi(x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
 // Fragment convention (lane l of a wave64):
 //   A: row i = l % 16, k = 8 * (l / 16) + e, e = 0..7

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(
       yk = fmaf(Sr[1], cur.kx.y, yk);
       yk = fmaf(Sr[2], cur.kx.z, yk);
       yk = fmaf(Sr[3], cur.kx.w, yk);
-      yk = wave64_sum(yk);
+      yk = wave64_sum_uniform(yk);
       const float u = be * (vt - al * yk);
       if (kOut) {
         const int t = __builtin_amdgcn_readlane(t_l, pos);
