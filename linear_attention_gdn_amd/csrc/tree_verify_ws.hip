@@ -479,6 +479,12 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
 
   // gated form (gdn_layer_verify): Y = bf16(O * SiLU(gate)) for node t and the
   // four state rows srow4 .. srow4 + 3, with gdn_gate_merge's arithmetic
+  auto store_gated_s = [&](size_t o, const f32x4& x, const f32x4& sg) {
+    u32x2 w;
+    w.x = (uint32_t)to_bf16(x.x * sg.x) | ((uint32_t)to_bf16(x.y * sg.y) << 16);
+    w.y = (uint32_t)to_bf16(x.z * sg.z) | ((uint32_t)to_bf16(x.w * sg.w) << 16);
+    *reinterpret_cast<u32x2*>(ga.Y + o) = w;
+  };
   auto store_gated = [&](int t, size_t o, const f32x4& x) {
     const float* gp = ga.gate + ((size_t)b * N + t) * ga.ldg + h * dv + srow4;
     u32x2 w;
@@ -643,6 +649,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   // state waves: contraction (with the committed rows written back), R
   f32x4 yacc[2 * NQT];
   f32x4 rv[NQT];
+  f32x4 gsl[GATE ? NQT : 1];  // gated form: SiLU(gate) of node 16 i + l16, rows srow4 .. + 3
   if (!head) {
 #pragma unroll
     for (int i = 0; i < 2 * NQT; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -714,6 +721,16 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
         const float vv = sok ? widen1(vreg[nb][r]) : 0.f;
         rv[nb][r] = sm.beta[t] * (vv - sm.eG[t] * yacc[NQT + nb][r]);
       }
+    // gated form: the gate's SiLU for the epilogue's outputs, formed before
+    // the barrier (the same operations as in the epilogue's product)
+    if constexpr (GATE) {
+#pragma unroll
+      for (int i = 0; i < NQT; ++i) {
+        const int t = clampi(16 * i + l16, N - 1);
+        const float* gp = ga.gate + ((size_t)b * N + t) * ga.ldg + h * dv + clampi(srow4, dv - 4);
+        gsl[i] = f32x4{silu(gp[0]), silu(gp[1]), silu(gp[2]), silu(gp[3])};
+      }
+    }
   }
 
   if (head && deep) {  // uniform: blocked forward substitution, as in tree_verify.hip
@@ -828,7 +845,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
       if (t < N && sok4) {
         const size_t o = (((size_t)b * N + t) * H + h) * dv + srow4;
         if constexpr (GATE)
-          store_gated(t, o, ot[i]);
+          store_gated_s(o, ot[i], gsl[i]);
         else
           __builtin_nontemporal_store(ot[i], reinterpret_cast<f32x4*>(out + o));
       }
