@@ -67,7 +67,8 @@ __device__ inline u32x4 bload16nt(__amdgpu_buffer_rsrc_t r, int off) {
 template <int MT, int NT, int WAVES>
 __device__ inline void linear_epilogue(const float (&red)[WAVES][MT * 16][NT * 16 + 4], int tid,
                                        int nthreads, int M, int Nc, int n0, const float* R,
-                                       float* C, bf16_t* Cb) {
+                                       float* C, bf16_t* Cb, bool pre = false,
+                                       f32x4 rpre = f32x4{0.f, 0.f, 0.f, 0.f}) {
   constexpr int C4 = NT * 4;  // float4 columns per tile row
   for (int idx = tid; idx < MT * 16 * C4; idx += nthreads) {
     const int m = idx / C4;
@@ -78,7 +79,7 @@ __device__ inline void linear_epilogue(const float (&red)[WAVES][MT * 16][NT * 1
 #pragma unroll
     for (int w = 1; w < WAVES; ++w) v += *reinterpret_cast<const f32x4*>(&red[w][m][c]);
     const size_t o = (size_t)m * Nc + n;
-    if (R) v += load4(R + o);
+    if (R) v += (pre && idx == tid) ? rpre : load4(R + o);
     if (C) *reinterpret_cast<f32x4*>(C + o) = v;
     if (Cb) *reinterpret_cast<u32x2*>(Cb + o) = pack_bf16x4(v);
   }
@@ -112,7 +113,7 @@ __device__ inline int wfrag_off(int nt, int ks, int li, int lg, int K) {
   return ((16 * nt + li) * K + 32 * ks + 8 * lg) * 2;
 }
 
-template <int MT, int NT, int KS, bool PK>
+template <int MT, int NT, int KS, bool PK, bool HR>
 __global__ __launch_bounds__(512) void linear_w8_kernel(int M, int Nc, int K,
                                                         const bf16_t* __restrict__ A,
                                                         const bf16_t* __restrict__ W,
@@ -148,6 +149,16 @@ __global__ __launch_bounds__(512) void linear_w8_kernel(int M, int Nc, int K,
     for (int mt = 0; mt < MT; ++mt)
       a[s][mt] = bload16(rA, ((16 * mt + li) * K + w * kw + 8 * lg) * 2 + 64 * s);
   }
+  // with a residual (HR), this thread's epilogue entry of it (the epilogue has
+  // at most one entry per thread) is requested with the operands, so its
+  // memory round trip does not follow the reduction
+  static_assert(MT * 16 * NT * 4 <= 512, "one epilogue entry per thread");
+  f32x4 rpre = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (HR) {
+    const int m = clampi(tid / (NT * 4), M - 1);
+    const int n = clampi(n0 + 4 * (tid % (NT * 4)), Nc - 4);
+    rpre = load4(R + (size_t)m * Nc + n);
+  }
   // Keep every load above this point: the scheduler would otherwise sink
   // them next to their MFMAs and serialise the memory round trips.
   __builtin_amdgcn_sched_barrier(0);
@@ -166,7 +177,7 @@ __global__ __launch_bounds__(512) void linear_w8_kernel(int M, int Nc, int K,
                                    __builtin_bit_cast(bf16x8, b[s][nt]), acc[mt][nt]);
   linear_stash<MT, NT, 8>(red, w, li, lg, acc);
   __syncthreads();
-  linear_epilogue<MT, NT, 8>(red, tid, 512, M, Nc, n0, R, C, Cb);
+  linear_epilogue<MT, NT, 8>(red, tid, 512, M, Nc, n0, R, C, Cb, HR, rpre);
 }
 
 // General form for other K: 4 waves split K into quarters and run a loop
@@ -257,16 +268,22 @@ hipError_t launch_linear_mn(int M, int Nc, int K, const bf16_t* A, const bf16_t*
   const dim3 grid((Nc + 16 * NT - 1) / (16 * NT), (M + 16 * MT - 1) / (16 * MT));
   const int ks = K / 256;
   if (ks * (MT + NT) <= 48 && (ks == 1 || ks == 2 || ks == 4 || ks == 8)) {
+#define GDN_W8(KSV)                                                                            \
+  do {                                                                                         \
+    if (R)                                                                                     \
+      hipLaunchKernelGGL((linear_w8_kernel<MT, NT, KSV, PK, true>), grid, dim3(512), 0, stream, \
+                         M, Nc, K, A, W, R, C, Cb);                                            \
+    else                                                                                       \
+      hipLaunchKernelGGL((linear_w8_kernel<MT, NT, KSV, PK, false>), grid, dim3(512), 0,       \
+                         stream, M, Nc, K, A, W, R, C, Cb);                                    \
+  } while (0)
     switch (ks) {
-      case 1: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 1, PK>), grid, dim3(512), 0,
-                                 stream, M, Nc, K, A, W, R, C, Cb); break;
-      case 2: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 2, PK>), grid, dim3(512), 0,
-                                 stream, M, Nc, K, A, W, R, C, Cb); break;
-      case 4: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 4, PK>), grid, dim3(512), 0,
-                                 stream, M, Nc, K, A, W, R, C, Cb); break;
-      default: hipLaunchKernelGGL((linear_w8_kernel<MT, NT, 8, PK>), grid, dim3(512), 0,
-                                  stream, M, Nc, K, A, W, R, C, Cb); break;
+      case 1: GDN_W8(1); break;
+      case 2: GDN_W8(2); break;
+      case 4: GDN_W8(4); break;
+      default: GDN_W8(8); break;
     }
+#undef GDN_W8
   } else if ((K / 128) % 4 == 0 && MT + NT <= 4) {
     hipLaunchKernelGGL((linear_kernel<MT, NT, 4, PK>), grid, dim3(256), 0, stream, M, Nc,
                        K, A, W, R, C, Cb);
