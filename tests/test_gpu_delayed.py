@@ -124,12 +124,33 @@ def _prev_record(prev: W.Draft):
 ])
 def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo,
                                                    new_topo):
-    seed = 7 * B + Np + N
+    _fused_equals_separate(dtype, B, Np, N, H, dk, dv, prev_topo, new_topo, reject=False)
+
+
+# The split-role kernel's rejected-draft path with a pending commit: 64-row
+# tiles (commit applied from global memory there) with short and long
+# previous paths, and 16-row tiles (commit applied before the first wait on
+# the head waves).  The last sequence's new draft is not topological.
+@pytest.mark.parametrize("B,Np,N,H,prev_topo", [
+    (8, 64, 64, 8, "branching"),
+    (8, 64, 64, 8, "spine"),
+    (1, 32, 32, 8, "window"),
+])
+def test_delayed_tree_verify_rejected_draft_is_commit_then_verify(B, Np, N, H, prev_topo):
+    _fused_equals_separate("bf16", B, Np, N, H, 256, 256, prev_topo, "branching", reject=True)
+
+
+def _fused_equals_separate(dtype, B, Np, N, H, dk, dv, prev_topo, new_topo, reject):
+    seed = 7 * B + Np + N + (1000 if reject else 0)
     accept = "full" if prev_topo == "chain" else "leaf_geometric"
     prev = W.make_draft(B, Np, H, dk, dv, topology=prev_topo, accept=accept, dtype=dtype,
                         seed=seed)
     new = W.make_draft(B, N, H, dk, dv, topology=new_topo, accept="none", dtype=dtype,
                        seed=seed + 1)
+    if reject:
+        bad = new.parents.copy()
+        bad[B - 1, N - 2] = N - 1  # a parent after its child
+        new = new.replace(parents=bad)
     rec_prev, tp = _prev_record(prev)
     tn = dev_tensors(new)
     rng = np.random.default_rng(seed)
@@ -156,6 +177,10 @@ def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, p
         torch.cuda.synchronize()
         for a, b_ in zip(*outs):
             assert torch.equal(a, b_), last
+        if reject:
+            dst = outs[1][4]
+            assert int(dst[B - 1]) == G.GDN_ERR_TOPOLOGY
+            assert (outs[1][1][B - 1] == 0).all()
 
 
 def test_delayed_tree_commit_lands_when_new_topology_is_rejected():
