@@ -121,6 +121,9 @@ def _prev_record(prev: W.Draft):
     # group of four) and ragged dk, dv and N with short paths
     ("bf16", 8, 64, 16, 8, 256, 256, "chain", "window"),
     ("bf16", 32, 23, 17, 8, 72, 100, "random", "random"),
+    # 32-row tiles: full, and ragged with a 40-node accepted path
+    ("bf16", 4, 40, 40, 8, 256, 256, "branching", "branching"),
+    ("bf16", 6, 40, 29, 8, 96, 168, "chain", "random"),
 ])
 def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo,
                                                    new_topo):
@@ -209,6 +212,7 @@ def test_delayed_tree_commit_lands_when_new_topology_is_rejected():
     (1, 32, 32, 8, 256, 256, "window", False, False),
     (2, 9, 17, 3, 64, 40, "random", True, False),        # ragged: N and dv not multiples of 16
     (8, 64, 64, 8, 256, 256, "branching", True, False),  # wide tiles
+    (4, 40, 40, 8, 256, 256, "branching", True, True),   # 32-row tiles, one draft rejected
     (2, 9, 17, 3, 64, 40, "random", True, True),         # sequence 1's new parents rejected
     (2, 12, 12, 2, 32, 16, "random", False, True),
 ])

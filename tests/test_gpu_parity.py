@@ -144,6 +144,10 @@ SHAPES = [
     # registers, ragged dv (a partial last tile) and N
     (32, 37, 8, 72, 100, "bf16", "random"),
     (16, 24, 16, 40, 68, "f32", "spine"),
+    # 32-row state tiles (batch x heads x dv / 64 < 256 <= batch x heads x dv / 32):
+    # full and ragged (a partial last tile, dk and N off the 16 grid)
+    (4, 40, 8, 256, 256, "bf16", "branching"),
+    (6, 29, 8, 96, 168, "bf16", "random"),
 ]
 
 
