@@ -18,7 +18,10 @@
 // bf16 keys instead of an FP32 matrix W.
 //
 // One kernel, one workgroup (4 waves) per (sequence, head, tile of BV state
-// rows).  Each workgroup:
+// rows).  It serves FP32 q/k/v at every tile width, and bf16 q/k/v when even
+// 16-row tiles would give fewer than 128 workgroups (8-row tiles); every
+// other bf16 launch takes the split-role kernel of tree_verify_ws.hip, which
+// computes the same quantities.  Each workgroup:
 //   0. issues one round of loads: Q and K of its head (staged in LDS as bf16,
 //      rows padded against bank conflicts), parents / g / beta, and last its
 //      S0 tile (straight into MFMA B-fragment registers) and V tile.  Loads
