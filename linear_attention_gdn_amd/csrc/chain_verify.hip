@@ -379,8 +379,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     yq = fmaf(S[2], o.qc.z, yq);
     yk = fmaf(S[3], o.kc.w, yk);
     yq = fmaf(S[3], o.qc.w, yq);
-    yk = wave64_sum_uniform(yk);
-    yq = wave64_sum_hi(yq);  // complete in lanes 48..63 only
+    wave64_sum2_uniform(yk, yq, yk, yq);  // both wave-uniform
     const float u = be * (vt - al * yk);
     S[0] = fmaf(u, o.kc.x, al * S[0]);
     S[1] = fmaf(u, o.kc.y, al * S[1]);

@@ -225,6 +225,22 @@ __device__ inline float wave64_sum_uniform(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
+// Two sums over the whole wave, both as wave-uniform values, from one
+// reduction: v_permlane32_swap of the two registers leaves a's upper-half
+// lanes beside a's lower half and b's lower half beside b's upper half, so
+// one add gives lanes 0..31 a's and lanes 32..63 b's pairwise partials; the
+// DPP row sums and one row broadcast then complete a in lane 31 and b in
+// lane 63, read into scalar registers.
+__device__ inline void wave64_sum2_uniform(float a, float b, float& sa, float& sb) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, a),
+                                                   __builtin_bit_cast(unsigned, b), false, false);
+  float x = __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+  x = row16_sum(x);
+  x += dpp_f32<0x142>(x);  // row_bcast:15: rows 1 and 3 complete
+  sa = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  sb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
 // Fragment convention (lane l of a wave64):
 //   A: row i = l % 16, k = 8 * (l / 16) + e, e = 0..7

@@ -299,15 +299,19 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(
       yk = fmaf(Sr[1], cur.kx.y, yk);
       yk = fmaf(Sr[2], cur.kx.z, yk);
       yk = fmaf(Sr[3], cur.kx.w, yk);
-      yk = wave64_sum_uniform(yk);
-      const float u = be * (vt - al * yk);
+      float yq = 0.f;
       if (kOut) {
-        const int t = __builtin_amdgcn_readlane(t_l, pos);
-        float yq = Sr[0] * cur.qx.x;
+        yq = Sr[0] * cur.qx.x;
         yq = fmaf(Sr[1], cur.qx.y, yq);
         yq = fmaf(Sr[2], cur.qx.z, yq);
         yq = fmaf(Sr[3], cur.qx.w, yq);
-        yq = wave64_sum_hi(yq);  // complete in lanes 48..63
+        wave64_sum2_uniform(yk, yq, yk, yq);  // both wave-uniform
+      } else {
+        yk = wave64_sum_uniform(yk);
+      }
+      const float u = be * (vt - al * yk);
+      if (kOut) {
+        const int t = __builtin_amdgcn_readlane(t_l, pos);
         if (store_lane) {
           out[(size_t)(b * N + t) * H * dv + orow] = scale * fmaf(cur.kq, u, al * yq);
           if (MODE == kHybrid) rec.up[((size_t)bh * N + t) * dv + orow - (size_t)h * dv] = u;
