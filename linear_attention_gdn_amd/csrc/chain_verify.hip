@@ -354,10 +354,15 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
   };
   const SK* kq_lane = skq + sc;
   const f32x4* sc_row = ssc + rl;
-  auto fetch = [&](int t, Ops& o) {
-    o.kc = mask4(widen4(kq_lane[2 * t * cpr]), cok);
-    o.qc = mask4(widen4(kq_lane[(2 * t + 1) * cpr]), cok);
-    o.sc = sc_row[t * kChainRows];
+  // operands of the next step in order (steps are fetched 0, 1, 2, ...)
+  const SK* kq_next = kq_lane;
+  const f32x4* sc_next = sc_row;
+  auto fetch = [&](Ops& o) {
+    o.kc = mask4(widen4(kq_next[0]), cok);
+    o.qc = mask4(widen4(kq_next[cpr]), cok);
+    o.sc = sc_next[0];
+    kq_next += 2 * cpr;
+    sc_next += kChainRows;
   };
   // lane 63 holds y_q and stores the step's output and u'; the row is the
   // wave's, so the pointers are wave-uniform (scalar registers, scalar
@@ -403,14 +408,14 @@ __global__ __launch_bounds__(kChainThreads) void chain_verify_kernel(
     asm volatile("" : "+v"(o.sc));
   };
   Ops A, Bo;
-  fetch(0, A);
+  fetch(A);
   opaque(A);
   for (int t = 0; t < N; t += 2) {
-    fetch(t + 1, Bo);
+    fetch(Bo);
     run(A);
     opaque(Bo);
     if (t + 1 < N) {  // uniform
-      fetch(t + 2, A);
+      fetch(A);
       run(Bo);
       opaque(A);
     }
