@@ -16,7 +16,10 @@
 //     the masked and scaled A and Attn, and T = (I + A)^{-1} (per-node path
 //     solves; blocked forward substitution for paths deeper than 16);
 //   state waves (4 .. 3 + SW): wave 4 + c owns state rows 16 c .. 16 c + 15
-//     of the tile.  They request their state rows and V at once (straight
+//     of the tile (16-row tiles of the delayed form instead have two, waves
+//     4 and 5, each with half of the rows' columns, the second handing its
+//     contraction sums to the first, which alone runs the epilogue).  They
+//     request their state rows and V at once (straight
 //     into MFMA operand registers); for the delayed form each finds the
 //     previous draft's accepted path itself and requests the path's k rows
 //     (staged in LDS together) and u' of its rows, and the path is applied to
@@ -43,8 +46,15 @@ namespace gdn {
 
 constexpr int kWsChunk = 16;  // accepted-path nodes staged per round by each state wave
 
+// State waves per tile: one per 16 rows, except for 16-row tiles with a
+// delayed commit, whose 16 rows are shared by two waves that split the
+// state's columns (the commit and the contraction then run on both).
+template <int SW, bool DLY>
+constexpr int ws_state_waves() { return SW == 1 && DLY ? 2 : SW; }
+
 template <bool DLY, int SW>
 struct WsLds {
+  static constexpr int NSW = ws_state_waves<SW, DLY>();
   alignas(16) bf16_t qk[kQKRows * kQKStride];  // Q rows, then K rows (bf16, zero-padded)
   alignas(16) float A[kMaxNodes * kLd];        // A (FP32)
   alignas(16) float QK[kMaxNodes * kLd];       // Attn (split bf16)
@@ -54,12 +64,15 @@ struct WsLds {
   int bad;
   int sync;   // arrivals at the head waves' own barriers
   int csync;  // arrivals of the state waves at the staged k rows
+  int ysync;  // 16-row tiles: the second state wave's partial contraction is in yx
   // delayed commit: per state wave the accepted path (root first) and its
   // coefficients; the k rows of the path's first kWsChunk nodes (zero rows
   // past the path), staged by the state waves together
-  int dnode[DLY ? SW : 1][kMaxNodes];
-  float dc[DLY ? SW : 1][kMaxNodes];
+  int dnode[DLY ? NSW : 1][kMaxNodes];
+  float dc[DLY ? NSW : 1][kMaxNodes];
   alignas(16) bf16_t ck[DLY ? kWsChunk * kMaxDim : 8];
+  // 16-row tiles: the second state wave's contraction accumulators [i][lane]
+  alignas(16) f32x4 yx[NSW > SW ? 2 * (kMaxNodes / 16) : 1][64];
 };
 
 // The head waves synchronise among themselves through an LDS counter, so the
@@ -90,7 +103,7 @@ __device__ inline void ws_sync(int* ctr, int target) {
 }
 
 template <int NQT, bool DLY, int SW, bool GATE>
-__global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
+__global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_ws_kernel(
     int N, int H, int dk, int dv, int ntiles, float* __restrict__ S0,
     const int32_t* __restrict__ parents, const bf16_t* __restrict__ q,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ beta,
@@ -101,6 +114,17 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   constexpr int BV = 16 * SW;  // state rows per tile: 16 per state wave
   constexpr int Np = 16 * NQT;
   constexpr int KS = kMaxDim / 32;          // 32-wide k steps of the contraction
+  // 16-row tiles with a delayed commit: two state waves on the same rows,
+  // each holding, committing and contracting half of the state's columns
+  // (k steps kbase .. + KSL - 1); otherwise one state wave per 16 rows with
+  // every column
+  constexpr int NSW = ws_state_waves<SW, DLY>();
+  constexpr bool KSPLIT = NSW > SW;
+  // 16-row tiles without the delayed commit: the one state wave sums the two
+  // column halves apart and adds them at the end, the split form's order, so
+  // that the delayed form with no path to apply is bitwise this one
+  constexpr bool kHalves = SW == 1 && !KSPLIT;
+  constexpr int KSL = KSPLIT ? KS / 2 : KS;
 
   __shared__ WsLds<DLY, SW> sm;
   bf16_t* const QKs = sm.qk;
@@ -124,13 +148,14 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   const int r0 = tile * BV;
   // state waves: rows 16 cj .. 16 cj + 15 of the tile; lane l16's row (as an
   // MFMA operand) and the four rows 16 cj + 4 lg .. + 3 (as a transposed result)
-  const int cj = wave >= 4 ? wave - 4 : 0;
+  const int cj = (wave >= 4 && !KSPLIT) ? wave - 4 : 0;
+  const int kbase = (wave >= 4 && KSPLIT) ? KSL * (wave - 4) : 0;  // first k step of this wave
   const int srow = r0 + 16 * cj + l16;
   const bool sok = srow < dv;
   const int srow4 = r0 + 16 * cj + 4 * lg;
   const bool sok4 = srow4 < dv;  // dv % 4 == 0: all four rows or none
 
-  if (tid == 0) sm.sync = 0, sm.csync = 0;
+  if (tid == 0) sm.sync = 0, sm.csync = 0, sm.ysync = 0;
   __syncthreads();  // the counter is zero before any wave arrives
   // the head waves carry the chain of dependent per-head steps: their
   // instructions go first when both roles compete for a SIMD or the memory
@@ -143,7 +168,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   constexpr int qk_total = 2 * Np * qk_cpr;
   constexpr int QKB = qk_total / 256;  // chunks per head thread
   static_assert(qk_total % 256 == 0, "every head thread stages QKB chunks");
-  f32x4 Sraw[KS][2];
+  f32x4 Sraw[KSL][2];  // this wave's state columns 32 (kbase + i) + 8 lg .. + 7 of its row
   bf16_t vreg[NQT][4];
   int dn_s = 0;  // state waves: length of the previous draft's accepted path
   // Delayed commit (state waves): the previous draft's accepted path applied
@@ -162,7 +187,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
   // requested after the state rows and the whole commit is applied while the
   // head waves still wait for Q and K.
   constexpr bool kBlockCommit = SW == 4;
-  constexpr int KQ = kWsChunk * (kMaxDim / 8) / (64 * SW);  // 16-byte k chunks per lane
+  constexpr int KQ = kWsChunk * (kMaxDim / 8) / (64 * NSW);  // 16-byte k chunks per lane
   u32x4 kq[DLY ? KQ : 1];
   float upr[kWsChunk / 4];  // u' of path node 4 m + lg for this lane's state row
   float s0c = 1.f;          // e^{G_last}
@@ -240,7 +265,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
 #pragma unroll
     for (int m = 0; m < kWsChunk / 4; ++m) {
       if (m < ng) {  // uniform
-        const bf16_t* kr0 = sm.ck + (4 * m + lg) * kMaxDim + 32 * ks + kcol;
+        const bf16_t* kr0 = sm.ck + (4 * m + lg) * kMaxDim + 32 * (kbase + ks) + kcol;
         Sraw[ks][0] = mfma16x16x4f32(widen1(kr0[0]), cuv[m], Sraw[ks][0]);
         Sraw[ks][1] = mfma16x16x4f32(widen1(kr0[4]), cuv[m], Sraw[ks][1]);
       }
@@ -254,7 +279,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     const int* const dnode = sm.dnode[DLY ? sw : 0];
     const float* const dc = sm.dc[DLY ? sw : 0];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KSL; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         Sraw[ks][0][e] = Sraw[ks][0][e] * s0c;
@@ -268,19 +293,19 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
       const float c = dc[jc] * prev.up[((size_t)bh * Npv + nd) * dv + clampi(srow, dv - 1)];
       const float cuv = on ? c : -0.0f;
       const bf16_t* kr0 = prev.K + ((size_t)bh * Npv + nd) * dk;
-      float av[KS][2];
+      float av[KSL][2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KSL; ++ks)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-          av[ks][hf] = on ? widen1(kr0[clampi(32 * ks + 4 * hf + kcol, dk - 1)]) : 0.f;
+          av[ks][hf] = on ? widen1(kr0[clampi(32 * (kbase + ks) + 4 * hf + kcol, dk - 1)]) : 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KSL; ++ks)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) Sraw[ks][hf] = mfma16x16x4f32(av[ks][hf], cuv, Sraw[ks][hf]);
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
+    for (int ks = 0; ks < KSL; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
   };
   // c u' of path node 4 m + lg for this lane's state row (the commit kernel's
   // product), -0 past the path
@@ -299,9 +324,9 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     } else {
       float cuv[kWsChunk / 4];
       make_cuv(dn, cuv);
-      ws_wait(&sm.csync, SW);  // every state wave's share of the k rows is in LDS
+      ws_wait(&sm.csync, NSW);  // every state wave's share of the k rows is in LDS
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KSL; ++ks)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           Sraw[ks][0][e] = Sraw[ks][0][e] * s0c;
@@ -312,20 +337,20 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
 #pragma unroll
       for (int m = 0; m < kWsChunk / 4; ++m) {
         if (4 * m < dn) {  // uniform
-          const bf16_t* kr0 = sm.ck + (4 * m + lg) * kMaxDim + kcol;
-          float av[KS][2];
+          const bf16_t* kr0 = sm.ck + (4 * m + lg) * kMaxDim + 32 * kbase + kcol;
+          float av[KSL][2];
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
+          for (int ks = 0; ks < KSL; ++ks)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) av[ks][hf] = widen1(kr0[32 * ks + 4 * hf]);
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
+          for (int ks = 0; ks < KSL; ++ks)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) Sraw[ks][hf] = mfma16x16x4f32(av[ks][hf], cuv[m], Sraw[ks][hf]);
         }
       }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
+      for (int ks = 0; ks < KSL; ++ks) mfma_drain(Sraw[ks][0], Sraw[ks][1]);
     }
   };
 
@@ -437,8 +462,8 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     // tiles) and leave less to write back when the kernel ends.
     const float* sptr = S0 + ((size_t)bh * dv + clampi(srow, dv - 1)) * dk;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int kk = clampi(32 * ks + koff, dk - 8);
+    for (int ks = 0; ks < KSL; ++ks) {
+      const int kk = clampi(32 * (kbase + ks) + koff, dk - 8);
       Sraw[ks][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sptr + kk));
       Sraw[ks][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sptr + kk + 4));
     }
@@ -469,7 +494,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
 
   // write-back of the committed columns 32 ks + 8 lg .. + 7 of this lane's row
   auto dly_store = [&](int ks) {
-    const int col = 32 * ks + koff;
+    const int col = 32 * (kbase + ks) + koff;
     if (sok && col < dk) {
       float* wp = S0 + ((size_t)bh * dv + srow) * dk + col;
       __builtin_nontemporal_store(Sraw[ks][0], reinterpret_cast<f32x4*>(wp));
@@ -498,10 +523,10 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
       if (DLY && dn_s > 0) {  // uniform
         if (kBlockCommit) commit_global(dn_s);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dly_store(ks);
+        for (int ks = 0; ks < KSL; ++ks) dly_store(ks);
       }
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      for (int t0 = 0; t0 < N; t0 += 16) {
+      for (int t0 = 0; t0 < N && kbase == 0; t0 += 16) {  // one wave per row
         const int t = t0 + l16;
         if (t < N && sok4) {
           const size_t o = (((size_t)b * N + t) * H + h) * dv + srow4;
@@ -648,11 +673,14 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
 
   // state waves: contraction (with the committed rows written back), R
   f32x4 yacc[2 * NQT];
+  f32x4 yacc2[kHalves ? 2 * NQT : 1];  // 16-row tiles: the sums over the second half
   f32x4 rv[NQT];
   f32x4 gsl[GATE ? NQT : 1];  // gated form: SiLU(gate) of node 16 i + l16, rows srow4 .. + 3
   if (!head) {
 #pragma unroll
     for (int i = 0; i < 2 * NQT; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < (kHalves ? 2 * NQT : 1); ++i) yacc2[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     // 4. Y: the K row tiles as K S0^T (rows = nodes, as the B operand of
     // T R), the Q row tiles transposed as S0 Q^T (each lane then holds four
     // consecutive state rows of one node, as O^T needs).  The next k step's
@@ -661,7 +689,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     auto aload = [&](int ks, bf16x8 (&a)[2 * NQT]) {
 #pragma unroll
       for (int i = 0; i < 2 * NQT; ++i)
-        a[i] = lds_bf16x8(QKs + (16 * i + l16) * kQKStride + 32 * ks + koff);
+        a[i] = lds_bf16x8(QKs + (16 * i + l16) * kQKStride + 32 * (kbase + ks) + koff);
     };
     // With a delayed commit, the committed columns of each k step are written
     // back as the step is contracted: the memory system accepts the stores
@@ -674,14 +702,14 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     if (DLY && kBlockCommit && dn_s > kWsChunk) commit_global(dn_s);
     if (lcm) {
       make_cuv(dn_s, cuv);
-      ws_wait(&sm.csync, SW);  // every state wave's share of the k rows is in LDS
+      ws_wait(&sm.csync, NSW);  // every state wave's share of the k rows is in LDS
     }
     // block ks of the (committed) rows: written back, then split into the
     // bf16 hi + lo operands of the contraction
     bf16x8 bhi[2], blo[2];
     auto prep = [&](int ks) {
       if (wb) dly_store(ks);
-      const bool okk = sok && 32 * ks + koff < dk;
+      const bool okk = sok && 32 * (kbase + ks) + koff < dk;
       split8(mask4(Sraw[ks][0], okk), mask4(Sraw[ks][1], okk), bhi[ks & 1], blo[ks & 1]);
     };
     if (lcm) {
@@ -691,26 +719,49 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     prep(0);
     aload(0, afr[0]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {  // zero-padded past dk: no branch
-      if (ks + 1 < KS) aload(ks + 1, afr[(ks + 1) & 1]);
-      if (lcm && ks + 1 < KS) commit_ks(ks + 1, ngc, cuv);
+    for (int ks = 0; ks < KSL; ++ks) {  // zero-padded past dk: no branch
+      if (ks + 1 < KSL) aload(ks + 1, afr[(ks + 1) & 1]);
+      if (lcm && ks + 1 < KSL) commit_ks(ks + 1, ngc, cuv);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2 * NQT; ++i) {
+        f32x4& acc = (kHalves && 2 * ks >= KSL) ? yacc2[kHalves ? i : 0] : yacc[i];
         if (i < NQT) {
-          yacc[i] = mfma16x16x32(bhi[ks & 1], afr[ks & 1][i], yacc[i]);
-          yacc[i] = mfma16x16x32(blo[ks & 1], afr[ks & 1][i], yacc[i]);
+          acc = mfma16x16x32(bhi[ks & 1], afr[ks & 1][i], acc);
+          acc = mfma16x16x32(blo[ks & 1], afr[ks & 1][i], acc);
         } else {
-          yacc[i] = mfma16x16x32(afr[ks & 1][i], bhi[ks & 1], yacc[i]);
-          yacc[i] = mfma16x16x32(afr[ks & 1][i], blo[ks & 1], yacc[i]);
+          acc = mfma16x16x32(afr[ks & 1][i], bhi[ks & 1], acc);
+          acc = mfma16x16x32(afr[ks & 1][i], blo[ks & 1], acc);
         }
       }
-      if (ks + 1 < KS) {
+      if (ks + 1 < KSL) {
         if (lcm) mfma_drain(Sraw[ks + 1][0], Sraw[ks + 1][1]);
         prep(ks + 1);
       }
     }
     mfma_drain_all(yacc);
+    if constexpr (kHalves) {
+      mfma_drain_all(yacc2);
+#pragma unroll
+      for (int i = 0; i < 2 * NQT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[i][r] += yacc2[i][r];
+    }
+    if constexpr (KSPLIT) {  // uniform: the second wave's half of the sums goes to the first
+      if (kbase != 0) {
+#pragma unroll
+        for (int i = 0; i < 2 * NQT; ++i) sm.yx[i][lane] = yacc[i];
+        ws_arrive(&sm.ysync);
+      } else {
+        ws_wait(&sm.ysync, 1);
+#pragma unroll
+        for (int i = 0; i < 2 * NQT; ++i) {
+          const f32x4 x = sm.yx[i][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yacc[i][r] += x[r];
+        }
+      }
+    }
     // R = diag(beta) (V - diag(e^G) K S0^T): lane (row srow, lg) holds nodes
     // 16 nb + 4 lg + r
 #pragma unroll
@@ -766,7 +817,7 @@ __global__ __launch_bounds__(256 + 64 * SW) void tree_ws_kernel(
     }
   }
   __syncthreads();  // T and Attn are complete; the only barrier of both roles after the start
-  if (head) return;
+  if (head || kbase != 0) return;  // (16-row tiles: the first state wave finishes the tile)
 
   // ---- 5. epilogue (state waves): U' = T R, its transpose for the record,
   // O^T = (Attn U')^T + scale e^G (S0 Q^T); T and Attn are lower triangular,
@@ -866,14 +917,15 @@ hipError_t launch_ws_g(int B, int N, int H, int dk, int dv, float* S0, const int
                        hipStream_t stream) {
   const int ntiles = (dv + 16 * SW - 1) / (16 * SW);
   const long grid = (long)B * H * ntiles;
-  const dim3 block(256 + 64 * SW);
   if (prev_factors) {
+    const dim3 block(256 + 64 * ws_state_waves<SW, true>());
     const RecordLayout Lp = record_layout(B, Npv, H, dk, dv, GDN_BF16);
     const Record<bf16_t> prev = record_views<bf16_t>(const_cast<void*>(prev_factors), Lp);
     hipLaunchKernelGGL((tree_ws_kernel<NQT, true, SW, GATE>), dim3((unsigned)grid), block, 0,
                        stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out,
                        rec, mask_out, dev_status, prev, Npv, last, commit_status, ga);
   } else {
+    const dim3 block(256 + 64 * ws_state_waves<SW, false>());
     hipLaunchKernelGGL((tree_ws_kernel<NQT, false, SW, GATE>), dim3((unsigned)grid), block, 0,
                        stream, N, H, dk, dv, ntiles, S0, parents, q, k, v, beta, g, scale, out,
                        rec, mask_out, dev_status, Record<bf16_t>{}, 1, nullptr, nullptr, ga);
