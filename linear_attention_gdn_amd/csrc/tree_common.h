@@ -57,11 +57,18 @@ __device__ inline int xcd_logical_id(int bid, int nblocks) {
   return (bid % kXcds) * (nblocks / kXcds) + bid / kXcds;
 }
 
-constexpr int kLd = kMaxNodes + 8;         // row stride (floats) of N x N matrices: 288 B
-constexpr int kLdH = kLd;                  // row stride (bf16) of split matrices: 144 B
+// LDS row strides.  FP32 N x N rows of 272 B: the four row groups of a
+// 16 x 16 tile's stores (rows 4 lg + r) start 16 banks apart.  Split bf16
+// rows of 144 B keep every row 16-byte aligned for the 4-wave kernel's
+// 16-byte fragment reads.  Staged Q/K rows of 544 B: a 16-byte fragment read
+// of 16 rows is free of bank conflicts (528-byte rows measured eight times
+// the conflict stalls of the whole kernel).
+constexpr int kLd = kMaxNodes + 4;         // row stride (floats) of FP32 N x N matrices
+constexpr int kLdH = kMaxNodes + 8;        // row stride (bf16) of split matrices
 constexpr int kSplitLo = kMaxNodes * kLdH; // bf16 offset of the lo half of a split matrix
+constexpr int kMatFloats = kMaxNodes * kLdH; // floats of a region holding either form
 constexpr int kQKRows = 2 * kMaxNodes;     // Q rows then K rows
-constexpr int kQKStride = kMaxDim + 8;     // bf16 elements per staged row
+constexpr int kQKStride = kMaxDim + 16;    // bf16 elements per staged row
 constexpr int kQKBytes = kQKRows * kQKStride * 2;
 constexpr int kPathMax = 16;               // register-resident path solve up to this depth
 

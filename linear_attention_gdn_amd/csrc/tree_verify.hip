@@ -76,7 +76,7 @@ namespace gdn {
 template <int BV>
 struct TreeLds {
   static constexpr int kBVT = ((BV + 15) / 16) * 16;            // padded tile width
-  static constexpr int kMat = kMaxNodes * kLd * 4;               // one N x N float matrix
+  static constexpr int kMat = kMatFloats * 4;                    // one N x N matrix region
   static constexpr int kSplitT = kBVT * kLdH * 2 * 2;            // R^T or U'^T, hi + lo
   static constexpr int kRegionA = kQKBytes > 2 * kSplitT ? kQKBytes : 2 * kSplitT;
   static constexpr int kOffKK = kRegionA;        // K K^T -> A (FP32)

@@ -46,6 +46,11 @@ namespace gdn {
 
 constexpr int kWsChunk = 16;  // accepted-path nodes staged per round by each state wave
 
+// Split bf16 matrices (Attn, T) here have 136-byte rows, read 8 bytes at a
+// time: the four row groups of a tile's stores then start on different banks.
+constexpr int kLdS = kMaxNodes + 4;
+constexpr int kSplitLoS = kMaxNodes * kLdS;
+
 // State waves per tile: one per 16 rows, except for 16-row tiles with a
 // delayed commit, whose 16 rows are shared by two waves that split the
 // state's columns (the commit and the contraction then run on both).
@@ -56,9 +61,9 @@ template <bool DLY, int SW>
 struct WsLds {
   static constexpr int NSW = ws_state_waves<SW, DLY>();
   alignas(16) bf16_t qk[kQKRows * kQKStride];  // Q rows, then K rows (bf16, zero-padded)
-  alignas(16) float A[kMaxNodes * kLd];        // A (FP32)
-  alignas(16) float QK[kMaxNodes * kLd];       // Attn (split bf16)
-  alignas(16) float T[kMaxNodes * kLd];        // T: zeros, then FP32 rows or split bf16
+  alignas(16) float A[kMatFloats];        // A (FP32)
+  alignas(16) float QK[kMatFloats];       // Attn (split bf16)
+  alignas(16) float T[kMatFloats];        // T: zeros, then FP32 rows or split bf16
   uint64_t mask[kMaxNodes];
   float G[kMaxNodes], eG[kMaxNodes], beta[kMaxNodes];
   int bad;
@@ -380,7 +385,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
     // (while the loads are in flight) T and A start as zeros: the Gram tiles write only A's lower-triangle
     // blocks, and the path solves multiply the entries above the diagonal by
     // exact zeros, which needs them finite
-    for (int idx = tid; idx < kMaxNodes * kLd / 4; idx += 256) {
+    for (int idx = tid; idx < kMatFloats / 4; idx += 256) {
       reinterpret_cast<f32x4*>(Tl)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
       reinterpret_cast<f32x4*>(KK)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -604,7 +609,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
             const bool on = (m[r] >> j) & 1ull;
             const float dec = __expf(gr[r] - gj);
             if constexpr (isq)
-              store_split1(Attn + t * kLdH + j, kSplitLo, on ? scale * dec * acc[r] : 0.f);
+              store_split1(Attn + t * kLdS + j, kSplitLoS, on ? scale * dec * acc[r] : 0.f);
             else
               KK[t * kLd + j] = (on && j != t) ? br[r] * dec * acc[r] : 0.f;
           }
@@ -656,7 +661,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
       const int t = tid;
       const uint64_t m = sm.mask[t];
       const int d = __popcll(m);
-      auto put_split = [&](int j, float x) { store_split1(Ts + t * kLdH + j, kSplitLo, x); };
+      auto put_split = [&](int j, float x) { store_split1(Ts + t * kLdS + j, kSplitLoS, x); };
       auto put_f32 = [&](int j, float x) { Tl[t * kLd + j] = x; };
       if (deep) {
         const uint64_t mb = m & (0xFFFFull << (16 * (t / 16)));
@@ -834,8 +839,8 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
         if constexpr (kDeep) {
           split4(*reinterpret_cast<const f32x4*>(Tl + row * kLd + col), th[x], tl[x]);
         } else {
-          th[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Ts + row * kLdH + col));
-          tl[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Ts + kSplitLo + row * kLdH + col));
+          th[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Ts + row * kLdS + col));
+          tl[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Ts + kSplitLoS + row * kLdS + col));
         }
       }
     s16x4 rh[NQT], rl[NQT];
@@ -861,9 +866,9 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
     for (int i = 0, x = 0; i < NQT; ++i)
 #pragma unroll
       for (int kb = 0; kb <= i; ++kb, ++x) {
-        const int o = (16 * i + l16) * kLdH + 16 * kb + 4 * lg;
+        const int o = (16 * i + l16) * kLdS + 16 * kb + 4 * lg;
         ah[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Attn + o));
-        al[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Attn + kSplitLo + o));
+        al[x] = __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(Attn + kSplitLoS + o));
       }
     mfma_drain_all(ua);
     s16x4 uh[NQT], ul[NQT];
