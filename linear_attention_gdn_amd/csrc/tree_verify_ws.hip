@@ -50,6 +50,9 @@ constexpr int kWsChunk = 16;  // accepted-path nodes staged per round by each st
 // time: the four row groups of a tile's stores then start on different banks.
 constexpr int kLdS = kMaxNodes + 4;
 constexpr int kSplitLoS = kMaxNodes * kLdS;
+// Staged k rows of the delayed commit: 576-byte rows, so the commit's reads
+// of four path nodes' rows (one per lane group) start on different banks.
+constexpr int kCkStride = kMaxDim + 32;
 
 // State waves per tile: one per 16 rows, except for 16-row tiles with a
 // delayed commit, whose 16 rows are shared by two waves that split the
@@ -75,7 +78,7 @@ struct WsLds {
   // past the path), staged by the state waves together
   int dnode[DLY ? NSW : 1][kMaxNodes];
   float dc[DLY ? NSW : 1][kMaxNodes];
-  alignas(16) bf16_t ck[DLY ? kWsChunk * kMaxDim : 8];
+  alignas(16) bf16_t ck[DLY ? kWsChunk * kCkStride : 8];
   // 16-row tiles: the second state wave's contraction accumulators [i][lane]
   alignas(16) f32x4 yx[NSW > SW ? 2 * (kMaxNodes / 16) : 1][64];
 };
@@ -241,7 +244,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
     for (int x = 0; x < KQ; ++x) {
       const int idx = 64 * KQ * sw + lane + 64 * x;
       const int j = idx / (kMaxDim / 8), c8 = 8 * (idx % (kMaxDim / 8));
-      *reinterpret_cast<u32x4*>(sm.ck + j * kMaxDim + c8) = (j < dn && c8 < dk) ? kq[x] : z;
+      *reinterpret_cast<u32x4*>(sm.ck + j * kCkStride + c8) = (j < dn && c8 < dk) ? kq[x] : z;
     }
     ws_arrive(&sm.csync);
   };
@@ -270,7 +273,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
 #pragma unroll
     for (int m = 0; m < kWsChunk / 4; ++m) {
       if (m < ng) {  // uniform
-        const bf16_t* kr0 = sm.ck + (4 * m + lg) * kMaxDim + 32 * (kbase + ks) + kcol;
+        const bf16_t* kr0 = sm.ck + (4 * m + lg) * kCkStride + 32 * (kbase + ks) + kcol;
         Sraw[ks][0] = mfma16x16x4f32(widen1(kr0[0]), cuv[m], Sraw[ks][0]);
         Sraw[ks][1] = mfma16x16x4f32(widen1(kr0[4]), cuv[m], Sraw[ks][1]);
       }
@@ -342,7 +345,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
 #pragma unroll
       for (int m = 0; m < kWsChunk / 4; ++m) {
         if (4 * m < dn) {  // uniform
-          const bf16_t* kr0 = sm.ck + (4 * m + lg) * kMaxDim + 32 * kbase + kcol;
+          const bf16_t* kr0 = sm.ck + (4 * m + lg) * kCkStride + 32 * kbase + kcol;
           float av[KSL][2];
 #pragma unroll
           for (int ks = 0; ks < KSL; ++ks)
