@@ -16,10 +16,10 @@
 //     the masked and scaled A and Attn, and T = (I + A)^{-1} (per-node path
 //     solves; blocked forward substitution for paths deeper than 16);
 //   state waves (4 .. 3 + SW): wave 4 + c owns state rows 16 c .. 16 c + 15
-//     of the tile (16-row tiles of the delayed form instead have two, waves
-//     4 and 5, each with half of the rows' columns, the second handing its
-//     contraction sums to the first, which alone runs the epilogue).  They
-//     request their state rows and V at once (straight
+//     of the tile (16-row tiles of the delayed form instead have four,
+//     waves 4-7, each with a quarter of the rows' columns, the other three
+//     handing their contraction sums to the first, which alone runs the
+//     epilogue).  They request their state rows and V at once (straight
 //     into MFMA operand registers); for the delayed form each finds the
 //     previous draft's accepted path itself and requests the path's k rows
 //     (staged in LDS together) and u' of its rows, and the path is applied to
@@ -55,10 +55,11 @@ constexpr int kSplitLoS = kMaxNodes * kLdS;
 constexpr int kCkStride = kMaxDim + 32;
 
 // State waves per tile: one per 16 rows, except for 16-row tiles with a
-// delayed commit, whose 16 rows are shared by two waves that split the
-// state's columns (the commit and the contraction then run on both).
+// delayed commit, whose 16 rows are shared by four waves that split the
+// state's columns (the commit and the contraction then run on all four, one
+// per SIMD).
 template <int SW, bool DLY>
-constexpr int ws_state_waves() { return SW == 1 && DLY ? 2 : SW; }
+constexpr int ws_state_waves() { return SW == 1 && DLY ? 4 : SW; }
 
 template <bool DLY, int SW>
 struct WsLds {
@@ -72,15 +73,15 @@ struct WsLds {
   int bad;
   int sync;   // arrivals at the head waves' own barriers
   int csync;  // arrivals of the state waves at the staged k rows
-  int ysync;  // 16-row tiles: the second state wave's partial contraction is in yx
+  int ysync;  // 16-row tiles: arrivals of the other state waves' partial contractions in yx
   // delayed commit: per state wave the accepted path (root first) and its
   // coefficients; the k rows of the path's first kWsChunk nodes (zero rows
   // past the path), staged by the state waves together
   int dnode[DLY ? NSW : 1][kMaxNodes];
   float dc[DLY ? NSW : 1][kMaxNodes];
   alignas(16) bf16_t ck[DLY ? kWsChunk * kCkStride : 8];
-  // 16-row tiles: the second state wave's contraction accumulators [i][lane]
-  alignas(16) f32x4 yx[NSW > SW ? 2 * (kMaxNodes / 16) : 1][64];
+  // 16-row tiles: the other state waves' contraction accumulators [wave - 5][i][lane]
+  alignas(16) f32x4 yx[NSW > SW ? NSW - 1 : 1][NSW > SW ? 2 * (kMaxNodes / 16) : 1][64];
 };
 
 // The head waves synchronise among themselves through an LDS counter, so the
@@ -122,17 +123,20 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
   constexpr int BV = 16 * SW;  // state rows per tile: 16 per state wave
   constexpr int Np = 16 * NQT;
   constexpr int KS = kMaxDim / 32;          // 32-wide k steps of the contraction
-  // 16-row tiles with a delayed commit: two state waves on the same rows,
-  // each holding, committing and contracting half of the state's columns
+  // 16-row tiles with a delayed commit: four state waves on the same rows,
+  // each holding, committing and contracting a quarter of the state's columns
   // (k steps kbase .. + KSL - 1); otherwise one state wave per 16 rows with
   // every column
   constexpr int NSW = ws_state_waves<SW, DLY>();
   constexpr bool KSPLIT = NSW > SW;
-  // 16-row tiles without the delayed commit: the one state wave sums the two
-  // column halves apart and adds them at the end, the split form's order, so
-  // that the delayed form with no path to apply is bitwise this one
+  // 16-row tiles without the delayed commit: the one state wave sums the four
+  // column quarters apart (parts 1-3 in two accumulator sets in turn) and
+  // adds them in part order, the split form's order, so that the delayed form
+  // with no path to apply is bitwise this one
+  constexpr int kParts = SW == 1 ? 4 : 1;  // column parts of a 16-row tile
+  constexpr int KPART = KS / kParts;      // k steps per part
   constexpr bool kHalves = SW == 1 && !KSPLIT;
-  constexpr int KSL = KSPLIT ? KS / 2 : KS;
+  constexpr int KSL = KSPLIT ? KPART : KS;
 
   __shared__ WsLds<DLY, SW> sm;
   bf16_t* const QKs = sm.qk;
@@ -363,16 +367,9 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
   };
 
   if (head) {
-    u32x4 qkw[QKB];
-#pragma unroll
-    for (int x = 0; x < QKB; ++x) {
-      const int idx = tid + 256 * x;
-      const int r = idx / qk_cpr;
-      const bool isq = r < Np;
-      const int t = clampi(isq ? r : r - Np, N - 1);
-      const int c8 = clampi(8 * (idx % qk_cpr), dk - 8);
-      qkw[x] = *reinterpret_cast<const u32x4*>((isq ? q : k) + (((size_t)b * N + t) * H + h) * dk + c8);
-    }
+    // The topology's inputs first: wave 0 builds the topology while Q and K
+    // are still in flight (loads complete in order, so inputs requested after
+    // Q and K would wait for all of them).
     const int tn = clampi(lane, N - 1);
     const int pl = parents[(size_t)b * N + tn];
     const float gl = g[((size_t)b * N + tn) * H + h];
@@ -383,6 +380,16 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
       last_v = last_acc[b];
       pmask_l = prev.mask[(size_t)b * Npv + clampi(lane, Npv - 1)];
     }
+    u32x4 qkw[QKB];
+#pragma unroll
+    for (int x = 0; x < QKB; ++x) {
+      const int idx = tid + 256 * x;
+      const int r = idx / qk_cpr;
+      const bool isq = r < Np;
+      const int t = clampi(isq ? r : r - Np, N - 1);
+      const int c8 = clampi(8 * (idx % qk_cpr), dk - 8);
+      qkw[x] = *reinterpret_cast<const u32x4*>((isq ? q : k) + (((size_t)b * N + t) * H + h) * dk + c8);
+    }
     // the head's loads are queued: the state waves may now request theirs
     ws_arrive(&sm.sync);
     // (while the loads are in flight) T and A start as zeros: the Gram tiles write only A's lower-triangle
@@ -392,24 +399,19 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
       reinterpret_cast<f32x4*>(Tl)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
       reinterpret_cast<f32x4*>(KK)[idx] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-#pragma unroll
-    for (int x = 0; x < QKB; ++x) {  // no branch: a load under one is waited for at once
-      const int idx = tid + 256 * x;
-      const int r = idx / qk_cpr;
-      const int t = r < Np ? r : r - Np;
-      const int c8 = 8 * (idx % qk_cpr);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
-    }
 
-    // 1. wave 0: parents -> validation, ancestor-or-self masks and G
+    // 1. wave 0: parents -> validation, ancestor-or-self masks and G (its
+    // global stores follow the staging, which would otherwise wait for them)
+    uint64_t m = 0ull;
+    float G = 0.f;
+    bool anybad = false;
     if (wave == 0) {
       const int t = lane;
       const int p = t < N ? pl : -1;
       const bool bad = t < N && (p < -1 || p >= t);
-      const uint64_t anybad = __ballot(bad);
-      uint64_t m = t < N ? (1ull << t) : 0ull;
-      float G = t < N ? gl : 0.f;
+      anybad = __ballot(bad) != 0ull;
+      m = t < N ? (1ull << t) : 0ull;
+      G = t < N ? gl : 0.f;
       int a = (t < N && !bad) ? p : -1;
       for (int r = 0; r < 6; ++r) {  // 2^6 = 64 >= path length
         if (__ballot(a >= 0) == 0ull) break;  // uniform: every path is complete
@@ -428,7 +430,19 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
       sm.G[t] = G;
       sm.eG[t] = expf(G);
       sm.beta[t] = t < N ? bl : 0.f;
-      if (t == 0) sm.bad = anybad != 0ull;
+      if (t == 0) sm.bad = anybad;
+    }
+#pragma unroll
+    for (int x = 0; x < QKB; ++x) {  // no branch: a load under one is waited for at once
+      const int idx = tid + 256 * x;
+      const int r = idx / qk_cpr;
+      const int t = r < Np ? r : r - Np;
+      const int c8 = 8 * (idx % qk_cpr);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(QKs + r * kQKStride + c8) = (t < N && c8 < dk) ? qkw[x] : z;
+    }
+    if (wave == 0) {
+      const int t = lane;
       if (tile == 0 && t < N) {
         rec.G[(size_t)bh * N + t] = anybad ? 0.f : G;
         if (h == 0) {
@@ -681,14 +695,14 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
 
   // state waves: contraction (with the committed rows written back), R
   f32x4 yacc[2 * NQT];
-  f32x4 yacc2[kHalves ? 2 * NQT : 1];  // 16-row tiles: the sums over the second half
+  f32x4 yacc2[2][kHalves ? 2 * NQT : 1];  // 16-row tiles: the sums over parts 1-3 (two sets in turn)
   f32x4 rv[NQT];
   f32x4 gsl[GATE ? NQT : 1];  // gated form: SiLU(gate) of node 16 i + l16, rows srow4 .. + 3
   if (!head) {
 #pragma unroll
     for (int i = 0; i < 2 * NQT; ++i) yacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < (kHalves ? 2 * NQT : 1); ++i) yacc2[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < (kHalves ? 2 * NQT : 1); ++i) yacc2[0][i] = yacc2[1][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     // 4. Y: the K row tiles as K S0^T (rows = nodes, as the B operand of
     // T R), the Q row tiles transposed as S0 Q^T (each lane then holds four
     // consecutive state rows of one node, as O^T needs).  The next k step's
@@ -733,7 +747,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 2 * NQT; ++i) {
-        f32x4& acc = (kHalves && 2 * ks >= KSL) ? yacc2[kHalves ? i : 0] : yacc[i];
+        f32x4& acc = (kHalves && ks >= KPART) ? yacc2[kHalves ? ((ks / KPART - 1) & 1) : 0][kHalves ? i : 0] : yacc[i];
         if (i < NQT) {
           acc = mfma16x16x32(bhi[ks & 1], afr[ks & 1][i], acc);
           acc = mfma16x16x32(blo[ks & 1], afr[ks & 1][i], acc);
@@ -742,32 +756,44 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
           acc = mfma16x16x32(afr[ks & 1][i], blo[ks & 1], acc);
         }
       }
+      if (kHalves && ks == 2 * KPART) {  // part 1 is complete: added first, its set reused by part 3
+#pragma unroll
+        for (int i = 0; i < 2 * NQT; ++i) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) yacc[i][r] += yacc2[0][i][r];
+          yacc2[0][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
       if (ks + 1 < KSL) {
         if (lcm) mfma_drain(Sraw[ks + 1][0], Sraw[ks + 1][1]);
         prep(ks + 1);
       }
     }
     mfma_drain_all(yacc);
-    if constexpr (kHalves) {
-      mfma_drain_all(yacc2);
+    if constexpr (kHalves) {  // parts 2 and 3, in order
+      mfma_drain_all(yacc2[0]);
+      mfma_drain_all(yacc2[1]);
 #pragma unroll
       for (int i = 0; i < 2 * NQT; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yacc[i][r] += yacc2[i][r];
+        for (int r = 0; r < 4; ++r) yacc[i][r] = (yacc[i][r] + yacc2[1][i][r]) + yacc2[0][i][r];
     }
-    if constexpr (KSPLIT) {  // uniform: the second wave's half of the sums goes to the first
-      if (kbase != 0) {
+    if constexpr (KSPLIT) {  // uniform: the other waves' parts of the sums go to the first, in order
+      const int part = kbase / KSL;
+      if (part != 0) {
 #pragma unroll
-        for (int i = 0; i < 2 * NQT; ++i) sm.yx[i][lane] = yacc[i];
+        for (int i = 0; i < 2 * NQT; ++i) sm.yx[part - 1][i][lane] = yacc[i];
         ws_arrive(&sm.ysync);
       } else {
-        ws_wait(&sm.ysync, 1);
+        ws_wait(&sm.ysync, NSW - 1);
 #pragma unroll
-        for (int i = 0; i < 2 * NQT; ++i) {
-          const f32x4 x = sm.yx[i][lane];
+        for (int p = 0; p < NSW - 1; ++p)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) yacc[i][r] += x[r];
-        }
+          for (int i = 0; i < 2 * NQT; ++i) {
+            const f32x4 x = sm.yx[p][i][lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[i][r] += x[r];
+          }
       }
     }
     // R = diag(beta) (V - diag(e^G) K S0^T): lane (row srow, lg) holds nodes

@@ -109,8 +109,8 @@ def _prev_record(prev: W.Draft):
 
 
 @pytest.mark.parametrize("dtype,B,Np,N,H,dk,dv,prev_topo,new_topo", [
-    ("bf16", 1, 32, 32, 8, 256, 256, "window", "window"),      # BV = 8 tiles
-    ("bf16", 8, 64, 64, 8, 256, 256, "branching", "branching"),  # BV = 64 tiles
+    ("bf16", 1, 32, 32, 8, 256, 256, "window", "window"),      # 16-row tiles
+    ("bf16", 8, 64, 64, 8, 256, 256, "branching", "branching"),  # 64-row tiles
     ("bf16", 2, 40, 12, 3, 64, 40, "chain", "random"),         # 40-node path: 3 chunks
     ("f32", 2, 9, 17, 2, 40, 24, "random", "window"),
     ("bf16", 1, 5, 1, 1, 16, 8, "binary", "chain"),
@@ -124,6 +124,11 @@ def _prev_record(prev: W.Draft):
     # 32-row tiles: full, and ragged with a 40-node accepted path
     ("bf16", 4, 40, 40, 8, 256, 256, "branching", "branching"),
     ("bf16", 6, 40, 29, 8, 96, 168, "chain", "random"),
+    # 16-row tiles (four state waves, a quarter of the columns each): ragged
+    # dk (the last two quarters all padding) and dv (a half last tile), and a
+    # 40-node accepted path (commit from global memory)
+    ("bf16", 1, 24, 20, 16, 96, 120, "random", "branching"),
+    ("bf16", 2, 40, 12, 8, 256, 256, "chain", "random"),
 ])
 def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo,
                                                    new_topo):

@@ -148,6 +148,10 @@ SHAPES = [
     # full and ragged (a partial last tile, dk and N off the 16 grid)
     (4, 40, 8, 256, 256, "bf16", "branching"),
     (6, 29, 8, 96, 168, "bf16", "random"),
+    # 16-row state tiles (the column parts summed apart): ragged dk and dv, and
+    # a 40-node chain (the blocked solve)
+    (1, 20, 16, 96, 120, "bf16", "branching"),
+    (2, 40, 8, 256, 256, "bf16", "chain"),
 ]
 
 
