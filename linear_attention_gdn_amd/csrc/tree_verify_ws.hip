@@ -587,17 +587,18 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
     }
     // 2-3. Gram blocks Q K^T and K K^T, lower-triangle tiles: wave w takes
     // row block pair w / 2 of Q (w even) or of K (w odd), as in
-    // tree_verify.hip; each tile is masked, decayed and scaled in registers
+    // tree_verify.hip (with two row blocks, one row block per wave, so all
+    // four waves take part); each tile is masked, decayed and scaled in registers
     // into A (FP32) or Attn (split bf16), so no N x N pass follows.  Only the
     // lower-triangle blocks are ever read.
     auto gram_job = [&](auto wc) {
       constexpr int Wc = decltype(wc)::value;
-      constexpr int npairs = (NQT + 1) / 2;
+      constexpr int npairs = NQT > 2 ? (NQT + 1) / 2 : NQT;
       if constexpr (Wc < 2 * npairs) {
         constexpr bool isq = Wc % 2 == 0;
         constexpr int ra = NQT - 1 - Wc / 2;
         constexpr int rs = Wc / 2;
-        constexpr bool two = rs < ra;
+        constexpr bool two = NQT > 2 && rs < ra;
         const bf16_t* rows = QKs + (isq ? 0 : Np) * kQKStride;
         bf16x8 fa[KS], fs[two ? KS : 1], kb[2][KS];
         // per-row values of this lane's four rows 4 lg + r of each row block
