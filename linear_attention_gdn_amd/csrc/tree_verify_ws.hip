@@ -16,10 +16,10 @@
 //     the masked and scaled A and Attn, and T = (I + A)^{-1} (per-node path
 //     solves; blocked forward substitution for paths deeper than 16);
 //   state waves (4 .. 3 + SW): wave 4 + c owns state rows 16 c .. 16 c + 15
-//     of the tile (16-row tiles of the delayed form instead have four,
-//     waves 4-7, each with a quarter of the rows' columns, the other three
-//     handing their contraction sums to the first, which alone runs the
-//     epilogue).  They request their state rows and V at once (straight
+//     of the tile (16- and 32-row tiles of the delayed form instead have
+//     four, waves 4-7, 4 / SW per 16-row group, each with one part of the
+//     group's columns, the others handing their contraction sums to the
+//     group's first, which alone runs the epilogue).  They request their state rows and V at once (straight
 //     into MFMA operand registers); for the delayed form each finds the
 //     previous draft's accepted path itself and requests the path's k rows
 //     (staged in LDS together) and u' of its rows, and the path is applied to
@@ -54,12 +54,12 @@ constexpr int kSplitLoS = kMaxNodes * kLdS;
 // of four path nodes' rows (one per lane group) start on different banks.
 constexpr int kCkStride = kMaxDim + 32;
 
-// State waves per tile: one per 16 rows, except for 16-row tiles with a
-// delayed commit, whose 16 rows are shared by four waves that split the
-// state's columns (the commit and the contraction then run on all four, one
-// per SIMD).
+// State waves per tile: one per 16 rows, except with a delayed commit, where
+// 16- and 32-row tiles also have four, one per SIMD: each 16-row group's rows
+// are shared by 4 / SW waves that split the state's columns (the commit and
+// the contraction then run on all four).
 template <int SW, bool DLY>
-constexpr int ws_state_waves() { return SW == 1 && DLY ? 4 : SW; }
+constexpr int ws_state_waves() { return DLY && SW < 4 ? 4 : SW; }
 
 template <bool DLY, int SW>
 struct WsLds {
@@ -73,15 +73,15 @@ struct WsLds {
   int bad;
   int sync;   // arrivals at the head waves' own barriers
   int csync;  // arrivals of the state waves at the staged k rows
-  int ysync;  // 16-row tiles: arrivals of the other state waves' partial contractions in yx
+  int ysync[4];  // per 16-row group: arrivals of the other parts' contractions in yx
   // delayed commit: per state wave the accepted path (root first) and its
   // coefficients; the k rows of the path's first kWsChunk nodes (zero rows
   // past the path), staged by the state waves together
   int dnode[DLY ? NSW : 1][kMaxNodes];
   float dc[DLY ? NSW : 1][kMaxNodes];
   alignas(16) bf16_t ck[DLY ? kWsChunk * kCkStride : 8];
-  // 16-row tiles: the other state waves' contraction accumulators [wave - 5][i][lane]
-  alignas(16) f32x4 yx[NSW > SW ? NSW - 1 : 1][NSW > SW ? 2 * (kMaxNodes / 16) : 1][64];
+  // split tiles: the other parts' contraction accumulators [group][part - 1][i][lane]
+  alignas(16) f32x4 yx[NSW > SW ? SW : 1][NSW > SW ? NSW / SW - 1 : 1][NSW > SW ? 2 * (kMaxNodes / 16) : 1][64];
 };
 
 // The head waves synchronise among themselves through an LDS counter, so the
@@ -123,19 +123,19 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
   constexpr int BV = 16 * SW;  // state rows per tile: 16 per state wave
   constexpr int Np = 16 * NQT;
   constexpr int KS = kMaxDim / 32;          // 32-wide k steps of the contraction
-  // 16-row tiles with a delayed commit: four state waves on the same rows,
-  // each holding, committing and contracting a quarter of the state's columns
-  // (k steps kbase .. + KSL - 1); otherwise one state wave per 16 rows with
-  // every column
+  // 16- and 32-row tiles with a delayed commit: 4 / SW state waves on the
+  // same 16 rows, each holding, committing and contracting one part of the
+  // state's columns (k steps kbase .. + KSL - 1); otherwise one state wave
+  // per 16 rows with every column
   constexpr int NSW = ws_state_waves<SW, DLY>();
   constexpr bool KSPLIT = NSW > SW;
-  // 16-row tiles without the delayed commit: the one state wave sums the four
-  // column quarters apart (parts 1-3 in two accumulator sets in turn) and
-  // adds them in part order, the split form's order, so that the delayed form
-  // with no path to apply is bitwise this one
-  constexpr int kParts = SW == 1 ? 4 : 1;  // column parts of a 16-row tile
-  constexpr int KPART = KS / kParts;      // k steps per part
-  constexpr bool kHalves = SW == 1 && !KSPLIT;
+  // Without the delayed commit the one state wave of a 16-row group sums the
+  // same column parts apart (parts 1-3 in two accumulator sets in turn) and
+  // adds them in part order, the split form's order, so that the delayed
+  // form with no path to apply is bitwise this one
+  constexpr int kParts = SW < 4 ? 4 / SW : 1;  // column parts per 16-row group
+  constexpr int KPART = KS / kParts;          // k steps per part
+  constexpr bool kHalves = kParts > 1 && !KSPLIT;
   constexpr int KSL = KSPLIT ? KPART : KS;
 
   __shared__ WsLds<DLY, SW> sm;
@@ -160,14 +160,14 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
   const int r0 = tile * BV;
   // state waves: rows 16 cj .. 16 cj + 15 of the tile; lane l16's row (as an
   // MFMA operand) and the four rows 16 cj + 4 lg .. + 3 (as a transposed result)
-  const int cj = (wave >= 4 && !KSPLIT) ? wave - 4 : 0;
-  const int kbase = (wave >= 4 && KSPLIT) ? KSL * (wave - 4) : 0;  // first k step of this wave
+  const int cj = wave >= 4 ? (KSPLIT ? (wave - 4) / kParts : wave - 4) : 0;
+  const int kbase = (wave >= 4 && KSPLIT) ? KSL * ((wave - 4) % kParts) : 0;  // first k step of this wave
   const int srow = r0 + 16 * cj + l16;
   const bool sok = srow < dv;
   const int srow4 = r0 + 16 * cj + 4 * lg;
   const bool sok4 = srow4 < dv;  // dv % 4 == 0: all four rows or none
 
-  if (tid == 0) sm.sync = 0, sm.csync = 0, sm.ysync = 0;
+  if (tid == 0) sm.sync = 0, sm.csync = 0, sm.ysync[0] = sm.ysync[1] = sm.ysync[2] = sm.ysync[3] = 0;
   __syncthreads();  // the counter is zero before any wave arrives
   // the head waves carry the chain of dependent per-head steps: their
   // instructions go first when both roles compete for a SIMD or the memory
@@ -771,27 +771,33 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
       }
     }
     mfma_drain_all(yacc);
-    if constexpr (kHalves) {  // parts 2 and 3, in order
+    if constexpr (kHalves && kParts == 4) {  // parts 2 and 3, in order
       mfma_drain_all(yacc2[0]);
       mfma_drain_all(yacc2[1]);
 #pragma unroll
       for (int i = 0; i < 2 * NQT; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) yacc[i][r] = (yacc[i][r] + yacc2[1][i][r]) + yacc2[0][i][r];
+    } else if constexpr (kHalves) {  // part 1
+      mfma_drain_all(yacc2[0]);
+#pragma unroll
+      for (int i = 0; i < 2 * NQT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[i][r] += yacc2[0][i][r];
     }
     if constexpr (KSPLIT) {  // uniform: the other waves' parts of the sums go to the first, in order
       const int part = kbase / KSL;
       if (part != 0) {
 #pragma unroll
-        for (int i = 0; i < 2 * NQT; ++i) sm.yx[part - 1][i][lane] = yacc[i];
-        ws_arrive(&sm.ysync);
+        for (int i = 0; i < 2 * NQT; ++i) sm.yx[cj][part - 1][i][lane] = yacc[i];
+        ws_arrive(&sm.ysync[cj]);
       } else {
-        ws_wait(&sm.ysync, NSW - 1);
+        ws_wait(&sm.ysync[cj], kParts - 1);
 #pragma unroll
-        for (int p = 0; p < NSW - 1; ++p)
+        for (int p = 0; p < kParts - 1; ++p)
 #pragma unroll
           for (int i = 0; i < 2 * NQT; ++i) {
-            const f32x4 x = sm.yx[p][i][lane];
+            const f32x4 x = sm.yx[cj][p][i][lane];
 #pragma unroll
             for (int r = 0; r < 4; ++r) yacc[i][r] += x[r];
           }
