@@ -642,6 +642,23 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
           for (int ks = 0; ks < KS; ++ks)
             dstf[ks] = lds_bf16x8(QKs + (Np + 16 * ct + l16) * kQKStride + 32 * ks + koff);
         };
+        if constexpr (!two && ra <= 1) {
+          // one row block of at most two tiles: both column tiles at once,
+          // two independent product chains that hide each other's latency
+          constexpr bool pair = ra == 1;
+          kload(0, kb[0]);
+          if constexpr (pair) kload(1, kb[1]);
+          f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            acc0 = mfma16x16x32(fa[ks], kb[0][ks], acc0);
+            if constexpr (pair) acc1 = mfma16x16x32(fa[ks], kb[1][ks], acc1);
+          }
+          mfma_drain(acc0, acc1);
+          put(ra, 0, acc0, mra, gra, bra);
+          if constexpr (pair) put(ra, 1, acc1, mra, gra, bra);
+          return;
+        }
         kload(0, kb[0]);
 #pragma unroll
         for (int ct = 0; ct <= ra; ++ct) {
