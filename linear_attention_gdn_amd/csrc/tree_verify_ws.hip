@@ -130,9 +130,9 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
   constexpr int NSW = ws_state_waves<SW, DLY>();
   constexpr bool KSPLIT = NSW > SW;
   // Without the delayed commit the one state wave of a 16-row group sums the
-  // same column parts apart (parts 1-3 in two accumulator sets in turn) and
-  // adds them in part order, the split form's order, so that the delayed
-  // form with no path to apply is bitwise this one
+  // same column parts apart (the parts after the first in two accumulator
+  // sets used in turn) and adds them in part order, the split form's order,
+  // so that the delayed form with no path to apply is bitwise this one
   constexpr int kParts = SW < 4 ? 4 / SW : 1;  // column parts per 16-row group
   constexpr int KPART = KS / kParts;          // k steps per part
   constexpr bool kHalves = kParts > 1 && !KSPLIT;
@@ -713,7 +713,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
 
   // state waves: contraction (with the committed rows written back), R
   f32x4 yacc[2 * NQT];
-  f32x4 yacc2[2][kHalves ? 2 * NQT : 1];  // 16-row tiles: the sums over parts 1-3 (two sets in turn)
+  f32x4 yacc2[2][kHalves ? 2 * NQT : 1];  // 16- and 32-row tiles: the sums over the later parts
   f32x4 rv[NQT];
   f32x4 gsl[GATE ? NQT : 1];  // gated form: SiLU(gate) of node 16 i + l16, rows srow4 .. + 3
   if (!head) {
@@ -875,7 +875,7 @@ __global__ __launch_bounds__((256 + 64 * ws_state_waves<SW, DLY>())) void tree_w
     }
   }
   __syncthreads();  // T and Attn are complete; the only barrier of both roles after the start
-  if (head || kbase != 0) return;  // (16-row tiles: the first state wave finishes the tile)
+  if (head || kbase != 0) return;  // (split tiles: each group's first state wave finishes it)
 
   // ---- 5. epilogue (state waves): U' = T R, its transpose for the record,
   // O^T = (Attn U')^T + scale e^G (S0 Q^T); T and Attn are lower triangular,
