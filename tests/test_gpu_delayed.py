@@ -129,6 +129,9 @@ def _prev_record(prev: W.Draft):
     # 40-node accepted path (commit from global memory)
     ("bf16", 1, 24, 20, 16, 96, 120, "random", "branching"),
     ("bf16", 2, 40, 12, 8, 256, 256, "chain", "random"),
+    # 32-row tiles, deep drafts on both sides (a 48-node accepted path, the
+    # blocked solve)
+    ("bf16", 4, 48, 48, 8, 256, 256, "spine", "spine"),
 ])
 def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, prev_topo,
                                                    new_topo):
@@ -137,12 +140,14 @@ def test_delayed_tree_verify_is_commit_then_verify(dtype, B, Np, N, H, dk, dv, p
 
 # The split-role kernel's rejected-draft path with a pending commit: 64-row
 # tiles (commit applied from global memory there) with short and long
-# previous paths, and 16-row tiles (commit applied before the first wait on
-# the head waves).  The last sequence's new draft is not topological.
+# previous paths, and 16- and 32-row tiles (commit applied before the first
+# wait on the head waves, split over four state waves).  The last sequence's
+# new draft is not topological.
 @pytest.mark.parametrize("B,Np,N,H,prev_topo", [
     (8, 64, 64, 8, "branching"),
     (8, 64, 64, 8, "spine"),
     (1, 32, 32, 8, "window"),
+    (4, 40, 40, 8, "spine"),
 ])
 def test_delayed_tree_verify_rejected_draft_is_commit_then_verify(B, Np, N, H, prev_topo):
     _fused_equals_separate("bf16", B, Np, N, H, 256, 256, prev_topo, "branching", reject=True)
